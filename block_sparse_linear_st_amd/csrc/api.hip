@@ -1,0 +1,344 @@
+// api.hip - the extern "C" entry points of libsalad (declared in include/salad.h):
+// argument validation, workspace planning and the launch sequence of each call.
+#include <algorithm>
+#include <cmath>
+
+#include "internal.h"
+
+namespace salad {
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int shape_status(const salad_shape* s) {
+  if (s == nullptr) return SALAD_EINVAL;
+  if (s->batch < 1 || s->heads < 1 || s->T < 1 || s->H < 1 || s->W < 1 || s->block < 1 ||
+      s->head_dim < 1)
+    return SALAD_EINVAL;
+  if (s->dtype != SALAD_F32 && s->dtype != SALAD_BF16) return SALAD_EINVAL;
+  if (s->head_dim != 64 && s->head_dim != 128) return SALAD_EUNSUPPORTED;
+  if (s->block != 64 && s->block != 128) return SALAD_EUNSUPPORTED;
+  if (s->heads > SALAD_MAX_HEADS) return SALAD_EUNSUPPORTED;
+  const int64_t N = (int64_t)s->T * s->H * s->W;
+  if (N > INT32_MAX / 2) return SALAD_EUNSUPPORTED;
+  const int64_t nb = (N + s->block - 1) / s->block;
+  if ((int64_t)s->n_pad != nb * s->block) return SALAD_EINVAL;
+  if (nb > 46340) return SALAD_EUNSUPPORTED;  // nb*nb must fit int32
+  if ((int64_t)s->batch * s->heads * nb + 1 > INT32_MAX) return SALAD_EUNSUPPORTED;
+  return SALAD_OK;
+}
+
+int spec_status(const salad_shape* s, const salad_mask_spec* specs) {
+  if (specs == nullptr) return SALAD_EINVAL;
+  const int64_t nb = s->n_pad / s->block;
+  for (int h = 0; h < s->heads; ++h) {
+    const salad_mask_spec& sp = specs[h];
+    if (sp.kind == SALAD_MASK_WINDOW) {
+      if (sp.t_window < 0) return SALAD_EINVAL;
+    } else if (sp.kind == SALAD_MASK_TOPK) {
+      if (nb > 8192) return SALAD_EUNSUPPORTED;
+    } else {
+      return SALAD_EINVAL;
+    }
+    if (!std::isfinite(sp.density)) return SALAD_EINVAL;
+  }
+  return SALAD_OK;
+}
+
+// K for a window head: floor(density * nb * nb + 0.5), -1 = keep every candidate.
+int64_t window_count(float density, int64_t nb) {
+  if (density <= 0.0f) return -1;
+  return (int64_t)std::floor((double)density * (double)nb * (double)nb + 0.5);
+}
+
+int64_t topk_count(float density, int64_t nb) {
+  int64_t k = (int64_t)std::floor((double)density * (double)nb + 0.5);
+  return std::min<int64_t>(std::max<int64_t>(k, 1), nb);
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? SALAD_OK : SALAD_EHIP; }
+
+}  // namespace
+
+bool make_geom(const salad_shape* s, Geom* g) {
+  if (shape_status(s) != SALAD_OK) return false;
+  g->B = s->batch;
+  g->Hh = s->heads;
+  g->D = s->head_dim;
+  g->T = s->T;
+  g->H = s->H;
+  g->W = s->W;
+  g->N = s->T * s->H * s->W;
+  g->n_pad = s->n_pad;
+  g->blk = s->block;
+  g->nb = s->n_pad / s->block;
+  return true;
+}
+
+Workspace plan_workspace(const Geom& g, int dtype) {
+  Workspace L{};
+  const size_t BH = (size_t)g.B * g.Hh, D = g.D, nb = g.nb;
+  // mask build
+  size_t off = 0;
+  L.hist_bins = 1 + (size_t)std::max(g.H, g.W) * nb;
+  L.off_hist = off;   off = align_up(off + (size_t)g.Hh * L.hist_bins * 4);
+  L.off_thr = off;    off = align_up(off + (size_t)g.Hh * 8);
+  L.off_flags = off;  off = align_up(off + (size_t)g.Hh * 4);
+  L.off_rowcnt = off; off = align_up(off + BH * nb * 4);
+  L.off_psum_q = off; off = align_up(off + BH * nb * D * 4);
+  L.off_psum_k = off; off = align_up(off + BH * nb * D * 4);
+  L.mask_end = off;
+  // linear state: about 512 workgroups in all, 64-token granularity
+  int splits = (int)std::max<size_t>(1, (512 + BH - 1) / BH);
+  splits = std::min(splits, (g.N + 63) / 64);
+  int chunk = (g.N + splits - 1) / splits;
+  chunk = (chunk + 63) / 64 * 64;
+  splits = (g.N + chunk - 1) / chunk;
+  L.lin_splits = splits;
+  L.lin_chunk = chunk;
+  off = 0;  // the two phases never overlap in time on one stream
+  L.off_spart = off;  off = align_up(off + (size_t)splits * BH * D * D * 4);
+  L.off_zpart = off;  off = align_up(off + (size_t)splits * BH * D * 4);
+  L.off_z = off;      off = align_up(off + BH * D * 4);
+  const size_t esz = dtype == SALAD_BF16 ? 2 : 4;
+  L.off_sft_hi = off; off = align_up(off + BH * D * D * esz);
+  L.off_sft_lo = off; off = align_up(off + (dtype == SALAD_BF16 ? BH * D * D * 2 : 0));
+  L.lin_end = off;
+  L.bytes = std::max(L.mask_end, L.lin_end);
+  return L;
+}
+
+}  // namespace salad
+
+using namespace salad;
+
+extern "C" {
+
+int salad_version(void) { return SALAD_VERSION; }
+
+const char* salad_status_str(int status) {
+  switch (status) {
+    case SALAD_OK: return "ok";
+    case SALAD_EINVAL: return "invalid argument";
+    case SALAD_EUNSUPPORTED: return "unsupported shape (head_dim/block not 64 or 128, too many heads or blocks)";
+    case SALAD_ENOSPACE: return "workspace or col_idx capacity too small";
+    case SALAD_EINFEASIBLE: return "window density exceeds the candidate block pairs";
+    case SALAD_EHIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int64_t salad_mask_nnz_max(const salad_shape* shape, const salad_mask_spec* specs) {
+  int st = shape_status(shape);
+  if (st != SALAD_OK) return st;
+  st = spec_status(shape, specs);
+  if (st != SALAD_OK) return st;
+  const int64_t nb = shape->n_pad / shape->block;
+  int64_t total = 0;
+  for (int h = 0; h < shape->heads; ++h) {
+    const salad_mask_spec& sp = specs[h];
+    int64_t per;
+    if (sp.kind == SALAD_MASK_WINDOW) {
+      const int64_t K = window_count(sp.density, nb);
+      per = K < 0 ? nb * nb : std::min(K, nb * nb);
+    } else {
+      per = topk_count(sp.density, nb) * nb;
+    }
+    total += per * shape->batch;
+  }
+  return total;
+}
+
+size_t salad_workspace_bytes(const salad_shape* shape) {
+  Geom g;
+  if (!make_geom(shape, &g)) return 0;
+  return plan_workspace(g, shape->dtype).bytes;
+}
+
+int salad_build_mask(const salad_shape* shape, const salad_mask_spec* specs, const void* q,
+                     const void* k, int32_t* row_ptr, int32_t* col_idx, int64_t col_cap,
+                     int32_t* info, const float* w_g, float* gate, void* ws, size_t ws_bytes,
+                     void* stream) {
+  Geom g;
+  int st = shape_status(shape);
+  if (st != SALAD_OK) return st;
+  make_geom(shape, &g);
+  st = spec_status(shape, specs);
+  if (st != SALAD_OK) return st;
+  bool any_topk = false;
+  for (int h = 0; h < g.Hh; ++h) any_topk |= specs[h].kind == SALAD_MASK_TOPK;
+  if ((w_g == nullptr) != (gate == nullptr)) return SALAD_EINVAL;
+  const bool want_gate = gate != nullptr;
+  if (!row_ptr || !col_idx || !ws) return SALAD_EINVAL;
+  if ((any_topk || want_gate) && (!q || !aligned16(q))) return SALAD_EINVAL;
+  if (any_topk && (!k || !aligned16(k))) return SALAD_EINVAL;
+  if (!aligned16(ws)) return SALAD_EINVAL;
+  const Workspace L = plan_workspace(g, shape->dtype);
+  if (ws_bytes < L.bytes) return SALAD_ENOSPACE;
+  const int64_t need = salad_mask_nnz_max(shape, specs);
+  if (need < 0) return (int)need;
+  if (col_cap < need) return SALAD_ENOSPACE;
+  HeadTable ht{};
+  ht.n_heads = g.Hh;
+  for (int h = 0; h < g.Hh; ++h) {
+    ht.kind[h] = specs[h].kind;
+    ht.t_window[h] = specs[h].t_window;
+    ht.r_max[h] = specs[h].r_max;
+    ht.count[h] = (int)(specs[h].kind == SALAD_MASK_WINDOW ? window_count(specs[h].density, g.nb)
+                                                           : topk_count(specs[h].density, g.nb));
+  }
+  return hip_status(launch_build_mask(g, shape->dtype, ht, q, k, row_ptr, col_idx, col_cap, info,
+                                      w_g, gate, static_cast<char*>(ws), L,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+int salad_gate_from_q(const salad_shape* shape, const void* q, const float* w_g, float* gate,
+                      void* ws, size_t ws_bytes, void* stream) {
+  Geom g;
+  const int st = shape_status(shape);
+  if (st != SALAD_OK) return st;
+  make_geom(shape, &g);
+  if (!q || !w_g || !gate || !ws || !aligned16(q) || !aligned16(ws)) return SALAD_EINVAL;
+  const Workspace L = plan_workspace(g, shape->dtype);
+  if (ws_bytes < L.bytes) return SALAD_ENOSPACE;
+  return hip_status(launch_gate_from_q(g, shape->dtype, q, w_g, gate, static_cast<char*>(ws), L,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int salad_linear_state(const salad_shape* shape, const void* k, const void* v, float* S, float* z,
+                       void* ws, size_t ws_bytes, void* stream) {
+  Geom g;
+  const int st = shape_status(shape);
+  if (st != SALAD_OK) return st;
+  make_geom(shape, &g);
+  if (!k || !v || !S || !z || !ws || !aligned16(k) || !aligned16(v) || !aligned16(ws))
+    return SALAD_EINVAL;
+  const Workspace L = plan_workspace(g, shape->dtype);
+  if (ws_bytes < L.bytes) return SALAD_ENOSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  hipError_t e = launch_linear_state(g, shape->dtype, k, v, w, L, s);
+  if (e != hipSuccess) return SALAD_EHIP;
+  return hip_status(launch_linear_fold(g, shape->dtype, nullptr, nullptr, 2, S, z, w, L, s));
+}
+
+namespace {
+
+int attn_common(const salad_shape* shape, const void* q, const void* k, const void* v,
+                const int32_t* row_ptr, const int32_t* col_idx, void* ws, size_t ws_bytes,
+                Geom* g, Workspace* L) {
+  const int st = shape_status(shape);
+  if (st != SALAD_OK) return st;
+  make_geom(shape, g);
+  if (!q || !k || !v || !row_ptr || !col_idx || !ws) return SALAD_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(ws)) return SALAD_EINVAL;
+  *L = plan_workspace(*g, shape->dtype);
+  if (ws_bytes < L->bytes) return SALAD_ENOSPACE;
+  return SALAD_OK;
+}
+
+hipError_t run_attn(const Geom& g, int dtype, const AttnArgs& a, hipStream_t s) {
+  return dtype == SALAD_BF16 ? launch_attn_bf16(g, a, s) : launch_attn_f32(g, a, s);
+}
+
+}  // namespace
+
+int salad_linear_prepare(const salad_shape* shape, const void* k, const void* v,
+                         const float* gate, const void* w_lin, void* ws, size_t ws_bytes,
+                         void* stream) {
+  Geom g;
+  const int st = shape_status(shape);
+  if (st != SALAD_OK) return st;
+  make_geom(shape, &g);
+  if (!k || !v || !gate || !w_lin || !ws || !aligned16(k) || !aligned16(v) || !aligned16(ws))
+    return SALAD_EINVAL;
+  const Workspace L = plan_workspace(g, shape->dtype);
+  if (ws_bytes < L.bytes) return SALAD_ENOSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  hipError_t e = launch_linear_state(g, shape->dtype, k, v, w, L, s);
+  if (e == hipSuccess) e = launch_linear_fold(g, shape->dtype, gate, w_lin, 0, nullptr, nullptr, w, L, s);
+  return hip_status(e);
+}
+
+int salad_attn_apply(const salad_shape* shape, const void* q, const void* k, const void* v,
+                     const int32_t* row_ptr, const int32_t* col_idx, const float* gate, float eps,
+                     float scale, float drop_tau, void* out, void* ws, size_t ws_bytes,
+                     void* stream) {
+  Geom g;
+  Workspace L;
+  int st = attn_common(shape, q, k, v, row_ptr, col_idx, ws, ws_bytes, &g, &L);
+  if (st != SALAD_OK) return st;
+  if (!gate || !out || !aligned16(out) || !(eps >= 0.0f) || !std::isfinite(scale) ||
+      std::isnan(drop_tau))
+    return SALAD_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  AttnArgs a{};
+  a.q = q; a.k = k; a.v = v; a.out = out;
+  a.row_ptr = row_ptr; a.col_idx = col_idx;
+  a.sft_hi = w + L.off_sft_hi; a.sft_lo = w + L.off_sft_lo;
+  a.z = reinterpret_cast<const float*>(w + L.off_z);
+  a.gate = gate; a.drop_tau = drop_tau; a.eps = eps;
+  a.scale = scale > 0.0f ? scale : 1.0f / std::sqrt((float)g.D);
+  a.has_sparse = 1; a.has_lin = 1;
+  return hip_status(run_attn(g, shape->dtype, a, s));
+}
+
+int salad_attn_fwd(const salad_shape* shape, const void* q, const void* k, const void* v,
+                   const int32_t* row_ptr, const int32_t* col_idx, const float* gate,
+                   const void* w_lin, float eps, float scale, float drop_tau, void* out, void* ws,
+                   size_t ws_bytes, void* stream) {
+  Geom g;
+  Workspace L;
+  int st = attn_common(shape, q, k, v, row_ptr, col_idx, ws, ws_bytes, &g, &L);
+  if (st != SALAD_OK) return st;
+  if (!gate || !w_lin || !out || !aligned16(out) || !(eps >= 0.0f) || !std::isfinite(scale) ||
+      std::isnan(drop_tau))
+    return SALAD_EINVAL;
+  st = salad_linear_prepare(shape, k, v, gate, w_lin, ws, ws_bytes, stream);
+  if (st != SALAD_OK) return st;
+  return salad_attn_apply(shape, q, k, v, row_ptr, col_idx, gate, eps, scale, drop_tau, out, ws,
+                          ws_bytes, stream);
+}
+
+int salad_attn_fwd_branches(const salad_shape* shape, const void* q, const void* k, const void* v,
+                            const int32_t* row_ptr, const int32_t* col_idx, float eps, float scale,
+                            void* out_sparse, void* out_lin, void* ws, size_t ws_bytes,
+                            void* stream) {
+  Geom g;
+  Workspace L;
+  int st = attn_common(shape, q, k, v, row_ptr, col_idx, ws, ws_bytes, &g, &L);
+  if (st != SALAD_OK) return st;
+  if ((out_sparse && !aligned16(out_sparse)) || (out_lin && !aligned16(out_lin)) ||
+      !(eps >= 0.0f) || !std::isfinite(scale))
+    return SALAD_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  AttnArgs a{};
+  a.q = q; a.k = k; a.v = v;
+  a.row_ptr = row_ptr; a.col_idx = col_idx;
+  a.sft_hi = w + L.off_sft_hi; a.sft_lo = w + L.off_sft_lo;
+  a.z = reinterpret_cast<const float*>(w + L.off_z);
+  a.gate = nullptr; a.drop_tau = 0.0f; a.eps = eps;
+  a.scale = scale > 0.0f ? scale : 1.0f / std::sqrt((float)g.D);
+  if (out_sparse) {
+    a.out = out_sparse; a.has_sparse = 1; a.has_lin = 0;
+    if (run_attn(g, shape->dtype, a, s) != hipSuccess) return SALAD_EHIP;
+  }
+  if (out_lin) {
+    hipError_t e = launch_linear_state(g, shape->dtype, k, v, w, L, s);
+    if (e == hipSuccess) e = launch_linear_fold(g, shape->dtype, nullptr, nullptr, 1, nullptr, nullptr, w, L, s);
+    if (e != hipSuccess) return SALAD_EHIP;
+    a.out = out_lin; a.has_sparse = 0; a.has_lin = 1;
+    if (run_attn(g, shape->dtype, a, s) != hipSuccess) return SALAD_EHIP;
+  }
+  return SALAD_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,100 @@
+// Internal declarations shared by the HIP translation units of libsalad.
+// Nothing here is part of the public interface (include/salad.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "salad.h"
+
+#define SALAD_HIDDEN __attribute__((visibility("hidden")))
+
+namespace salad {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kRstarInf = 1 << 30;
+
+// Geometry of the latent grid and its blocking, as kernels see it.
+struct Geom {
+  int B, Hh, D;     // batch, heads, head_dim
+  int T, H, W;      // latent grid
+  int N, n_pad, blk, nb;
+};
+
+// Per-head mask parameters, passed by value in kernel arguments.
+struct HeadTable {
+  int n_heads;
+  int kind[SALAD_MAX_HEADS];       // salad_mask_kind
+  int t_window[SALAD_MAX_HEADS];
+  int r_max[SALAD_MAX_HEADS];
+  int count[SALAD_MAX_HEADS];      // window: K pairs (-1 = keep all); top-k: k per row
+  int pool[SALAD_MAX_HEADS];       // pool Q (bit 0) / K (bit 1) for this head
+};
+
+// Workspace layout for one shape, computed on the host.
+struct Workspace {
+  size_t bytes;
+  // mask build
+  size_t off_hist, hist_bins;      // int32 [heads][hist_bins]
+  size_t off_thr;                  // int64 [heads] threshold keys
+  size_t off_flags;                // int32 [heads] infeasible flags
+  size_t off_rowcnt;               // int32 [B*H*nb]
+  size_t off_psum_q, off_psum_k;   // float [B*H*nb*D]
+  // linear state
+  int lin_splits, lin_chunk;
+  size_t off_spart, off_zpart;     // float [splits][B*H][D*D], [splits][B*H][D]
+  size_t off_z;                    // float [B*H][D]
+  size_t off_sft_hi, off_sft_lo;   // folded state, transposed: bf16 or f32 [B*H][D*D]
+  size_t mask_end, lin_end;
+};
+
+SALAD_HIDDEN bool make_geom(const salad_shape* s, Geom* g);
+SALAD_HIDDEN Workspace plan_workspace(const Geom& g, int dtype);
+
+// ---- mask builder (mask.hip) ------------------------------------------------
+SALAD_HIDDEN hipError_t launch_build_mask(const Geom& g, int dtype, const HeadTable& ht,
+                                          const void* q, const void* k, int32_t* row_ptr,
+                                          int32_t* col_idx, int64_t col_cap, int32_t* info,
+                                          const float* w_g, float* gate, char* ws,
+                                          const Workspace& L, hipStream_t st);
+SALAD_HIDDEN hipError_t launch_gate_from_q(const Geom& g, int dtype, const void* q,
+                                           const float* w_g, float* gate, char* ws,
+                                           const Workspace& L, hipStream_t st);
+
+// ---- linear state (linear.hip) ----------------------------------------------
+SALAD_HIDDEN hipError_t launch_linear_state(const Geom& g, int dtype, const void* k,
+                                            const void* v, char* ws, const Workspace& L,
+                                            hipStream_t st);
+// Reduce the split partials and fold.  mode 0: folded state g*S*W_lin (fused
+// forward); 1: S itself (linear branch alone); 2: reduce only.  S_out / z_out
+// (may be null) receive the fp32 state; z always lands in the workspace.
+SALAD_HIDDEN hipError_t launch_linear_fold(const Geom& g, int dtype, const float* gate,
+                                           const void* w_lin, int mode, float* S_out,
+                                           float* z_out, char* ws, const Workspace& L,
+                                           hipStream_t st);
+
+// ---- attention (attn_bf16.hip, attn_f32.hip) --------------------------------
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  const void* sft_hi;   // folded linear state, transposed [BH][D][D] (bf16 hi or f32)
+  const void* sft_lo;   // bf16 lo part (bf16 path only)
+  const float* z;       // [BH][D]
+  const float* gate;    // [BH] (branch dropping), may be null
+  float drop_tau;
+  float eps;
+  float scale;
+  int has_sparse;
+  int has_lin;
+};
+SALAD_HIDDEN hipError_t launch_attn_bf16(const Geom& g, const AttnArgs& a, hipStream_t st);
+SALAD_HIDDEN hipError_t launch_attn_f32(const Geom& g, const AttnArgs& a, hipStream_t st);
+
+}  // namespace salad

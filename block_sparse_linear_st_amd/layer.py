@@ -1,0 +1,61 @@
+"""Convenience wrapper that owns the device buffers of one hybrid-attention layer.
+
+Buffer ownership and argument marshalling only; every computation is a call
+into libsalad through ``block_sparse_linear_st_amd.salad``.
+"""
+
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+import torch
+
+from . import salad as S
+
+_TORCH_DTYPE = {S.SALAD_F32: torch.float32, S.SALAD_BF16: torch.bfloat16}
+
+
+class SaladLayer:
+    """One layer shape plus per-head mask specs, with workspace and CSR buffers."""
+
+    def __init__(self, batch: int, heads: int, head_dim: int, T: int, H: int, W: int, block: int,
+                 dtype: int, specs: Sequence, device: str = "cuda"):
+        self.shape = S.make_shape(batch, heads, head_dim, T, H, W, block, dtype)
+        self.specs = S.make_specs(specs)
+        self.device = torch.device(device)
+        self.torch_dtype = _TORCH_DTYPE[dtype]
+        self.N = T * H * W
+        self.nb = self.shape.n_pad // block
+        ws_bytes = S.salad_workspace_bytes(self.shape)
+        if ws_bytes == 0:
+            raise S.SaladError(S.SALAD_EINVAL, "invalid or unsupported layer shape")
+        self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=self.device)
+        self.row_ptr = torch.empty(batch * heads * self.nb + 1, dtype=torch.int32, device=self.device)
+        self.col_idx = torch.empty(max(1, S.salad_mask_nnz_max(self.shape, self.specs)), dtype=torch.int32,
+                                   device=self.device)
+        self.info = torch.zeros(1, dtype=torch.int32, device=self.device)
+
+    def tensor_shape(self):
+        s = self.shape
+        return (s.batch, s.heads, s.n_pad, s.head_dim)
+
+    def build_mask(self, q: Optional[torch.Tensor] = None, k: Optional[torch.Tensor] = None,
+                   w_g: Optional[torch.Tensor] = None, gate: Optional[torch.Tensor] = None, stream=None):
+        S.salad_build_mask(self.shape, self.specs, q, k, self.row_ptr, self.col_idx, self.info, w_g, gate,
+                           self.ws, stream)
+
+    def gate_from_q(self, q, w_g, gate, stream=None):
+        S.salad_gate_from_q(self.shape, q, w_g, gate, self.ws, stream)
+
+    def linear_state(self, k, v, S_out, z_out, stream=None):
+        S.salad_linear_state(self.shape, k, v, S_out, z_out, self.ws, stream)
+
+    def forward(self, q, k, v, gate, w_lin, out, eps: float = 1e-6, scale: float = 0.0,
+                drop_tau: float = 0.0, stream=None):
+        S.salad_attn_fwd(self.shape, q, k, v, self.row_ptr, self.col_idx, gate, w_lin, eps, scale, drop_tau,
+                         out, self.ws, stream)
+        return out
+
+    def branches(self, q, k, v, out_sparse, out_lin, eps: float = 1e-6, scale: float = 0.0, stream=None):
+        S.salad_attn_fwd_branches(self.shape, q, k, v, self.row_ptr, self.col_idx, eps, scale, out_sparse,
+                                  out_lin, self.ws, stream)

@@ -1,0 +1,210 @@
+/*
+ * salad.h - C interface of the hybrid block-sparse + ReLU-linear attention
+ * operator for AMD Instinct MI355X (gfx950).
+ *
+ * The operator (SALAD, "High-Sparsity Attention paralleling with Linear
+ * Attention for Diffusion Transformer"): a sparse softmax-attention branch over
+ * the key blocks a block mask keeps, and beside it a ReLU linear-attention
+ * branch over all tokens that shares Q, K and V; the linear output passes a
+ * projection and a scalar gate in (0,1) and is added to the sparse output.
+ * Sources: the "SALAD" explainer on gist.science, technical summary sections
+ * 2.1 (two parallel branches, shared Q/K/V, ReLU linear attention), 2.2
+ * (zero-initialised projection, sigmoid-bounded scale s), 2.3 (dropping
+ * low-scale branches at inference) and 5 (sliding-window and Top-K masks); the
+ * sciencestack "SALAD" page, TL;DR and abstract (90% sparsity, input-dependent
+ * scalar gate) and Figure 1 (spatio-temporal sliding window, ST-SWA).
+ *
+ * Conventions shared by every entry point:
+ *  - Tensors q, k, v, out are [batch, heads, n_pad, head_dim], contiguous,
+ *    head_dim innermost, in the shape's dtype (fp32 or bf16).  Token n of the
+ *    latent grid (T, H, W) is frame-major: t = n / (H*W), y = (n / W) % H,
+ *    x = n % W.  Tokens N = T*H*W .. n_pad-1 are padding: their contents are
+ *    never read into a result (any bit pattern is allowed) and output rows
+ *    there are written as 0.
+ *  - A block mask is CSR over rows r = (b*heads + h)*nb + qb, nb = n_pad/block:
+ *    row_ptr int32 [batch*heads*nb + 1], col_idx int32, key blocks ascending
+ *    within a row.
+ *  - Every pointer argument except the shape and spec structs is DEVICE memory
+ *    owned by the caller; the library allocates nothing, keeps no pointer after
+ *    it returns, and holds no global mutable state (thread-safe).
+ *  - `stream` is a hipStream_t (NULL = the null stream).  All device work is
+ *    enqueued on it; no call synchronises.  Calls sharing one workspace must be
+ *    ordered on one stream.
+ *  - Arguments are validated before any launch; on error nothing is enqueued
+ *    and a negative salad_status is returned.  A failed launch returns
+ *    SALAD_EHIP.  The library never prints or aborts.
+ *  - Device pointers must be 16-byte aligned.
+ */
+#ifndef SALAD_H
+#define SALAD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SALAD_VERSION 100 /* 1.0.0 */
+
+#if defined(__GNUC__)
+#define SALAD_API __attribute__((visibility("default")))
+#else
+#define SALAD_API
+#endif
+#define SALAD_MAX_HEADS 128
+
+typedef enum {
+  SALAD_OK = 0,
+  SALAD_EINVAL = -1,        /* bad argument (null pointer, inconsistent shape) */
+  SALAD_EUNSUPPORTED = -2,  /* valid but not built: head_dim not 64/128, block not 64/128, heads > 128 */
+  SALAD_ENOSPACE = -3,      /* workspace or col_idx capacity too small */
+  SALAD_EINFEASIBLE = -4,   /* (reported through `info`, see salad_build_mask) */
+  SALAD_EHIP = -5           /* a HIP launch failed */
+} salad_status;
+
+typedef enum { SALAD_F32 = 0, SALAD_BF16 = 1 } salad_dtype;
+
+typedef enum { SALAD_MASK_WINDOW = 0, SALAD_MASK_TOPK = 1 } salad_mask_kind;
+
+/* Layer shape.  Requirements: batch, heads >= 1; heads <= SALAD_MAX_HEADS;
+ * head_dim in {64, 128}; T, H, W >= 1; block in {64, 128};
+ * n_pad == ceil(T*H*W / block) * block (so every block holds a valid token). */
+typedef struct {
+  int32_t batch, heads, head_dim;
+  int32_t T, H, W;
+  int32_t n_pad, block;
+  int32_t dtype; /* salad_dtype */
+} salad_shape;
+
+/* Mask request for one head (host struct, one per head).
+ *
+ * SALAD_MASK_WINDOW - static spatio-temporal sliding window ("SALAD" explainer,
+ *   section 5; sciencestack Figure 1, ST-SWA).  r*(qb, kb) is the least
+ *   Chebyshev spatial distance max(|dy|, |dx|) over token pairs of the two
+ *   blocks at most t_window frames apart (infinite if none).  Candidates have
+ *   finite r* and, when r_max >= 0, r* <= r_max.  density <= 0 keeps every
+ *   candidate; otherwise candidates are ranked by (qb != kb, r*, |qb - kb|, qb,
+ *   kb) and the first K = floor(density * nb * nb + 0.5) are kept (the diagonal
+ *   ranks first).  Identical for every batch index.
+ * SALAD_MASK_TOPK - dynamic Top-K over pooled block scores ("SALAD" explainer,
+ *   section 5).  pq, pk = float32 block means of Q and K over valid tokens
+ *   (sequential float32 sum in token order, then one division); score(qb, kb) =
+ *   sequential float32 sum over channels of separately rounded products
+ *   pq[c]*pk[c]; each query block keeps the k = max(1, floor(density*nb + 0.5))
+ *   highest (capped at nb), ties to the lower kb.  t_window, r_max unused. */
+typedef struct {
+  int32_t kind;     /* salad_mask_kind */
+  int32_t t_window; /* window: +- frames */
+  int32_t r_max;    /* window: spatial cap, -1 = none */
+  float density;    /* fraction of block pairs kept */
+} salad_mask_spec;
+
+/* Version number (SALAD_VERSION of the built library). */
+SALAD_API int salad_version(void);
+
+/* Static description of a status code; never NULL. */
+SALAD_API const char* salad_status_str(int status);
+
+/* Upper bound on the number of col_idx entries salad_build_mask writes for this
+ * shape and these specs (exact unless a window head has density <= 0, where the
+ * bound is nb*nb per (b, h)).  Pure host function.  Negative salad_status on
+ * invalid arguments. */
+SALAD_API int64_t salad_mask_nnz_max(const salad_shape* shape, const salad_mask_spec* specs);
+
+/* Device workspace, in bytes, that salad_build_mask, salad_gate_from_q,
+ * salad_linear_state, salad_attn_fwd and salad_attn_fwd_branches need for this
+ * shape (one buffer serves all of them).  Pure host function; 0 on invalid
+ * shape. */
+SALAD_API size_t salad_workspace_bytes(const salad_shape* shape);
+
+/* Build the CSR block mask for every (b, h) from the per-head specs.
+ *   specs    host array [heads]
+ *   q, k     device tensors; q is read when some head is SALAD_MASK_TOPK or a
+ *            gate is requested, k when some head is SALAD_MASK_TOPK (either may
+ *            be NULL when not read)
+ *   row_ptr  device int32 [batch*heads*nb + 1], written
+ *   col_idx  device int32 [col_cap], written in [0, row_ptr[last])
+ *   col_cap  must be >= salad_mask_nnz_max(shape, specs), else SALAD_ENOSPACE
+ *   info     device int32 [1] or NULL: receives the number of window heads that
+ *            asked for more pairs than they have candidates (those heads keep
+ *            all their candidates); 0 means every request was met
+ *   w_g, gate  optional (both NULL, or both device pointers): also compute
+ *            the gate of salad_gate_from_q from the same pass over Q that pools
+ *            the query blocks, saving a second read of Q
+ *   ws       device workspace of ws_bytes >= salad_workspace_bytes(shape)
+ * The static window part depends only on the shape and specs and may be cached
+ * by the caller. */
+SALAD_API int salad_build_mask(const salad_shape* shape, const salad_mask_spec* specs,
+                     const void* q, const void* k,
+                     int32_t* row_ptr, int32_t* col_idx, int64_t col_cap,
+                     int32_t* info, const float* w_g, float* gate,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Gate from Q: gate[b*heads + h] = sigmoid(mean over the N valid tokens of
+ * q[b, h, n, :] . w_g), the stand-in used here for the input-aware scale s of
+ * the "SALAD" explainer, section 2.2.  w_g: device float [head_dim];
+ * gate: device float [batch*heads]. */
+SALAD_API int salad_gate_from_q(const salad_shape* shape, const void* q, const float* w_g,
+                      float* gate, void* ws, size_t ws_bytes, void* stream);
+
+/* Linear-attention state ("SALAD" explainer, section 2.1: ReLU linear
+ * attention, O(N)): S[b,h] = sum over valid tokens n of ReLU(k_n) v_n^T
+ * (head_dim x head_dim, row index over k's channel) and z[b,h] = sum over
+ * valid n of ReLU(k_n), accumulated in fp32 in a fixed order (bitwise
+ * reproducible run to run).  S: device float [batch*heads*head_dim*head_dim];
+ * z: device float [batch*heads*head_dim]. */
+SALAD_API int salad_linear_state(const salad_shape* shape, const void* k, const void* v,
+                       float* S, float* z, void* ws, size_t ws_bytes, void* stream);
+
+/* The fused layer forward:
+ *   out[i] = o_s[i] + gate[b,h] * (o_l[i] . w_lin)        for tokens i < N
+ *   out[i] = 0                                             for N <= i < n_pad
+ * o_s: softmax attention of query i over the keys (< N) of the key blocks its
+ *   query block keeps in (row_ptr, col_idx), logits scale*<q_i,k_j>; a row
+ *   keeping no block gives 0.
+ * o_l: ReLU(q_i)^T S / (ReLU(q_i)^T z + eps) with S, z as salad_linear_state.
+ *   gate   device float [batch*heads], values in (0,1) by the method's design
+ *          (any finite value is accepted)
+ *   w_lin  device [head_dim*head_dim] in the shape's dtype, row-major, applied
+ *          on the right (o_l . w_lin), shared by all heads
+ *   eps    > 0 keeps the ReLU normaliser finite
+ *   scale  softmax scale; <= 0 selects 1/sqrt(head_dim)
+ *   drop_tau  branch dropping ("SALAD" explainer, section 2.3): heads whose
+ *          gate < drop_tau skip the linear branch entirely (out = o_s);
+ *          pass 0 to keep every branch
+ *   out    device, shape of q */
+SALAD_API int salad_attn_fwd(const salad_shape* shape, const void* q, const void* k, const void* v,
+                   const int32_t* row_ptr, const int32_t* col_idx,
+                   const float* gate, const void* w_lin, float eps, float scale,
+                   float drop_tau, void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* salad_attn_fwd in two calls, for callers that reuse the linear state or
+ * time the steps apart.  salad_linear_prepare computes S and z (as
+ * salad_linear_state) and keeps, in the workspace, the state with gate and
+ * projection folded in: S'' = gate[b,h] * S . w_lin.  salad_attn_apply then
+ * runs the sparse branch and the linear epilogue in one kernel, reading that
+ * folded state: its gate argument serves branch dropping only and must be the
+ * gate given to salad_linear_prepare.  Between the two calls the workspace
+ * must not be used by another call.  salad_attn_fwd == prepare + apply. */
+SALAD_API int salad_linear_prepare(const salad_shape* shape, const void* k, const void* v,
+                                   const float* gate, const void* w_lin, void* ws,
+                                   size_t ws_bytes, void* stream);
+SALAD_API int salad_attn_apply(const salad_shape* shape, const void* q, const void* k,
+                               const void* v, const int32_t* row_ptr, const int32_t* col_idx,
+                               const float* gate, float eps, float scale, float drop_tau,
+                               void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* The two branches separately, for parity checks: out_sparse = o_s and
+ * out_lin = o_l (before projection and gate), both shaped like q, rows >= N
+ * zero.  Either output pointer may be NULL to skip that branch. */
+SALAD_API int salad_attn_fwd_branches(const salad_shape* shape, const void* q, const void* k,
+                            const void* v, const int32_t* row_ptr, const int32_t* col_idx,
+                            float eps, float scale, void* out_sparse, void* out_lin,
+                            void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SALAD_H */

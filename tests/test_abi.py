@@ -1,0 +1,118 @@
+"""The C-ABI library: it loads, exports what include/salad.h declares, and its
+host-only paths (sizing, validation before any launch) behave.  No kernel runs
+here, so these tests need no GPU."""
+
+import ctypes
+import os
+
+import pytest
+
+from block_sparse_linear_st_amd import salad as S
+from synth import CONFIGS, HeadSpec
+
+LIB = S.LIB_PATH
+
+
+def _lib():
+    if not os.path.exists(LIB):
+        pytest.skip("libsalad.so not built (python -m block_sparse_linear_st_amd.build)")
+    return S.lib()
+
+
+def test_exports_every_declared_function():
+    L = _lib()
+    names = S.header_functions()
+    assert "salad_attn_fwd" in names and "salad_build_mask" in names
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(S._SIGS), "binding signatures and header disagree"
+    assert S.salad_version() == 100
+
+
+def _shape(name, **over):
+    c = CONFIGS[name]
+    sh = S.make_shape(c.batch, c.heads, c.head_dim, c.T, c.H, c.W, c.block,
+                      S.SALAD_BF16 if c.dtype == "bf16" else S.SALAD_F32)
+    for k, v in over.items():
+        setattr(sh, k, v)
+    return sh
+
+
+def test_status_strings():
+    _lib()
+    for st in (0, -1, -2, -3, -4, -5, 7):
+        assert isinstance(S.salad_status_str(st), str) and S.salad_status_str(st)
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+def test_nnz_bound_matches_counts(name):
+    _lib()
+    from oracle import masks as om
+    c = CONFIGS[name]
+    sh = _shape(name)
+    n = S.salad_mask_nnz_max(sh, S.make_specs(c.specs))
+    expect = 0
+    for sp in c.specs:
+        if sp.kind == om.WINDOW:
+            expect += (c.nb * c.nb if sp.density <= 0 else om.window_count(sp.density, c.nb, c.nb)) * c.batch
+        else:
+            expect += om.topk_count(sp.density, c.nb) * c.nb * c.batch
+    assert n == expect
+
+
+def test_workspace_and_shape_validation():
+    _lib()
+    assert S.salad_workspace_bytes(_shape("c3")) > 0
+    assert S.salad_workspace_bytes(_shape("c3", head_dim=96)) == 0
+    assert S.salad_workspace_bytes(_shape("c3", block=32)) == 0
+    assert S.salad_workspace_bytes(_shape("c3", n_pad=32760)) == 0  # not a multiple of the block
+    assert S.salad_workspace_bytes(_shape("c3", n_pad=32768 + 64)) == 0  # a whole padded block
+    assert S.salad_workspace_bytes(_shape("c3", heads=129)) == 0
+    assert S.salad_workspace_bytes(_shape("c3", dtype=5)) == 0
+    specs = S.make_specs(CONFIGS["c3"].specs)
+    assert S.lib().salad_mask_nnz_max(ctypes.byref(_shape("c3", head_dim=96)), specs) == S.SALAD_EUNSUPPORTED
+    assert S.lib().salad_mask_nnz_max(ctypes.byref(_shape("c3", n_pad=5)), specs) == S.SALAD_EINVAL
+    bad = S.make_specs([HeadSpec(7, 1, -1, 0.1)] * 12)
+    assert S.lib().salad_mask_nnz_max(ctypes.byref(_shape("c3")), bad) == S.SALAD_EINVAL
+
+
+def test_entry_points_reject_bad_arguments_before_launch():
+    L = _lib()
+    sh = _shape("c3")
+    specs = S.make_specs(CONFIGS["c3"].specs)
+    fake = ctypes.c_void_p(0x100000)  # never dereferenced: validation fails first
+    ws_bytes = S.salad_workspace_bytes(sh)
+    # null shape / null buffers
+    assert L.salad_build_mask(None, specs, None, None, fake, fake, 10 ** 7, None, None, None, fake, ws_bytes, None) == S.SALAD_EINVAL
+    assert L.salad_build_mask(ctypes.byref(sh), specs, None, None, None, fake, 10 ** 7, None, None, None, fake, ws_bytes, None) == S.SALAD_EINVAL
+    # col_idx too small, workspace too small
+    assert L.salad_build_mask(ctypes.byref(sh), specs, None, None, fake, fake, 10, None, None, None, fake, ws_bytes, None) == S.SALAD_ENOSPACE
+    assert L.salad_build_mask(ctypes.byref(sh), specs, None, None, fake, fake, 10 ** 7, None, None, None, fake, 16, None) == S.SALAD_ENOSPACE
+    # gate without w_g
+    assert L.salad_build_mask(ctypes.byref(sh), specs, fake, None, fake, fake, 10 ** 7, None, None, fake, fake, ws_bytes, None) == S.SALAD_EINVAL
+    # top-k heads need q and k
+    topk = S.make_specs(CONFIGS["c4"].specs[:12])
+    assert L.salad_build_mask(ctypes.byref(sh), topk, None, None, fake, fake, 10 ** 7, None, None, None, fake, ws_bytes, None) == S.SALAD_EINVAL
+    # misaligned pointers
+    odd = ctypes.c_void_p(0x100004)
+    assert L.salad_attn_fwd(ctypes.byref(sh), odd, fake, fake, fake, fake, fake, fake, 1e-6, 0.0, 0.0, fake, fake, ws_bytes, None) == S.SALAD_EINVAL
+    # missing gate / w_lin / out; bad eps
+    assert L.salad_attn_fwd(ctypes.byref(sh), fake, fake, fake, fake, fake, None, fake, 1e-6, 0.0, 0.0, fake, fake, ws_bytes, None) == S.SALAD_EINVAL
+    assert L.salad_attn_fwd(ctypes.byref(sh), fake, fake, fake, fake, fake, fake, None, 1e-6, 0.0, 0.0, fake, fake, ws_bytes, None) == S.SALAD_EINVAL
+    assert L.salad_attn_fwd(ctypes.byref(sh), fake, fake, fake, fake, fake, fake, fake, -1.0, 0.0, 0.0, fake, fake, ws_bytes, None) == S.SALAD_EINVAL
+    assert L.salad_attn_fwd(ctypes.byref(sh), fake, fake, fake, fake, fake, fake, fake, 1e-6, 0.0, 0.0, fake, fake, 1, None) == S.SALAD_ENOSPACE
+    assert L.salad_attn_apply(ctypes.byref(sh), fake, fake, fake, fake, fake, None, 1e-6, 0.0, 0.0, fake, fake, ws_bytes, None) == S.SALAD_EINVAL
+    assert L.salad_linear_prepare(ctypes.byref(sh), fake, fake, None, fake, fake, ws_bytes, None) == S.SALAD_EINVAL
+    assert L.salad_linear_state(ctypes.byref(sh), fake, None, fake, fake, fake, ws_bytes, None) == S.SALAD_EINVAL
+    assert L.salad_gate_from_q(ctypes.byref(sh), fake, None, fake, fake, ws_bytes, None) == S.SALAD_EINVAL
+    assert L.salad_attn_fwd_branches(ctypes.byref(_shape("c3", block=32)), fake, fake, fake, fake, fake, 1e-6, 0.0, fake, None, fake, ws_bytes, None) == S.SALAD_EUNSUPPORTED
+
+
+def test_binding_refuses_host_tensors():
+    _lib()
+    import torch
+    c = CONFIGS["c1"]
+    sh = _shape("c1")
+    t = torch.zeros(4)
+    with pytest.raises(S.SaladError):
+        S.salad_linear_state(sh, t, t, t, t, t)

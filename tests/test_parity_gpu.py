@@ -1,0 +1,323 @@
+"""GPU parity: the HIP path through the C-ABI against the CPU oracle.
+
+Bars: CSR row_ptr / col_idx bit-exact; bf16 outputs max-abs <= 2e-2 and
+rel-L2 <= 1e-2 against the fp64 oracle on the same bf16-rounded inputs; fp32
+outputs max-abs <= 1e-4.  Small layers are compared element by element in
+full; the 32k- and 148k-token layers on sampled query blocks (first, second,
+middle, last-with-tail blocks of several heads plus random ones), which the
+oracle computes one by one from the dense definition.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from helpers import (BF16_MAX_ABS, BF16_REL_L2, F32_MAX_ABS, assert_close, device_tensors, inputs,
+                     make_layer, oracle_csr, sample_blocks, to_numpy)
+from synth import CONFIGS, HeadSpec, LayerConfig, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _gate_tensor(inp, cfg):
+    if inp.gate is not None:
+        return torch.from_numpy(inp.gate).cuda()
+    return torch.zeros(cfg.batch * cfg.heads, dtype=torch.float32, device="cuda")
+
+
+def _run_mask(name, layer=None, q=None, k=None, want_gate=False):
+    cfg = CONFIGS[name]
+    inp = inputs(name)
+    layer = layer or make_layer(cfg)
+    if q is None:
+        q, k, _, _ = device_tensors(inp)
+    gate = w_g = None
+    if want_gate:
+        w_g = torch.from_numpy(inp.w_g).cuda()
+        gate = torch.empty(cfg.batch * cfg.heads, dtype=torch.float32, device="cuda")
+    layer.build_mask(q, k, w_g, gate)
+    torch.cuda.synchronize()
+    return layer, gate
+
+
+# ------------------------------------------------------------------ masks
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+def test_mask_csr_bit_exact(name):
+    print(f"mask parity {name}", flush=True)
+    layer, _ = _run_mask(name)
+    rp, ci = oracle_csr(name)
+    got_rp = layer.row_ptr.cpu().numpy()
+    np.testing.assert_array_equal(got_rp, rp)
+    got_ci = layer.col_idx[:rp[-1]].cpu().numpy()
+    np.testing.assert_array_equal(got_ci, ci)
+    assert int(layer.info.item()) == 0
+
+
+def test_gate_from_q_c4():
+    print("gate parity c4", flush=True)
+    cfg = CONFIGS["c4"]
+    inp = inputs("c4")
+    layer, gate_fused = _run_mask("c4", want_gate=True)
+    q, _, _, _ = device_tensors(inp)
+    gate2 = torch.empty_like(gate_fused)
+    layer.gate_from_q(q, torch.from_numpy(inp.w_g).cuda(), gate2)
+    torch.cuda.synchronize()
+    ref = oracle.gate_from_q(inp.q, inp.w_g, cfg.N)
+    np.testing.assert_allclose(gate_fused.cpu().numpy(), ref, rtol=1e-5, atol=1e-6)
+    np.testing.assert_array_equal(gate_fused.cpu().numpy(), gate2.cpu().numpy())
+
+
+def test_window_infeasible_reported():
+    cfg = CONFIGS["c1"]
+    specs = [HeadSpec(0, 1, -1, 0.9), HeadSpec(0, 1, -1, 0.5)]  # 14.4 and 8 pairs; 10 candidates
+    layer = make_layer(cfg, specs=specs)
+    layer.build_mask()
+    torch.cuda.synchronize()
+    assert int(layer.info.item()) == 1
+    rp = layer.row_ptr.cpu().numpy()
+    assert rp[4] == 10 and rp[8] - rp[4] == 8  # head 0 keeps its 10 candidates, head 1 its 8
+
+
+# ------------------------------------------------------------------ linear state
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3"])
+def test_linear_state(name):
+    print(f"linear state {name}", flush=True)
+    cfg = CONFIGS[name]
+    inp = inputs(name)
+    layer = make_layer(cfg)
+    _, k, v, _ = device_tensors(inp)
+    BH, d = cfg.batch * cfg.heads, cfg.head_dim
+    S_out = torch.empty(BH * d * d, dtype=torch.float32, device="cuda")
+    z_out = torch.empty(BH * d, dtype=torch.float32, device="cuda")
+    layer.linear_state(k, v, S_out, z_out)
+    torch.cuda.synchronize()
+    S_ref, z_ref = oracle.linear_state(inp.k, inp.v, cfg.N)
+    S_got = S_out.cpu().numpy().reshape(S_ref.shape)
+    z_got = z_out.cpu().numpy().reshape(z_ref.shape)
+    # fp32 accumulation of exact products over N terms
+    assert_close(S_got, S_ref, 1e-5 * np.abs(S_ref).max() * np.sqrt(cfg.N), 1e-5, f"S {name}")
+    assert_close(z_got, z_ref, 1e-6 * np.abs(z_ref).max() * np.sqrt(cfg.N), 1e-6, f"z {name}")
+    # bitwise reproducible
+    S2 = torch.empty_like(S_out)
+    z2 = torch.empty_like(z_out)
+    layer.linear_state(k, v, S2, z2)
+    torch.cuda.synchronize()
+    assert torch.equal(S2, S_out) and torch.equal(z2, z_out)
+
+
+# ------------------------------------------------------------------ full forward, small layers
+
+def _forward(name, dtype=None, v_shift=0.0, canary=False, drop_tau=0.0, gate_override=None, w_override=None):
+    cfg = CONFIGS[name]
+    inp = inputs(name, canary)
+    layer = make_layer(cfg, dtype)
+    q, k, v, w = device_tensors(inp, dtype)
+    if v_shift:
+        v = v + v_shift
+    layer.build_mask(q, k)
+    gate = _gate_tensor(inp, cfg) if gate_override is None else gate_override
+    if w_override is not None:
+        w = w_override
+    out = torch.empty_like(q)
+    layer.forward(q, k, v, gate, w, out, eps=cfg.eps, drop_tau=drop_tau)
+    o_s = torch.empty_like(q)
+    o_l = torch.empty_like(q)
+    layer.branches(q, k, v, o_s, o_l, eps=cfg.eps)
+    torch.cuda.synchronize()
+    return layer, out, o_s, o_l
+
+
+def test_forward_c1_fp32():
+    cfg = CONFIGS["c1"]
+    inp = inputs("c1")
+    _, out, o_s, o_l = _forward("c1")
+    rp, ci = oracle_csr("c1")
+    ref, ref_s, ref_l = oracle.layer_forward(inp.q, inp.k, inp.v, rp, ci, inp.gate, inp.w_lin, cfg.N, cfg.block, cfg.eps)
+    assert_close(to_numpy(out), ref, F32_MAX_ABS, 1e-5, "c1 out fp32")
+    assert_close(to_numpy(o_s), ref_s, F32_MAX_ABS, 1e-5, "c1 sparse fp32")
+    assert_close(to_numpy(o_l), ref_l, F32_MAX_ABS, 1e-4, "c1 linear fp32")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_forward_c2(dtype):
+    cfg = CONFIGS["c2"]
+    inp = inputs("c2")
+    _, out, o_s, o_l = _forward("c2", dtype)
+    rp, ci = oracle_csr("c2")
+    ref, ref_s, ref_l = oracle.layer_forward(inp.q, inp.k, inp.v, rp, ci, inp.gate, inp.w_lin, cfg.N, cfg.block, cfg.eps)
+    if dtype == "bf16":
+        assert_close(to_numpy(out), ref, BF16_MAX_ABS, BF16_REL_L2, "c2 out bf16")
+        assert_close(to_numpy(o_s), ref_s, BF16_MAX_ABS, BF16_REL_L2, "c2 sparse bf16")
+        assert_close(to_numpy(o_l), ref_l, BF16_MAX_ABS, BF16_REL_L2, "c2 linear bf16 (own norm)")
+    else:
+        assert_close(to_numpy(out), ref, F32_MAX_ABS, 1e-5, "c2 out fp32")
+        assert_close(to_numpy(o_s), ref_s, F32_MAX_ABS, 1e-5, "c2 sparse fp32")
+        assert_close(to_numpy(o_l), ref_l, F32_MAX_ABS, 1e-4, "c2 linear fp32")
+
+
+def test_linear_branch_shifted_v_c2():
+    """V + 1 makes o_l of order 1, so the linear branch is visible at the bf16 bar."""
+    cfg = CONFIGS["c2"]
+    inp = inputs("c2")
+    _, out, o_s, o_l = _forward("c2", v_shift=1.0)
+    v1 = inp.v + np.float32(1.0)
+    ref_l = oracle.linear_attention(inp.q, inp.k, v1, cfg.N, cfg.eps)
+    assert_close(to_numpy(o_l), ref_l, BF16_MAX_ABS, BF16_REL_L2, "c2 linear, V+1")
+    rp, ci = oracle_csr("c2")
+    ref, _, _ = oracle.layer_forward(inp.q, inp.k, v1, rp, ci, inp.gate, inp.w_lin, cfg.N, cfg.block, cfg.eps)
+    assert_close(to_numpy(out), ref, BF16_MAX_ABS, BF16_REL_L2, "c2 out, V+1")
+
+
+def test_gate_zero_and_projection_zero_give_sparse_bitwise():
+    cfg = CONFIGS["c2"]
+    zero_g = torch.zeros(cfg.batch * cfg.heads, dtype=torch.float32, device="cuda")
+    _, out, o_s, _ = _forward("c2", gate_override=zero_g)
+    assert torch.equal(out, o_s)
+    zero_w = torch.zeros(cfg.head_dim, cfg.head_dim, dtype=torch.bfloat16, device="cuda")
+    _, out2, o_s2, _ = _forward("c2", w_override=zero_w)
+    assert torch.equal(out2, o_s2)
+
+
+def test_branch_dropping():
+    cfg = CONFIGS["c2"]
+    inp = inputs("c2")
+    tau = float(np.median(inp.gate))
+    _, out, o_s, _ = _forward("c2", drop_tau=tau)
+    _, full, _, _ = _forward("c2")
+    for h in range(cfg.heads):
+        if inp.gate[h] < tau:
+            assert torch.equal(out[0, h], o_s[0, h]), h
+        else:
+            assert torch.equal(out[0, h], full[0, h]), h
+
+
+# ------------------------------------------------------------------ large layers, sampled rows
+
+@pytest.mark.parametrize("name", ["c3", "c4", "c5"])
+def test_forward_sampled_large(name):
+    print(f"sampled forward {name}", flush=True)
+    cfg = CONFIGS[name]
+    inp = inputs(name)
+    layer = make_layer(cfg)
+    q, k, v, w = device_tensors(inp)
+    if cfg.gate_kind == "from_q":
+        gate = torch.empty(cfg.batch * cfg.heads, dtype=torch.float32, device="cuda")
+        layer.build_mask(q, k, torch.from_numpy(inp.w_g).cuda(), gate)
+    else:
+        gate = _gate_tensor(inp, cfg)
+        layer.build_mask(q, k)
+    out = torch.empty_like(q)
+    layer.forward(q, k, v, gate, w, out, eps=cfg.eps)
+    o_s = torch.empty_like(q)
+    o_l = torch.empty_like(q)
+    layer.branches(q, k, v, o_s, o_l, eps=cfg.eps)
+    torch.cuda.synchronize()
+    rp = layer.row_ptr.cpu().numpy()
+    ci = layer.col_idx[:rp[-1]].cpu().numpy()
+    orp, oci = oracle_csr(name)
+    np.testing.assert_array_equal(rp, orp)
+    np.testing.assert_array_equal(ci, oci)
+    g = gate.cpu().numpy().astype(np.float64)
+    if cfg.gate_kind == "from_q":
+        np.testing.assert_allclose(g, oracle.gate_from_q(inp.q, inp.w_g, cfg.N), rtol=1e-5, atol=1e-6)
+    picks = sample_blocks(cfg)
+    ref, ref_s, ref_l = oracle.layer_forward(inp.q, inp.k, inp.v, orp, oci, g, inp.w_lin, cfg.N, cfg.block,
+                                             cfg.eps, qblocks=picks)
+    blk = cfg.block
+    got = np.stack([to_numpy(out[b, h, qb * blk:(qb + 1) * blk]) for b, h, qb in picks])
+    got_s = np.stack([to_numpy(o_s[b, h, qb * blk:(qb + 1) * blk]) for b, h, qb in picks])
+    got_l = np.stack([to_numpy(o_l[b, h, qb * blk:(qb + 1) * blk]) for b, h, qb in picks])
+    assert_close(got, ref, BF16_MAX_ABS, BF16_REL_L2, f"{name} out (sampled)")
+    assert_close(got_s, ref_s, BF16_MAX_ABS, BF16_REL_L2, f"{name} sparse (sampled)")
+    assert_close(got_l, ref_l, BF16_MAX_ABS, BF16_REL_L2, f"{name} linear (sampled, own norm)")
+    # padded rows are zero
+    if cfg.n_pad > cfg.N:
+        assert torch.count_nonzero(out[:, :, cfg.N:]).item() == 0
+    # run-to-run bitwise determinism of the fused forward
+    out2 = torch.empty_like(q)
+    layer.forward(q, k, v, gate, w, out2, eps=cfg.eps)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+
+
+def test_tail_canary_c3():
+    """Padding filled with 1e4 must not change a single output bit."""
+    cfg = CONFIGS["c3"]
+    _, out0, _, _ = _forward("c3")
+    _, out1, _, _ = _forward("c3", canary=True)
+    assert torch.equal(out0, out1)
+    assert torch.count_nonzero(out1[:, :, cfg.N:]).item() == 0
+
+
+# ------------------------------------------------------------------ ragged and degenerate layers
+
+RAGGED = [
+    # (batch, heads, d, T, H, W, block, dtype, specs)
+    (1, 2, 64, 3, 5, 7, 64, "bf16", [HeadSpec(0, 1, -1, 0.0), HeadSpec(1, 0, -1, 0.5)]),
+    (2, 3, 128, 3, 5, 7, 64, "bf16", [HeadSpec(0, 0, 2, 0.0), HeadSpec(1, 0, -1, 0.34), HeadSpec(0, 1, -1, 0.6)]),
+    (1, 2, 64, 2, 7, 9, 128, "bf16", [HeadSpec(1, 0, -1, 1.0), HeadSpec(0, 1, -1, 0.0)]),
+    (1, 2, 128, 5, 9, 11, 128, "bf16", [HeadSpec(0, 2, -1, 0.3), HeadSpec(1, 0, -1, 0.2)]),
+    (1, 3, 128, 3, 6, 37, 64, "f32", [HeadSpec(0, 1, 3, 0.0), HeadSpec(1, 0, -1, 0.1), HeadSpec(0, 1, -1, 0.15)]),
+    (2, 2, 64, 4, 8, 9, 128, "f32", [HeadSpec(1, 0, -1, 0.5), HeadSpec(0, 1, -1, 0.5)]),
+    (1, 128, 64, 1, 4, 40, 64, "bf16", [HeadSpec(h % 2, 1, -1, 0.5) for h in range(128)]),
+]
+
+
+@pytest.mark.parametrize("case", RAGGED, ids=[f"r{i}" for i in range(len(RAGGED))])
+def test_ragged_layers(case):
+    B, Hh, d, T, H, W, blk, dt, specs = case
+    print(f"ragged {case[:8]}", flush=True)
+    cfg = LayerConfig(name="ragged", seed=11, batch=B, heads=Hh, head_dim=d, T=T, H=H, W=W, block=blk,
+                      dtype=dt, specs=tuple(specs), gate_kind="uniform")
+    inp = make_inputs(cfg, canary=True)
+    layer = make_layer(cfg)
+    q, k, v, w = device_tensors(inp)
+    layer.build_mask(q, k)
+    gate = torch.from_numpy(inp.gate).cuda()
+    out = torch.empty_like(q)
+    layer.forward(q, k, v, gate, w, out, eps=cfg.eps)
+    torch.cuda.synchronize()
+    keep = oracle.build_masks(T, H, W, blk, specs, B, inp.q, inp.k)
+    rp, ci = oracle.csr_from_keep(keep)
+    np.testing.assert_array_equal(layer.row_ptr.cpu().numpy(), rp)
+    np.testing.assert_array_equal(layer.col_idx[:rp[-1]].cpu().numpy(), ci)
+    ref, _, _ = oracle.layer_forward(inp.q, inp.k, inp.v, rp, ci, inp.gate, inp.w_lin, cfg.N, blk, cfg.eps)
+    if dt == "bf16":
+        assert_close(to_numpy(out), ref, BF16_MAX_ABS, BF16_REL_L2, f"ragged {case[:8]}")
+    else:
+        assert_close(to_numpy(out), ref, F32_MAX_ABS, 1e-5, f"ragged {case[:8]}")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_empty_and_hand_built_rows(dt):
+    """A hand-built CSR with empty rows: those rows carry only the linear branch."""
+    from block_sparse_linear_st_amd import salad as S
+    cfg = LayerConfig(name="holes", seed=12, batch=1, heads=2, head_dim=64, T=2, H=8, W=16, block=64,
+                      dtype=dt, specs=(HeadSpec(0, 1, -1, 0.0),) * 2, gate_kind="uniform")
+    inp = make_inputs(cfg)
+    layer = make_layer(cfg)
+    q, k, v, w = device_tensors(inp)
+    rng = np.random.default_rng(3)
+    keep = rng.random((1, 2, cfg.nb, cfg.nb)) < 0.4
+    keep[0, 0, 1] = False
+    keep[0, 1, :] = False
+    keep[0, 1, 2, 3] = True
+    rp, ci = oracle.csr_from_keep(keep)
+    layer.row_ptr.copy_(torch.from_numpy(rp))
+    layer.col_idx[:len(ci)].copy_(torch.from_numpy(ci))
+    gate = torch.from_numpy(inp.gate).cuda()
+    out = torch.empty_like(q)
+    layer.forward(q, k, v, gate, w, out, eps=cfg.eps)
+    o_s = torch.empty_like(q)
+    layer.branches(q, k, v, o_s, None, eps=cfg.eps)
+    torch.cuda.synchronize()
+    ref, ref_s, _ = oracle.layer_forward(inp.q, inp.k, inp.v, rp, ci, inp.gate, inp.w_lin, cfg.N, cfg.block, cfg.eps)
+    tol = (BF16_MAX_ABS, BF16_REL_L2) if dt == "bf16" else (F32_MAX_ABS, 1e-5)
+    assert_close(to_numpy(out), ref, *tol, f"holes {dt}")
+    assert_close(to_numpy(o_s), ref_s, *tol, f"holes sparse {dt}")
+    assert torch.count_nonzero(o_s[0, 0, 64:128]).item() == 0
+    assert torch.count_nonzero(o_s[0, 1, :128]).item() == 0
