@@ -47,7 +47,21 @@ def parse():
     ap.add_argument("--config", default="c3")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 512 MiB device copy (torch copy_) 5 times, to scale HBM byte counters")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """A copy of known size: 512 MiB read + 512 MiB written per launch."""
+    import torch
+    n = 512 * 1024 * 1024
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}), flush=True)
 
 
 def cpu_baseline(cfg, inp, row_ptr, col_idx, gate, budget_s):
@@ -92,6 +106,9 @@ def main():
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               f"(the layer shards by head with no communication, see DESIGN.md)", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import torch
 
     from block_sparse_linear_st_amd import salad as S

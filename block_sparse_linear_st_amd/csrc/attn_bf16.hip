@@ -3,32 +3,34 @@
 // One workgroup (4 waves) owns 128 query rows: two 64-token query blocks, or
 // one 128-token block.  Each wave owns 32 rows.  The workgroup walks the
 // ascending union of its query blocks' kept key-block lists (a two-way merge of
-// the CSR rows) in 64-key tiles; a wave computes a tile only when its own
-// query block keeps that key block, so dropped blocks cost nothing and shared
-// ones are loaded once for both query blocks.
+// the CSR rows, read through the scalar cache) in 64-key tiles; a wave computes
+// a tile only when its own query block keeps that key block, so dropped blocks
+// cost nothing and key blocks kept by both query blocks are loaded once.
 //
 // Per tile, with MFMA 32x32x16 bf16 (fp32 accumulate):
-//   S^T = K Q^T      A = K tile from LDS, B = Q fragments kept in registers
-//   online softmax   per query row; a row's 64 scores sit in one lane pair
-//                    (lanes l and l^32), so row max and sum need one exchange
-//   O^T += V^T P^T   A = V^T tile from LDS, B = P straight from the S^T
-//                    accumulators (bf16), no shuffles
-// Working in the transposed orientation keeps every per-query quantity
-// (max, sum, rescale factor) in the lane that owns the query.
+//   S^T = K Q^T      A = K tile (LDS), B = Q fragments held in registers
+//   online softmax   a row's 64 scores sit in lanes l and l^32, so the row max
+//                    and row sum need one v_permlane32_swap each
+//   O^T += V^T P^T   A = V^T fragments read from the row-major V tile with the
+//                    gfx950 LDS transpose read (ds_read_b64_tr_b16), B = P taken
+//                    straight from the S^T accumulators, converted to bf16
+// The transposed orientation keeps every per-query quantity (max, sum, scale)
+// in the lane that owns the query.  The softmax rescale is lazy: the running
+// max used for the exponentials only moves when a row's max grows by more than
+// 2^8, so most tiles skip rescaling O; the final O/l is exact either way.
 //
-// K/V tiles are double buffered: the next tile's global loads are issued into
-// registers before the current tile's MFMAs and written to the other LDS
-// buffer after them; one barrier per tile.  V is written transposed, with the
-// key order inside every 16-key group permuted so that each MFMA A-fragment is
-// one 16-byte LDS read and matches the key order the S^T accumulator hands to
-// P.
+// K/V tiles travel HBM -> LDS with global_load_lds_dwordx4 (no registers, no
+// VALU), double buffered: the next tile's loads are issued before the current
+// tile's MFMAs.  Rows are 16-byte-chunk XOR-swizzled so that the K fragment
+// reads (16 consecutive rows, one chunk) and the V transpose reads (4 rows x 4
+// chunks per half-wave) spread over all banks.
 //
 // Epilogue: o_s = O / l; the linear branch ("SALAD" explainer, section 2.1)
-// and its gated projection (section 2.2) arrive pre-folded as
-// S''^T = (g S W_lin)^T (hi + lo bf16), so g*(o_l W_lin) = (S''^T ReLU(Q)^T) /
+// and its gated projection (section 2.2) arrive pre-folded as S''^T =
+// (g S W_lin)^T in hi + lo bf16, so g*(o_l W_lin) = (S''^T ReLU(Q)^T) /
 // (ReLU(Q) z + eps) is 2*(D/32)*(D/16) more MFMAs on the Q fragments already
-// in registers.  Heads whose gate is below drop_tau skip it (section 2.3).
-// The 128 x D bf16 result is staged through LDS for 16-byte coalesced stores.
+// in registers.  Heads whose gate is below drop_tau skip it (section 2.3).  The
+// 128 x D bf16 result is staged through LDS for 16-byte coalesced stores.
 //
 // Work items map to workgroups so that each XCD (blockIdx % 8) gets a
 // contiguous range of (head, query group) items: neighbouring query blocks,
@@ -38,106 +40,29 @@
 namespace salad {
 namespace {
 
-constexpr int kTK = 64;        // keys per LDS tile
-constexpr int kVST = kTK + 8;  // V^T row stride (bf16): 144 B keeps A-fragment reads conflict-free
+constexpr int kTK = 64;  // keys per LDS tile
 
-__device__ inline int vt_pos(int key) {
-  // position of a key inside its 16-key group so that lane group g's slots
-  // j = 0..7 (keys (j/4)*8 + g*4 + j%4) are contiguous
-  const int k = key & 15;
-  return (key & ~15) | (((k >> 2) & 1) << 3) | ((k >> 3) << 2) | (k & 3);
-}
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+typedef __attribute__((address_space(3))) void* lds_ptr;
 
 template <int D>
-struct Smem {
-  static constexpr int KST = D + 8;                         // K row stride (bf16)
-  static constexpr int K_ELEMS = kTK * KST;
-  static constexpr int V_ELEMS = D * kVST;
-  static constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;
-  static constexpr int BYTES = 2 * BUF_ELEMS * 2;
-  static constexpr int OST = D + 8;                         // output staging stride
-  static_assert(128 * OST <= 2 * BUF_ELEMS, "output staging must fit");
-};
-
-// Two-way merge over the kept lists of the workgroup's query blocks, expanded
-// into 64-key tiles.  All values are uniform across the workgroup.
-struct TileIter {
-  const int32_t* col;
-  int i0, e0, i1, e1, c0, c1;
-  int kb, sub, flags;
-  bool valid;
-  __device__ void init(const int32_t* col_idx, int b0, int en0, int b1, int en1) {
-    col = col_idx;
-    i0 = b0; e0 = en0; i1 = b1; e1 = en1;
-    c0 = i0 < e0 ? col[i0] : INT32_MAX;
-    c1 = i1 < e1 ? col[i1] : INT32_MAX;
-    sub = 0;
-    take();
-  }
-  __device__ void take() {
-    kb = min(c0, c1);
-    valid = kb != INT32_MAX;
-    flags = (c0 == kb ? 1 : 0) | (c1 == kb ? 2 : 0);
-    if (c0 == kb) { ++i0; c0 = i0 < e0 ? col[i0] : INT32_MAX; }
-    if (c1 == kb) { ++i1; c1 = i1 < e1 ? col[i1] : INT32_MAX; }
-    sub = 0;
-  }
-  // advance to the next tile; sub-tiles lying wholly in the padding are skipped
-  __device__ void next(int blk, int N) {
-    if (sub + 1 < blk / kTK && kb * blk + (sub + 1) * kTK < N) { ++sub; return; }
-    take();
-  }
-  __device__ int key0(int blk) const { return kb * blk + sub * kTK; }
-};
-
-template <int D>
-struct TileRegs {
-  static constexpr int CPR = D / 8;               // 16-byte chunks per row
-  static constexpr int KCH = kTK * CPR / 256;     // K chunks per thread
-  static constexpr int VPR = (kTK / 2) * CPR / 256;  // V key-pair chunks per thread
-  uint4 k[KCH];
-  uint4 v[VPR][2];
-
-  __device__ void load(const __bf16* Kb, const __bf16* Vb, int key0, int N, int tid) {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int ch = tid + 256 * i, key = ch / CPR, dc = ch % CPR;
-      const int n = key0 + key;
-      k[i] = (unsigned)n < (unsigned)N ? *reinterpret_cast<const uint4*>(Kb + (int64_t)n * D + dc * 8)
-                   : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < VPR; ++i) {
-      const int pc = tid + 256 * i, kp = pc / CPR, dc = pc % CPR;
-      const int n = key0 + 2 * kp;
-      v[i][0] = (unsigned)n < (unsigned)N ? *reinterpret_cast<const uint4*>(Vb + (int64_t)n * D + dc * 8)
-                      : make_uint4(0, 0, 0, 0);
-      v[i][1] = (unsigned)(n + 1) < (unsigned)N ? *reinterpret_cast<const uint4*>(Vb + (int64_t)(n + 1) * D + dc * 8)
-                          : make_uint4(0, 0, 0, 0);
-    }
-  }
-
-  __device__ void store(__bf16* Ks, __bf16* Vt, int tid) const {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int ch = tid + 256 * i, key = ch / CPR, dc = ch % CPR;
-      *reinterpret_cast<uint4*>(Ks + key * Smem<D>::KST + dc * 8) = k[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VPR; ++i) {
-      const int pc = tid + 256 * i, kp = pc / CPR, dc = pc % CPR;
-      const int pos = vt_pos(2 * kp);  // even, and 2kp+1 lands at pos+1
-      const uint32_t a[4] = {v[i][0].x, v[i][0].y, v[i][0].z, v[i][0].w};
-      const uint32_t b[4] = {v[i][1].x, v[i][1].y, v[i][1].z, v[i][1].w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t lo = (a[j] & 0xffffu) | (b[j] << 16);
-        const uint32_t hi = (a[j] >> 16) | (b[j] & 0xffff0000u);
-        *reinterpret_cast<uint32_t*>(Vt + (dc * 8 + 2 * j) * kVST + pos) = lo;
-        *reinterpret_cast<uint32_t*>(Vt + (dc * 8 + 2 * j + 1) * kVST + pos) = hi;
-      }
-    }
-  }
+struct Lay {
+  static constexpr int CPR = D / 8;             // 16-byte chunks per row
+  static constexpr int ROW_B = D * 2;           // bytes per row
+  static constexpr int TILE_B = kTK * ROW_B;    // one K or V tile
+  static constexpr int BUF_B = 2 * TILE_B;      // K then V
+  static constexpr int RPB = 16 / CPR;          // rows per 256-byte bank period
+  static constexpr int LOADS = kTK * CPR / 256; // 1 KiB loads per thread per tile (K or V)
+  static constexpr int OST = D + 8;             // output staging stride (bf16)
+  static_assert(128 * OST * 2 <= 2 * BUF_B, "output staging must fit");
+  static_assert(2 * D * D * 2 <= 2 * BUF_B, "folded linear state (hi + lo) must fit");
+  // 16 consecutive rows reading one logical chunk hit 16 different physical chunks
+  __device__ static int kswz(int r) { return (r / RPB) % CPR; }
+  // 4 consecutive rows x 4 consecutive chunks (a half-wave transpose read) are disjoint
+  __device__ static int vswz(int r) { return 4 * ((r / RPB) % (CPR / 4)); }
 };
 
 __device__ inline bf16x8 load_bf16x8(const __bf16* p) {
@@ -153,20 +78,166 @@ __device__ inline bf16x8 relu8(bf16x8 x) {
   return __builtin_bit_cast(bf16x8, u);
 }
 
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+
+// the own value combined with the one of lane l ^ 32 (max or sum), bit-identical in both lanes
+__device__ inline float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// One direct HBM -> LDS load: every lane's 16 bytes at gptr land at LDS byte
+// address m0_base + 16 * lane.  Written as inline asm so that the compiler,
+// which cannot tell the two LDS buffers apart, does not stall every LDS read
+// until this load lands; the kernel waits for it explicitly (vmcnt) before the
+// barrier that publishes the buffer.  The instruction has no register result.
+// s_waitcnt vmcnt(0) as a compiler-visible instruction (gfx9 encoding: vmcnt 0,
+// expcnt 7, lgkmcnt 15), so the compiler knows every vector load has landed.
+__device__ __attribute__((always_inline)) inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+__device__ __attribute__((always_inline)) inline void lds_dma16(const void* gptr, uint32_t m0_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(m0_base)
+               : "memory", "m0");
+}
+
+// Issue the loads of one 64-key K and V tile into the LDS buffer at byte
+// address `buf`.  Rows past the last valid token load row N-1 instead (always
+// in bounds, always finite); their scores are masked to -inf, so they
+// contribute exact zeros.
+template <int D>
+__device__ __attribute__((always_inline)) inline void issue_tile(uint32_t buf, const __bf16* Kb,
+                                                                 const __bf16* Vb, int key0, int N,
+                                                                 int wave, int lane) {
+  using LY = Lay<D>;
+#pragma unroll
+  for (int i = 0; i < LY::LOADS; ++i) {
+    const int blk1k = wave * LY::LOADS + i;  // which 1 KiB of the tile this instruction fills
+    const int P = blk1k * 64 + lane;         // physical 16-byte chunk in the tile
+    const int r = P / LY::CPR, p = P % LY::CPR;
+    const int n = min(max(key0 + r, 0), N - 1);
+    lds_dma16(Kb + (int64_t)n * D + (p ^ LY::kswz(r)) * 8, buf + blk1k * 1024);
+    lds_dma16(Vb + (int64_t)n * D + (p ^ LY::vswz(r)) * 8, buf + LY::TILE_B + blk1k * 1024);
+  }
+}
+
+// S^T, softmax and O^T update of one wave on one tile held in `buf`.
+template <int D>
+__device__ __attribute__((always_inline)) inline void compute_tile(const unsigned char* buf, const bf16x8 (&qf)[D / 16],
+                                    f32x16 (&o)[D / 32], float& m_used, float& l_run, int key0,
+                                    int N, float c_log2, int lane) {
+  using LY = Lay<D>;
+  constexpr int NC = D / 16, NT = D / 32;
+  const int g32 = lane >> 5, l32 = lane & 31;
+  const unsigned char* Kt = buf;
+  const unsigned char* Vt = buf + LY::TILE_B;
+
+  f32x16 s[2];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[kt][i] = 0.0f;
+    const int row = kt * 32 + l32;
+    const unsigned char* rp = Kt + row * LY::ROW_B;
+    const int sw = LY::kswz(row);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const bf16x8 kf = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const uint4*>(rp + (((2 * c + g32) ^ sw) << 4)));
+      s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], s[kt], 0, 0, 0);
+    }
+  }
+  // mask padded keys (only the tile that holds token N-1 and beyond)
+  if (key0 + kTK > N) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = key0 + kt * 32 + (i >> 2) * 8 + g32 * 4 + (i & 3);
+        if (key >= N) s[kt][i] = -INFINITY;
+      }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
+  mx = pair_max(mx) * c_log2;
+  // lazy rescale: move the reference max only when some row grew by more than 2^8
+  if (__ballot(mx > m_used + 8.0f)) {
+    const float m_new = fmaxf(m_used, mx);
+    const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_used - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
+    m_used = m_new;
+  }
+  const float neg_m = m_used == -INFINITY ? 0.0f : -m_used;
+  float rs = 0.0f;
+  bf16x8 pf[4];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float p[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        p[j] = __builtin_amdgcn_exp2f(fmaf(s[kt][h * 8 + j], c_log2, neg_m));
+        rs += p[j];
+      }
+      const uint4 u = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                 pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
+      pf[kt * 2 + h] = __builtin_bit_cast(bf16x8, u);
+    }
+  l_run += pair_sum(rs);
+
+  // O^T += V^T P^T.  For 16-key step ks and half h, lane (group a = lane/16,
+  // s = lane%16) points the transpose read at key ks*16 + 8h + 4*g32 + s/4 and
+  // channels t*32 + 16*(a%2) + 4*(s%4) .. +3; lane i of the group then holds
+  // channel t*32 + 16*(a%2) + i of those 4 keys, which are the keys its P
+  // fragment carries in slots 4h .. 4h+3.
+  const int sl = lane & 15, dh = (lane >> 4) & 1;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int chunk = 4 * t + 2 * dh + ((sl & 3) >> 1);
+    const int inb = (sl & 1) * 8;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      uint2 tr[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int row = ks * 16 + 8 * h + 4 * g32 + (sl >> 2);
+        const unsigned char* ad = Vt + row * LY::ROW_B + ((chunk ^ LY::vswz(row)) << 4) + inb;
+        tr[h] = __builtin_bit_cast(
+            uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(ad)));
+      }
+      const uint4 u = make_uint4(tr[0].x, tr[0].y, tr[1].x, tr[1].y);
+      o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, u), pf[ks], o[t], 0, 0, 0);
+    }
+  }
+}
+
 template <int D, int BLK>
 __global__ void __launch_bounds__(256, 2)
-k_attn_bf16(Geom g, AttnArgs a, int n_items, float scale_log2) {
+k_attn_bf16(Geom g, AttnArgs a, int n_items, float c_log2) {
+  using LY = Lay<D>;
   constexpr int QPW = 128 / BLK;  // query blocks per workgroup
-  constexpr int NC = D / 16;      // 16-wide d chunks (QK^T contraction steps)
-  constexpr int NT = D / 32;      // 32-wide d tiles of the output
-  using SM = Smem<D>;
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  __bf16* smem = reinterpret_cast<__bf16*>(smem_raw);
+  constexpr int NC = D / 16;
+  constexpr int NT = D / 32;
+  constexpr int TPB = BLK / kTK;  // 64-key tiles per key block
+  __shared__ __align__(1024) unsigned char smem[2 * LY::BUF_B];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g32 = lane >> 5, l32 = lane & 31;
 
-  // XCD-aware item order: workgroup w runs on XCD w % 8; give each XCD a
+  // XCD-aware item order: workgroup w runs on XCD w % 8; each XCD gets a
   // contiguous range of items.
   const int per_xcd = (int)(gridDim.x >> 3);
   const int item = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
@@ -175,114 +246,75 @@ k_attn_bf16(Geom g, AttnArgs a, int n_items, float scale_log2) {
   const int bh = item / qgroups, qg = item - bh * qgroups;
   const int qb_base = qg * QPW;
   const int qsub = QPW == 2 ? (wave >> 1) : 0;
-  const int my_qb = qb_base + qsub;
-  const bool wave_rows = my_qb < g.nb;
-  const int row0 = qb_base * BLK + wave * 32;  // first query row of this wave
+  const bool wave_rows = qb_base + qsub < g.nb;
+  const int row0 = qb_base * BLK + wave * 32;
   const int my_row = row0 + l32;
 
   const __bf16* Qb = static_cast<const __bf16*>(a.q) + (int64_t)bh * g.n_pad * D;
   const __bf16* Kb = static_cast<const __bf16*>(a.k) + (int64_t)bh * g.n_pad * D;
   const __bf16* Vb = static_cast<const __bf16*>(a.v) + (int64_t)bh * g.n_pad * D;
 
-  // Q fragments (B operand of S^T = K Q^T): row my_row, d = c*16 + g32*8 .. +7
   bf16x8 qf[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     if (wave_rows && my_row < g.N) qf[c] = load_bf16x8(Qb + (int64_t)my_row * D + c * 16 + g32 * 8);
     else qf[c] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
   }
+  wait_vmem();  // Q is in registers before the loop's own loads start
 
   f32x16 o[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[t][i] = 0.0f;
-  float m_run = -INFINITY, l_run = 0.0f;
+  float m_used = -INFINITY, l_run = 0.0f;
 
   if (a.has_sparse) {
-    const int64_t rbase = (int64_t)bh * g.nb;
-    int b0 = 0, e0 = 0, b1 = 0, e1 = 0;
-    if (qb_base < g.nb) { b0 = a.row_ptr[rbase + qb_base]; e0 = a.row_ptr[rbase + qb_base + 1]; }
-    if (QPW == 2 && qb_base + 1 < g.nb) { b1 = a.row_ptr[rbase + qb_base + 1]; e1 = a.row_ptr[rbase + qb_base + 2]; }
-    TileIter it;
-    it.init(a.col_idx, b0, e0, b1, e1);
-    TileRegs<D> regs;
-    int buf = 0;
-    if (it.valid) {
-      regs.load(Kb, Vb, it.key0(BLK), g.N, tid);
-      regs.store(smem, smem + SM::K_ELEMS, tid);
-    }
-    __syncthreads();
-    while (it.valid) {
-      const int key0 = it.key0(BLK);
-      const int flags = it.flags;
-      TileIter nx = it;
-      nx.next(BLK, g.N);
-      if (nx.valid) regs.load(Kb, Vb, nx.key0(BLK), g.N, tid);
-
-      const __bf16* Ks = smem + buf * SM::BUF_ELEMS;
-      const __bf16* Vt = Ks + SM::K_ELEMS;
-      if (wave_rows && ((flags >> qsub) & 1)) {
-        f32x16 s[2];
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) s[kt][i] = 0.0f;
-#pragma unroll
-          for (int c = 0; c < NC; ++c) {
-            const bf16x8 kf = load_bf16x8(Ks + (kt * 32 + l32) * SM::KST + c * 16 + g32 * 8);
-            s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], s[kt], 0, 0, 0);
-          }
-        }
-        // scale, mask padded keys, row max
-        float mx = -INFINITY;
-        const bool tail = key0 + kTK > g.N;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            float x = s[kt][i] * scale_log2;
-            if (tail) {
-              const int key = key0 + kt * 32 + (i >> 2) * 8 + g32 * 4 + (i & 3);
-              if (key >= g.N) x = -INFINITY;
-            }
-            s[kt][i] = x;
-            mx = fmaxf(mx, x);
-          }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        float rs = 0.0f;
-        bf16x8 pf[4];
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float p = __builtin_amdgcn_exp2f(s[kt][i] - m_use);
-            rs += p;
-            pf[kt * 2 + (i >> 3)][i & 7] = (__bf16)p;
-          }
-        rs += __shfl_xor(rs, 32);
-        l_run = l_run * alpha + rs;
-        m_run = m_new;
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) {
-            const bf16x8 vf = load_bf16x8(Vt + (t * 32 + l32) * kVST + ks * 16 + g32 * 8);
-            o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], o[t], 0, 0, 0);
-          }
+    // kept lists of the workgroup's query blocks, read through the scalar cache
+    const const_i32_ptr col = (const_i32_ptr)a.col_idx;
+    const const_i32_ptr rptr = (const_i32_ptr)a.row_ptr;
+    const int64_t rbase = (int64_t)bh * g.nb + qb_base;
+    int i0 = 0, e0 = 0, i1 = 0, e1 = 0;
+    if (qb_base < g.nb) { i0 = rptr[rbase]; e0 = rptr[rbase + 1]; }
+    if (QPW == 2 && qb_base + 1 < g.nb) { i1 = e0; e1 = rptr[rbase + 2]; }
+    int c0 = i0 < e0 ? col[i0] : INT32_MAX;
+    int c1 = i1 < e1 ? col[i1] : INT32_MAX;
+    // current tile
+    int kb = 0, sub = 0, flags = 0;
+    bool valid = false;
+    auto advance = [&](int& nkb, int& nsub, int& nflags, bool& nvalid) __attribute__((always_inline)) {
+      if (valid && sub + 1 < TPB && kb * BLK + (sub + 1) * kTK < g.N) {
+        nkb = kb; nsub = sub + 1; nflags = flags; nvalid = true;
+        return;
       }
-      if (nx.valid) regs.store(smem + (buf ^ 1) * SM::BUF_ELEMS,
-                               smem + (buf ^ 1) * SM::BUF_ELEMS + SM::K_ELEMS, tid);
-      __syncthreads();
-      buf ^= 1;
-      it = nx;
+      nkb = min(c0, c1);
+      nvalid = nkb != INT32_MAX;
+      nflags = (c0 == nkb ? 1 : 0) | (c1 == nkb ? 2 : 0);
+      nsub = 0;
+      if (c0 == nkb) { ++i0; c0 = i0 < e0 ? col[i0] : INT32_MAX; }
+      if (c1 == nkb) { ++i1; c1 = i1 < e1 ? col[i1] : INT32_MAX; }
+    };
+    advance(kb, sub, flags, valid);
+    // LDS byte address of the buffers (uniform); the wave index is uniform too
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    if (valid) issue_tile<D>(lds0, Kb, Vb, kb * BLK + sub * kTK, g.N, wave_u, lane);
+    wait_vmem();
+    __syncthreads();
+    int cur = 0;
+    while (valid) {
+      int nkb, nsub, nflags;
+      bool nvalid;
+      advance(nkb, nsub, nflags, nvalid);
+      if (nvalid)
+        issue_tile<D>(lds0 + (cur ^ 1) * LY::BUF_B, Kb, Vb, nkb * BLK + nsub * kTK, g.N, wave_u, lane);
+      if (wave_rows && ((flags >> qsub) & 1))
+        compute_tile<D>(smem + cur * LY::BUF_B, qf, o, m_used, l_run, kb * BLK + sub * kTK, g.N,
+                        c_log2, lane);
+      wait_vmem();  // the next tile has landed in LDS ...
+      __syncthreads();  // ... for every wave, and nobody still reads the current one
+      kb = nkb; sub = nsub; flags = nflags; valid = nvalid;
+      cur ^= 1;
     }
   }
 
@@ -294,10 +326,24 @@ k_attn_bf16(Geom g, AttnArgs a, int n_items, float scale_log2) {
     for (int i = 0; i < 16; ++i) o[t][i] *= inv_l;
 
   bool lin = a.has_lin != 0;
-  if (lin && a.gate != nullptr && a.gate[bh] < a.drop_tau) lin = false;
-  if (lin && wave_rows) {
+  if (lin && a.gate != nullptr && a.gate[bh] < a.drop_tau) lin = false;  // uniform
+  if (lin) {
+    // S''^T (hi, lo) of this head into LDS, rows swizzled like K tiles: every
+    // wave reads all of it, so one copy per workgroup instead of one per wave
     const __bf16* hi = static_cast<const __bf16*>(a.sft_hi) + (int64_t)bh * D * D;
     const __bf16* lo = static_cast<const __bf16*>(a.sft_lo) + (int64_t)bh * D * D;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    constexpr int PER = D * LY::CPR / 256;  // 1 KiB loads per wave per matrix
+    __syncthreads();  // the tile buffers are free
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int blk1k = wave_u * PER + i;
+      const int P = blk1k * 64 + lane;
+      const int r = P / LY::CPR, p = P % LY::CPR;
+      lds_dma16(hi + r * D + (p ^ LY::kswz(r)) * 8, lds0 + blk1k * 1024);
+      lds_dma16(lo + r * D + (p ^ LY::kswz(r)) * 8, lds0 + D * D * 2 + blk1k * 1024);
+    }
     const float* z = a.z + (int64_t)bh * D;
     bf16x8 rq[NC];
     float den = 0.0f;
@@ -307,45 +353,47 @@ k_attn_bf16(Geom g, AttnArgs a, int n_items, float scale_log2) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) den += (float)rq[c][j] * z[c * 16 + g32 * 8 + j];
     }
-    den += __shfl_xor(den, 32);
+    den = pair_sum(den);
     const float inv_den = 1.0f / (den + a.eps);
+    wait_vmem();
+    __syncthreads();
+    if (wave_rows) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      f32x16 la;
+      for (int t = 0; t < NT; ++t) {
+        const int row = t * 32 + l32;
+        const unsigned char* rh = smem + row * LY::ROW_B;
+        const unsigned char* rl = rh + D * D * 2;
+        const int sw = LY::kswz(row);
+        f32x16 la;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) la[i] = 0.0f;
+        for (int i = 0; i < 16; ++i) la[i] = 0.0f;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const int64_t off = (int64_t)(t * 32 + l32) * D + c * 16 + g32 * 8;
-        la = __builtin_amdgcn_mfma_f32_32x32x16_bf16(load_bf16x8(hi + off), rq[c], la, 0, 0, 0);
-        la = __builtin_amdgcn_mfma_f32_32x32x16_bf16(load_bf16x8(lo + off), rq[c], la, 0, 0, 0);
+        for (int c = 0; c < NC; ++c) {
+          const int off = ((2 * c + g32) ^ sw) << 4;
+          la = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(rh + off)), rq[c], la, 0, 0, 0);
+          la = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(rl + off)), rq[c], la, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[t][i] += la[i] * inv_den;
       }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[t][i] += la[i] * inv_den;
     }
   }
 
   // stage [128 rows][D] bf16 through LDS, then 16-byte coalesced stores
   __syncthreads();
-  __bf16* ost = smem;
+  __bf16* ost = reinterpret_cast<__bf16*>(smem);
   const bool row_ok = wave_rows && my_row < g.N;
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
       const int d0 = t * 32 + i4 * 8 + g32 * 4;
-      uint32_t w0, w1;
-      if (row_ok) {
-        const uint32_t b0 = __builtin_bit_cast(uint16_t, (__bf16)o[t][i4 * 4 + 0]);
-        const uint32_t b1 = __builtin_bit_cast(uint16_t, (__bf16)o[t][i4 * 4 + 1]);
-        const uint32_t b2 = __builtin_bit_cast(uint16_t, (__bf16)o[t][i4 * 4 + 2]);
-        const uint32_t b3 = __builtin_bit_cast(uint16_t, (__bf16)o[t][i4 * 4 + 3]);
-        w0 = b0 | (b1 << 16);
-        w1 = b2 | (b3 << 16);
-      } else {
-        w0 = 0; w1 = 0;
-      }
-      *reinterpret_cast<uint2*>(ost + (wave * 32 + l32) * SM::OST + d0) = make_uint2(w0, w1);
+      uint2 w = make_uint2(0, 0);
+      if (row_ok) w = make_uint2(pack_bf16x2(o[t][i4 * 4 + 0], o[t][i4 * 4 + 1]),
+                                 pack_bf16x2(o[t][i4 * 4 + 2], o[t][i4 * 4 + 3]));
+      *reinterpret_cast<uint2*>(ost + (wave * 32 + l32) * LY::OST + d0) = w;
     }
   __syncthreads();
   __bf16* Ob = static_cast<__bf16*>(a.out) + (int64_t)bh * g.n_pad * D;
@@ -355,7 +403,7 @@ k_attn_bf16(Geom g, AttnArgs a, int n_items, float scale_log2) {
     const int row = qb_base * BLK + r;
     if (row < g.n_pad)
       *reinterpret_cast<uint4*>(Ob + (int64_t)row * D + dc * 8) =
-          *reinterpret_cast<const uint4*>(ost + r * SM::OST + dc * 8);
+          *reinterpret_cast<const uint4*>(ost + r * LY::OST + dc * 8);
   }
 }
 
@@ -365,14 +413,8 @@ hipError_t launch(const Geom& g, const AttnArgs& a, hipStream_t st) {
   const int qgroups = (g.nb + QPW - 1) / QPW;
   const int n_items = g.B * g.Hh * qgroups;
   const int grid = (n_items + 7) / 8 * 8;
-  const float scale_log2 = a.scale * 1.4426950408889634f;
-  // more than 64 KiB of dynamic LDS must be opted into once per kernel
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&k_attn_bf16<D, BLK>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, Smem<D>::BYTES);
-  if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((k_attn_bf16<D, BLK>), dim3(grid), dim3(256), Smem<D>::BYTES, st, g, a,
-                     n_items, scale_log2);
+  const float c_log2 = a.scale * 1.4426950408889634f;
+  hipLaunchKernelGGL((k_attn_bf16<D, BLK>), dim3(grid), dim3(256), 0, st, g, a, n_items, c_log2);
   return hipGetLastError();
 }
 
