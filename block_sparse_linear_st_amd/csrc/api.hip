@@ -29,6 +29,7 @@ int shape_status(const salad_shape* s) {
   const int64_t nb = (N + s->block - 1) / s->block;
   if ((int64_t)s->n_pad != nb * s->block) return SALAD_EINVAL;
   if (nb > 46340) return SALAD_EUNSUPPORTED;  // nb*nb must fit int32
+  if (s->H > 65534 || s->W > 65534) return SALAD_EUNSUPPORTED;  // r* is stored in 16 bits
   if ((int64_t)s->batch * s->heads * nb + 1 > INT32_MAX) return SALAD_EUNSUPPORTED;
   return SALAD_OK;
 }
@@ -41,7 +42,7 @@ int spec_status(const salad_shape* s, const salad_mask_spec* specs) {
     if (sp.kind == SALAD_MASK_WINDOW) {
       if (sp.t_window < 0) return SALAD_EINVAL;
     } else if (sp.kind == SALAD_MASK_TOPK) {
-      if (nb > 8192) return SALAD_EUNSUPPORTED;
+      if (nb > 4096) return SALAD_EUNSUPPORTED;  // top-k keeps 4 rows of scores in LDS
     } else {
       return SALAD_EINVAL;
     }
@@ -86,7 +87,8 @@ Workspace plan_workspace(const Geom& g, int dtype) {
   // mask build
   size_t off = 0;
   L.hist_bins = 1 + (size_t)std::max(g.H, g.W) * nb;
-  L.off_hist = off;   off = align_up(off + (size_t)g.Hh * L.hist_bins * 4);
+  L.off_rt = off;     off = align_up(off + nb * nb * 2);
+  L.off_hist = off;   off = align_up(off + L.hist_bins * 4);
   L.off_thr = off;    off = align_up(off + (size_t)g.Hh * 8);
   L.off_flags = off;  off = align_up(off + (size_t)g.Hh * 4);
   L.off_rowcnt = off; off = align_up(off + BH * nb * 4);

@@ -32,13 +32,15 @@ struct HeadTable {
   int r_max[SALAD_MAX_HEADS];
   int count[SALAD_MAX_HEADS];      // window: K pairs (-1 = keep all); top-k: k per row
   int pool[SALAD_MAX_HEADS];       // pool Q (bit 0) / K (bit 1) for this head
+  int group[SALAD_MAX_HEADS];      // window heads: index of their (t_window, r_max) group
 };
 
 // Workspace layout for one shape, computed on the host.
 struct Workspace {
   size_t bytes;
   // mask build
-  size_t off_hist, hist_bins;      // int32 [heads][hist_bins]
+  size_t off_rt;                   // uint16 [nb][nb]: r* of one window group (0xffff = no candidate)
+  size_t off_hist, hist_bins;      // int32 [hist_bins]: that group's candidates per rank bin
   size_t off_thr;                  // int64 [heads] threshold keys
   size_t off_flags;                // int32 [heads] infeasible flags
   size_t off_rowcnt;               // int32 [B*H*nb]

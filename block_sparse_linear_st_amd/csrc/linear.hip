@@ -5,13 +5,15 @@
 // attention, O(N)).  Two passes:
 //
 //  1. k_lin_partial_*: grid (splits, B*H).  Each workgroup reduces one token
-//     chunk of one head into a D x D fp32 partial.  The bf16 kernel stages 64
-//     tokens of ReLU(K) and V in LDS, token-major, and runs 32x32x16 bf16 MFMAs
-//     with the token index as the contraction (each operand lane gathers 8
-//     tokens of one channel); products of bf16 values are exact and the sums are
-//     fp32.  The fp32 kernel does the same with VALU FMAs.
+//     chunk of one head into a D x D fp32 partial.  The bf16 kernel streams
+//     64-token tiles of K and V straight into LDS (double buffered) and runs
+//     32x32x16 bf16 MFMAs with the token index as the contraction; both
+//     operands are read with the LDS transpose read, ReLU is applied to the K
+//     fragment in registers.  Products of bf16 values are exact and the sums
+//     are fp32.  The fp32 kernel does the same with VALU FMAs.
 //  2. k_lin_fold: grid (B*H, D/8).  Sums the partials over the splits in a fixed
-//     order (bitwise reproducible), then, for the fused forward, folds gate and
+//     order (bitwise reproducible; loads batched 8 splits deep), then, for the
+//     fused forward, folds gate and
 //     projection into the state:  S'' = g * S * W_lin, so that the attention
 //     epilogue computes g*(o_l W_lin) = ReLU(q)^T S'' / (ReLU(q)^T z + eps) with
 //     one product.  S'' is stored transposed ([dv][dk]) because that is the
@@ -34,110 +36,152 @@ __device__ inline uint32_t relu_bf16x2(uint32_t w) {
   return lo | hi;
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// s_waitcnt vmcnt(0) as a compiler-visible instruction (gfx9 encoding)
+__device__ __attribute__((always_inline)) inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// one direct HBM -> LDS load (lane l's 16 bytes land at m0_base + 16 l); inline
+// asm so that the compiler does not stall LDS reads of the other buffer on it
+__device__ __attribute__((always_inline)) inline void lds_dma16(const void* gptr, uint32_t m0_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(m0_base)
+               : "memory", "m0");
+}
+
+__device__ __attribute__((always_inline)) inline uint4 relu_u4(uint4 u) {
+  u.x = relu_bf16x2(u.x); u.y = relu_bf16x2(u.y); u.z = relu_bf16x2(u.z); u.w = relu_bf16x2(u.w);
+  return u;
+}
+
+// Token-major tiles of K and V (64 tokens x D bf16) go HBM -> LDS directly.
+// Both MFMA operands need 8 tokens of one channel per lane: they come from the
+// gfx950 LDS transpose read.  For 16-token step ks and half h, lane (group
+// a = lane/16, s = lane%16) points at token ks*16 + 8h + 4*(lane/32) + s/4 and
+// channels c0 + 16*(a%2) + 4*(s%4) .. +3; lane i of the group receives channel
+// c0 + 16*(a%2) + i of those 4 tokens, i.e. operand slots 4h .. 4h+3.  A and B
+// use the same token for the same slot, so the contraction is over tokens.
 template <int D>
-__global__ void __launch_bounds__(256)
+struct LinLay {
+  static constexpr int CPR = D / 8;
+  static constexpr int ROW_B = D * 2;
+  static constexpr int TILE_B = kTok * ROW_B;
+  static constexpr int BUF_B = 2 * TILE_B;
+  static constexpr int RPB = 16 / CPR;
+  static constexpr int LOADS = kTok * CPR / 256;
+  __device__ static int swz(int r) { return 4 * ((r / RPB) % (CPR / 4)); }
+};
+
+template <int D>
+__device__ __attribute__((always_inline)) inline bf16x8 tr_frag(const unsigned char* tile, int ks, int c0,
+                                                               int lane) {
+  using LY = LinLay<D>;
+  const int sl = lane & 15, a = lane >> 4;
+  const int chunk = (c0 >> 3) + 2 * (a & 1) + ((sl & 3) >> 1);
+  uint2 tr[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int row = ks * 16 + 8 * h + 4 * (lane >> 5) + (sl >> 2);
+    const unsigned char* ad = tile + row * LY::ROW_B + ((chunk ^ LY::swz(row)) << 4) + (sl & 1) * 8;
+    tr[h] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                          (__attribute__((address_space(3))) s16x4*)(ad)));
+  }
+  return __builtin_bit_cast(bf16x8, make_uint4(tr[0].x, tr[0].y, tr[1].x, tr[1].y));
+}
+
+template <int D>
+__global__ void __launch_bounds__(256, 2)
 k_lin_partial_bf16(Geom g, const __bf16* __restrict__ K, const __bf16* __restrict__ V, int chunk,
                    float* __restrict__ spart, float* __restrict__ zpart) {
-  constexpr int ST = D + 8;            // LDS row stride (bf16)
-  constexpr int CPR = D / 8;           // 16-byte chunks per token row
-  constexpr int NCH = kTok * CPR / 256;  // chunks per thread per tensor
+  using LY = LinLay<D>;
   constexpr int TD = D / 32;           // 32-wide output tiles per dimension
   constexpr int TPW = TD * TD / 4;     // output tiles per wave
-  __shared__ __align__(16) __bf16 Ks[kTok * ST];
-  __shared__ __align__(16) __bf16 Vs[kTok * ST];
-  __shared__ float zred[256 / CPR][D];
+  __shared__ __align__(1024) unsigned char smem[2 * LY::BUF_B];
 
   const int split = blockIdx.x, bh = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n0 = split * chunk, n1 = min(g.N, n0 + chunk);
   const __bf16* Kb = K + (int64_t)bh * g.n_pad * D;
   const __bf16* Vb = V + (int64_t)bh * g.n_pad * D;
+  // output tiles of this wave: D=128 -> row tile = wave, col tiles 0..3;
+  // D=64 -> row tile wave/2, col tile wave%2
+  const int ti = TD == 4 ? wave : wave >> 1;
+  const int tj0 = TD == 4 ? 0 : (wave & 1);
 
   f32x16 acc[TPW];
 #pragma unroll
   for (int t = 0; t < TPW; ++t)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[t][i] = 0.0f;
-  float zacc[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) zacc[j] = 0.0f;
+  float zacc = 0.0f;
 
-  // output tiles of this wave: D=128 -> row tile = wave, col tiles 0..3;
-  // D=64 -> row tile wave/2, col tile wave%2
-  const int ti = TD == 4 ? wave : wave >> 1;
-  const int tj0 = TD == 4 ? 0 : (wave & 1);
-  const int gsel = lane >> 5, l32 = lane & 31;
-
-  for (int nt = n0; nt < n1; nt += kTok) {
-    uint4 kr[NCH], vr[NCH];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  auto issue = [&](int t0, int buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int ch = tid + 256 * i, tok = ch / CPR, dc = ch % CPR;
-      const int n = nt + tok;
-      if (n < n1) {
-        kr[i] = *reinterpret_cast<const uint4*>(Kb + (int64_t)n * D + dc * 8);
-        vr[i] = *reinterpret_cast<const uint4*>(Vb + (int64_t)n * D + dc * 8);
-      } else {
-        kr[i] = make_uint4(0, 0, 0, 0);
-        vr[i] = make_uint4(0, 0, 0, 0);
-      }
-      kr[i].x = relu_bf16x2(kr[i].x);
-      kr[i].y = relu_bf16x2(kr[i].y);
-      kr[i].z = relu_bf16x2(kr[i].z);
-      kr[i].w = relu_bf16x2(kr[i].w);
+    for (int i = 0; i < LY::LOADS; ++i) {
+      const int blk1k = wave_u * LY::LOADS + i;
+      const int P = blk1k * 64 + lane;
+      const int r = P / LY::CPR, p = P % LY::CPR;
+      const int n = min(t0 + r, g.N - 1);
+      const int c = (p ^ LY::swz(r)) * 8;
+      lds_dma16(Kb + (int64_t)n * D + c, lds0 + buf * LY::BUF_B + blk1k * 1024);
+      lds_dma16(Vb + (int64_t)n * D + c, lds0 + buf * LY::BUF_B + LY::TILE_B + blk1k * 1024);
     }
-    __syncthreads();  // previous tile fully consumed
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int ch = tid + 256 * i, tok = ch / CPR, dc = ch % CPR;
-      *reinterpret_cast<uint4*>(Ks + tok * ST + dc * 8) = kr[i];
-      *reinterpret_cast<uint4*>(Vs + tok * ST + dc * 8) = vr[i];
-      const uint32_t w[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        zacc[2 * j] += __uint_as_float(w[j] << 16);
-        zacc[2 * j + 1] += __uint_as_float(w[j] & 0xffff0000u);
-      }
-    }
-    __syncthreads();
+  };
+  issue(n0, 0);
+  wait_vmem();
+  __syncthreads();
+  int cur = 0;
+  for (int t0 = n0; t0 < n1; t0 += kTok) {
+    if (t0 + kTok < n1) issue(t0 + kTok, cur ^ 1);
+    const unsigned char* Kt = smem + cur * LY::BUF_B;
+    const unsigned char* Vt = Kt + LY::TILE_B;
+    const int valid = n1 - t0;  // tokens of this tile inside the chunk
 #pragma unroll
     for (int ks = 0; ks < kTok / 16; ++ks) {
-      const int tok0 = ks * 16 + gsel * 8;
-      bf16x8 a;
+      uint4 au = relu_u4(__builtin_bit_cast(uint4, tr_frag<D>(Kt, ks, ti * 32, lane)));
+      if (valid < kTok) {  // zero the slots of tokens past the chunk end
+        const int tb = ks * 16 + 4 * (lane >> 5);
+        if (tb + 0 >= valid) { au.x &= 0xffff0000u; }
+        if (tb + 1 >= valid) { au.x &= 0x0000ffffu; }
+        if (tb + 2 >= valid) { au.y &= 0xffff0000u; }
+        if (tb + 3 >= valid) { au.y &= 0x0000ffffu; }
+        if (tb + 8 >= valid) { au.z &= 0xffff0000u; }
+        if (tb + 9 >= valid) { au.z &= 0x0000ffffu; }
+        if (tb + 10 >= valid) { au.w &= 0xffff0000u; }
+        if (tb + 11 >= valid) { au.w &= 0x0000ffffu; }
+      }
+      const bf16x8 af = __builtin_bit_cast(bf16x8, au);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) a[j] = Ks[(tok0 + j) * ST + ti * 32 + l32];
+      for (int j = 0; j < 8; ++j) zacc += (float)af[j];
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
         const int tj = TD == 4 ? t : tj0;
-        bf16x8 b;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) b[j] = Vs[(tok0 + j) * ST + tj * 32 + l32];
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, tr_frag<D>(Vt, ks, tj * 32, lane), acc[t], 0, 0, 0);
       }
     }
+    wait_vmem();
+    __syncthreads();
+    cur ^= 1;
   }
 
-  // partial S: lane holds rows (i/4)*8 + gsel*4 + i%4 of tile ti, column l32 of tile tj
+  // partial S: lane holds rows (i/4)*8 + (lane/32)*4 + i%4 of tile ti, column lane%32 of tile tj
+  const int g32 = lane >> 5, l32 = lane & 31;
   float* sp = spart + ((int64_t)split * g.B * g.Hh + bh) * D * D;
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     const int tj = TD == 4 ? t : tj0;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int r = ti * 32 + (i >> 2) * 8 + gsel * 4 + (i & 3);
+      const int r = ti * 32 + (i >> 2) * 8 + g32 * 4 + (i & 3);
       sp[r * D + tj * 32 + l32] = acc[t][i];
     }
   }
-  // z: threads sharing tid % CPR hold the same 8 channels
-  const int dc = tid % CPR, grp = tid / CPR;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) zred[grp][dc * 8 + j] = zacc[j];
-  __syncthreads();
-  if (tid < D) {
-    float s = 0.0f;
-    for (int r = 0; r < 256 / CPR; ++r) s += zred[r][tid];
-    zpart[((int64_t)split * g.B * g.Hh + bh) * D + tid] = s;
-  }
+  // z: the lane pair (l, l^32) covers all tokens of channel ti*32 + l%32
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(zacc), __float_as_uint(zacc), false, false);
+  const float zs = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  if (tj0 == 0 && lane < 32) zpart[((int64_t)split * g.B * g.Hh + bh) * D + ti * 32 + l32] = zs;
 }
 
 template <int D>
@@ -178,7 +222,8 @@ k_lin_partial_f32(Geom g, const float* __restrict__ K, const float* __restrict__
   if (c0 == 0) zpart[((int64_t)split * g.B * g.Hh + bh) * D + r] = zacc;
 }
 
-// grid (B*H, D/8), 256 threads.  mode 0: S'' = g*S*W; 1: S'' = S; 2: state only.
+// grid (B*H, D/8), 256 threads: reduce 8 rows of S over the splits, in split
+// order, then fold.  mode 0: S'' = g*S*W; 1: S'' = S; 2: state only.
 template <typename WT, bool BF16OUT>
 __global__ void __launch_bounds__(256)
 k_lin_fold(Geom g, int splits, const float* __restrict__ spart, const float* __restrict__ zpart,
@@ -189,12 +234,29 @@ k_lin_fold(Geom g, int splits, const float* __restrict__ spart, const float* __r
   __shared__ float Srows[FR][128];
   const int D = g.D, bh = blockIdx.x, r0 = blockIdx.y * FR, tid = threadIdx.x;
   const int64_t BH = (int64_t)g.B * g.Hh;
-  for (int i = tid; i < FR * D; i += 256) {
-    const int rr = i / D, c = i % D;
-    float s = 0.0f;
-    for (int sp = 0; sp < splits; ++sp) s += spart[((int64_t)sp * BH + bh) * D * D + (r0 + rr) * D + c];
-    Srows[rr][c] = s;
-    if (S_out) S_out[(int64_t)bh * D * D + (r0 + rr) * D + c] = s;
+  const int nvec = FR * D / 4;  // float4s in this row block (256 or 128)
+  if (tid < nvec) {
+    const int e = tid * 4;  // element offset inside the row block
+    const float* src = spart + (int64_t)bh * D * D + (int64_t)r0 * D + e;
+    const int64_t stride = BH * D * D;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    int sp = 0;
+    for (; sp + 8 <= splits; sp += 8) {
+      float4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const float4*>(src + (sp + u) * stride);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        acc.x += v[u].x; acc.y += v[u].y; acc.z += v[u].z; acc.w += v[u].w;
+      }
+    }
+    for (; sp < splits; ++sp) {
+      const float4 v = *reinterpret_cast<const float4*>(src + sp * stride);
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    const int rr = e / D, c = e % D;
+    Srows[rr][c] = acc.x; Srows[rr][c + 1] = acc.y; Srows[rr][c + 2] = acc.z; Srows[rr][c + 3] = acc.w;
+    if (S_out) *reinterpret_cast<float4*>(S_out + (int64_t)bh * D * D + (int64_t)r0 * D + e) = acc;
   }
   if (blockIdx.y == 0) {
     for (int c = tid; c < D; c += 256) {
@@ -207,7 +269,7 @@ k_lin_fold(Geom g, int splits, const float* __restrict__ spart, const float* __r
   if (mode == 2) return;
   __syncthreads();
   const float gv = mode == 0 ? gate[bh] : 1.0f;
-  // S''[r0+rr][j] for j = column; stored transposed at [j][r0+rr]
+  // S''[r0+rr][j] for column j, stored transposed at [j][r0+rr]
   for (int i = tid; i < FR * D; i += 256) {
     const int j = i / FR, rr = i % FR;
     float v;

@@ -2,21 +2,22 @@
 // pooled-score top-k, emitted as CSR lists of kept key blocks.
 //
 // The masks follow the readings stated in include/salad.h (salad_mask_spec).
-// Window: every block pair's r* is recomputed on the fly from the horizontal
-// runs of the two blocks (a block covers at most ceil(block/W)+1 runs), so no
-// r* table is stored.  Selecting the first K pairs in (qb!=kb, r*, |qb-kb|, qb,
-// kb) order is done with one histogram over a combined bin (0 for the
-// diagonal, 1 + r*·nb + |qb-kb| otherwise), a per-head scan that finds the bin
-// holding the K-th pair, and a scan over query blocks inside that bin (a bin
-// holds at most two pairs per query block, kb = qb -+ |qb-kb|).  The K-th
-// pair's packed key (bin·nb² + qb·nb + kb) is then the keep threshold.
+// Window: r* of every block pair is computed once per (t_window, r_max) group
+// from the horizontal runs of the two blocks (a block covers at most
+// ceil(block/W)+1 runs) into a uint16 table in the workspace.  Selecting the
+// first K pairs in (qb!=kb, r*, |qb-kb|, qb, kb) order takes one histogram over
+// a combined bin (0 for the diagonal, 1 + r*·nb + |qb-kb| otherwise), a
+// per-head scan that finds the bin holding the K-th pair, and a scan over query
+// blocks inside that bin (a bin holds at most two pairs per query block,
+// kb = qb -+ |qb-kb|).  The K-th pair's packed key (bin·nb² + qb·nb + kb) is
+// then the keep threshold; row counts and the CSR emit are table lookups.
 //
 // Top-k: block sums in float32, sequential in token order, one division per
 // mean, scores as a sequential float32 sum of separately rounded products.
 // This file is compiled with floating-point contraction off so that no
-// multiply-add is fused: the ranking is reproducible bit for bit.  Each row's
-// scores become 64-bit keys (descending score, then ascending kb), are sorted
-// in LDS with a bitonic network, and the first k kb's are emitted ascending.
+// multiply-add is fused: the ranking is reproducible bit for bit.  One wave
+// per row selects the k largest scores (ties to the lower kb) with a bitwise
+// radix search over order-preserving 32-bit keys and emits them ascending.
 #include <algorithm>
 
 #include "internal.h"
@@ -69,43 +70,65 @@ __global__ void k_fill_i32(int32_t* p, int64_t n, int32_t v) {
     p[i] = v;
 }
 
-// grid (nb, heads): histogram of the candidate pairs of query block qb.
-__global__ void k_window_hist(Geom g, HeadTable ht, int32_t* hist, int64_t hist_bins) {
-  const int h = blockIdx.y, qb = blockIdx.x;
-  if (ht.kind[h] != SALAD_MASK_WINDOW || ht.count[h] < 0) return;
-  int32_t* hh = hist + (int64_t)h * hist_bins;
+constexpr uint16_t kNoCand = 0xffff;
+
+// grid (nb): r* of every (qb, kb) pair for one (t_window, r_max) group, as a
+// uint16 table (kNoCand when the pair is no candidate), plus, when `hist` is
+// given, the number of candidates in each rank bin.
+__global__ void __launch_bounds__(256)
+k_window_rstar(Geom g, int tw, int rmax, uint16_t* rt, int32_t* hist) {
+  const int qb = blockIdx.x;
   for (int kb = threadIdx.x; kb < g.nb; kb += blockDim.x) {
-    const int r = rstar_pair(g, qb, kb, ht.t_window[h]);
-    if (!window_candidate(r, ht.r_max[h])) continue;
-    atomicAdd(&hh[pair_bin(qb, kb, r, g.nb)], 1);
+    const int r = rstar_pair(g, qb, kb, tw);
+    const bool cand = window_candidate(r, rmax);
+    rt[(int64_t)qb * g.nb + kb] = cand ? (uint16_t)r : kNoCand;
+    if (cand && hist) atomicAdd(&hist[pair_bin(qb, kb, r, g.nb)], 1);
   }
 }
 
-// Block-wide exclusive scan of one int64 per thread (kScanThreads threads).
+// Block-wide exclusive scan of one int64 per thread (kScanThreads threads):
+// shuffle scan inside each wave, then one wave scans the 16 wave totals.
 __device__ int64_t block_exclusive_scan(int64_t v, int64_t* tmp, int64_t* total) {
-  const int t = threadIdx.x;
-  tmp[t] = v;
-  __syncthreads();
-  for (int off = 1; off < kScanThreads; off <<= 1) {
-    const int64_t add = t >= off ? tmp[t - off] : 0;
-    __syncthreads();
-    tmp[t] += add;
-    __syncthreads();
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  int64_t x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int64_t y = __shfl_up(x, off);
+    if (lane >= off) x += y;
   }
-  const int64_t incl = tmp[t];
-  if (total) *total = tmp[kScanThreads - 1];
+  if (lane == 63) tmp[w] = x;
   __syncthreads();
-  return incl - v;
+  if (w == 0) {
+    int64_t s = lane < kScanThreads / 64 ? tmp[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < kScanThreads / 64; off <<= 1) {
+      const int64_t y = __shfl_up(s, off);
+      if (lane >= off) s += y;
+    }
+    if (lane < kScanThreads / 64) tmp[kScanThreads / 64 + lane] = s;
+  }
+  __syncthreads();
+  const int64_t before = w == 0 ? 0 : tmp[kScanThreads / 64 + w - 1];
+  if (total) *total = tmp[kScanThreads / 64 + kScanThreads / 64 - 1];
+  __syncthreads();
+  return before + x - v;
 }
 
-// grid (heads), kScanThreads threads: the keep threshold of each window head.
+__device__ inline int64_t rt_key(const uint16_t* rt, const Geom& g, int qb, int kb, bool* cand) {
+  const uint16_t r = rt[(int64_t)qb * g.nb + kb];
+  *cand = r != kNoCand;
+  return pair_key(pair_bin(qb, kb, r, g.nb), qb, kb, g.nb);
+}
+
+// grid (heads), kScanThreads threads: the keep threshold of each window head of
+// group `grp` (its r* table and histogram are current).
 __global__ void __launch_bounds__(kScanThreads)
-k_window_threshold(Geom g, HeadTable ht, const int32_t* hist, int64_t hist_bins,
-                   int64_t* thr, int32_t* flags) {
-  __shared__ int64_t tmp[kScanThreads];
+k_window_threshold(Geom g, HeadTable ht, int grp, const uint16_t* rt, const int32_t* hist,
+                   int64_t hist_bins, int64_t* thr, int32_t* flags) {
+  __shared__ int64_t tmp[2 * kScanThreads / 64];
   __shared__ int64_t s_bin, s_need;
   const int h = blockIdx.x, t = threadIdx.x;
-  if (ht.kind[h] != SALAD_MASK_WINDOW) return;
+  if (ht.kind[h] != SALAD_MASK_WINDOW || ht.group[h] != grp) return;
   const int64_t K = ht.count[h];
   if (K < 0) {  // keep every candidate
     if (t == 0) { thr[h] = INT64_MAX; flags[h] = 0; }
@@ -115,16 +138,14 @@ k_window_threshold(Geom g, HeadTable ht, const int32_t* hist, int64_t hist_bins,
     if (t == 0) { thr[h] = -1; flags[h] = 0; }
     return;
   }
-  const int32_t* hh = hist + (int64_t)h * hist_bins;
-  // 1) the bin that holds the K-th pair
-  const int64_t seg = (hist_bins + kScanThreads - 1) / kScanThreads;
+  // 1) the bin that holds the K-th pair (segments of whole int4s, loads batched)
+  const int64_t seg = (hist_bins + 4 * kScanThreads - 1) / (4 * kScanThreads) * 4;
   const int64_t lo = min((int64_t)t * seg, hist_bins), hi = min(lo + seg, hist_bins);
   int64_t local = 0;
-  for (int64_t b = lo; b < hi; ++b) local += hh[b];
+#pragma unroll 8
+  for (int64_t b = lo; b < hi; ++b) local += hist[b];
   int64_t total;
   const int64_t excl = block_exclusive_scan(local, tmp, &total);
-  if (t == 0) { s_bin = -1; s_need = 0; }
-  __syncthreads();
   if (total < K) {  // infeasible: keep all candidates and report it
     if (t == 0) { thr[h] = INT64_MAX; flags[h] = 1; }
     return;
@@ -132,20 +153,19 @@ k_window_threshold(Geom g, HeadTable ht, const int32_t* hist, int64_t hist_bins,
   if (excl < K && K <= excl + local) {
     int64_t cum = excl;
     for (int64_t b = lo; b < hi; ++b) {
-      if (cum + hh[b] >= K) { s_bin = b; s_need = K - cum; break; }
-      cum += hh[b];
+      if (cum + hist[b] >= K) { s_bin = b; s_need = K - cum; break; }
+      cum += hist[b];
     }
   }
   __syncthreads();
   const int64_t bin = s_bin, need = s_need;
   // 2) inside that bin, pairs run in (qb, kb) order with at most two per qb
-  const int tw = ht.t_window[h], rmax = ht.r_max[h];
-  const int r = bin == 0 ? 0 : (int)((bin - 1) / g.nb);
   const int dd = bin == 0 ? 0 : (int)((bin - 1) % g.nb);
   auto in_bin = [&](int qb, int kb) -> bool {
     if (kb < 0 || kb >= g.nb) return false;
-    const int rr = rstar_pair(g, qb, kb, tw);
-    return window_candidate(rr, rmax) && pair_bin(qb, kb, rr, g.nb) == bin;
+    bool cand;
+    const int64_t key = rt_key(rt, g, qb, kb, &cand);
+    return cand && key / ((int64_t)g.nb * g.nb) == bin;
   };
   const int qseg = (g.nb + kScanThreads - 1) / kScanThreads;
   const int qlo = min(t * qseg, g.nb), qhi = min(qlo + qseg, g.nb);
@@ -172,43 +192,48 @@ k_window_threshold(Geom g, HeadTable ht, const int32_t* hist, int64_t hist_bins,
       cum += c;
     }
   }
-  (void)r;
 }
 
-__device__ inline bool window_keep(const Geom& g, int qb, int kb, int tw, int rmax, int64_t thr) {
-  const int r = rstar_pair(g, qb, kb, tw);
-  if (!window_candidate(r, rmax)) return false;
-  if (thr == INT64_MAX) return true;
-  return pair_key(pair_bin(qb, kb, r, g.nb), qb, kb, g.nb) <= thr;
+__device__ inline bool window_keep(const uint16_t* rt, const Geom& g, int qb, int kb, int64_t thr) {
+  bool cand;
+  const int64_t key = rt_key(rt, g, qb, kb, &cand);
+  return cand && (thr == INT64_MAX || key <= thr);
 }
 
 // grid (nb, heads), one wave: kept blocks per row, replicated over the batch.
+// Window heads of group `grp` count from the r* table; top-k heads (when
+// `topk` is set) have k per row.
 __global__ void __launch_bounds__(64)
-k_row_counts(Geom g, HeadTable ht, const int64_t* thr, int32_t* rowcnt) {
+k_row_counts(Geom g, HeadTable ht, int grp, int topk, const uint16_t* rt, const int64_t* thr,
+             int32_t* rowcnt) {
   const int qb = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
   int cnt;
   if (ht.kind[h] == SALAD_MASK_WINDOW) {
+    if (ht.group[h] != grp) return;
     int local = 0;
     const int64_t th = thr[h];
-    for (int kb = lane; kb < g.nb; kb += 64)
-      local += window_keep(g, qb, kb, ht.t_window[h], ht.r_max[h], th) ? 1 : 0;
+    for (int kb = lane; kb < g.nb; kb += 64) local += window_keep(rt, g, qb, kb, th) ? 1 : 0;
     for (int off = 32; off > 0; off >>= 1) local += __shfl_xor(local, off);
     cnt = local;
   } else {
+    if (!topk) return;
     cnt = ht.count[h];
   }
   if (lane == 0)
     for (int b = 0; b < g.B; ++b) rowcnt[((int64_t)b * g.Hh + h) * g.nb + qb] = cnt;
 }
 
-// One workgroup: row_ptr = exclusive scan of the row counts.
+// One workgroup: row_ptr = exclusive scan of the row counts; info = number of
+// infeasible window heads.
 __global__ void __launch_bounds__(kScanThreads)
-k_scan_rows(const int32_t* rowcnt, int64_t rows, int32_t* row_ptr) {
-  __shared__ int64_t tmp[kScanThreads];
+k_scan_rows(const int32_t* rowcnt, int64_t rows, int32_t* row_ptr, HeadTable ht,
+            const int32_t* flags, int32_t* info) {
+  __shared__ int64_t tmp[2 * kScanThreads / 64];
   const int t = threadIdx.x;
   const int64_t seg = (rows + kScanThreads - 1) / kScanThreads;
   const int64_t lo = min((int64_t)t * seg, rows), hi = min(lo + seg, rows);
   int64_t local = 0;
+#pragma unroll 8
   for (int64_t r = lo; r < hi; ++r) local += rowcnt[r];
   int64_t total;
   int64_t run = block_exclusive_scan(local, tmp, &total);
@@ -216,20 +241,28 @@ k_scan_rows(const int32_t* rowcnt, int64_t rows, int32_t* row_ptr) {
     row_ptr[r] = (int32_t)run;
     run += rowcnt[r];
   }
-  if (t == 0) row_ptr[rows] = (int32_t)total;
+  if (t == 0) {
+    row_ptr[rows] = (int32_t)total;
+    if (info) {
+      int n = 0;
+      for (int h = 0; h < ht.n_heads; ++h)
+        if (ht.kind[h] == SALAD_MASK_WINDOW) n += flags[h];
+      info[0] = n;
+    }
+  }
 }
 
-// grid (nb, heads), one wave: kept key blocks of window rows, ascending.
+// grid (nb, heads), one wave: kept key blocks of the window rows of group `grp`, ascending.
 __global__ void __launch_bounds__(64)
-k_window_emit(Geom g, HeadTable ht, const int64_t* thr, const int32_t* row_ptr,
-              int32_t* col_idx, int64_t col_cap) {
+k_window_emit(Geom g, HeadTable ht, int grp, const uint16_t* rt, const int64_t* thr,
+              const int32_t* row_ptr, int32_t* col_idx, int64_t col_cap) {
   const int qb = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
-  if (ht.kind[h] != SALAD_MASK_WINDOW) return;
+  if (ht.kind[h] != SALAD_MASK_WINDOW || ht.group[h] != grp) return;
   const int64_t th = thr[h];
   int off = 0;
   for (int kb0 = 0; kb0 < g.nb; kb0 += 64) {
     const int kb = kb0 + lane;
-    const bool keep = kb < g.nb && window_keep(g, qb, kb, ht.t_window[h], ht.r_max[h], th);
+    const bool keep = kb < g.nb && window_keep(rt, g, qb, kb, th);
     const uint64_t m = __ballot(keep);
     const int rank = __popcll(m & ((1ull << lane) - 1ull));
     if (keep) {
@@ -268,8 +301,9 @@ struct Load8<float> {
   }
 };
 
-// grid (ceil(B*H*nb*(D/8) / 256), 2): per (b, h, block) sequential float32 sums
-// of 8 channels per thread; blockIdx.y selects Q (0) or K (1).
+// grid (ceil(B*H*nb*(D/8) / 256), 2): per (b, h, block) the float32 mean of 8
+// channels per thread (sequential sum in token order, one correctly rounded
+// division); blockIdx.y selects Q (0) or K (1).
 template <typename T>
 __global__ void __launch_bounds__(256)
 k_pool(Geom g, HeadTable ht, const T* q, const T* k, float* psum_q, float* psum_k) {
@@ -306,8 +340,9 @@ k_pool(Geom g, HeadTable ht, const T* q, const T* k, float* psum_q, float* psum_
     for (int j = 0; j < 8; ++j) acc[j] = acc[j] + f[j];
   }
   float* dst = (which == 0 ? psum_q : psum_k) + u * g.D + cg * 8;
+  const float nv = (float)nvalid;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) dst[j] = acc[j];
+  for (int j = 0; j < 8; ++j) dst[j] = __fdiv_rn(acc[j], nv);
 }
 
 __device__ inline uint32_t ordered_bits(float s) {
@@ -315,121 +350,144 @@ __device__ inline uint32_t ordered_bits(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// grid (ceil(nb / rows_per_wg), B*H), 256 threads: scores, top-k and emit for
-// rows_per_wg query blocks of one (b, h).  Dynamic LDS layout:
-//   pq[rows][D] | scores[rows][nb] | union{ pk[64][D+1], keys[nbp2] u64 + flags[nb] }
+// grid (ceil(nb / R), B*H), 256 threads (4 waves): scores, top-k and emit for
+// R query blocks of one (b, h).  Dynamic LDS: pqT[D][R] | pkT[D][65] |
+// scores[R][nb] (transposed query means, one transposed 64-key-block tile with
+// a padded stride, the scores).  Scores: all waves share a tile, lane = key
+// block, wave w owns rows w*R/4 .. +R/4; each score is the sequential float32
+// sum over channels 0..D-1 of separately rounded products.  Selection: one
+// wave per row finds the k-th largest order-preserving 32-bit key by a bitwise
+// radix search whose counts are ballot popcounts over keys held in registers,
+// keeps every larger key and the first remaining equal keys in kb order, and
+// emits the kept kb's ascending.
+template <int D, int R, int MAXK>
 __global__ void __launch_bounds__(256)
-k_topk(Geom g, HeadTable ht, const float* psum_q, const float* psum_k, int rows_per_wg,
-       int nbp2, const int32_t* row_ptr, int32_t* col_idx, int64_t col_cap) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  const int bh = blockIdx.y, h = bh % g.Hh, t = threadIdx.x;
+k_topk(Geom g, HeadTable ht, const float* __restrict__ pmean_q, const float* __restrict__ pmean_k,
+       const int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx, int64_t col_cap) {
+  // MAXK: key blocks per lane held in registers by the selection (nb <= 64 * MAXK)
+  constexpr int RW = R / 4;  // score rows per wave
+  constexpr int PKS = 65;    // pkT row stride (floats)
+  extern __shared__ __align__(16) float tk_smem[];
+  const int bh = blockIdx.y, h = bh % g.Hh, t = threadIdx.x, wave = t >> 6, lane = t & 63;
   if (ht.kind[h] != SALAD_MASK_TOPK) return;
-  const int D = g.D, nb = g.nb;
-  const int qb0 = blockIdx.x * rows_per_wg;
-  const int rows = min(rows_per_wg, nb - qb0);
-  float* pq = reinterpret_cast<float*>(smem);
-  float* scores = pq + rows_per_wg * D;
-  unsigned char* tail = reinterpret_cast<unsigned char*>(scores + (size_t)rows_per_wg * nb);
-  float* pk = reinterpret_cast<float*>(tail);
-  uint64_t* keys = reinterpret_cast<uint64_t*>(tail);
-  int32_t* flags = reinterpret_cast<int32_t*>(keys + nbp2);
-
-  auto nvalid = [&](int b) { return (float)min(g.blk, g.N - b * g.blk); };
-  for (int i = t; i < rows * D; i += 256) {
+  const int nb = g.nb;
+  const int qb0 = blockIdx.x * R;
+  const int rows = min(R, nb - qb0);
+  float* pqT = tk_smem;
+  float* pkT = pqT + D * R;
+  float* scores = pkT + D * PKS;
+  for (int i = t; i < R * D; i += 256) {
     const int r = i / D, c = i - r * D;
-    pq[r * D + c] = __fdiv_rn(psum_q[((int64_t)bh * nb + qb0 + r) * D + c], nvalid(qb0 + r));
+    pqT[c * R + r] = r < rows ? pmean_q[((int64_t)bh * nb + qb0 + r) * D + c] : 0.0f;
   }
-  // scores, 64 key blocks at a time
   for (int kb0 = 0; kb0 < nb; kb0 += 64) {
-    const int nk = min(64, nb - kb0);
     __syncthreads();
-    for (int i = t; i < nk * D; i += 256) {
+    for (int i = t; i < 64 * D; i += 256) {
       const int kk = i / D, c = i - kk * D;
-      pk[kk * (D + 1) + c] =
-          __fdiv_rn(psum_k[((int64_t)bh * nb + kb0 + kk) * D + c], nvalid(kb0 + kk));
+      pkT[c * PKS + kk] = pmean_k[((int64_t)bh * nb + min(kb0 + kk, nb - 1)) * D + c];
     }
     __syncthreads();
-    for (int i = t; i < rows * 64; i += 256) {
-      const int r = i / 64, kk = i - r * 64;
-      if (kk >= nk) continue;
-      float acc = 0.0f;
-      const float* a = pq + r * D;
-      const float* b = pk + kk * (D + 1);
-      for (int c = 0; c < D; ++c) {
-        const float prod = a[c] * b[c];
-        acc = acc + prod;
+    float acc[RW];
+#pragma unroll
+    for (int j = 0; j < RW; ++j) acc[j] = 0.0f;
+#pragma unroll 8
+    for (int c = 0; c < D; ++c) {
+      const float kv = pkT[c * PKS + lane];
+      const float* qv = pqT + c * R + wave * RW;
+#pragma unroll
+      for (int j = 0; j < RW; ++j) {
+        const float prod = qv[j] * kv;
+        acc[j] = acc[j] + prod;
       }
-      scores[(size_t)r * nb + kb0 + kk] = acc;
+    }
+    const int kb = kb0 + lane;
+    if (kb < nb) {
+#pragma unroll
+      for (int j = 0; j < RW; ++j)
+        if (wave * RW + j < rows) scores[(size_t)(wave * RW + j) * nb + kb] = acc[j];
     }
   }
   __syncthreads();
   const int kkeep = ht.count[h];
-  for (int r = 0; r < rows; ++r) {
-    for (int i = t; i < nbp2; i += 256)
-      keys[i] = i < nb ? ((uint64_t)(~ordered_bits(scores[(size_t)r * nb + i])) << 32) | (uint32_t)i
-                       : ~0ull;
-    __syncthreads();
-    for (int size = 2; size <= nbp2; size <<= 1) {
-      for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        for (int i = t; i < nbp2 / 2; i += 256) {
-          const int lo = 2 * stride * (i / stride) + (i % stride);
-          const int hi = lo + stride;
-          const bool asc = (lo & size) == 0;
-          const uint64_t a = keys[lo], b = keys[hi];
-          if ((a > b) == asc) { keys[lo] = b; keys[hi] = a; }
-        }
-        __syncthreads();
+  const int kpl = (nb + 63) / 64;
+  const uint64_t lt = (1ull << lane) - 1ull;
+  for (int r = wave; r < rows; r += 4) {
+    const float* srow = scores + (size_t)r * nb;
+    uint32_t key[MAXK];
+#pragma unroll
+    for (int m = 0; m < MAXK; ++m) {
+      if (m < kpl) {
+        const int kb = m * 64 + lane;
+        key[m] = kb < nb ? ordered_bits(srow[kb]) : 0u;  // real keys are never 0
       }
     }
-    for (int i = t; i < nb; i += 256) flags[i] = 0;
-    __syncthreads();
-    for (int i = t; i < kkeep; i += 256) flags[(int)(keys[i] & 0xffffffffu)] = 1;
-    __syncthreads();
-    // compact ascending: wave 0 walks the flags 64 at a time
-    if (t < 64) {
-      const int64_t base = row_ptr[(int64_t)bh * nb + qb0 + r];
-      int off = 0;
-      for (int kb0 = 0; kb0 < nb; kb0 += 64) {
-        const int kb = kb0 + t;
-        const bool keep = kb < nb && flags[kb];
-        const uint64_t m = __ballot(keep);
+    uint32_t prefix = 0, bits = 0;
+    int krem = kkeep;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t bmask = bits | (1u << bit), cand = prefix | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int m = 0; m < MAXK; ++m)
+        if (m < kpl) cnt += __popcll(__ballot((key[m] & bmask) == cand));
+      if (cnt >= krem) prefix = cand;
+      else krem -= cnt;
+      bits = bmask;
+    }
+    const int64_t base = row_ptr[(int64_t)bh * nb + qb0 + r];
+    int off = 0, eq_seen = 0;
+#pragma unroll
+    for (int m = 0; m < MAXK; ++m) {
+      if (m < kpl) {
+        const int kb = m * 64 + lane;
+        const bool eq = key[m] == prefix;
+        const uint64_t me = __ballot(eq);
+        const bool keep = key[m] > prefix || (eq && eq_seen + __popcll(me & lt) < krem);
+        eq_seen += __popcll(me);
+        const uint64_t mk = __ballot(keep);
         if (keep) {
-          const int64_t pos = base + off + __popcll(m & ((1ull << t) - 1ull));
+          const int64_t pos = base + off + __popcll(mk & lt);
           if (pos < col_cap) col_idx[pos] = kb;
         }
-        off += __popcll(m);
+        off += __popcll(mk);
       }
     }
-    __syncthreads();
   }
 }
 
-// grid (B*H), 256 threads: gate = sigmoid(mean(Q) . w_g) from the block sums.
+// grid (B*H), 256 threads: gate = sigmoid(mean(Q) . w_g) from the block means,
+// each weighted by its valid-token count.  Thread t accumulates channel t % D
+// over every (256/D)-th block, in order, in fp64; the partial sums then
+// combine in a fixed order.
 __global__ void __launch_bounds__(256)
-k_gate(Geom g, const float* psum_q, const float* w_g, float* gate) {
+k_gate(Geom g, const float* pmean_q, const float* w_g, float* gate) {
   __shared__ double red[256];
   const int bh = blockIdx.x, t = threadIdx.x;
-  double part = 0.0;
-  for (int c = t; c < g.D; c += 256) {
-    double s = 0.0;
-    for (int b = 0; b < g.nb; ++b) s += (double)psum_q[((int64_t)bh * g.nb + b) * g.D + c];
-    part += (s / (double)g.N) * (double)w_g[c];
+  const int parts = 256 / g.D, c = t % g.D, part = t / g.D;
+  const float* src = pmean_q + (int64_t)bh * g.nb * g.D + c;
+  auto nv = [&](int b) { return (double)min(g.blk, g.N - b * g.blk); };
+  double s = 0.0;
+  int b = part;
+  for (; b + 7 * parts < g.nb; b += 8 * parts) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = src[(int64_t)(b + u * parts) * g.D];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += (double)v[u] * nv(b + u * parts);
   }
-  red[t] = part;
+  for (; b < g.nb; b += parts) s += (double)src[(int64_t)b * g.D] * nv(b);
+  red[t] = s;
   __syncthreads();
-  for (int off = 128; off > 0; off >>= 1) {
-    if (t < off) red[t] += red[t + off];
-    __syncthreads();
+  if (t < g.D) {
+    double tot = 0.0;
+    for (int p = 0; p < parts; ++p) tot += red[p * g.D + t];
+    red[t] = (tot / (double)g.N) * (double)w_g[t];
   }
-  if (t == 0) gate[bh] = (float)(1.0 / (1.0 + exp(-red[0])));
-}
-
-__global__ void k_info(const int32_t* flags, HeadTable ht, int32_t* info) {
-  if (threadIdx.x != 0) return;
-  int n = 0;
-  for (int h = 0; h < ht.n_heads; ++h)
-    if (ht.kind[h] == SALAD_MASK_WINDOW) n += flags[h];
-  info[0] = n;
+  __syncthreads();
+  if (t == 0) {
+    double dot = 0.0;
+    for (int i = 0; i < g.D; ++i) dot += red[i];
+    gate[bh] = (float)(1.0 / (1.0 + exp(-dot)));
+  }
 }
 
 template <typename T>
@@ -442,6 +500,31 @@ hipError_t launch_pool(const Geom& g, const HeadTable& ht, const void* q, const 
   return hipGetLastError();
 }
 
+template <int D, int R, int MAXK>
+hipError_t launch_topk_r(const Geom& g, const HeadTable& ht, const float* pq, const float* pk,
+                         const int32_t* row_ptr, int32_t* col_idx, int64_t col_cap, hipStream_t st) {
+  const size_t lds = ((size_t)R * D + (size_t)D * 65 + (size_t)R * g.nb) * 4;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&k_topk<D, R, MAXK>), hipFuncAttributeMaxDynamicSharedMemorySize,
+      160 * 1024);
+  if (attr != hipSuccess) return attr;
+  dim3 grid((g.nb + R - 1) / R, g.B * g.Hh);
+  hipLaunchKernelGGL((k_topk<D, R, MAXK>), grid, dim3(256), lds, st, g, ht, pq, pk, row_ptr, col_idx,
+                     col_cap);
+  return hipGetLastError();
+}
+
+// rows per workgroup (R x nb scores stay within about 48 KiB of LDS) and keys
+// per lane in the selection, by the number of key blocks
+template <int D>
+hipError_t launch_topk(const Geom& g, const HeadTable& ht, const float* pq, const float* pk,
+                       const int32_t* row_ptr, int32_t* col_idx, int64_t col_cap, hipStream_t st) {
+  if (g.nb <= 512) return launch_topk_r<D, 16, 8>(g, ht, pq, pk, row_ptr, col_idx, col_cap, st);
+  if (g.nb <= 768) return launch_topk_r<D, 16, 12>(g, ht, pq, pk, row_ptr, col_idx, col_cap, st);
+  if (g.nb <= 1536) return launch_topk_r<D, 8, 24>(g, ht, pq, pk, row_ptr, col_idx, col_cap, st);
+  return launch_topk_r<D, 4, 64>(g, ht, pq, pk, row_ptr, col_idx, col_cap, st);
+}
+
 }  // namespace
 
 hipError_t launch_build_mask(const Geom& g, int dtype, const HeadTable& ht0, const void* q,
@@ -449,13 +532,32 @@ hipError_t launch_build_mask(const Geom& g, int dtype, const HeadTable& ht0, con
                              int32_t* info, const float* w_g, float* gate, char* ws,
                              const Workspace& L, hipStream_t st) {
   HeadTable ht = ht0;
-  bool any_window = false, any_topk = false;
+  bool any_topk = false;
+  // window heads sharing (t_window, r_max) share one r* table and histogram
+  int n_groups = 0;
+  int grp_tw[SALAD_MAX_HEADS], grp_rmax[SALAD_MAX_HEADS];
+  bool grp_ranked[SALAD_MAX_HEADS];
   for (int h = 0; h < g.Hh; ++h) {
     ht.pool[h] = 0;
-    if (ht.kind[h] == SALAD_MASK_WINDOW) any_window = true;
-    else { any_topk = true; ht.pool[h] = 3; }
+    ht.group[h] = -1;
+    if (ht.kind[h] == SALAD_MASK_WINDOW) {
+      int gi = 0;
+      while (gi < n_groups && !(grp_tw[gi] == ht.t_window[h] && grp_rmax[gi] == ht.r_max[h])) ++gi;
+      if (gi == n_groups) {
+        grp_tw[gi] = ht.t_window[h];
+        grp_rmax[gi] = ht.r_max[h];
+        grp_ranked[gi] = false;
+        ++n_groups;
+      }
+      ht.group[h] = gi;
+      if (ht.count[h] >= 0) grp_ranked[gi] = true;
+    } else {
+      any_topk = true;
+      ht.pool[h] = 3;
+    }
     if (gate) ht.pool[h] |= 1;
   }
+  uint16_t* rt = reinterpret_cast<uint16_t*>(ws + L.off_rt);
   int32_t* hist = reinterpret_cast<int32_t*>(ws + L.off_hist);
   int64_t* thr = reinterpret_cast<int64_t*>(ws + L.off_thr);
   int32_t* flags = reinterpret_cast<int32_t*>(ws + L.off_flags);
@@ -463,43 +565,44 @@ hipError_t launch_build_mask(const Geom& g, int dtype, const HeadTable& ht0, con
   float* psq = reinterpret_cast<float*>(ws + L.off_psum_q);
   float* psk = reinterpret_cast<float*>(ws + L.off_psum_k);
 
-  hipLaunchKernelGGL(k_fill_i32, dim3(1), dim3(256), 0, st, flags, (int64_t)g.Hh, 0);
-  if (any_window) {
-    const int64_t nhist = (int64_t)g.Hh * (int64_t)L.hist_bins;
-    hipLaunchKernelGGL(k_fill_i32, dim3((unsigned)std::min<int64_t>((nhist + 255) / 256, 65535)),
-                       dim3(256), 0, st, hist, nhist, 0);
-    hipLaunchKernelGGL(k_window_hist, dim3(g.nb, g.Hh), dim3(256), 0, st, g, ht, hist,
-                       (int64_t)L.hist_bins);
-    hipLaunchKernelGGL(k_window_threshold, dim3(g.Hh), dim3(kScanThreads), 0, st, g, ht, hist,
-                       (int64_t)L.hist_bins, thr, flags);
-  }
   if (any_topk || gate) {
     hipError_t e = dtype == SALAD_BF16 ? launch_pool<__bf16>(g, ht, q, k, psq, psk, st)
                                        : launch_pool<float>(g, ht, q, k, psq, psk, st);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(k_row_counts, dim3(g.nb, g.Hh), dim3(64), 0, st, g, ht, thr, rowcnt);
+  // counts: every window group in turn (its r* table lives in the workspace)
+  for (int gi = 0; gi < n_groups; ++gi) {
+    int32_t* h_ptr = nullptr;
+    if (grp_ranked[gi]) {
+      hipLaunchKernelGGL(k_fill_i32, dim3((unsigned)std::min<size_t>((L.hist_bins + 255) / 256, 4096)),
+                         dim3(256), 0, st, hist, (int64_t)L.hist_bins, 0);
+      h_ptr = hist;
+    }
+    hipLaunchKernelGGL(k_window_rstar, dim3(g.nb), dim3(256), 0, st, g, grp_tw[gi], grp_rmax[gi], rt, h_ptr);
+    hipLaunchKernelGGL(k_window_threshold, dim3(g.Hh), dim3(kScanThreads), 0, st, g, ht, gi, rt, hist,
+                       (int64_t)L.hist_bins, thr, flags);
+    hipLaunchKernelGGL(k_row_counts, dim3(g.nb, g.Hh), dim3(64), 0, st, g, ht, gi,
+                       (int)(any_topk && gi == 0), rt, thr, rowcnt);
+  }
+  if (n_groups == 0)
+    hipLaunchKernelGGL(k_row_counts, dim3(g.nb, g.Hh), dim3(64), 0, st, g, ht, -1, 1, rt, thr, rowcnt);
   const int64_t rows = (int64_t)g.B * g.Hh * g.nb;
-  hipLaunchKernelGGL(k_scan_rows, dim3(1), dim3(kScanThreads), 0, st, rowcnt, rows, row_ptr);
-  if (any_window)
-    hipLaunchKernelGGL(k_window_emit, dim3(g.nb, g.Hh), dim3(64), 0, st, g, ht, thr, row_ptr,
-                       col_idx, col_cap);
-  if (any_topk) {
-    int rpw = g.nb <= 512 ? 16 : g.nb <= 1024 ? 8 : g.nb <= 2048 ? 4 : g.nb <= 4096 ? 2 : 1;
-    int nbp2 = 1;
-    while (nbp2 < g.nb) nbp2 <<= 1;
-    const size_t tail = std::max<size_t>((size_t)64 * (g.D + 1) * 4, (size_t)nbp2 * 8 + (size_t)g.nb * 4);
-    const size_t lds = (size_t)rpw * g.D * 4 + (size_t)rpw * g.nb * 4 + tail;
-    dim3 grid((g.nb + rpw - 1) / rpw, g.B * g.Hh);
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&k_topk), hipFuncAttributeMaxDynamicSharedMemorySize,
-        160 * 1024);
-    if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL(k_topk, grid, dim3(256), lds, st, g, ht, psq, psk, rpw, nbp2, row_ptr,
+  hipLaunchKernelGGL(k_scan_rows, dim3(1), dim3(kScanThreads), 0, st, rowcnt, rows, row_ptr, ht, flags,
+                     info);
+  // emit: the last group's table is still current; the others are rebuilt
+  for (int gi = n_groups - 1; gi >= 0; --gi) {
+    if (gi != n_groups - 1)
+      hipLaunchKernelGGL(k_window_rstar, dim3(g.nb), dim3(256), 0, st, g, grp_tw[gi], grp_rmax[gi], rt,
+                         nullptr);
+    hipLaunchKernelGGL(k_window_emit, dim3(g.nb, g.Hh), dim3(64), 0, st, g, ht, gi, rt, thr, row_ptr,
                        col_idx, col_cap);
   }
+  if (any_topk) {
+    hipError_t e = g.D == 128 ? launch_topk<128>(g, ht, psq, psk, row_ptr, col_idx, col_cap, st)
+                              : launch_topk<64>(g, ht, psq, psk, row_ptr, col_idx, col_cap, st);
+    if (e != hipSuccess) return e;
+  }
   if (gate) hipLaunchKernelGGL(k_gate, dim3(g.B * g.Hh), dim3(256), 0, st, g, psq, w_g, gate);
-  if (info) hipLaunchKernelGGL(k_info, dim3(1), dim3(64), 0, st, flags, ht, info);
   return hipGetLastError();
 }
 
