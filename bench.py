@@ -34,9 +34,29 @@ if ROOT not in sys.path:
 
 METRIC = "dense-equiv TFLOP/s and ms/layer, hybrid sparse+linear attn at 90% sparsity"
 PEAK_BF16_TFLOPS = 2500.0
-# HBM bytes per dispatch of the attention kernel, from rocprofv3 FETCH_SIZE/WRITE_SIZE
-# runs on this kernel (see profiles/); None until measured for the current kernel.
-ATTN_TRAFFIC_BYTES = {}
+ATTN_SRC = os.path.join(ROOT, "block_sparse_linear_st_amd", "csrc", "attn_bf16.hip")
+# HBM bytes per dispatch of the attention kernel from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE runs (KiB per dispatch), valid only for the kernel source they were
+# taken on (sha256 prefix); scaled by a plain 512 MiB copy, which reads
+# FETCH_SIZE = 262156.7 KiB and WRITE_SIZE = 524288 KiB.
+ATTN_COUNTERS = {
+    "source_sha256": "5b7ee86d90d9414f",
+    "fetch_scale": 524288.0 / 262156.7,
+    "write_scale": 1.0,
+    "c3": {"fetch_kib": 168579.7, "write_kib": 98304.0},
+}
+
+
+def attn_traffic_bytes(config: str):
+    """Measured HBM bytes per attention launch, or None if not measured for this source."""
+    import hashlib
+    with open(ATTN_SRC, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()[:16]
+    rec = ATTN_COUNTERS.get(config)
+    if rec is None or sha != ATTN_COUNTERS["source_sha256"]:
+        return None
+    return round(1024.0 * (rec["fetch_kib"] * ATTN_COUNTERS["fetch_scale"] +
+                           rec["write_kib"] * ATTN_COUNTERS["write_scale"]))
 
 
 def parse():
@@ -207,7 +227,8 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": ATTN_TRAFFIC_BYTES.get(cfg.name),
+            "traffic": attn_traffic_bytes(cfg.name),
+            "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "algorithmic_flop_per_launch": kept_flop,
         },
         "cpu_baseline": None,
