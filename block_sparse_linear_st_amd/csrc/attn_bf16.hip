@@ -92,29 +92,73 @@ __device__ inline float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// s_waitcnt vmcnt(0) as a compiler-visible instruction (gfx9 encoding: vmcnt 0,
+// expcnt 7, lgkmcnt 15), so the compiler knows every vector load has landed.
+__device__ __attribute__((always_inline)) inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // One direct HBM -> LDS load: every lane's 16 bytes at gptr land at LDS byte
 // address m0_base + 16 * lane.  Written as inline asm so that the compiler,
 // which cannot tell the two LDS buffers apart, does not stall every LDS read
 // until this load lands; the kernel waits for it explicitly (vmcnt) before the
 // barrier that publishes the buffer.  The instruction has no register result.
-// s_waitcnt vmcnt(0) as a compiler-visible instruction (gfx9 encoding: vmcnt 0,
-// expcnt 7, lgkmcnt 15), so the compiler knows every vector load has landed.
-__device__ __attribute__((always_inline)) inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
+// M0 is set inside the asm; the compiler uses M0 nowhere in these kernels.
 __device__ __attribute__((always_inline)) inline void lds_dma16(const void* gptr, uint32_t m0_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(m0_base)
                : "memory", "m0");
 }
+// The same with a wave-uniform 64-bit base in SGPRs and a 32-bit lane offset.
+__device__ __attribute__((always_inline)) inline void lds_dma16_s(uint32_t voff, const void* sbase,
+                                                                  uint32_t m0_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0_base)
+               : "memory", "m0");
+}
+
+__device__ __attribute__((always_inline)) inline const __bf16* uniform_ptr(const __bf16* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return reinterpret_cast<const __bf16*>(((uint64_t)hi << 32) | lo);
+}
+
+// Per-lane byte offsets, inside a 64-key tile, of the 16-byte chunks this lane
+// loads (row r, logical chunk p ^ swizzle(r)); they do not depend on the tile.
+template <int D>
+struct DmaOffsets {
+  uint32_t k[Lay<D>::LOADS], v[Lay<D>::LOADS];
+  __device__ void init(int wave, int lane) {
+    using LY = Lay<D>;
+#pragma unroll
+    for (int i = 0; i < LY::LOADS; ++i) {
+      const int P = (wave * LY::LOADS + i) * 64 + lane;
+      const int r = P / LY::CPR, p = P % LY::CPR;
+      k[i] = (uint32_t)(r * LY::ROW_B + ((p ^ LY::kswz(r)) << 4));
+      v[i] = (uint32_t)(r * LY::ROW_B + ((p ^ LY::vswz(r)) << 4));
+    }
+  }
+};
 
 // Issue the loads of one 64-key K and V tile into the LDS buffer at byte
-// address `buf`.  Rows past the last valid token load row N-1 instead (always
-// in bounds, always finite); their scores are masked to -inf, so they
-// contribute exact zeros.
+// address `buf`.  Whole tiles use a uniform base plus the fixed lane offsets;
+// the tile that runs past the last valid token loads row N-1 in place of the
+// missing rows (always in bounds, always finite); their scores are masked to
+// -inf, so they contribute exact zeros.
 template <int D>
 __device__ __attribute__((always_inline)) inline void issue_tile(uint32_t buf, const __bf16* Kb,
                                                                  const __bf16* Vb, int key0, int N,
-                                                                 int wave, int lane) {
+                                                                 int wave, int lane,
+                                                                 const DmaOffsets<D>& off) {
   using LY = Lay<D>;
+  if (key0 + kTK <= N) {
+    const __bf16* kbase = uniform_ptr(Kb + (int64_t)key0 * D);
+    const __bf16* vbase = uniform_ptr(Vb + (int64_t)key0 * D);
+#pragma unroll
+    for (int i = 0; i < LY::LOADS; ++i) {
+      const uint32_t m0 = buf + (wave * LY::LOADS + i) * 1024;
+      lds_dma16_s(off.k[i], kbase, m0);
+      lds_dma16_s(off.v[i], vbase, m0 + LY::TILE_B);
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < LY::LOADS; ++i) {
     const int blk1k = wave * LY::LOADS + i;  // which 1 KiB of the tile this instruction fills
@@ -137,19 +181,29 @@ __device__ __attribute__((always_inline)) inline void compute_tile(const unsigne
   const unsigned char* Kt = buf;
   const unsigned char* Vt = buf + LY::TILE_B;
 
+  // S^T = K Q^T: two accumulator chains (key rows 0-31 and 32-63) interleaved,
+  // K fragments read two contraction steps ahead of their MFMA
   f32x16 s[2];
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
+  for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[kt][i] = 0.0f;
-    const int row = kt * 32 + l32;
-    const unsigned char* rp = Kt + row * LY::ROW_B;
-    const int sw = LY::kswz(row);
+  {
+    const unsigned char* rp0 = Kt + l32 * LY::ROW_B;
+    const unsigned char* rp1 = Kt + (32 + l32) * LY::ROW_B;
+    const int sw = LY::kswz(l32);  // equal for rows l32 and 32 + l32
+    auto kfrag = [&](const unsigned char* rp, int c) __attribute__((always_inline)) {
+      return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(rp + (((2 * c + g32) ^ sw) << 4)));
+    };
+    bf16x8 a0 = kfrag(rp0, 0), b0 = kfrag(rp1, 0);
+    bf16x8 a1 = kfrag(rp0, 1), b1 = kfrag(rp1, 1);
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      const bf16x8 kf = __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const uint4*>(rp + (((2 * c + g32) ^ sw) << 4)));
-      s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], s[kt], 0, 0, 0);
+      bf16x8 a2 = a1, b2 = b1;
+      if (c + 2 < NC) { a2 = kfrag(rp0, c + 2); b2 = kfrag(rp1, c + 2); }
+      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[c], s[0], 0, 0, 0);
+      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, qf[c], s[1], 0, 0, 0);
+      a0 = a1; b0 = b1; a1 = a2; b1 = b2;
     }
   }
   // mask padded keys (only the tile that holds token N-1 and beyond)
@@ -180,6 +234,9 @@ __device__ __attribute__((always_inline)) inline void compute_tile(const unsigne
     m_used = m_new;
   }
   const float neg_m = m_used == -INFINITY ? 0.0f : -m_used;
+  // P in bf16; the row sum adds the same rounded values the PV product uses
+  // (v_dot2 with (1, 1) sums a packed pair in fp32)
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   float rs = 0.0f;
   bf16x8 pf[4];
 #pragma unroll
@@ -188,13 +245,14 @@ __device__ __attribute__((always_inline)) inline void compute_tile(const unsigne
     for (int h = 0; h < 2; ++h) {
       float p[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        p[j] = __builtin_amdgcn_exp2f(fmaf(s[kt][h * 8 + j], c_log2, neg_m));
-        rs += p[j];
+      for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(fmaf(s[kt][h * 8 + j], c_log2, neg_m));
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        w[j] = pack_bf16x2(p[2 * j], p[2 * j + 1]);
+        rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[j]), ones, rs, false);
       }
-      const uint4 u = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                                 pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
-      pf[kt * 2 + h] = __builtin_bit_cast(bf16x8, u);
+      pf[kt * 2 + h] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
     }
   l_run += pair_sum(rs);
 
@@ -203,24 +261,35 @@ __device__ __attribute__((always_inline)) inline void compute_tile(const unsigne
   // channels t*32 + 16*(a%2) + 4*(s%4) .. +3; lane i of the group then holds
   // channel t*32 + 16*(a%2) + i of those 4 keys, which are the keys its P
   // fragment carries in slots 4h .. 4h+3.
+  // The NT output tiles are independent chains; the V fragments of the next
+  // 16-key step are read while the current step's MFMAs run.
   const int sl = lane & 15, dh = (lane >> 4) & 1;
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
+  const int inb = (sl & 1) * 8;
+  auto vfrag = [&](int t, int ks) __attribute__((always_inline)) {
     const int chunk = 4 * t + 2 * dh + ((sl & 3) >> 1);
-    const int inb = (sl & 1) * 8;
+    uint2 tr[2];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      uint2 tr[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int row = ks * 16 + 8 * h + 4 * g32 + (sl >> 2);
-        const unsigned char* ad = Vt + row * LY::ROW_B + ((chunk ^ LY::vswz(row)) << 4) + inb;
-        tr[h] = __builtin_bit_cast(
-            uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(ad)));
-      }
-      const uint4 u = make_uint4(tr[0].x, tr[0].y, tr[1].x, tr[1].y);
-      o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, u), pf[ks], o[t], 0, 0, 0);
+    for (int h = 0; h < 2; ++h) {
+      const int row = ks * 16 + 8 * h + 4 * g32 + (sl >> 2);
+      const unsigned char* ad = Vt + row * LY::ROW_B + ((chunk ^ LY::vswz(row)) << 4) + inb;
+      tr[h] = __builtin_bit_cast(
+          uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(ad)));
     }
+    return __builtin_bit_cast(bf16x8, make_uint4(tr[0].x, tr[0].y, tr[1].x, tr[1].y));
+  };
+  bf16x8 vf[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) vf[t] = vfrag(t, 0);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    bf16x8 vn[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) vn[t] = ks + 1 < 4 ? vfrag(t, ks + 1) : vf[t];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t], pf[ks], o[t], 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) vf[t] = vn[t];
   }
 }
 
@@ -298,7 +367,9 @@ k_attn_bf16(Geom g, AttnArgs a, int n_items, float c_log2) {
     // LDS byte address of the buffers (uniform); the wave index is uniform too
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    if (valid) issue_tile<D>(lds0, Kb, Vb, kb * BLK + sub * kTK, g.N, wave_u, lane);
+    DmaOffsets<D> doff;
+    doff.init(wave_u, lane);
+    if (valid) issue_tile<D>(lds0, Kb, Vb, kb * BLK + sub * kTK, g.N, wave_u, lane, doff);
     wait_vmem();
     __syncthreads();
     int cur = 0;
@@ -307,7 +378,8 @@ k_attn_bf16(Geom g, AttnArgs a, int n_items, float c_log2) {
       bool nvalid;
       advance(nkb, nsub, nflags, nvalid);
       if (nvalid)
-        issue_tile<D>(lds0 + (cur ^ 1) * LY::BUF_B, Kb, Vb, nkb * BLK + nsub * kTK, g.N, wave_u, lane);
+        issue_tile<D>(lds0 + (cur ^ 1) * LY::BUF_B, Kb, Vb, nkb * BLK + nsub * kTK, g.N, wave_u, lane,
+                      doff);
       if (wave_rows && ((flags >> qsub) & 1))
         compute_tile<D>(smem + cur * LY::BUF_B, qf, o, m_used, l_run, kb * BLK + sub * kTK, g.N,
                         c_log2, lane);
