@@ -38,12 +38,12 @@ ATTN_SRC = os.path.join(ROOT, "block_sparse_linear_st_amd", "csrc", "attn_bf16.h
 # HBM bytes per dispatch of the attention kernel from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE runs (KiB per dispatch), valid only for the kernel source they were
 # taken on (sha256 prefix); scaled by a plain 512 MiB copy, which reads
-# FETCH_SIZE = 262156.7 KiB and WRITE_SIZE = 524288 KiB.
+# FETCH_SIZE = 262157.8 KiB and WRITE_SIZE = 524288 KiB.
 ATTN_COUNTERS = {
-    "source_sha256": "5b7ee86d90d9414f",
-    "fetch_scale": 524288.0 / 262156.7,
+    "source_sha256": "89ed0cefb24f002b",
+    "fetch_scale": 524288.0 / 262157.8,
     "write_scale": 1.0,
-    "c3": {"fetch_kib": 168579.7, "write_kib": 98304.0},
+    "c3": {"fetch_kib": 165768.2, "write_kib": 98304.0},
 }
 
 
