@@ -162,7 +162,7 @@ def main():
         layer.build_mask(q, k, w_g, gate if from_q else None, stream=sp)
         if ev is not None:
             ev[1].record(stream)
-        S.salad_linear_prepare(layer.shape, k, v, gate, w, layer.ws, sp)
+        S.salad_linear_prepare(layer.shape, k, v, gate, w, layer.ws, sp, drop_tau=0.0)
         if ev is not None:
             ev[2].record(stream)
         S.salad_attn_apply(layer.shape, q, k, v, layer.row_ptr, layer.col_idx, gate, cfg.eps, 0.0, 0.0,

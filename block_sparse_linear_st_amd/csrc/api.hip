@@ -224,9 +224,9 @@ int salad_linear_state(const salad_shape* shape, const void* k, const void* v, f
   if (ws_bytes < L.bytes) return SALAD_ENOSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(ws);
-  hipError_t e = launch_linear_state(g, shape->dtype, k, v, w, L, s);
+  hipError_t e = launch_linear_state(g, shape->dtype, k, v, nullptr, 0.0f, w, L, s);
   if (e != hipSuccess) return SALAD_EHIP;
-  return hip_status(launch_linear_fold(g, shape->dtype, nullptr, nullptr, 2, S, z, w, L, s));
+  return hip_status(launch_linear_fold(g, shape->dtype, nullptr, nullptr, 2, 0.0f, S, z, w, L, s));
 }
 
 namespace {
@@ -251,20 +251,22 @@ hipError_t run_attn(const Geom& g, int dtype, const AttnArgs& a, hipStream_t s) 
 }  // namespace
 
 int salad_linear_prepare(const salad_shape* shape, const void* k, const void* v,
-                         const float* gate, const void* w_lin, void* ws, size_t ws_bytes,
-                         void* stream) {
+                         const float* gate, const void* w_lin, float drop_tau, void* ws,
+                         size_t ws_bytes, void* stream) {
   Geom g;
   const int st = shape_status(shape);
   if (st != SALAD_OK) return st;
   make_geom(shape, &g);
-  if (!k || !v || !gate || !w_lin || !ws || !aligned16(k) || !aligned16(v) || !aligned16(ws))
+  if (!k || !v || !gate || !w_lin || !ws || !aligned16(k) || !aligned16(v) || !aligned16(ws) ||
+      std::isnan(drop_tau))
     return SALAD_EINVAL;
   const Workspace L = plan_workspace(g, shape->dtype);
   if (ws_bytes < L.bytes) return SALAD_ENOSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(ws);
-  hipError_t e = launch_linear_state(g, shape->dtype, k, v, w, L, s);
-  if (e == hipSuccess) e = launch_linear_fold(g, shape->dtype, gate, w_lin, 0, nullptr, nullptr, w, L, s);
+  hipError_t e = launch_linear_state(g, shape->dtype, k, v, gate, drop_tau, w, L, s);
+  if (e == hipSuccess)
+    e = launch_linear_fold(g, shape->dtype, gate, w_lin, 0, drop_tau, nullptr, nullptr, w, L, s);
   return hip_status(e);
 }
 
@@ -303,7 +305,7 @@ int salad_attn_fwd(const salad_shape* shape, const void* q, const void* k, const
   if (!gate || !w_lin || !out || !aligned16(out) || !(eps >= 0.0f) || !std::isfinite(scale) ||
       std::isnan(drop_tau))
     return SALAD_EINVAL;
-  st = salad_linear_prepare(shape, k, v, gate, w_lin, ws, ws_bytes, stream);
+  st = salad_linear_prepare(shape, k, v, gate, w_lin, drop_tau, ws, ws_bytes, stream);
   if (st != SALAD_OK) return st;
   return salad_attn_apply(shape, q, k, v, row_ptr, col_idx, gate, eps, scale, drop_tau, out, ws,
                           ws_bytes, stream);
@@ -334,8 +336,9 @@ int salad_attn_fwd_branches(const salad_shape* shape, const void* q, const void*
     if (run_attn(g, shape->dtype, a, s) != hipSuccess) return SALAD_EHIP;
   }
   if (out_lin) {
-    hipError_t e = launch_linear_state(g, shape->dtype, k, v, w, L, s);
-    if (e == hipSuccess) e = launch_linear_fold(g, shape->dtype, nullptr, nullptr, 1, nullptr, nullptr, w, L, s);
+    hipError_t e = launch_linear_state(g, shape->dtype, k, v, nullptr, 0.0f, w, L, s);
+    if (e == hipSuccess)
+      e = launch_linear_fold(g, shape->dtype, nullptr, nullptr, 1, 0.0f, nullptr, nullptr, w, L, s);
     if (e != hipSuccess) return SALAD_EHIP;
     a.out = out_lin; a.has_sparse = 0; a.has_lin = 1;
     if (run_attn(g, shape->dtype, a, s) != hipSuccess) return SALAD_EHIP;

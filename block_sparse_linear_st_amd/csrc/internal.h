@@ -67,16 +67,19 @@ SALAD_HIDDEN hipError_t launch_gate_from_q(const Geom& g, int dtype, const void*
                                            const Workspace& L, hipStream_t st);
 
 // ---- linear state (linear.hip) ----------------------------------------------
+// Split partials of S and z.  With a gate, heads whose gate < drop_tau are
+// skipped (nothing written for them).
 SALAD_HIDDEN hipError_t launch_linear_state(const Geom& g, int dtype, const void* k,
-                                            const void* v, char* ws, const Workspace& L,
-                                            hipStream_t st);
+                                            const void* v, const float* gate, float drop_tau,
+                                            char* ws, const Workspace& L, hipStream_t st);
 // Reduce the split partials and fold.  mode 0: folded state g*S*W_lin (fused
-// forward); 1: S itself (linear branch alone); 2: reduce only.  S_out / z_out
-// (may be null) receive the fp32 state; z always lands in the workspace.
+// forward; heads with g < drop_tau skipped); 1: S itself (linear branch
+// alone); 2: reduce only.  S_out / z_out (may be null) receive the fp32
+// state; z always lands in the workspace.
 SALAD_HIDDEN hipError_t launch_linear_fold(const Geom& g, int dtype, const float* gate,
-                                           const void* w_lin, int mode, float* S_out,
-                                           float* z_out, char* ws, const Workspace& L,
-                                           hipStream_t st);
+                                           const void* w_lin, int mode, float drop_tau,
+                                           float* S_out, float* z_out, char* ws,
+                                           const Workspace& L, hipStream_t st);
 
 // ---- attention (attn_bf16.hip, attn_f32.hip) --------------------------------
 struct AttnArgs {

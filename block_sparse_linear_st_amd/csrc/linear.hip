@@ -92,8 +92,10 @@ __device__ __attribute__((always_inline)) inline bf16x8 tr_frag(const unsigned c
 template <int D>
 __global__ void __launch_bounds__(256, 2)
 k_lin_partial_bf16(Geom g, const __bf16* __restrict__ K, const __bf16* __restrict__ V, int chunk,
-                   float* __restrict__ spart, float* __restrict__ zpart) {
+                   float* __restrict__ spart, float* __restrict__ zpart, const float* __restrict__ gate,
+                   float drop_tau) {
   using LY = LinLay<D>;
+  if (gate != nullptr && gate[blockIdx.y] < drop_tau) return;  // dropped head: no linear state
   constexpr int TD = D / 32;           // 32-wide output tiles per dimension
   constexpr int TPW = TD * TD / 4;     // output tiles per wave
   __shared__ __align__(1024) unsigned char smem[2 * LY::BUF_B];
@@ -187,7 +189,9 @@ k_lin_partial_bf16(Geom g, const __bf16* __restrict__ K, const __bf16* __restric
 template <int D>
 __global__ void __launch_bounds__(256)
 k_lin_partial_f32(Geom g, const float* __restrict__ K, const float* __restrict__ V, int chunk,
-                  float* __restrict__ spart, float* __restrict__ zpart) {
+                  float* __restrict__ spart, float* __restrict__ zpart, const float* __restrict__ gate,
+                  float drop_tau) {
+  if (gate != nullptr && gate[blockIdx.y] < drop_tau) return;  // dropped head: no linear state
   constexpr int TT = 32;                 // tokens per LDS tile
   constexpr int COLS = D * D / 256;      // outputs per thread (one row segment)
   constexpr int SEGS = D / COLS;         // row segments
@@ -223,16 +227,18 @@ k_lin_partial_f32(Geom g, const float* __restrict__ K, const float* __restrict__
 }
 
 // grid (B*H, D/8), 256 threads: reduce 8 rows of S over the splits, in split
-// order, then fold.  mode 0: S'' = g*S*W; 1: S'' = S; 2: state only.
+// order, then fold.  mode 0: S'' = g*S*W; 1: S'' = S; 2: state only.  In mode
+// 0 heads with g < drop_tau are skipped (their partials were never written).
 template <typename WT, bool BF16OUT>
 __global__ void __launch_bounds__(256)
 k_lin_fold(Geom g, int splits, const float* __restrict__ spart, const float* __restrict__ zpart,
-           const float* __restrict__ gate, const WT* __restrict__ w, int mode,
+           const float* __restrict__ gate, const WT* __restrict__ w, int mode, float drop_tau,
            float* __restrict__ S_out, float* __restrict__ z_out, float* __restrict__ z_ws,
            void* __restrict__ sft_hi, void* __restrict__ sft_lo) {
   constexpr int FR = 8;
   __shared__ float Srows[FR][128];
   const int D = g.D, bh = blockIdx.x, r0 = blockIdx.y * FR, tid = threadIdx.x;
+  if (mode == 0 && gate[bh] < drop_tau) return;
   const int64_t BH = (int64_t)g.B * g.Hh;
   const int nvec = FR * D / 4;  // float4s in this row block (256 or 128)
   if (tid < nvec) {
@@ -294,8 +300,9 @@ k_lin_fold(Geom g, int splits, const float* __restrict__ spart, const float* __r
 
 }  // namespace
 
-hipError_t launch_linear_state(const Geom& g, int dtype, const void* k, const void* v, char* ws,
-                               const Workspace& L, hipStream_t st) {
+hipError_t launch_linear_state(const Geom& g, int dtype, const void* k, const void* v,
+                               const float* gate, float drop_tau, char* ws, const Workspace& L,
+                               hipStream_t st) {
   float* spart = reinterpret_cast<float*>(ws + L.off_spart);
   float* zpart = reinterpret_cast<float*>(ws + L.off_zpart);
   dim3 grid(L.lin_splits, g.B * g.Hh);
@@ -303,27 +310,27 @@ hipError_t launch_linear_state(const Geom& g, int dtype, const void* k, const vo
     if (g.D == 128)
       hipLaunchKernelGGL(k_lin_partial_bf16<128>, grid, dim3(256), 0, st, g,
                          static_cast<const __bf16*>(k), static_cast<const __bf16*>(v), L.lin_chunk,
-                         spart, zpart);
+                         spart, zpart, gate, drop_tau);
     else
       hipLaunchKernelGGL(k_lin_partial_bf16<64>, grid, dim3(256), 0, st, g,
                          static_cast<const __bf16*>(k), static_cast<const __bf16*>(v), L.lin_chunk,
-                         spart, zpart);
+                         spart, zpart, gate, drop_tau);
   } else {
     if (g.D == 128)
       hipLaunchKernelGGL(k_lin_partial_f32<128>, grid, dim3(256), 0, st, g,
                          static_cast<const float*>(k), static_cast<const float*>(v), L.lin_chunk,
-                         spart, zpart);
+                         spart, zpart, gate, drop_tau);
     else
       hipLaunchKernelGGL(k_lin_partial_f32<64>, grid, dim3(256), 0, st, g,
                          static_cast<const float*>(k), static_cast<const float*>(v), L.lin_chunk,
-                         spart, zpart);
+                         spart, zpart, gate, drop_tau);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_linear_fold(const Geom& g, int dtype, const float* gate, const void* w_lin,
-                              int mode, float* S_out, float* z_out, char* ws, const Workspace& L,
-                              hipStream_t st) {
+                              int mode, float drop_tau, float* S_out, float* z_out, char* ws,
+                              const Workspace& L, hipStream_t st) {
   const float* spart = reinterpret_cast<const float*>(ws + L.off_spart);
   const float* zpart = reinterpret_cast<const float*>(ws + L.off_zpart);
   float* z_ws = reinterpret_cast<float*>(ws + L.off_z);
@@ -332,11 +339,11 @@ hipError_t launch_linear_fold(const Geom& g, int dtype, const float* gate, const
   dim3 grid(g.B * g.Hh, g.D / 8);
   if (dtype == SALAD_BF16)
     hipLaunchKernelGGL((k_lin_fold<__bf16, true>), grid, dim3(256), 0, st, g, L.lin_splits, spart,
-                       zpart, gate, static_cast<const __bf16*>(w_lin), mode, S_out, z_out, z_ws,
+                       zpart, gate, static_cast<const __bf16*>(w_lin), mode, drop_tau, S_out, z_out, z_ws,
                        hi, lo);
   else
     hipLaunchKernelGGL((k_lin_fold<float, false>), grid, dim3(256), 0, st, g, L.lin_splits, spart,
-                       zpart, gate, static_cast<const float*>(w_lin), mode, S_out, z_out, z_ws, hi,
+                       zpart, gate, static_cast<const float*>(w_lin), mode, drop_tau, S_out, z_out, z_ws, hi,
                        lo);
   return hipGetLastError();
 }

@@ -63,7 +63,8 @@ _SIGS = {
     "salad_linear_state": (ctypes.c_int, [ctypes.POINTER(salad_shape), _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "salad_attn_fwd": (ctypes.c_int, [ctypes.POINTER(salad_shape), _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                       _f, _f, _f, _vp, _vp, _sz, _vp]),
-    "salad_linear_prepare": (ctypes.c_int, [ctypes.POINTER(salad_shape), _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "salad_linear_prepare": (ctypes.c_int, [ctypes.POINTER(salad_shape), _vp, _vp, _vp, _vp, ctypes.c_float,
+                                            _vp, _sz, _vp]),
     "salad_attn_apply": (ctypes.c_int, [ctypes.POINTER(salad_shape), _vp, _vp, _vp, _vp, _vp, _vp,
                                         _f, _f, _f, _vp, _vp, _sz, _vp]),
     "salad_attn_fwd_branches": (ctypes.c_int, [ctypes.POINTER(salad_shape), _vp, _vp, _vp, _vp, _vp,
@@ -182,9 +183,9 @@ def salad_attn_fwd_branches(shape, q, k, v, row_ptr, col_idx, eps, scale, out_sp
                                          ws.numel(), _stream(stream)), "salad_attn_fwd_branches")
 
 
-def salad_linear_prepare(shape, k, v, gate, w_lin, ws, stream=None):
-    _check(lib().salad_linear_prepare(ctypes.byref(shape), _p(k), _p(v), _p(gate), _p(w_lin), _p(ws),
-                                      ws.numel(), _stream(stream)), "salad_linear_prepare")
+def salad_linear_prepare(shape, k, v, gate, w_lin, ws, stream=None, drop_tau=0.0):
+    _check(lib().salad_linear_prepare(ctypes.byref(shape), _p(k), _p(v), _p(gate), _p(w_lin), drop_tau,
+                                      _p(ws), ws.numel(), _stream(stream)), "salad_linear_prepare")
 
 
 def salad_attn_apply(shape, q, k, v, row_ptr, col_idx, gate, eps, scale, drop_tau, out, ws, stream=None):

@@ -171,8 +171,8 @@ SALAD_API int salad_linear_state(const salad_shape* shape, const void* k, const 
  *   eps    > 0 keeps the ReLU normaliser finite
  *   scale  softmax scale; <= 0 selects 1/sqrt(head_dim)
  *   drop_tau  branch dropping ("SALAD" explainer, section 2.3): heads whose
- *          gate < drop_tau skip the linear branch entirely (out = o_s);
- *          pass 0 to keep every branch
+ *          gate < drop_tau skip the linear branch entirely: no linear state
+ *          is computed for them and out = o_s; pass 0 to keep every branch
  *   out    device, shape of q */
 SALAD_API int salad_attn_fwd(const salad_shape* shape, const void* q, const void* k, const void* v,
                    const int32_t* row_ptr, const int32_t* col_idx,
@@ -185,10 +185,14 @@ SALAD_API int salad_attn_fwd(const salad_shape* shape, const void* q, const void
  * projection folded in: S'' = gate[b,h] * S . w_lin.  salad_attn_apply then
  * runs the sparse branch and the linear epilogue in one kernel, reading that
  * folded state: its gate argument serves branch dropping only and must be the
- * gate given to salad_linear_prepare.  Between the two calls the workspace
- * must not be used by another call.  salad_attn_fwd == prepare + apply. */
+ * gate given to salad_linear_prepare.  Branch dropping ("SALAD" explainer,
+ * section 2.3) starts here: salad_linear_prepare computes no state for heads
+ * with gate < drop_tau (their workspace slots are left as they were), so
+ * salad_attn_apply must get a drop_tau at least as large.  Between the two
+ * calls the workspace must not be used by another call.  salad_attn_fwd ==
+ * prepare + apply with the same drop_tau. */
 SALAD_API int salad_linear_prepare(const salad_shape* shape, const void* k, const void* v,
-                                   const float* gate, const void* w_lin, void* ws,
+                                   const float* gate, const void* w_lin, float drop_tau, void* ws,
                                    size_t ws_bytes, void* stream);
 SALAD_API int salad_attn_apply(const salad_shape* shape, const void* q, const void* k,
                                const void* v, const int32_t* row_ptr, const int32_t* col_idx,

@@ -102,7 +102,8 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert L.salad_attn_fwd(ctypes.byref(sh), fake, fake, fake, fake, fake, fake, fake, -1.0, 0.0, 0.0, fake, fake, ws_bytes, None) == S.SALAD_EINVAL
     assert L.salad_attn_fwd(ctypes.byref(sh), fake, fake, fake, fake, fake, fake, fake, 1e-6, 0.0, 0.0, fake, fake, 1, None) == S.SALAD_ENOSPACE
     assert L.salad_attn_apply(ctypes.byref(sh), fake, fake, fake, fake, fake, None, 1e-6, 0.0, 0.0, fake, fake, ws_bytes, None) == S.SALAD_EINVAL
-    assert L.salad_linear_prepare(ctypes.byref(sh), fake, fake, None, fake, fake, ws_bytes, None) == S.SALAD_EINVAL
+    assert L.salad_linear_prepare(ctypes.byref(sh), fake, fake, None, fake, 0.0, fake, ws_bytes, None) == S.SALAD_EINVAL
+    assert L.salad_linear_prepare(ctypes.byref(sh), fake, fake, fake, fake, float("nan"), fake, ws_bytes, None) == S.SALAD_EINVAL
     assert L.salad_linear_state(ctypes.byref(sh), fake, None, fake, fake, fake, ws_bytes, None) == S.SALAD_EINVAL
     assert L.salad_gate_from_q(ctypes.byref(sh), fake, None, fake, fake, ws_bytes, None) == S.SALAD_EINVAL
     assert L.salad_attn_fwd_branches(ctypes.byref(_shape("c3", block=32)), fake, fake, fake, fake, fake, 1e-6, 0.0, fake, None, fake, ws_bytes, None) == S.SALAD_EUNSUPPORTED

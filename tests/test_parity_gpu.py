@@ -20,6 +20,8 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
+from block_sparse_linear_st_amd import salad as S  # noqa: E402
+
 
 def _gate_tensor(inp, cfg):
     if inp.gate is not None:
@@ -193,6 +195,30 @@ def test_branch_dropping():
             assert torch.equal(out[0, h], o_s[0, h]), h
         else:
             assert torch.equal(out[0, h], full[0, h]), h
+
+
+def test_branch_dropping_split_calls_skip_the_state():
+    """prepare + apply with drop_tau: no linear state is computed for dropped heads, so their workspace slots may
+    hold anything (here NaN bytes) without reaching the output; kept heads match the fused call bit for bit."""
+    cfg = CONFIGS["c2"]
+    inp = inputs("c2")
+    tau = float(np.median(inp.gate))
+    layer = make_layer(cfg, None)
+    q, k, v, w = device_tensors(inp, None)
+    layer.build_mask(q, k)
+    gate = _gate_tensor(inp, cfg)
+    layer.ws.fill_(0xFF)  # NaN in every fp32 / bf16 slot
+    S.salad_linear_prepare(layer.shape, k, v, gate, w, layer.ws, drop_tau=tau)
+    out = torch.empty_like(q)
+    S.salad_attn_apply(layer.shape, q, k, v, layer.row_ptr, layer.col_idx, gate, cfg.eps, 0.0, tau, out, layer.ws)
+    _, fused, o_s, _ = _forward("c2", drop_tau=tau)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out.float()).all())
+    for h in range(cfg.heads):
+        if inp.gate[h] < tau:
+            assert torch.equal(out[0, h], o_s[0, h]), h
+        else:
+            assert torch.equal(out[0, h], fused[0, h]), h
 
 
 # ------------------------------------------------------------------ large layers, sampled rows
