@@ -94,6 +94,7 @@ Workspace plan_workspace(const Geom& g, int dtype) {
   L.off_rowcnt = off; off = align_up(off + BH * nb * 4);
   L.off_psum_q = off; off = align_up(off + BH * nb * D * 4);
   L.off_psum_k = off; off = align_up(off + BH * nb * D * 4);
+  L.off_scores = off; off = align_up(off + (size_t)topk_heads_per_batch(g) * nb * nb * 4);
   L.mask_end = off;
   // linear state: about 512 workgroups in all, 64-token granularity
   int splits = (int)std::max<size_t>(1, (512 + BH - 1) / BH);

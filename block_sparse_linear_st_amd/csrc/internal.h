@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "salad.h"
 
 #define SALAD_HIDDEN __attribute__((visibility("hidden")))
@@ -45,6 +47,7 @@ struct Workspace {
   size_t off_flags;                // int32 [heads] infeasible flags
   size_t off_rowcnt;               // int32 [B*H*nb]
   size_t off_psum_q, off_psum_k;   // float [B*H*nb*D]
+  size_t off_scores;               // float [heads per batch][nb][nb] (top-k scores)
   // linear state
   int lin_splits, lin_chunk;
   size_t off_spart, off_zpart;     // float [splits][B*H][D*D], [splits][B*H][D]
@@ -65,6 +68,14 @@ SALAD_HIDDEN hipError_t launch_build_mask(const Geom& g, int dtype, const HeadTa
 SALAD_HIDDEN hipError_t launch_gate_from_q(const Geom& g, int dtype, const void* q,
                                            const float* w_g, float* gate, char* ws,
                                            const Workspace& L, hipStream_t st);
+
+// Heads whose top-k scores (nb x nb floats each) the workspace holds at once:
+// all of them up to 64 MiB of scores, at least one.
+inline int topk_heads_per_batch(const Geom& g) {
+  const int64_t per_head = (int64_t)g.nb * g.nb * 4;
+  const int64_t cap = ((int64_t)64 << 20) / per_head;
+  return (int)std::max<int64_t>(1, std::min<int64_t>((int64_t)g.B * g.Hh, cap));
+}
 
 // ---- linear state (linear.hip) ----------------------------------------------
 // Split partials of S and z.  With a gate, heads whose gate < drop_tau are

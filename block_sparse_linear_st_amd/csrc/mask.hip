@@ -350,106 +350,123 @@ __device__ inline uint32_t ordered_bits(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// grid (ceil(nb / R), B*H), 256 threads (4 waves): scores, top-k and emit for
-// R query blocks of one (b, h).  Dynamic LDS: pqT[D][R] | pkT[D][65] |
-// scores[R][nb] (transposed query means, one transposed 64-key-block tile with
-// a padded stride, the scores).  Scores: all waves share a tile, lane = key
-// block, wave w owns rows w*R/4 .. +R/4; each score is the sequential float32
-// sum over channels 0..D-1 of separately rounded products.  Selection: one
-// wave per row finds the k-th largest order-preserving 32-bit key by a bitwise
-// radix search whose counts are ballot popcounts over keys held in registers,
-// keeps every larger key and the first remaining equal keys in kb order, and
-// emits the kept kb's ascending.
-template <int D, int R, int MAXK>
-__global__ void __launch_bounds__(256)
-k_topk(Geom g, HeadTable ht, const float* __restrict__ pmean_q, const float* __restrict__ pmean_k,
-       const int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx, int64_t col_cap) {
-  // MAXK: key blocks per lane held in registers by the selection (nb <= 64 * MAXK)
-  constexpr int RW = R / 4;  // score rows per wave
-  constexpr int PKS = 65;    // pkT row stride (floats)
-  extern __shared__ __align__(16) float tk_smem[];
-  const int bh = blockIdx.y, h = bh % g.Hh, t = threadIdx.x, wave = t >> 6, lane = t & 63;
+// Scores of the pooled top-k rule for a batch of heads (bh0 ..): grid
+// (ceil(nb / 64) key tiles, ceil(nb / 128) row chunks, heads in the batch),
+// 256 threads.  Lane = key block: each lane holds its key block's D pooled
+// means in registers; each wave copies its 32 query blocks' means into its own
+// LDS rows and reads them back as broadcasts (every lane the same address), 8
+// rows at a time.  Each score is the sequential float32 sum over channels
+// 0..D-1 of separately rounded products (this file is compiled without FMA
+// contraction), the order the ranking is defined in.
+template <int D>
+__global__ void __launch_bounds__(256, 2)
+k_topk_scores(Geom g, HeadTable ht, const float* __restrict__ pmean_q, const float* __restrict__ pmean_k,
+              float* __restrict__ scores, int bh0) {
+  __shared__ __align__(16) float qrows[4][32 * D];
+  const int bh = bh0 + blockIdx.z, h = bh % g.Hh;
   if (ht.kind[h] != SALAD_MASK_TOPK) return;
-  const int nb = g.nb;
-  const int qb0 = blockIdx.x * R;
-  const int rows = min(R, nb - qb0);
-  float* pqT = tk_smem;
-  float* pkT = pqT + D * R;
-  float* scores = pkT + D * PKS;
-  for (int i = t; i < R * D; i += 256) {
-    const int r = i / D, c = i - r * D;
-    pqT[c * R + r] = r < rows ? pmean_q[((int64_t)bh * nb + qb0 + r) * D + c] : 0.0f;
+  const int nb = g.nb, t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int kb = blockIdx.x * 64 + lane;
+  const int qb0 = blockIdx.y * 128 + wave * 32;
+  const int rows = min(32, nb - qb0);  // may be <= 0 for the last chunk
+  float* ql = qrows[wave];
+  if (rows > 0) {
+    const float4* src = reinterpret_cast<const float4*>(pmean_q + ((int64_t)bh * nb + qb0) * D);
+    for (int i = lane; i < rows * D / 4; i += 64) reinterpret_cast<float4*>(ql)[i] = src[i];
   }
-  for (int kb0 = 0; kb0 < nb; kb0 += 64) {
-    __syncthreads();
-    for (int i = t; i < 64 * D; i += 256) {
-      const int kk = i / D, c = i - kk * D;
-      pkT[c * PKS + kk] = pmean_k[((int64_t)bh * nb + min(kb0 + kk, nb - 1)) * D + c];
-    }
-    __syncthreads();
-    float acc[RW];
+  float pkr[D];
+  {
+    const float4* src = reinterpret_cast<const float4*>(pmean_k + ((int64_t)bh * nb + min(kb, nb - 1)) * D);
 #pragma unroll
-    for (int j = 0; j < RW; ++j) acc[j] = 0.0f;
-#pragma unroll 8
-    for (int c = 0; c < D; ++c) {
-      const float kv = pkT[c * PKS + lane];
-      const float* qv = pqT + c * R + wave * RW;
-#pragma unroll
-      for (int j = 0; j < RW; ++j) {
-        const float prod = qv[j] * kv;
-        acc[j] = acc[j] + prod;
-      }
-    }
-    const int kb = kb0 + lane;
-    if (kb < nb) {
-#pragma unroll
-      for (int j = 0; j < RW; ++j)
-        if (wave * RW + j < rows) scores[(size_t)(wave * RW + j) * nb + kb] = acc[j];
+    for (int i = 0; i < D / 4; ++i) {
+      const float4 v = src[i];
+      pkr[4 * i] = v.x; pkr[4 * i + 1] = v.y; pkr[4 * i + 2] = v.z; pkr[4 * i + 3] = v.w;
     }
   }
   __syncthreads();
+  float* dst = scores + (int64_t)blockIdx.z * nb * nb;
+  for (int r0 = 0; r0 < rows; r0 += 8) {
+    float acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+#pragma unroll 4
+    for (int c4 = 0; c4 < D / 4; ++c4) {
+      float4 qv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        qv[j] = *reinterpret_cast<const float4*>(ql + min(r0 + j, rows - 1) * D + 4 * c4);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        acc[j] = acc[j] + qv[j].x * pkr[4 * c4];
+        acc[j] = acc[j] + qv[j].y * pkr[4 * c4 + 1];
+        acc[j] = acc[j] + qv[j].z * pkr[4 * c4 + 2];
+        acc[j] = acc[j] + qv[j].w * pkr[4 * c4 + 3];
+      }
+    }
+    if (kb < nb) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (r0 + j < rows) dst[(int64_t)(qb0 + r0 + j) * nb + kb] = acc[j];
+    }
+  }
+}
+
+// Top-k of each row of the scores of a batch of heads: grid (ceil(nb / 4),
+// heads in the batch), 256 threads, one wave per query block.  The wave finds
+// the k-th largest order-preserving 32-bit key by a bitwise radix search whose
+// counts are ballot popcounts over keys held in registers (MAXK per lane),
+// keeps every larger key and the first remaining equal keys in kb order, and
+// emits the kept kb's ascending.
+template <int MAXK>
+__global__ void __launch_bounds__(256)
+k_topk_select(Geom g, HeadTable ht, const float* __restrict__ scores, int bh0,
+              const int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx, int64_t col_cap) {
+  const int bh = bh0 + blockIdx.y, h = bh % g.Hh;
+  if (ht.kind[h] != SALAD_MASK_TOPK) return;
+  const int nb = g.nb, lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= nb) return;
+  const float* srow = scores + ((int64_t)blockIdx.y * nb + r) * nb;
   const int kkeep = ht.count[h];
   const int kpl = (nb + 63) / 64;
   const uint64_t lt = (1ull << lane) - 1ull;
-  for (int r = wave; r < rows; r += 4) {
-    const float* srow = scores + (size_t)r * nb;
-    uint32_t key[MAXK];
+  uint32_t key[MAXK];
 #pragma unroll
-    for (int m = 0; m < MAXK; ++m) {
-      if (m < kpl) {
-        const int kb = m * 64 + lane;
-        key[m] = kb < nb ? ordered_bits(srow[kb]) : 0u;  // real keys are never 0
-      }
+  for (int m = 0; m < MAXK; ++m) {
+    if (m < kpl) {
+      const int kb = m * 64 + lane;
+      key[m] = kb < nb ? ordered_bits(srow[kb]) : 0u;  // real keys are never 0
     }
-    uint32_t prefix = 0, bits = 0;
-    int krem = kkeep;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t bmask = bits | (1u << bit), cand = prefix | (1u << bit);
-      int cnt = 0;
+  }
+  uint32_t prefix = 0, bits = 0;
+  int krem = kkeep;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t bmask = bits | (1u << bit), cand = prefix | (1u << bit);
+    int cnt = 0;
 #pragma unroll
-      for (int m = 0; m < MAXK; ++m)
-        if (m < kpl) cnt += __popcll(__ballot((key[m] & bmask) == cand));
-      if (cnt >= krem) prefix = cand;
-      else krem -= cnt;
-      bits = bmask;
-    }
-    const int64_t base = row_ptr[(int64_t)bh * nb + qb0 + r];
-    int off = 0, eq_seen = 0;
+    for (int m = 0; m < MAXK; ++m)
+      if (m < kpl) cnt += __popcll(__ballot((key[m] & bmask) == cand));
+    if (cnt >= krem) prefix = cand;
+    else krem -= cnt;
+    bits = bmask;
+  }
+  const int64_t base = row_ptr[(int64_t)bh * nb + r];
+  int off = 0, eq_seen = 0;
 #pragma unroll
-    for (int m = 0; m < MAXK; ++m) {
-      if (m < kpl) {
-        const int kb = m * 64 + lane;
-        const bool eq = key[m] == prefix;
-        const uint64_t me = __ballot(eq);
-        const bool keep = key[m] > prefix || (eq && eq_seen + __popcll(me & lt) < krem);
-        eq_seen += __popcll(me);
-        const uint64_t mk = __ballot(keep);
-        if (keep) {
-          const int64_t pos = base + off + __popcll(mk & lt);
-          if (pos < col_cap) col_idx[pos] = kb;
-        }
-        off += __popcll(mk);
+  for (int m = 0; m < MAXK; ++m) {
+    if (m < kpl) {
+      const int kb = m * 64 + lane;
+      const bool eq = key[m] == prefix;
+      const uint64_t me = __ballot(eq);
+      const bool keep = key[m] > prefix || (eq && eq_seen + __popcll(me & lt) < krem);
+      eq_seen += __popcll(me);
+      const uint64_t mk = __ballot(keep);
+      if (keep) {
+        const int64_t pos = base + off + __popcll(mk & lt);
+        if (pos < col_cap) col_idx[pos] = kb;
       }
+      off += __popcll(mk);
     }
   }
 }
@@ -500,29 +517,35 @@ hipError_t launch_pool(const Geom& g, const HeadTable& ht, const void* q, const 
   return hipGetLastError();
 }
 
-template <int D, int R, int MAXK>
-hipError_t launch_topk_r(const Geom& g, const HeadTable& ht, const float* pq, const float* pk,
-                         const int32_t* row_ptr, int32_t* col_idx, int64_t col_cap, hipStream_t st) {
-  const size_t lds = ((size_t)R * D + (size_t)D * 65 + (size_t)R * g.nb) * 4;
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&k_topk<D, R, MAXK>), hipFuncAttributeMaxDynamicSharedMemorySize,
-      160 * 1024);
-  if (attr != hipSuccess) return attr;
-  dim3 grid((g.nb + R - 1) / R, g.B * g.Hh);
-  hipLaunchKernelGGL((k_topk<D, R, MAXK>), grid, dim3(256), lds, st, g, ht, pq, pk, row_ptr, col_idx,
+template <int MAXK>
+hipError_t launch_topk_select(const Geom& g, const HeadTable& ht, const float* scores, int bh0, int nbh,
+                              const int32_t* row_ptr, int32_t* col_idx, int64_t col_cap, hipStream_t st) {
+  dim3 grid((g.nb + 3) / 4, nbh);
+  hipLaunchKernelGGL(k_topk_select<MAXK>, grid, dim3(256), 0, st, g, ht, scores, bh0, row_ptr, col_idx,
                      col_cap);
   return hipGetLastError();
 }
 
-// rows per workgroup (R x nb scores stay within about 48 KiB of LDS) and keys
-// per lane in the selection, by the number of key blocks
+// Scores then selection, for as many heads at a time as the score buffer of
+// the workspace holds (topk_heads_per_batch heads).
 template <int D>
-hipError_t launch_topk(const Geom& g, const HeadTable& ht, const float* pq, const float* pk,
+hipError_t launch_topk(const Geom& g, const HeadTable& ht, const float* pq, const float* pk, float* scores,
                        const int32_t* row_ptr, int32_t* col_idx, int64_t col_cap, hipStream_t st) {
-  if (g.nb <= 512) return launch_topk_r<D, 16, 8>(g, ht, pq, pk, row_ptr, col_idx, col_cap, st);
-  if (g.nb <= 768) return launch_topk_r<D, 16, 12>(g, ht, pq, pk, row_ptr, col_idx, col_cap, st);
-  if (g.nb <= 1536) return launch_topk_r<D, 8, 24>(g, ht, pq, pk, row_ptr, col_idx, col_cap, st);
-  return launch_topk_r<D, 4, 64>(g, ht, pq, pk, row_ptr, col_idx, col_cap, st);
+  const int BH = g.B * g.Hh;
+  const int per = topk_heads_per_batch(g);
+  for (int bh0 = 0; bh0 < BH; bh0 += per) {
+    const int nbh = std::min(per, BH - bh0);
+    dim3 grid((g.nb + 63) / 64, (g.nb + 127) / 128, nbh);
+    hipLaunchKernelGGL(k_topk_scores<D>, grid, dim3(256), 0, st, g, ht, pq, pk, scores, bh0);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (g.nb <= 512) e = launch_topk_select<8>(g, ht, scores, bh0, nbh, row_ptr, col_idx, col_cap, st);
+    else if (g.nb <= 1024) e = launch_topk_select<16>(g, ht, scores, bh0, nbh, row_ptr, col_idx, col_cap, st);
+    else if (g.nb <= 2048) e = launch_topk_select<32>(g, ht, scores, bh0, nbh, row_ptr, col_idx, col_cap, st);
+    else e = launch_topk_select<64>(g, ht, scores, bh0, nbh, row_ptr, col_idx, col_cap, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace
@@ -598,8 +621,9 @@ hipError_t launch_build_mask(const Geom& g, int dtype, const HeadTable& ht0, con
                        col_idx, col_cap);
   }
   if (any_topk) {
-    hipError_t e = g.D == 128 ? launch_topk<128>(g, ht, psq, psk, row_ptr, col_idx, col_cap, st)
-                              : launch_topk<64>(g, ht, psq, psk, row_ptr, col_idx, col_cap, st);
+    float* scores = reinterpret_cast<float*>(ws + L.off_scores);
+    hipError_t e = g.D == 128 ? launch_topk<128>(g, ht, psq, psk, scores, row_ptr, col_idx, col_cap, st)
+                              : launch_topk<64>(g, ht, psq, psk, scores, row_ptr, col_idx, col_cap, st);
     if (e != hipSuccess) return e;
   }
   if (gate) hipLaunchKernelGGL(k_gate, dim3(g.B * g.Hh), dim3(256), 0, st, g, psq, w_g, gate);
