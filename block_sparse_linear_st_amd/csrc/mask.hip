@@ -351,62 +351,67 @@ __device__ inline uint32_t ordered_bits(float s) {
 }
 
 // Scores of the pooled top-k rule for a batch of heads (bh0 ..): grid
-// (ceil(nb / 64) key tiles, ceil(nb / 128) row chunks, heads in the batch),
-// 256 threads.  Lane = key block: each lane holds its key block's D pooled
-// means in registers; each wave copies its 32 query blocks' means into its own
-// LDS rows and reads them back as broadcasts (every lane the same address), 8
-// rows at a time.  Each score is the sequential float32 sum over channels
-// 0..D-1 of separately rounded products (this file is compiled without FMA
+// (ceil(nb / 64) key tiles, ceil(nb / 64) row chunks, heads in the batch),
+// 256 threads.  Lane = key block: the tile's 64 key blocks' pooled means sit in
+// LDS rows of D + 1 floats (lane l reads row l, channel c: bank (l + c) % 32,
+// no conflicts); each wave copies its 16 query blocks' means into its own LDS
+// rows and reads them as broadcasts (every lane the same address), 4 rows at a
+// time.  Each score is the sequential float32 sum over channels 0..D-1 of
+// separately rounded products (this file is compiled without FMA
 // contraction), the order the ranking is defined in.
 template <int D>
 __global__ void __launch_bounds__(256, 2)
 k_topk_scores(Geom g, HeadTable ht, const float* __restrict__ pmean_q, const float* __restrict__ pmean_k,
               float* __restrict__ scores, int bh0) {
-  __shared__ __align__(16) float qrows[4][32 * D];
+  constexpr int KS = D + 1;  // key row stride in LDS (floats)
+  constexpr int QR = 16;     // query blocks per wave
+  constexpr int RG = 4;      // rows in flight per lane
+  __shared__ __align__(16) float keys[64 * KS];
+  __shared__ __align__(16) float qrows[4][QR * D];
   const int bh = bh0 + blockIdx.z, h = bh % g.Hh;
   if (ht.kind[h] != SALAD_MASK_TOPK) return;
   const int nb = g.nb, t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int kb = blockIdx.x * 64 + lane;
-  const int qb0 = blockIdx.y * 128 + wave * 32;
-  const int rows = min(32, nb - qb0);  // may be <= 0 for the last chunk
+  const int kb0 = blockIdx.x * 64, kb = kb0 + lane;
+  const int qb0 = blockIdx.y * 64 + wave * QR;
+  const int rows = min(QR, nb - qb0);  // may be <= 0 for the last chunk
+#pragma unroll
+  for (int i = t; i < 64 * D / 4; i += 256) {  // 16-byte loads, issued together
+    const int kk = i / (D / 4), c = (i - kk * (D / 4)) * 4;
+    const float4 v = *reinterpret_cast<const float4*>(pmean_k + ((int64_t)bh * nb + min(kb0 + kk, nb - 1)) * D + c);
+    float* d = keys + kk * KS + c;
+    d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+  }
   float* ql = qrows[wave];
   if (rows > 0) {
     const float4* src = reinterpret_cast<const float4*>(pmean_q + ((int64_t)bh * nb + qb0) * D);
     for (int i = lane; i < rows * D / 4; i += 64) reinterpret_cast<float4*>(ql)[i] = src[i];
   }
-  float pkr[D];
-  {
-    const float4* src = reinterpret_cast<const float4*>(pmean_k + ((int64_t)bh * nb + min(kb, nb - 1)) * D);
-#pragma unroll
-    for (int i = 0; i < D / 4; ++i) {
-      const float4 v = src[i];
-      pkr[4 * i] = v.x; pkr[4 * i + 1] = v.y; pkr[4 * i + 2] = v.z; pkr[4 * i + 3] = v.w;
-    }
-  }
   __syncthreads();
+  const float* kr = keys + lane * KS;
   float* dst = scores + (int64_t)blockIdx.z * nb * nb;
-  for (int r0 = 0; r0 < rows; r0 += 8) {
-    float acc[8];
+  for (int r0 = 0; r0 < rows; r0 += RG) {
+    float acc[RG];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
-#pragma unroll 4
+    for (int j = 0; j < RG; ++j) acc[j] = 0.0f;
+    const float* qr[RG];
+#pragma unroll
+    for (int j = 0; j < RG; ++j) qr[j] = ql + min(r0 + j, rows - 1) * D;
+#pragma unroll 8
     for (int c4 = 0; c4 < D / 4; ++c4) {
-      float4 qv[8];
+      const float k0 = kr[4 * c4], k1 = kr[4 * c4 + 1], k2 = kr[4 * c4 + 2], k3 = kr[4 * c4 + 3];
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        qv[j] = *reinterpret_cast<const float4*>(ql + min(r0 + j, rows - 1) * D + 4 * c4);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        acc[j] = acc[j] + qv[j].x * pkr[4 * c4];
-        acc[j] = acc[j] + qv[j].y * pkr[4 * c4 + 1];
-        acc[j] = acc[j] + qv[j].z * pkr[4 * c4 + 2];
-        acc[j] = acc[j] + qv[j].w * pkr[4 * c4 + 3];
+      for (int j = 0; j < RG; ++j) {
+        const float4 q = *reinterpret_cast<const float4*>(qr[j] + 4 * c4);
+        acc[j] = acc[j] + q.x * k0;
+        acc[j] = acc[j] + q.y * k1;
+        acc[j] = acc[j] + q.z * k2;
+        acc[j] = acc[j] + q.w * k3;
       }
     }
     if (kb < nb) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
+      for (int j = 0; j < RG; ++j)
         if (r0 + j < rows) dst[(int64_t)(qb0 + r0 + j) * nb + kb] = acc[j];
     }
   }
@@ -535,7 +540,7 @@ hipError_t launch_topk(const Geom& g, const HeadTable& ht, const float* pq, cons
   const int per = topk_heads_per_batch(g);
   for (int bh0 = 0; bh0 < BH; bh0 += per) {
     const int nbh = std::min(per, BH - bh0);
-    dim3 grid((g.nb + 63) / 64, (g.nb + 127) / 128, nbh);
+    dim3 grid((g.nb + 63) / 64, (g.nb + 63) / 64, nbh);
     hipLaunchKernelGGL(k_topk_scores<D>, grid, dim3(256), 0, st, g, ht, pq, pk, scores, bh0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
