@@ -226,8 +226,8 @@ k_lin_partial_f32(Geom g, const float* __restrict__ K, const float* __restrict__
   if (c0 == 0) zpart[((int64_t)split * g.B * g.Hh + bh) * D + r] = zacc;
 }
 
-// grid (B*H, D/8), 256 threads: reduce 8 rows of S over the splits, in split
-// order, then fold.  mode 0: S'' = g*S*W; 1: S'' = S; 2: state only.  In mode
+// grid (B*H, D/2), 256 threads: reduce 2 rows of S over the splits (in
+// ordered parts), then fold.  mode 0: S'' = g*S*W; 1: S'' = S; 2: state only.  In mode
 // 0 heads with g < drop_tau are skipped (their partials were never written).
 template <typename WT, bool BF16OUT>
 __global__ void __launch_bounds__(256)
@@ -235,44 +235,75 @@ k_lin_fold(Geom g, int splits, const float* __restrict__ spart, const float* __r
            const float* __restrict__ gate, const WT* __restrict__ w, int mode, float drop_tau,
            float* __restrict__ S_out, float* __restrict__ z_out, float* __restrict__ z_ws,
            void* __restrict__ sft_hi, void* __restrict__ sft_lo) {
-  constexpr int FR = 8;
+  constexpr int FR = 2;  // rows of S per workgroup
   __shared__ float Srows[FR][128];
+  __shared__ float4 parts[256];
+  __shared__ WT Ws[128 * 128];  // W_lin, staged once per workgroup (mode 0)
   const int D = g.D, bh = blockIdx.x, r0 = blockIdx.y * FR, tid = threadIdx.x;
   if (mode == 0 && gate[bh] < drop_tau) return;
   const int64_t BH = (int64_t)g.B * g.Hh;
-  const int nvec = FR * D / 4;  // float4s in this row block (256 or 128)
-  if (tid < nvec) {
-    const int e = tid * 4;  // element offset inside the row block
+  const int nvec = FR * D / 4;  // float4s in this row block (64 or 32)
+  const int np = 256 / nvec;    // threads per float4 (4 or 8)
+  // np threads per float4: part p sums splits [p * len, (p + 1) * len) in
+  // split order with loads batched 8 deep; the parts then add in part order
+  // (a fixed order, so S is reproducible)
+  const int v = tid % nvec, part = tid / nvec;
+  const int len = (splits + np - 1) / np;
+  const int s0 = min(splits, part * len), s1 = min(splits, s0 + len);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  {
+    const int e = v * 4;  // element offset inside the row block
     const float* src = spart + (int64_t)bh * D * D + (int64_t)r0 * D + e;
     const int64_t stride = BH * D * D;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    int sp = 0;
-    for (; sp + 8 <= splits; sp += 8) {
-      float4 v[8];
+    int sp = s0;
+    for (; sp + 8 <= s1; sp += 8) {
+      float4 x[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const float4*>(src + (sp + u) * stride);
+      for (int u = 0; u < 8; ++u) x[u] = *reinterpret_cast<const float4*>(src + (sp + u) * stride);
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        acc.x += v[u].x; acc.y += v[u].y; acc.z += v[u].z; acc.w += v[u].w;
+        acc.x += x[u].x; acc.y += x[u].y; acc.z += x[u].z; acc.w += x[u].w;
       }
     }
-    for (; sp < splits; ++sp) {
-      const float4 v = *reinterpret_cast<const float4*>(src + sp * stride);
-      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    for (; sp < s1; ++sp) {
+      const float4 x = *reinterpret_cast<const float4*>(src + sp * stride);
+      acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
     }
-    const int rr = e / D, c = e % D;
+    parts[tid] = acc;
+  }
+  __syncthreads();
+  if (part == 0) {
+    for (int p = 1; p < np; ++p) {
+      const float4 b = parts[p * nvec + v];
+      acc.x += b.x; acc.y += b.y; acc.z += b.z; acc.w += b.w;
+    }
+    const int e = v * 4, rr = e / D, c = e % D;
     Srows[rr][c] = acc.x; Srows[rr][c + 1] = acc.y; Srows[rr][c + 2] = acc.z; Srows[rr][c + 3] = acc.w;
     if (S_out) *reinterpret_cast<float4*>(S_out + (int64_t)bh * D * D + (int64_t)r0 * D + e) = acc;
   }
   if (blockIdx.y == 0) {
     for (int c = tid; c < D; c += 256) {
+      // the same split order as above, loads batched 8 deep
+      const float* zp = zpart + (int64_t)bh * D + c;
+      const int64_t zstride = BH * D;
       float s = 0.0f;
-      for (int sp = 0; sp < splits; ++sp) s += zpart[((int64_t)sp * BH + bh) * D + c];
+      int sp = 0;
+      for (; sp + 8 <= splits; sp += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = zp[(sp + u) * zstride];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s += v[u];
+      }
+      for (; sp < splits; ++sp) s += zp[sp * zstride];
       z_ws[(int64_t)bh * D + c] = s;
       if (z_out) z_out[(int64_t)bh * D + c] = s;
     }
   }
   if (mode == 2) return;
+  if (mode == 0) {
+    for (int i = tid; i < D * D; i += 256) Ws[i] = w[i];
+  }
   __syncthreads();
   const float gv = mode == 0 ? gate[bh] : 1.0f;
   // S''[r0+rr][j] for column j, stored transposed at [j][r0+rr]
@@ -281,7 +312,7 @@ k_lin_fold(Geom g, int splits, const float* __restrict__ spart, const float* __r
     float v;
     if (mode == 0) {
       float s = 0.0f;
-      for (int kk = 0; kk < D; ++kk) s = fmaf(Srows[rr][kk], (float)w[kk * D + j], s);
+      for (int kk = 0; kk < D; ++kk) s = fmaf(Srows[rr][kk], (float)Ws[kk * D + j], s);
       v = gv * s;
     } else {
       v = Srows[rr][j];
@@ -336,7 +367,7 @@ hipError_t launch_linear_fold(const Geom& g, int dtype, const float* gate, const
   float* z_ws = reinterpret_cast<float*>(ws + L.off_z);
   void* hi = ws + L.off_sft_hi;
   void* lo = ws + L.off_sft_lo;
-  dim3 grid(g.B * g.Hh, g.D / 8);
+  dim3 grid(g.B * g.Hh, g.D / 2);
   if (dtype == SALAD_BF16)
     hipLaunchKernelGGL((k_lin_fold<__bf16, true>), grid, dim3(256), 0, st, g, L.lin_splits, spart,
                        zpart, gate, static_cast<const __bf16*>(w_lin), mode, drop_tau, S_out, z_out, z_ws,
