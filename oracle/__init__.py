@@ -51,6 +51,8 @@ from .masks import (
     keep_from_csr,
     pooled_means_f32,
     pooled_scores_f32,
+    sics_block_scores_f32,
+    sics_select,
     topk_count,
     topk_select,
     window_count,

@@ -1,4 +1,4 @@
-"""Oracle block masks: static spatio-temporal window and pooled-score top-k.
+"""Oracle block masks: static spatio-temporal window, pooled-score top-k and SICS.
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
@@ -32,6 +32,22 @@ Top-k (per head: density rho)
   forced.  Fixing the float32 order of operations makes the ranking, and hence
   the CSR, exactly reproducible.
 
+SICS (per head: density rho; the SPADE explainer's scheme generation, "Der
+sofortige Entscheidungsträger": blocks whose tokens agree, measured by the sum
+of intra-block cosine similarities, are the ones attention goes to)
+  For key block b, SICS(b) = sum over token pairs i, j of b (valid tokens
+  only) of cos(k_i, k_j) = || sum_i k_i / |k_i| ||^2, in a fixed float32
+  order: |k_i|^2 = sequential float32 sum over c of fl32(k[i,c]^2); a zero
+  vector contributes nothing, else khat[i,c] = fl32(k[i,c] / fl32(sqrt(|k_i|^2)))
+  (correctly rounded square root and division); s[c] = sequential float32 sum
+  over the block's tokens, in order, of khat[i,c]; SICS = sequential float32
+  sum over c of fl32(s[c]^2).  No fused multiply-add anywhere.  Per (b, h) the
+  m = max(1, floor(rho * nb + 0.5)) key blocks with the highest SICS are kept
+  (ties to the lower key block) for every query block, and each query block
+  also keeps its own (diagonal) block, so a row holds m or m + 1 blocks.  The
+  pages give the score's name and purpose only; this plain reading scores key
+  blocks and shares the selection across the query blocks of a head.
+
 Gate from Q (the stand-in for the input-aware scale s of explainer section 2.2)
   g = sigmoid(mean over valid tokens of Q[b, h, n, :] . w_g), in fp64.
 
@@ -50,6 +66,7 @@ RSTAR_INF = 1 << 30
 
 WINDOW = 0
 TOPK = 1
+SICS = 2
 
 
 class InfeasibleMask(ValueError):
@@ -210,6 +227,51 @@ def topk_select(scores: np.ndarray, density: float) -> np.ndarray:
     return keep
 
 
+# ---------------------------------------------------------------- SICS selection
+
+def sics_block_scores_f32(k: np.ndarray, N: int, block: int) -> np.ndarray:
+    """SICS of every key block in the canonical float32 order (module docstring).
+
+    k: float32 [B, H, n_pad, d] -> float32 [B, H, nb].
+    """
+    k = np.asarray(k, dtype=np.float32)
+    B, Hh, n_pad, d = k.shape
+    nb = n_pad // block
+    n2 = np.zeros((B, Hh, n_pad), dtype=np.float32)
+    for c in range(d):
+        n2 = n2 + k[..., c] * k[..., c]
+    r = np.sqrt(n2)
+    zero = n2 == 0
+    safe_r = np.where(zero, np.float32(1), r)
+    khat = np.where(zero[..., None], np.float32(0), k / safe_r[..., None]).astype(np.float32)
+    kb = khat.reshape(B, Hh, nb, block, d)
+    last_valid = N - (nb - 1) * block
+    acc = np.zeros((B, Hh, nb, d), dtype=np.float32)
+    for o in range(block):
+        if o < last_valid:
+            acc = acc + kb[:, :, :, o, :]
+        else:
+            acc[:, :, :-1] = acc[:, :, :-1] + kb[:, :, :-1, o, :]
+    sics = np.zeros((B, Hh, nb), dtype=np.float32)
+    for c in range(d):
+        sics = sics + acc[..., c] * acc[..., c]
+    return sics
+
+
+def sics_select(scores: np.ndarray, density: float) -> np.ndarray:
+    """keep[q, k] for one head: the top-m key blocks by SICS (ties to the lower block) plus the diagonal.
+
+    scores: float32 [nb] -> bool [nb, nb].
+    """
+    nb = scores.shape[-1]
+    m = topk_count(density, nb)
+    top = np.zeros(nb, dtype=bool)
+    top[np.argsort(-scores, kind="stable")[:m]] = True
+    keep = np.repeat(top[None, :], nb, axis=0)
+    keep[np.arange(nb), np.arange(nb)] = True
+    return keep
+
+
 # ---------------------------------------------------------------- gate
 
 def gate_from_q(q: np.ndarray, w_g: np.ndarray, N: int) -> np.ndarray:
@@ -248,6 +310,7 @@ def build_masks(T: int, H: int, W: int, block: int, specs: Iterable, batch: int,
     keep = np.zeros((batch, len(specs), nb, nb), dtype=bool)
     rstar_cache = {}
     pooled = None
+    sics = None
     for h, sp in enumerate(specs):
         if sp.kind == WINDOW:
             if sp.t_window not in rstar_cache:
@@ -259,6 +322,11 @@ def build_masks(T: int, H: int, W: int, block: int, specs: Iterable, batch: int,
                 pooled = (pooled_means_f32(q, N, block), pooled_means_f32(k, N, block))
             scores = pooled_scores_f32(pooled[0][:, h], pooled[1][:, h])
             keep[:, h] = topk_select(scores, sp.density)
+        elif sp.kind == SICS:
+            if sics is None:
+                sics = sics_block_scores_f32(k, N, block)
+            for b in range(batch):
+                keep[b, h] = sics_select(sics[b, h], sp.density)
         else:
             raise ValueError(f"unknown mask kind {sp.kind}")
     return keep

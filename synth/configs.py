@@ -1,4 +1,4 @@
-"""The five layer workloads (c1..c5) as plain parameters.
+"""The layer workloads (c1..c7) as plain parameters.
 
 c1  tiny CPU-checkable layer, fp32, 2 heads, d=64, grid 4x8x8, 64-token blocks,
     window of +-1 frame keeping every candidate block pair.
@@ -10,6 +10,10 @@ c4  large-DiT dynamic layer, bf16, 40 heads, d=128, same grid, pooled-score
 c5  long-video layer, bf16, 12 heads, d=128, grid 41x45x80 (147600 tokens
     padded to 147712), 128-token blocks, per-head density U(3%, 10%); heads 0-5
     use a +-2-frame window, heads 6-11 a pooled-score top-k.
+
+c6  small bf16 layer with SICS heads (top key blocks by the sum of intra-block
+    cosine similarities, 10%, plus the diagonal), c2's shape.
+c7  c3's shape (21x30x52, 12 heads, d=128) with SICS heads at 10%.
 
 The per-head densities of c5 are drawn here (stream 8 of the config's seed) so
 that every consumer sees the same mask specification.
@@ -24,13 +28,15 @@ import numpy as np
 
 WINDOW = 0
 TOPK = 1
+SICS = 2
 
 
 @dataclass(frozen=True)
 class HeadSpec:
     """Mask request for one head.
 
-    kind      WINDOW (static spatio-temporal window) or TOPK (pooled-score top-k)
+    kind      WINDOW (static spatio-temporal window), TOPK (pooled-score top-k) or SICS
+              (top key blocks by the sum of intra-block cosine similarities)
     t_window  window heads: keep token pairs at most this many frames apart
     r_max     window heads: cap on the spatial (Chebyshev) block distance, -1 = none
     density   fraction of block pairs to keep; <= 0 keeps every window candidate
@@ -114,6 +120,16 @@ def _build() -> dict:
         dtype="bf16", specs=specs5, gate_kind="uniform",
         description="long-video bf16 layer, 12 heads, d=128, 41x45x80 grid (147600 tokens), "
                     "128-token blocks, per-head density U(3%,10%), heads 0-5 window, 6-11 top-k")
+    cfgs["c6"] = LayerConfig(
+        name="c6", seed=6, batch=1, heads=12, head_dim=64, T=8, H=16, W=16, block=64,
+        dtype="bf16", specs=tuple(HeadSpec(SICS, 0, -1, 0.10) for _ in range(12)),
+        gate_kind="uniform",
+        description="small bf16 layer, 12 heads, d=64, 8x16x16 grid, SICS key blocks at 10% + diagonal")
+    cfgs["c7"] = LayerConfig(
+        name="c7", seed=7, batch=1, heads=12, head_dim=128, T=21, H=30, W=52, block=64,
+        dtype="bf16", specs=tuple(HeadSpec(SICS, 0, -1, 0.10) for _ in range(12)),
+        gate_kind="uniform",
+        description="bf16 layer, 12 heads, d=128, 21x30x52 grid (32760 tokens), SICS key blocks at 10% + diagonal")
     return cfgs
 
 

@@ -305,3 +305,105 @@ def test_build_masks_mixed_heads_c5_like_small():
     pk = om.pooled_means_f32(k, N, block)
     for b in range(2):
         np.testing.assert_array_equal(keep[b, 1], om.topk_select(_python_scores(pq[b, 1], pk[b, 1]), 0.25))
+
+
+# ------------------------------------------------------------ SICS
+
+def _sics_case_k(case):
+    k = np.asarray(case["k"], dtype=np.float32)
+    return k[None, None]  # [B=1, H=1, n_pad, d]
+
+
+@pytest.mark.parametrize("case", _load("sics_hand_cases.json")["cases"], ids=lambda c: c["name"])
+def test_sics_hand_cases(case):
+    s = om.sics_block_scores_f32(_sics_case_k(case), case["N"], case["block"])[0, 0]
+    assert s.tolist() == [float(x) for x in case["sics"]]
+    keep = om.sics_select(s, case["density"])
+    assert _rows(keep) == case["rows"]
+
+
+def _pairwise_cosine_sum(kblock):
+    """Sum over all token pairs of cos(k_i, k_j), fp64, pair by pair (zero vectors contribute 0)."""
+    kb = np.asarray(kblock, dtype=np.float64)
+    tot = 0.0
+    for a in kb:
+        na = math.sqrt(float(a @ a))
+        for b in kb:
+            nb_ = math.sqrt(float(b @ b))
+            if na > 0 and nb_ > 0:
+                tot += float(a @ b) / (na * nb_)
+    return tot
+
+
+@pytest.mark.parametrize("N,block,d", [(12, 4, 8), (10, 4, 8), (7, 3, 5)])
+def test_sics_equals_pairwise_cosine_sum(N, block, d):
+    rng = np.random.default_rng(1234 + N)
+    nb = -(-N // block)
+    k = rng.standard_normal((1, 2, nb * block, d)).astype(np.float32)
+    k[:, :, N:] = 1e4  # padding must not count
+    s = om.sics_block_scores_f32(k, N, block)
+    for h in range(2):
+        for b in range(nb):
+            toks = k[0, h, b * block:min((b + 1) * block, N)]
+            ref = _pairwise_cosine_sum(toks)
+            n = toks.shape[0]
+            assert abs(float(s[0, h, b]) - ref) <= 1e-5 * n * n, (h, b, float(s[0, h, b]), ref)
+
+
+def test_sics_closed_forms():
+    d, n = 16, 8
+    rng = np.random.default_rng(7)
+    v = rng.standard_normal(d).astype(np.float32)
+    scales = rng.uniform(0.5, 4.0, size=n).astype(np.float32)
+    parallel = (scales[:, None] * v[None, :]).astype(np.float32)
+    ortho = np.eye(d, dtype=np.float32)[:n] * np.float32(3.0)
+    opposite = np.stack([v, -2 * v] * (n // 2)).astype(np.float32)
+    k = np.concatenate([parallel, ortho, opposite])[None, None]
+    s = om.sics_block_scores_f32(k, 3 * n, n)[0, 0]
+    assert abs(s[0] - n * n) <= 1e-4 * n * n  # all agree: n^2
+    assert s[1] == n  # orthonormal directions: only the n self-pairs
+    assert abs(s[2]) <= 1e-5  # pairs cancel: 0
+
+
+def test_sics_select_structure_and_ties():
+    rng = np.random.default_rng(3)
+    scores = rng.integers(0, 5, size=40).astype(np.float32)  # many ties
+    for density in (0.05, 0.1, 0.3, 1.0):
+        keep = om.sics_select(scores, density)
+        m = om.topk_count(density, 40)
+        top = sorted(range(40), key=lambda j: (-scores[j], j))[:m]
+        for q in range(40):
+            expect = sorted(set(top) | {q})
+            assert np.nonzero(keep[q])[0].tolist() == expect
+    # -0 ranks like +0
+    z = np.array([0.0, -0.0, 1.0, -0.0], dtype=np.float32)
+    assert om.sics_select(z, 0.5)[3].tolist() == [True, False, True, True]
+
+
+def test_sics_planted_mistakes_are_caught():
+    case = _load("sics_hand_cases.json")["cases"][0]
+    k = _sics_case_k(case)
+    # forgetting the normalisation (sum of raw dot products) breaks the hand values
+    raw = np.asarray(k[0, 0], dtype=np.float64).reshape(3, 2, 2).sum(axis=1)
+    assert ((raw ** 2).sum(axis=1)).tolist() != case["sics"]
+    # summing cosines over distinct pairs only (no self pairs) breaks them too
+    s = om.sics_block_scores_f32(k, case["N"], case["block"])[0, 0]
+    assert (s - 2).tolist() != case["sics"]
+
+
+def test_build_masks_sics_heads():
+    specs = [HeadSpec(2, 0, -1, 0.1), HeadSpec(0, 1, -1, 0.1), HeadSpec(2, 0, -1, 0.25)]
+    rng = np.random.default_rng(11)
+    T, H, W, block = 4, 8, 8, 32
+    N = T * H * W
+    k = rng.standard_normal((2, 3, N, 16)).astype(np.float32)
+    q = rng.standard_normal((2, 3, N, 16)).astype(np.float32)
+    keep = om.build_masks(T, H, W, block, specs, 2, q, k)
+    s = om.sics_block_scores_f32(k, N, block)
+    for b in range(2):
+        for h in (0, 2):
+            assert np.array_equal(keep[b, h], om.sics_select(s[b, h], specs[h].density))
+        # diagonal always kept, every row m or m + 1 blocks
+        m = om.topk_count(0.1, N // block)
+        counts = keep[b, 0].sum(axis=1)
+        assert set(counts.tolist()) <= {m, m + 1} and keep[b, 0].diagonal().all()
