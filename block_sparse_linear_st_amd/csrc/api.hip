@@ -41,8 +41,8 @@ int spec_status(const salad_shape* s, const salad_mask_spec* specs) {
     const salad_mask_spec& sp = specs[h];
     if (sp.kind == SALAD_MASK_WINDOW) {
       if (sp.t_window < 0) return SALAD_EINVAL;
-    } else if (sp.kind == SALAD_MASK_TOPK) {
-      if (nb > 4096) return SALAD_EUNSUPPORTED;  // top-k keeps 4 rows of scores in LDS
+    } else if (sp.kind == SALAD_MASK_TOPK || sp.kind == SALAD_MASK_SICS) {
+      if (nb > 4096) return SALAD_EUNSUPPORTED;  // the selection holds a row's nb keys in one wave
     } else {
       return SALAD_EINVAL;
     }
@@ -95,6 +95,8 @@ Workspace plan_workspace(const Geom& g, int dtype) {
   L.off_psum_q = off; off = align_up(off + BH * nb * D * 4);
   L.off_psum_k = off; off = align_up(off + BH * nb * D * 4);
   L.off_scores = off; off = align_up(off + (size_t)topk_heads_per_batch(g) * nb * nb * 4);
+  L.off_sics = off;   off = align_up(off + BH * nb * 4);
+  L.off_sics_pack = off; off = align_up(off + BH * nb * 4);
   L.mask_end = off;
   // linear state: about 512 workgroups in all, 64-token granularity
   int splits = (int)std::max<size_t>(1, (512 + BH - 1) / BH);
@@ -149,8 +151,10 @@ int64_t salad_mask_nnz_max(const salad_shape* shape, const salad_mask_spec* spec
     if (sp.kind == SALAD_MASK_WINDOW) {
       const int64_t K = window_count(sp.density, nb);
       per = K < 0 ? nb * nb : std::min(K, nb * nb);
-    } else {
+    } else if (sp.kind == SALAD_MASK_TOPK) {
       per = topk_count(sp.density, nb) * nb;
+    } else {  // SICS: m kept blocks plus the diagonal when it is not among them
+      per = std::min<int64_t>(topk_count(sp.density, nb) + 1, nb) * nb;
     }
     total += per * shape->batch;
   }
@@ -173,13 +177,16 @@ int salad_build_mask(const salad_shape* shape, const salad_mask_spec* specs, con
   make_geom(shape, &g);
   st = spec_status(shape, specs);
   if (st != SALAD_OK) return st;
-  bool any_topk = false;
-  for (int h = 0; h < g.Hh; ++h) any_topk |= specs[h].kind == SALAD_MASK_TOPK;
+  bool any_topk = false, any_k = false;
+  for (int h = 0; h < g.Hh; ++h) {
+    any_topk |= specs[h].kind == SALAD_MASK_TOPK;
+    any_k |= specs[h].kind != SALAD_MASK_WINDOW;
+  }
   if ((w_g == nullptr) != (gate == nullptr)) return SALAD_EINVAL;
   const bool want_gate = gate != nullptr;
   if (!row_ptr || !col_idx || !ws) return SALAD_EINVAL;
   if ((any_topk || want_gate) && (!q || !aligned16(q))) return SALAD_EINVAL;
-  if (any_topk && (!k || !aligned16(k))) return SALAD_EINVAL;
+  if (any_k && (!k || !aligned16(k))) return SALAD_EINVAL;
   if (!aligned16(ws)) return SALAD_EINVAL;
   const Workspace L = plan_workspace(g, shape->dtype);
   if (ws_bytes < L.bytes) return SALAD_ENOSPACE;

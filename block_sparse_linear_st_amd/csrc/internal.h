@@ -48,6 +48,7 @@ struct Workspace {
   size_t off_rowcnt;               // int32 [B*H*nb]
   size_t off_psum_q, off_psum_k;   // float [B*H*nb*D]
   size_t off_scores;               // float [heads per batch][nb][nb] (top-k scores)
+  size_t off_sics, off_sics_pack;  // float / int32 [B*H*nb] (SICS scores, selection)
   // linear state
   int lin_splits, lin_chunk;
   size_t off_spart, off_zpart;     // float [splits][B*H][D*D], [splits][B*H][D]

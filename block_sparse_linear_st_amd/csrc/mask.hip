@@ -215,9 +215,11 @@ k_row_counts(Geom g, HeadTable ht, int grp, int topk, const uint16_t* rt, const 
     for (int kb = lane; kb < g.nb; kb += 64) local += window_keep(rt, g, qb, kb, th) ? 1 : 0;
     for (int off = 32; off > 0; off >>= 1) local += __shfl_xor(local, off);
     cnt = local;
-  } else {
+  } else if (ht.kind[h] == SALAD_MASK_TOPK) {
     if (!topk) return;
     cnt = ht.count[h];
+  } else {
+    return;  // SICS heads: k_sics_counts
   }
   if (lane == 0)
     for (int b = 0; b < g.B; ++b) rowcnt[((int64_t)b * g.Hh + h) * g.nb + qb] = cnt;
@@ -476,6 +478,172 @@ k_topk_select(Geom g, HeadTable ht, const float* __restrict__ scores, int bh0,
   }
 }
 
+// ---- SICS block mask ("SPADE" explainer, scheme generation: blocks whose
+// tokens agree, by the sum of intra-block cosine similarities, get attention).
+// SICS(b) = sum over valid token pairs of b of cos(k_i, k_j) = || sum_i
+// k_i / |k_i| ||^2, in a fixed float32 order (no FMA: this file is compiled
+// without contraction): |k_i|^2 sequential over channels; a zero vector
+// contributes 0, else khat = k / sqrt(|k|^2) with a correctly rounded square
+// root and division; s[c] sequential over the block's tokens in order; SICS =
+// sum over channels of s[c]^2, sequential.  Per (b, h) the m =
+// max(1, floor(rho * nb + 0.5)) highest blocks (ties to the lower kb) are
+// kept for every query block, plus the query block's own block.
+
+// grid (nb, B*H), 256 threads: SICS of one key block of a SICS head.
+template <typename T, int D, int BLK>
+__global__ void __launch_bounds__(256)
+k_sics_scores(Geom g, HeadTable ht, const T* __restrict__ K, float* __restrict__ sics) {
+  __shared__ float kl[BLK][D + 1];
+  __shared__ float rn[BLK];
+  __shared__ float sacc[D];
+  const int kb = blockIdx.x, bh = blockIdx.y, h = bh % g.Hh, t = threadIdx.x;
+  if (ht.kind[h] != SALAD_MASK_SICS) return;
+  const int n0 = kb * BLK, nv = min(BLK, g.N - n0);  // valid tokens, >= 1
+  const T* src = K + ((int64_t)bh * g.n_pad + n0) * D;
+  // 16-byte loads (all in flight before the LDS stores), converted to float
+  constexpr int VE = 16 / sizeof(T);               // elements per 16-byte load
+  constexpr int PER = (BLK * D / VE + 255) / 256;  // loads per thread
+  uint4 buf[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int i = (u * 256 + t) * VE;
+    if (i < nv * D) buf[u] = *reinterpret_cast<const uint4*>(src + i);
+  }
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int i = (u * 256 + t) * VE;
+    if (i < nv * D) {
+      const int r = i / D, c = i - r * D;
+      const T* e = reinterpret_cast<const T*>(&buf[u]);
+#pragma unroll
+      for (int j = 0; j < VE; ++j) kl[r][c + j] = (float)e[j];
+    }
+  }
+  __syncthreads();
+  if (t < nv) {
+    float n2 = 0.0f;
+#pragma unroll  // the reads run ahead of the (ordered) additions
+    for (int c = 0; c < D; ++c) n2 = n2 + kl[t][c] * kl[t][c];
+    rn[t] = n2 == 0.0f ? 0.0f : __fsqrt_rn(n2);
+  }
+  __syncthreads();
+  // unit keys in place, every element independently (all threads)
+  for (int i = t; i < nv * D; i += 256) {
+    const int r = i / D, c = i - r * D;
+    const float rr = rn[r];
+    kl[r][c] = rr == 0.0f ? 0.0f : __fdiv_rn(kl[r][c], rr);
+  }
+  __syncthreads();
+  if (t < D) {
+    float sc = 0.0f;
+    if (nv == BLK) {
+#pragma unroll
+      for (int i = 0; i < BLK; ++i) sc = sc + kl[i][t];
+    } else {
+      for (int i = 0; i < nv; ++i) sc = sc + kl[i][t];
+    }
+    sacc[t] = sc;
+  }
+  __syncthreads();
+  if (t == 0) {
+    float tot = 0.0f;
+#pragma unroll
+    for (int c = 0; c < D; ++c) tot = tot + sacc[c] * sacc[c];
+    sics[(int64_t)bh * g.nb + kb] = tot;
+  }
+}
+
+// grid (B*H), one wave: the m highest SICS blocks of a head (radix select on
+// order-preserving keys, ties to the lower kb).  pack[bh][kb] = 2 * (number
+// of kept blocks below kb) + (kb kept).
+template <int MAXK>
+__global__ void __launch_bounds__(64)
+k_sics_select(Geom g, HeadTable ht, const float* __restrict__ sics, int32_t* __restrict__ pack) {
+  const int bh = blockIdx.x, h = bh % g.Hh, lane = threadIdx.x;
+  if (ht.kind[h] != SALAD_MASK_SICS) return;
+  const int nb = g.nb, kpl = (nb + 63) / 64;
+  const float* srow = sics + (int64_t)bh * nb;
+  const uint64_t lt = (1ull << lane) - 1ull;
+  uint32_t key[MAXK];
+#pragma unroll
+  for (int m = 0; m < MAXK; ++m) {
+    if (m < kpl) {
+      const int kb = m * 64 + lane;
+      key[m] = kb < nb ? ordered_bits(srow[kb]) : 0u;  // real keys are never 0
+    }
+  }
+  uint32_t prefix = 0, bits = 0;
+  int krem = ht.count[h];
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t bmask = bits | (1u << bit), cand = prefix | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int m = 0; m < MAXK; ++m)
+      if (m < kpl) cnt += __popcll(__ballot((key[m] & bmask) == cand));
+    if (cnt >= krem) prefix = cand;
+    else krem -= cnt;
+    bits = bmask;
+  }
+  int running = 0, eq_seen = 0;
+#pragma unroll
+  for (int m = 0; m < MAXK; ++m) {
+    if (m < kpl) {
+      const int kb = m * 64 + lane;
+      const bool eq = key[m] == prefix;
+      const uint64_t me = __ballot(eq);
+      const bool keep = key[m] > prefix || (eq && eq_seen + __popcll(me & lt) < krem);
+      eq_seen += __popcll(me);
+      const uint64_t mk = __ballot(keep);
+      if (kb < nb) pack[(int64_t)bh * nb + kb] = 2 * (running + __popcll(mk & lt)) + (keep ? 1 : 0);
+      running += __popcll(mk);
+    }
+  }
+}
+
+// grid ceil(B*H*nb / 256): row counts of the SICS heads, m or m + 1.
+__global__ void __launch_bounds__(256)
+k_sics_counts(Geom g, HeadTable ht, const int32_t* __restrict__ pack, int32_t* __restrict__ rowcnt) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)g.B * g.Hh * g.nb) return;
+  const int h = (int)((i / g.nb) % g.Hh);
+  if (ht.kind[h] != SALAD_MASK_SICS) return;
+  rowcnt[i] = ht.count[h] + ((pack[i] & 1) ? 0 : 1);
+}
+
+// grid (nb, B*H), one wave: row qb of a SICS head = the kept blocks with qb
+// merged in, ascending.
+__global__ void __launch_bounds__(64)
+k_sics_emit(Geom g, HeadTable ht, const int32_t* __restrict__ pack, const int32_t* __restrict__ row_ptr,
+            int32_t* __restrict__ col_idx, int64_t col_cap) {
+  const int qb = blockIdx.x, bh = blockIdx.y, h = bh % g.Hh, lane = threadIdx.x;
+  if (ht.kind[h] != SALAD_MASK_SICS) return;
+  const int nb = g.nb;
+  const int32_t* pr = pack + (int64_t)bh * nb;
+  const int64_t base = row_ptr[(int64_t)bh * nb + qb];
+  const bool qkept = pr[qb] & 1;
+  for (int kb = lane; kb < nb; kb += 64) {
+    const int v = pr[kb];
+    if ((v & 1) || kb == qb) {
+      const int64_t pos = base + (v >> 1) + ((!qkept && kb > qb) ? 1 : 0);
+      if (pos < col_cap) col_idx[pos] = kb;
+    }
+  }
+}
+
+template <typename T>
+hipError_t launch_sics_scores(const Geom& g, const HeadTable& ht, const void* k, float* sics, hipStream_t st) {
+  dim3 grid(g.nb, g.B * g.Hh);
+  const T* K = static_cast<const T*>(k);
+  if (g.D == 128) {
+    if (g.blk == 64) hipLaunchKernelGGL((k_sics_scores<T, 128, 64>), grid, dim3(256), 0, st, g, ht, K, sics);
+    else hipLaunchKernelGGL((k_sics_scores<T, 128, 128>), grid, dim3(256), 0, st, g, ht, K, sics);
+  } else {
+    if (g.blk == 64) hipLaunchKernelGGL((k_sics_scores<T, 64, 64>), grid, dim3(256), 0, st, g, ht, K, sics);
+    else hipLaunchKernelGGL((k_sics_scores<T, 64, 128>), grid, dim3(256), 0, st, g, ht, K, sics);
+  }
+  return hipGetLastError();
+}
+
 // grid (B*H), 256 threads: gate = sigmoid(mean(Q) . w_g) from the block means,
 // each weighted by its valid-token count.  Thread t accumulates channel t % D
 // over every (256/D)-th block, in order, in fp64; the partial sums then
@@ -560,7 +728,7 @@ hipError_t launch_build_mask(const Geom& g, int dtype, const HeadTable& ht0, con
                              int32_t* info, const float* w_g, float* gate, char* ws,
                              const Workspace& L, hipStream_t st) {
   HeadTable ht = ht0;
-  bool any_topk = false;
+  bool any_topk = false, any_sics = false;
   // window heads sharing (t_window, r_max) share one r* table and histogram
   int n_groups = 0;
   int grp_tw[SALAD_MAX_HEADS], grp_rmax[SALAD_MAX_HEADS];
@@ -579,9 +747,11 @@ hipError_t launch_build_mask(const Geom& g, int dtype, const HeadTable& ht0, con
       }
       ht.group[h] = gi;
       if (ht.count[h] >= 0) grp_ranked[gi] = true;
-    } else {
+    } else if (ht.kind[h] == SALAD_MASK_TOPK) {
       any_topk = true;
       ht.pool[h] = 3;
+    } else {
+      any_sics = true;
     }
     if (gate) ht.pool[h] |= 1;
   }
@@ -615,8 +785,25 @@ hipError_t launch_build_mask(const Geom& g, int dtype, const HeadTable& ht0, con
   if (n_groups == 0)
     hipLaunchKernelGGL(k_row_counts, dim3(g.nb, g.Hh), dim3(64), 0, st, g, ht, -1, 1, rt, thr, rowcnt);
   const int64_t rows = (int64_t)g.B * g.Hh * g.nb;
+  float* sics = reinterpret_cast<float*>(ws + L.off_sics);
+  int32_t* pack = reinterpret_cast<int32_t*>(ws + L.off_sics_pack);
+  if (any_sics) {
+    hipError_t e = dtype == SALAD_BF16 ? launch_sics_scores<__bf16>(g, ht, k, sics, st)
+                                       : launch_sics_scores<float>(g, ht, k, sics, st);
+    if (e != hipSuccess) return e;
+    const dim3 sg(g.B * g.Hh);
+    if (g.nb <= 512) hipLaunchKernelGGL(k_sics_select<8>, sg, dim3(64), 0, st, g, ht, sics, pack);
+    else if (g.nb <= 1024) hipLaunchKernelGGL(k_sics_select<16>, sg, dim3(64), 0, st, g, ht, sics, pack);
+    else if (g.nb <= 2048) hipLaunchKernelGGL(k_sics_select<32>, sg, dim3(64), 0, st, g, ht, sics, pack);
+    else hipLaunchKernelGGL(k_sics_select<64>, sg, dim3(64), 0, st, g, ht, sics, pack);
+    hipLaunchKernelGGL(k_sics_counts, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, g, ht, pack,
+                       rowcnt);
+  }
   hipLaunchKernelGGL(k_scan_rows, dim3(1), dim3(kScanThreads), 0, st, rowcnt, rows, row_ptr, ht, flags,
                      info);
+  if (any_sics)
+    hipLaunchKernelGGL(k_sics_emit, dim3(g.nb, g.B * g.Hh), dim3(64), 0, st, g, ht, pack, row_ptr, col_idx,
+                       col_cap);
   // emit: the last group's table is still current; the others are rebuilt
   for (int gi = n_groups - 1; gi >= 0; --gi) {
     if (gi != n_groups - 1)

@@ -28,6 +28,7 @@ SALAD_F32 = 0
 SALAD_BF16 = 1
 SALAD_MASK_WINDOW = 0
 SALAD_MASK_TOPK = 1
+SALAD_MASK_SICS = 2
 
 
 class SaladError(RuntimeError):

@@ -65,7 +65,7 @@ typedef enum {
 
 typedef enum { SALAD_F32 = 0, SALAD_BF16 = 1 } salad_dtype;
 
-typedef enum { SALAD_MASK_WINDOW = 0, SALAD_MASK_TOPK = 1 } salad_mask_kind;
+typedef enum { SALAD_MASK_WINDOW = 0, SALAD_MASK_TOPK = 1, SALAD_MASK_SICS = 2 } salad_mask_kind;
 
 /* Layer shape.  Requirements: batch, heads >= 1; heads <= SALAD_MAX_HEADS;
  * head_dim in {64, 128}; T, H, W >= 1; block in {64, 128};
@@ -92,7 +92,17 @@ typedef struct {
  *   (sequential float32 sum in token order, then one division); score(qb, kb) =
  *   sequential float32 sum over channels of separately rounded products
  *   pq[c]*pk[c]; each query block keeps the k = max(1, floor(density*nb + 0.5))
- *   highest (capped at nb), ties to the lower kb.  t_window, r_max unused. */
+ *   highest (capped at nb), ties to the lower kb.  t_window, r_max unused.
+ * SALAD_MASK_SICS - key blocks scored by the sum of intra-block cosine
+ *   similarities ("SPADE" explainer, scheme generation, "Der sofortige
+ *   Entscheidungsträger"): SICS(kb) = sum over valid token pairs i, j of kb of
+ *   cos(k_i, k_j) = || sum_i k_i / |k_i| ||^2 in a fixed float32 order (|k|^2
+ *   sequential over channels; zero vectors contribute nothing; correctly
+ *   rounded sqrt and division; block sum sequential over tokens; squared norm
+ *   sequential over channels; no fused multiply-add).  Per (b, h) the m =
+ *   max(1, floor(density*nb + 0.5)) highest blocks (ties to the lower kb) are
+ *   kept for every query block, plus each query block's own block: m or m + 1
+ *   per row.  t_window, r_max unused. */
 typedef struct {
   int32_t kind;     /* salad_mask_kind */
   int32_t t_window; /* window: +- frames */
@@ -108,7 +118,7 @@ SALAD_API const char* salad_status_str(int status);
 
 /* Upper bound on the number of col_idx entries salad_build_mask writes for this
  * shape and these specs (exact unless a window head has density <= 0, where the
- * bound is nb*nb per (b, h)).  Pure host function.  Negative salad_status on
+ * bound is nb*nb per (b, h), or a head is SICS, bounded by (m + 1) * nb).  Pure host function.  Negative salad_status on
  * invalid arguments. */
 SALAD_API int64_t salad_mask_nnz_max(const salad_shape* shape, const salad_mask_spec* specs);
 
@@ -121,8 +131,8 @@ SALAD_API size_t salad_workspace_bytes(const salad_shape* shape);
 /* Build the CSR block mask for every (b, h) from the per-head specs.
  *   specs    host array [heads]
  *   q, k     device tensors; q is read when some head is SALAD_MASK_TOPK or a
- *            gate is requested, k when some head is SALAD_MASK_TOPK (either may
- *            be NULL when not read)
+ *            gate is requested, k when some head is SALAD_MASK_TOPK or
+ *            SALAD_MASK_SICS (either may be NULL when not read)
  *   row_ptr  device int32 [batch*heads*nb + 1], written
  *   col_idx  device int32 [col_cap], written in [0, row_ptr[last])
  *   col_cap  must be >= salad_mask_nnz_max(shape, specs), else SALAD_ENOSPACE

@@ -117,3 +117,22 @@ def test_binding_refuses_host_tensors():
     t = torch.zeros(4)
     with pytest.raises(S.SaladError):
         S.salad_linear_state(sh, t, t, t, t, t)
+
+
+def test_sics_specs():
+    """SICS heads: the bound is (m + 1) * nb per (b, h); K is required; nb above 4096 is not built."""
+    c = CONFIGS["c7"]
+    sh = _shape("c7")
+    specs = S.make_specs(c.specs)
+    from oracle import masks as om
+    m = om.topk_count(c.specs[0].density, c.nb)
+    assert S.salad_mask_nnz_max(sh, specs) == c.batch * c.heads * (m + 1) * c.nb
+    L = S.lib()
+    fake = ctypes.c_void_p(0x1000)
+    ws_bytes = S.salad_workspace_bytes(sh)
+    # k missing for a SICS head
+    assert L.salad_build_mask(ctypes.byref(sh), specs, fake, None, fake, fake, 10 ** 7, None, None, None, fake,
+                              ws_bytes, None) == S.SALAD_EINVAL
+    big = S.make_shape(1, 1, 128, 1, 1, 64 * 4097, 64, S.SALAD_BF16)
+    one = S.make_specs([c.specs[0]])
+    assert S.lib().salad_mask_nnz_max(ctypes.byref(big), one) == S.SALAD_EUNSUPPORTED

@@ -46,7 +46,7 @@ def _run_mask(name, layer=None, q=None, k=None, want_gate=False):
 
 # ------------------------------------------------------------------ masks
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5", "c6", "c7"])
 def test_mask_csr_bit_exact(name):
     print(f"mask parity {name}", flush=True)
     layer, _ = _run_mask(name)
@@ -56,6 +56,37 @@ def test_mask_csr_bit_exact(name):
     got_ci = layer.col_idx[:rp[-1]].cpu().numpy()
     np.testing.assert_array_equal(got_ci, ci)
     assert int(layer.info.item()) == 0
+
+
+def test_sics_mask_forward_c6():
+    """A layer whose heads use the SICS mask: full forward against the oracle on the oracle's CSR."""
+    cfg = CONFIGS["c6"]
+    inp = inputs("c6")
+    _, out, o_s, _ = _forward("c6")
+    rp, ci = oracle_csr("c6")
+    ref, ref_s, _ = oracle.layer_forward(inp.q, inp.k, inp.v, rp, ci, inp.gate, inp.w_lin, cfg.N, cfg.block, cfg.eps)
+    assert_close(to_numpy(out), ref, BF16_MAX_ABS, BF16_REL_L2, "c6 out bf16 (SICS mask)")
+    assert_close(to_numpy(o_s), ref_s, BF16_MAX_ABS, BF16_REL_L2, "c6 sparse bf16 (SICS mask)")
+
+
+def test_sics_rows_hold_m_or_m_plus_one_with_diagonal():
+    cfg = CONFIGS["c7"]
+    layer, _ = _run_mask("c7")
+    rp = layer.row_ptr.cpu().numpy().astype(np.int64)
+    ci = layer.col_idx[:rp[-1]].cpu().numpy()
+    m = oracle.topk_count(cfg.specs[0].density, cfg.nb)
+    counts = np.diff(rp)
+    assert set(counts.tolist()) <= {m, m + 1}
+    for h in range(cfg.heads):
+        first = None
+        for qb in range(cfg.nb):
+            r = h * cfg.nb + qb
+            row = ci[rp[r]:rp[r + 1]]
+            assert np.all(np.diff(row) > 0) and qb in row
+            kept = set(row.tolist()) - {qb} if counts[r] == m + 1 else set(row.tolist())
+            if counts[r] == m:
+                first = kept if first is None else first
+                assert kept == first  # every row of a head shares the kept set
 
 
 def test_gate_from_q_c4():
