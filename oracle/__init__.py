@@ -22,8 +22,11 @@ What it computes, and where the pages say so:
   TL;DR, input-dependent scalar gate).
 * Masks: a static spatio-temporal sliding window or a dynamic top-k over pooled
   block scores (explainer section 5, applies to sliding-window and Top-K sparse
-  attention; sciencestack Figure 1, ST-SWA).  The pages fix neither rule; the
-  readings used here are stated in ``masks.py``.
+  attention; sciencestack Figure 1, ST-SWA), or key blocks ranked by the sum of
+  intra-block cosine similarities (SPADE explainer, scheme generation).  The
+  pages fix none of the rules; the readings used here are stated in ``masks.py``.
+* Token order: frame-major runs or 3-D cuboid blocks (SPADE explainer, the
+  vDiT-SSR blueprint part); the storage rule is stated in ``layout.py``.
 
 All floating-point work is fp64 on the exact values of the (bf16 or fp32)
 inputs, except the pooled-score ranking of the top-k mask, whose fp32 order of
@@ -43,6 +46,7 @@ from .attention import (
     mix,
     sparse_attention,
 )
+from .layout import cuboid_order, permute_tokens, slot_coords
 from .masks import (
     InfeasibleMask,
     build_masks,
@@ -65,6 +69,7 @@ __all__ = [
     "InfeasibleMask",
     "build_masks",
     "csr_from_keep",
+    "cuboid_order",
     "gate_from_q",
     "keep_from_csr",
     "layer_forward",
@@ -72,8 +77,10 @@ __all__ = [
     "linear_attention_from_state",
     "linear_state",
     "mix",
+    "permute_tokens",
     "pooled_means_f32",
     "pooled_scores_f32",
+    "slot_coords",
     "sparse_attention",
     "topk_count",
     "topk_select",

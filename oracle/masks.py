@@ -81,27 +81,39 @@ def _token_coords(T: int, H: int, W: int):
 
 
 def window_rstar_bruteforce(T: int, H: int, W: int, block: int, t_window: int,
-                            qblocks: Optional[Sequence[int]] = None) -> np.ndarray:
+                            qblocks: Optional[Sequence[int]] = None,
+                            order: Optional[np.ndarray] = None) -> np.ndarray:
     """r*(q, k) by direct minimisation over every token pair (small grids, or a few rows).
 
-    Returns int64 [len(qblocks) or nb, nb]; RSTAR_INF marks "no pair within Tw frames".
+    ``order`` (from ``layout.cuboid_order``) gives the token stored at each slot;
+    None is the frame-major order.  Returns int64 [len(qblocks) or nb, nb];
+    RSTAR_INF marks "no pair within Tw frames".
     """
     N = T * H * W
     nb = -(-N // block)
     n_pad = nb * block
     t, y, x = _token_coords(T, H, W)
+    if order is not None:
+        order = np.asarray(order, dtype=np.int64)
+        t, y, x = t[order], y[order], x[order]
+    # int32 coordinates, padded to n_pad with a frame far outside every window
+    far = np.int32(-(4 * (T + H + W + t_window + 1)))
+    tp = np.full(n_pad, far, dtype=np.int32)
+    tp[:N] = t
+    yp = np.zeros(n_pad, dtype=np.int32)
+    yp[:N] = y
+    xp = np.zeros(n_pad, dtype=np.int32)
+    xp[:N] = x
     rows = range(nb) if qblocks is None else list(qblocks)
     out = np.full((len(rows), nb), RSTAR_INF, dtype=np.int64)
     for r, qb in enumerate(rows):
         i = np.arange(qb * block, min((qb + 1) * block, N))
         if i.size == 0:
             continue
-        dt = np.abs(t[i, None] - t[None, :])
-        dist = np.maximum(np.abs(y[i, None] - y[None, :]), np.abs(x[i, None] - x[None, :]))
-        dist = np.where(dt <= t_window, dist, RSTAR_INF)
-        full = np.full((i.size, n_pad), RSTAR_INF, dtype=np.int64)
-        full[:, :N] = dist
-        out[r] = full.reshape(i.size, nb, block).min(axis=(0, 2))
+        dt = np.abs(tp[i, None] - tp[None, :])
+        dist = np.maximum(np.abs(yp[i, None] - yp[None, :]), np.abs(xp[i, None] - xp[None, :]))
+        dist[dt > t_window] = RSTAR_INF
+        out[r] = dist.reshape(i.size, nb, block).min(axis=(0, 2))
     return out
 
 
@@ -302,8 +314,13 @@ def keep_from_csr(row_ptr: np.ndarray, col_idx: np.ndarray, B: int, Hh: int, nbq
 
 def build_masks(T: int, H: int, W: int, block: int, specs: Iterable, batch: int,
                 q: Optional[np.ndarray] = None, k: Optional[np.ndarray] = None,
-                rstar_method: str = "segments") -> np.ndarray:
-    """keep bool [B, H, nb, nb] for per-head specs (objects with kind, t_window, r_max, density)."""
+                rstar_method: str = "segments", order: Optional[np.ndarray] = None) -> np.ndarray:
+    """keep bool [B, H, nb, nb] for per-head specs (objects with kind, t_window, r_max, density).
+
+    q and k are in storage order.  With ``order`` (a cuboid storage order, see
+    ``layout.py``) window r* is taken by token-pair brute force on the stored
+    coordinates; top-k and SICS depend only on the stored tokens.
+    """
     specs = list(specs)
     N = T * H * W
     nb = -(-N // block)
@@ -314,8 +331,12 @@ def build_masks(T: int, H: int, W: int, block: int, specs: Iterable, batch: int,
     for h, sp in enumerate(specs):
         if sp.kind == WINDOW:
             if sp.t_window not in rstar_cache:
-                fn = window_rstar_segments if rstar_method == "segments" else window_rstar_bruteforce
-                rstar_cache[sp.t_window] = fn(T, H, W, block, sp.t_window)
+                if order is not None:
+                    rstar_cache[sp.t_window] = window_rstar_bruteforce(T, H, W, block, sp.t_window,
+                                                                       order=order)
+                else:
+                    fn = window_rstar_segments if rstar_method == "segments" else window_rstar_bruteforce
+                    rstar_cache[sp.t_window] = fn(T, H, W, block, sp.t_window)
             keep[:, h] = window_select(rstar_cache[sp.t_window], sp.r_max, sp.density)[None]
         elif sp.kind == TOPK:
             if pooled is None:

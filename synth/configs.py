@@ -14,6 +14,11 @@ c5  long-video layer, bf16, 12 heads, d=128, grid 41x45x80 (147600 tokens
 c6  small bf16 layer with SICS heads (top key blocks by the sum of intra-block
     cosine similarities, 10%, plus the diagonal), c2's shape.
 c7  c3's shape (21x30x52, 12 heads, d=128) with SICS heads at 10%.
+c8  c3's layer with 4x4x4 cuboid blocks (tokens stored cuboid by cuboid), 10%
+    window (+-1 frame).
+c9  small ragged cuboid layer, bf16, 4 heads, d=64, grid 5x10x14, 2x4x8 cuboids
+    (partial cuboids on every axis): two window heads, one top-k, one SICS,
+    gate from Q.
 
 The per-head densities of c5 are drawn here (stream 8 of the config's seed) so
 that every consumer sees the same mask specification.
@@ -66,6 +71,8 @@ class LayerConfig:
     eps: float = 1e-6
     description: str = ""
     extra: dict = field(default_factory=dict, compare=False)
+    # cuboid block shape (ct, ch, cw), product = block; (0, 0, 0) = frame-major runs
+    cuboid: Tuple[int, int, int] = (0, 0, 0)
 
     @property
     def N(self) -> int:
@@ -130,6 +137,19 @@ def _build() -> dict:
         dtype="bf16", specs=tuple(HeadSpec(SICS, 0, -1, 0.10) for _ in range(12)),
         gate_kind="uniform",
         description="bf16 layer, 12 heads, d=128, 21x30x52 grid (32760 tokens), SICS key blocks at 10% + diagonal")
+    cfgs["c8"] = LayerConfig(
+        name="c8", seed=8, batch=1, heads=12, head_dim=128, T=21, H=30, W=52, block=64,
+        dtype="bf16", specs=tuple(HeadSpec(WINDOW, 1, -1, 0.10) for _ in range(12)),
+        gate_kind="uniform", cuboid=(4, 4, 4),
+        description="bf16 layer, 12 heads, d=128, 21x30x52 grid (32760 tokens), 4x4x4 cuboid blocks, "
+                    "10% window")
+    cfgs["c9"] = LayerConfig(
+        name="c9", seed=9, batch=1, heads=4, head_dim=64, T=5, H=10, W=14, block=64,
+        dtype="bf16", specs=(HeadSpec(WINDOW, 1, -1, 0.30), HeadSpec(WINDOW, 0, 2, 0.0),
+                             HeadSpec(TOPK, 0, -1, 0.25), HeadSpec(SICS, 0, -1, 0.2)),
+        gate_kind="from_q", cuboid=(2, 4, 8),
+        description="small ragged cuboid layer, bf16, 4 heads, d=64, 5x10x14 grid, 2x4x8 cuboids, "
+                    "window/top-k/SICS heads, gate from Q")
     return cfgs
 
 
