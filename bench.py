@@ -9,6 +9,10 @@ which are resident in HBM before timing starts:
   2. salad_linear_prepare  linear state S, z (split-N reduction) folded with
                            gate and W_lin
   3. salad_attn_apply      block-sparse flash attention + linear epilogue
+Layers with cuboid blocks add salad_permute_tokens before (Q, K, V into the
+cuboid storage order) and after (the output back to frame-major order) inside
+the step: the conservative reading, since a model could keep its tokens in
+cuboid order through every layer.
 Prints one JSON line.  `value` is dense-equivalent TFLOP/s, 4*B*H*N^2*d over
 the step time; ms_per_step is the step time.  The roofline object covers the
 dominant kernel (the fused attention kernel), timed with HIP events on the
@@ -139,8 +143,9 @@ def main():
     torch.cuda.set_device(0)
     inp = make_inputs(cfg)
     bf = cfg.dtype == "bf16"
+    cub = tuple(cfg.cuboid) != (0, 0, 0)
     layer = SaladLayer(cfg.batch, cfg.heads, cfg.head_dim, cfg.T, cfg.H, cfg.W, cfg.block,
-                       S.SALAD_BF16 if bf else S.SALAD_F32, cfg.specs)
+                       S.SALAD_BF16 if bf else S.SALAD_F32, cfg.specs, cuboid=cfg.cuboid)
 
     def dev(x, bits):
         if bf:
@@ -153,22 +158,34 @@ def main():
         else torch.from_numpy(inp.gate).cuda()
     w_g = torch.from_numpy(inp.w_g).cuda() if from_q else None
     out = torch.empty_like(q)
+    # tensors in the layer's storage order (the frame-major ones themselves without cuboids)
+    qs, ks, vs, outs = (torch.empty_like(q) for _ in range(4)) if cub else (q, k, v, out)
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
 
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        layer.build_mask(q, k, w_g, gate if from_q else None, stream=sp)
+        if cub:
+            layer.to_storage(q, qs, stream=sp)
+            layer.to_storage(k, ks, stream=sp)
+            layer.to_storage(v, vs, stream=sp)
         if ev is not None:
             ev[1].record(stream)
-        S.salad_linear_prepare(layer.shape, k, v, gate, w, layer.ws, sp, drop_tau=0.0)
+        layer.build_mask(qs, ks, w_g, gate if from_q else None, stream=sp)
         if ev is not None:
             ev[2].record(stream)
-        S.salad_attn_apply(layer.shape, q, k, v, layer.row_ptr, layer.col_idx, gate, cfg.eps, 0.0, 0.0,
-                           out, layer.ws, sp)
+        S.salad_linear_prepare(layer.shape, ks, vs, gate, w, layer.ws, sp, drop_tau=0.0)
         if ev is not None:
             ev[3].record(stream)
+        S.salad_attn_apply(layer.shape, qs, ks, vs, layer.row_ptr, layer.col_idx, gate, cfg.eps, 0.0, 0.0,
+                           outs, layer.ws, sp)
+        if ev is not None:
+            ev[4].record(stream)
+        if cub:
+            layer.from_storage(outs, out, stream=sp)
+        if ev is not None:
+            ev[5].record(stream)
 
     for _ in range(args.warmup):
         step()
@@ -177,7 +194,7 @@ def main():
     # timed region: K whole steps
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start.record(stream)
     for i in range(args.steps):
@@ -186,9 +203,10 @@ def main():
     torch.cuda.synchronize()
     ms_total = t_start.elapsed_time(t_end)
     ms_step = ms_total / args.steps
-    ms_mask = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    ms_lin = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    ms_attn = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    ms_perm = float(np.mean([e[0].elapsed_time(e[1]) + e[4].elapsed_time(e[5]) for e in evs]))
+    ms_mask = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    ms_lin = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    ms_attn = float(np.mean([e[3].elapsed_time(e[4]) for e in evs]))
 
     row_ptr = layer.row_ptr.cpu().numpy()
     nnz = int(row_ptr[-1])
@@ -217,6 +235,7 @@ def main():
             "batch": cfg.batch, "heads": cfg.heads, "head_dim": cfg.head_dim,
             "grid": f"{cfg.T}x{cfg.H}x{cfg.W}", "tokens": cfg.N, "n_pad": cfg.n_pad, "block": cfg.block,
             "kept_block_pairs": nnz, "block_density": round(density, 6),
+            "block_shape": "x".join(str(c) for c in cfg.cuboid) if cub else "frame-major runs",
         },
         "ms_breakdown": {"mask": round(ms_mask, 5), "linear_prepare": round(ms_lin, 5),
                          "attn_kernel": round(ms_attn, 5)},
@@ -233,8 +252,17 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if cub:
+        result["ms_breakdown"]["permute_in_out"] = round(ms_perm, 5)
     if not args.no_cpu:
         g = gate.cpu().numpy().astype(np.float64)
+        if cub:  # the oracle runs on the same stored token order as the kernels
+            import dataclasses
+
+            import oracle
+            order = oracle.cuboid_order(cfg.T, cfg.H, cfg.W, cfg.cuboid)
+            inp = dataclasses.replace(inp, **{n: oracle.permute_tokens(getattr(inp, n), order)
+                                              for n in ("q", "k", "v")})
         result["cpu_baseline"] = cpu_baseline(cfg, inp, row_ptr, col_idx, g, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 

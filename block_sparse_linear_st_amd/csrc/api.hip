@@ -3,6 +3,7 @@
 #include <algorithm>
 #include <cmath>
 
+#include "cuboid.h"
 #include "internal.h"
 
 namespace salad {
@@ -31,6 +32,11 @@ int shape_status(const salad_shape* s) {
   if (nb > 46340) return SALAD_EUNSUPPORTED;  // nb*nb must fit int32
   if (s->H > 65534 || s->W > 65534) return SALAD_EUNSUPPORTED;  // r* is stored in 16 bits
   if ((int64_t)s->batch * s->heads * nb + 1 > INT32_MAX) return SALAD_EUNSUPPORTED;
+  const bool raster = s->cuboid_t == 0 && s->cuboid_h == 0 && s->cuboid_w == 0;
+  if (!raster) {
+    if (s->cuboid_t < 1 || s->cuboid_h < 1 || s->cuboid_w < 1) return SALAD_EINVAL;
+    if ((int64_t)s->cuboid_t * s->cuboid_h * s->cuboid_w != s->block) return SALAD_EINVAL;
+  }
   return SALAD_OK;
 }
 
@@ -81,7 +87,38 @@ bool make_geom(const salad_shape* s, Geom* g) {
   return true;
 }
 
-Workspace plan_workspace(const Geom& g, int dtype) {
+void make_cuboid(const salad_shape* s, Cuboid* c) {
+  *c = Cuboid{};
+  if (s->cuboid_t == 0) return;  // frame-major order
+  c->ct = s->cuboid_t;
+  c->ch = s->cuboid_h;
+  c->cw = s->cuboid_w;
+  c->nt = (s->T + c->ct - 1) / c->ct;
+  c->ny = (s->H + c->ch - 1) / c->ch;
+  c->nx = (s->W + c->cw - 1) / c->cw;
+  c->Ft = s->T / c->ct;
+  c->Fy = s->H / c->ch;
+  c->Fx = s->W / c->cw;
+  c->rt = s->T - (c->nt - 1) * c->ct;
+  c->ry = s->H - (c->ny - 1) * c->ch;
+  c->rx = s->W - (c->nx - 1) * c->cw;
+  c->F = c->Ft * c->Fy * c->Fx;
+  // Smallest partial cuboid: each axis takes its full extent (if any cuboid is
+  // full on it) or its remainder (if one is short), at least one remainder.
+  // An interval of `block` slots meets at most ceil(block / smallest) + 1
+  // pieces; each inner piece is one box and the two cut ones at most three.
+  int smallest = 0;
+  const int et[2] = {c->Ft > 0 ? c->ct : 0, c->rt < c->ct ? c->rt : 0};
+  const int ey[2] = {c->Fy > 0 ? c->ch : 0, c->ry < c->ch ? c->ry : 0};
+  const int ex[2] = {c->Fx > 0 ? c->cw : 0, c->rx < c->cw ? c->rx : 0};
+  for (int m = 1; m < 8; ++m) {
+    const int v = et[m & 1] * ey[(m >> 1) & 1] * ex[(m >> 2) & 1];
+    if (v > 0 && (smallest == 0 || v < smallest)) smallest = v;
+  }
+  c->box_cap = smallest == 0 ? 1 : (s->block + smallest - 1) / smallest + 1 + 4;
+}
+
+Workspace plan_workspace(const Geom& g, const Cuboid& cu, int dtype) {
   Workspace L{};
   const size_t BH = (size_t)g.B * g.Hh, D = g.D, nb = g.nb;
   // mask build
@@ -97,6 +134,9 @@ Workspace plan_workspace(const Geom& g, int dtype) {
   L.off_scores = off; off = align_up(off + (size_t)topk_heads_per_batch(g) * nb * nb * 4);
   L.off_sics = off;   off = align_up(off + BH * nb * 4);
   L.off_sics_pack = off; off = align_up(off + BH * nb * 4);
+  const size_t boxes = cu.ct == 0 ? 0 : nb;
+  L.off_nbox = off;   off = align_up(off + boxes * 4);
+  L.off_boxes = off;  off = align_up(off + boxes * (size_t)cu.box_cap * sizeof(Box));
   L.mask_end = off;
   // linear state: about 512 workgroups in all, 64-token granularity
   int splits = (int)std::max<size_t>(1, (512 + BH - 1) / BH);
@@ -117,6 +157,16 @@ Workspace plan_workspace(const Geom& g, int dtype) {
   L.bytes = std::max(L.mask_end, L.lin_end);
   return L;
 }
+
+namespace {
+
+Workspace plan_for(const salad_shape* s, const Geom& g) {
+  Cuboid cu;
+  make_cuboid(s, &cu);
+  return plan_workspace(g, cu, s->dtype);
+}
+
+}  // namespace
 
 }  // namespace salad
 
@@ -164,7 +214,7 @@ int64_t salad_mask_nnz_max(const salad_shape* shape, const salad_mask_spec* spec
 size_t salad_workspace_bytes(const salad_shape* shape) {
   Geom g;
   if (!make_geom(shape, &g)) return 0;
-  return plan_workspace(g, shape->dtype).bytes;
+  return plan_for(shape, g).bytes;
 }
 
 int salad_build_mask(const salad_shape* shape, const salad_mask_spec* specs, const void* q,
@@ -188,7 +238,7 @@ int salad_build_mask(const salad_shape* shape, const salad_mask_spec* specs, con
   if ((any_topk || want_gate) && (!q || !aligned16(q))) return SALAD_EINVAL;
   if (any_k && (!k || !aligned16(k))) return SALAD_EINVAL;
   if (!aligned16(ws)) return SALAD_EINVAL;
-  const Workspace L = plan_workspace(g, shape->dtype);
+  const Workspace L = plan_for(shape, g);
   if (ws_bytes < L.bytes) return SALAD_ENOSPACE;
   const int64_t need = salad_mask_nnz_max(shape, specs);
   if (need < 0) return (int)need;
@@ -202,9 +252,41 @@ int salad_build_mask(const salad_shape* shape, const salad_mask_spec* specs, con
     ht.count[h] = (int)(specs[h].kind == SALAD_MASK_WINDOW ? window_count(specs[h].density, g.nb)
                                                            : topk_count(specs[h].density, g.nb));
   }
-  return hip_status(launch_build_mask(g, shape->dtype, ht, q, k, row_ptr, col_idx, col_cap, info,
+  Cuboid cu;
+  make_cuboid(shape, &cu);
+  return hip_status(launch_build_mask(g, cu, shape->dtype, ht, q, k, row_ptr, col_idx, col_cap, info,
                                       w_g, gate, static_cast<char*>(ws), L,
                                       static_cast<hipStream_t>(stream)));
+}
+
+int salad_token_order(const salad_shape* shape, int32_t* order) {
+  Geom g;
+  const int st = shape_status(shape);
+  if (st != SALAD_OK) return st;
+  if (!order) return SALAD_EINVAL;
+  make_geom(shape, &g);
+  Cuboid cu;
+  make_cuboid(shape, &cu);
+  for (int p = 0; p < g.n_pad; ++p) order[p] = p < g.N ? slot_token(g, cu, p) : p;
+  return SALAD_OK;
+}
+
+int salad_permute_tokens(const salad_shape* shape, int inverse, const void* src, void* dst,
+                         void* stream) {
+  Geom g;
+  const int st = shape_status(shape);
+  if (st != SALAD_OK) return st;
+  if (!src || !dst || !aligned16(src) || !aligned16(dst) || (inverse != 0 && inverse != 1))
+    return SALAD_EINVAL;
+  make_geom(shape, &g);
+  const size_t bytes = (size_t)g.B * g.Hh * g.n_pad * g.D * (shape->dtype == SALAD_BF16 ? 2 : 4);
+  const char* s = static_cast<const char*>(src);
+  const char* d = static_cast<const char*>(dst);
+  if (s < d + bytes && d < s + bytes) return SALAD_EINVAL;  // overlapping buffers
+  Cuboid cu;
+  make_cuboid(shape, &cu);
+  return hip_status(launch_permute_tokens(g, cu, shape->dtype, inverse, src, dst,
+                                          static_cast<hipStream_t>(stream)));
 }
 
 int salad_gate_from_q(const salad_shape* shape, const void* q, const float* w_g, float* gate,
@@ -214,7 +296,7 @@ int salad_gate_from_q(const salad_shape* shape, const void* q, const float* w_g,
   if (st != SALAD_OK) return st;
   make_geom(shape, &g);
   if (!q || !w_g || !gate || !ws || !aligned16(q) || !aligned16(ws)) return SALAD_EINVAL;
-  const Workspace L = plan_workspace(g, shape->dtype);
+  const Workspace L = plan_for(shape, g);
   if (ws_bytes < L.bytes) return SALAD_ENOSPACE;
   return hip_status(launch_gate_from_q(g, shape->dtype, q, w_g, gate, static_cast<char*>(ws), L,
                                        static_cast<hipStream_t>(stream)));
@@ -228,7 +310,7 @@ int salad_linear_state(const salad_shape* shape, const void* k, const void* v, f
   make_geom(shape, &g);
   if (!k || !v || !S || !z || !ws || !aligned16(k) || !aligned16(v) || !aligned16(ws))
     return SALAD_EINVAL;
-  const Workspace L = plan_workspace(g, shape->dtype);
+  const Workspace L = plan_for(shape, g);
   if (ws_bytes < L.bytes) return SALAD_ENOSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(ws);
@@ -247,7 +329,7 @@ int attn_common(const salad_shape* shape, const void* q, const void* k, const vo
   make_geom(shape, g);
   if (!q || !k || !v || !row_ptr || !col_idx || !ws) return SALAD_EINVAL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(ws)) return SALAD_EINVAL;
-  *L = plan_workspace(*g, shape->dtype);
+  *L = plan_for(shape, *g);
   if (ws_bytes < L->bytes) return SALAD_ENOSPACE;
   return SALAD_OK;
 }
@@ -268,7 +350,7 @@ int salad_linear_prepare(const salad_shape* shape, const void* k, const void* v,
   if (!k || !v || !gate || !w_lin || !ws || !aligned16(k) || !aligned16(v) || !aligned16(ws) ||
       std::isnan(drop_tau))
     return SALAD_EINVAL;
-  const Workspace L = plan_workspace(g, shape->dtype);
+  const Workspace L = plan_for(shape, g);
   if (ws_bytes < L.bytes) return SALAD_ENOSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(ws);

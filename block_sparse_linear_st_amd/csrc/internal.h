@@ -26,6 +26,25 @@ struct Geom {
   int N, n_pad, blk, nb;
 };
 
+// Token storage order of a shape: frame-major runs (ct == 0) or cuboid blocks.
+// Tokens are stored cuboid by cuboid: every full ct x ch x cw cuboid in
+// lexicographic cuboid order (one block each), then the partial cuboids at the
+// grid's far edges in lexicographic order; frame-major inside a cuboid.
+struct Cuboid {
+  int ct, ch, cw;      // cuboid extents, 0 = frame-major order
+  int nt, ny, nx;      // cuboids per axis (rounded up)
+  int Ft, Fy, Fx;      // full cuboids per axis (rounded down)
+  int rt, ry, rx;      // extent of the last cuboid on each axis
+  int F;               // full cuboids: blocks [0, F) are exactly one cuboid each
+  int box_cap;         // boxes a block's token set can need (upper bound)
+};
+
+// Axis-aligned box of tokens, bounds inclusive: (t0, t1, y0, y1), (x0, x1, -, -).
+struct Box {
+  int4 ty;
+  int4 x;
+};
+
 // Per-head mask parameters, passed by value in kernel arguments.
 struct HeadTable {
   int n_heads;
@@ -49,6 +68,7 @@ struct Workspace {
   size_t off_psum_q, off_psum_k;   // float [B*H*nb*D]
   size_t off_scores;               // float [heads per batch][nb][nb] (top-k scores)
   size_t off_sics, off_sics_pack;  // float / int32 [B*H*nb] (SICS scores, selection)
+  size_t off_nbox, off_boxes;      // cuboid order: int32 [nb] box counts, Box [nb][box_cap]
   // linear state
   int lin_splits, lin_chunk;
   size_t off_spart, off_zpart;     // float [splits][B*H][D*D], [splits][B*H][D]
@@ -58,10 +78,20 @@ struct Workspace {
 };
 
 SALAD_HIDDEN bool make_geom(const salad_shape* s, Geom* g);
-SALAD_HIDDEN Workspace plan_workspace(const Geom& g, int dtype);
+SALAD_HIDDEN void make_cuboid(const salad_shape* s, Cuboid* c);
+SALAD_HIDDEN Workspace plan_workspace(const Geom& g, const Cuboid& cu, int dtype);
+
+// ---- token order (layout.hip) -----------------------------------------------
+SALAD_HIDDEN hipError_t launch_permute_tokens(const Geom& g, const Cuboid& cu, int dtype,
+                                              int inverse, const void* src, void* dst,
+                                              hipStream_t st);
+// Box lists of every block's token set (cuboid order only) into the workspace.
+SALAD_HIDDEN hipError_t launch_block_boxes(const Geom& g, const Cuboid& cu, char* ws,
+                                           const Workspace& L, hipStream_t st);
 
 // ---- mask builder (mask.hip) ------------------------------------------------
-SALAD_HIDDEN hipError_t launch_build_mask(const Geom& g, int dtype, const HeadTable& ht,
+SALAD_HIDDEN hipError_t launch_build_mask(const Geom& g, const Cuboid& cu, int dtype,
+                                          const HeadTable& ht,
                                           const void* q, const void* k, int32_t* row_ptr,
                                           int32_t* col_idx, int64_t col_cap, int32_t* info,
                                           const float* w_g, float* gate, char* ws,

@@ -1,10 +1,11 @@
-// mask.hip - block-mask builder for gfx950: static spatio-temporal window and
-// pooled-score top-k, emitted as CSR lists of kept key blocks.
+// mask.hip - block-mask builder for gfx950: static spatio-temporal window,
+// pooled-score top-k and SICS, emitted as CSR lists of kept key blocks.
 //
 // The masks follow the readings stated in include/salad.h (salad_mask_spec).
 // Window: r* of every block pair is computed once per (t_window, r_max) group
 // from the horizontal runs of the two blocks (a block covers at most
-// ceil(block/W)+1 runs) into a uint16 table in the workspace.  Selecting the
+// ceil(block/W)+1 runs), or in cuboid order from the blocks' box lists, into a
+// uint16 table in the workspace.  Selecting the
 // first K pairs in (qb!=kb, r*, |qb-kb|, qb, kb) order takes one histogram over
 // a combined bin (0 for the diagonal, 1 + r*·nb + |qb-kb| otherwise), a
 // per-head scan that finds the bin holding the K-th pair, and a scan over query
@@ -20,6 +21,7 @@
 // radix search over order-preserving 32-bit keys and emits them ascending.
 #include <algorithm>
 
+#include "cuboid.h"
 #include "internal.h"
 
 #pragma clang fp contract(off)
@@ -83,6 +85,40 @@ k_window_rstar(Geom g, int tw, int rmax, uint16_t* rt, int32_t* hist) {
     const bool cand = window_candidate(r, rmax);
     rt[(int64_t)qb * g.nb + kb] = cand ? (uint16_t)r : kNoCand;
     if (cand && hist) atomicAdd(&hist[pair_bin(qb, kb, r, g.nb)], 1);
+  }
+}
+
+// Cuboid order: the same table from the blocks' box lists.  Between two boxes
+// the least Chebyshev distance over token pairs at most tw frames apart is
+// max(y gap, x gap) when the frame gap is <= tw (the three ranges of a box
+// vary independently), else infinite; r* is the least over box pairs.
+constexpr int kMaxBoxCap = 136;
+
+__global__ void __launch_bounds__(256)
+k_window_rstar_boxes(Geom g, int cap, const int32_t* __restrict__ nbox, const Box* __restrict__ boxes,
+                     int tw, int rmax, uint16_t* rt, int32_t* hist) {
+  __shared__ Box qbx[kMaxBoxCap];
+  const int qb = blockIdx.x;
+  const int nq = nbox[qb];
+  for (int i = threadIdx.x; i < nq; i += blockDim.x) qbx[i] = boxes[(int64_t)qb * cap + i];
+  __syncthreads();
+  for (int kb = threadIdx.x; kb < g.nb; kb += blockDim.x) {
+    const int nk = nbox[kb];
+    int best = kRstarInf;
+    for (int j = 0; j < nk; ++j) {
+      const Box kx = boxes[(int64_t)kb * cap + j];
+      for (int i = 0; i < nq; ++i) {
+        const Box& qx = qbx[i];
+        const int tgap = max(0, max(kx.ty.x - qx.ty.y, qx.ty.x - kx.ty.y));
+        if (tgap > tw) continue;
+        const int ygap = max(0, max(kx.ty.z - qx.ty.w, qx.ty.z - kx.ty.w));
+        const int xgap = max(0, max(kx.x.x - qx.x.y, qx.x.x - kx.x.y));
+        best = min(best, max(ygap, xgap));
+      }
+    }
+    const bool cand = window_candidate(best, rmax);
+    rt[(int64_t)qb * g.nb + kb] = cand ? (uint16_t)best : kNoCand;
+    if (cand && hist) atomicAdd(&hist[pair_bin(qb, kb, best, g.nb)], 1);
   }
 }
 
@@ -723,7 +759,8 @@ hipError_t launch_topk(const Geom& g, const HeadTable& ht, const float* pq, cons
 
 }  // namespace
 
-hipError_t launch_build_mask(const Geom& g, int dtype, const HeadTable& ht0, const void* q,
+hipError_t launch_build_mask(const Geom& g, const Cuboid& cu, int dtype, const HeadTable& ht0,
+                             const void* q,
                              const void* k, int32_t* row_ptr, int32_t* col_idx, int64_t col_cap,
                              int32_t* info, const float* w_g, float* gate, char* ws,
                              const Workspace& L, hipStream_t st) {
@@ -768,6 +805,20 @@ hipError_t launch_build_mask(const Geom& g, int dtype, const HeadTable& ht0, con
                                        : launch_pool<float>(g, ht, q, k, psq, psk, st);
     if (e != hipSuccess) return e;
   }
+  const int32_t* nbox = reinterpret_cast<const int32_t*>(ws + L.off_nbox);
+  const Box* boxes = reinterpret_cast<const Box*>(ws + L.off_boxes);
+  if (cu.ct != 0 && cu.box_cap > kMaxBoxCap) return hipErrorInvalidValue;
+  auto rstar = [&](int gi, int32_t* h) {
+    if (cu.ct == 0)
+      hipLaunchKernelGGL(k_window_rstar, dim3(g.nb), dim3(256), 0, st, g, grp_tw[gi], grp_rmax[gi], rt, h);
+    else
+      hipLaunchKernelGGL(k_window_rstar_boxes, dim3(g.nb), dim3(256), 0, st, g, cu.box_cap, nbox, boxes,
+                         grp_tw[gi], grp_rmax[gi], rt, h);
+  };
+  if (cu.ct != 0 && n_groups > 0) {
+    hipError_t e = launch_block_boxes(g, cu, ws, L, st);
+    if (e != hipSuccess) return e;
+  }
   // counts: every window group in turn (its r* table lives in the workspace)
   for (int gi = 0; gi < n_groups; ++gi) {
     int32_t* h_ptr = nullptr;
@@ -776,7 +827,7 @@ hipError_t launch_build_mask(const Geom& g, int dtype, const HeadTable& ht0, con
                          dim3(256), 0, st, hist, (int64_t)L.hist_bins, 0);
       h_ptr = hist;
     }
-    hipLaunchKernelGGL(k_window_rstar, dim3(g.nb), dim3(256), 0, st, g, grp_tw[gi], grp_rmax[gi], rt, h_ptr);
+    rstar(gi, h_ptr);
     hipLaunchKernelGGL(k_window_threshold, dim3(g.Hh), dim3(kScanThreads), 0, st, g, ht, gi, rt, hist,
                        (int64_t)L.hist_bins, thr, flags);
     hipLaunchKernelGGL(k_row_counts, dim3(g.nb, g.Hh), dim3(64), 0, st, g, ht, gi,
@@ -806,9 +857,7 @@ hipError_t launch_build_mask(const Geom& g, int dtype, const HeadTable& ht0, con
                        col_cap);
   // emit: the last group's table is still current; the others are rebuilt
   for (int gi = n_groups - 1; gi >= 0; --gi) {
-    if (gi != n_groups - 1)
-      hipLaunchKernelGGL(k_window_rstar, dim3(g.nb), dim3(256), 0, st, g, grp_tw[gi], grp_rmax[gi], rt,
-                         nullptr);
+    if (gi != n_groups - 1) rstar(gi, nullptr);
     hipLaunchKernelGGL(k_window_emit, dim3(g.nb, g.Hh), dim3(64), 0, st, g, ht, gi, rt, thr, row_ptr,
                        col_idx, col_cap);
   }

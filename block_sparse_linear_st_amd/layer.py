@@ -19,8 +19,8 @@ class SaladLayer:
     """One layer shape plus per-head mask specs, with workspace and CSR buffers."""
 
     def __init__(self, batch: int, heads: int, head_dim: int, T: int, H: int, W: int, block: int,
-                 dtype: int, specs: Sequence, device: str = "cuda"):
-        self.shape = S.make_shape(batch, heads, head_dim, T, H, W, block, dtype)
+                 dtype: int, specs: Sequence, device: str = "cuda", cuboid=(0, 0, 0)):
+        self.shape = S.make_shape(batch, heads, head_dim, T, H, W, block, dtype, cuboid=cuboid)
         self.specs = S.make_specs(specs)
         self.device = torch.device(device)
         self.torch_dtype = _TORCH_DTYPE[dtype]
@@ -38,6 +38,16 @@ class SaladLayer:
     def tensor_shape(self):
         s = self.shape
         return (s.batch, s.heads, s.n_pad, s.head_dim)
+
+    def to_storage(self, src: torch.Tensor, dst: torch.Tensor, stream=None):
+        """Frame-major src -> dst in the layer's storage order (a copy for frame-major layers)."""
+        S.salad_permute_tokens(self.shape, 0, src, dst, stream)
+        return dst
+
+    def from_storage(self, src: torch.Tensor, dst: torch.Tensor, stream=None):
+        """Storage-order src -> frame-major dst."""
+        S.salad_permute_tokens(self.shape, 1, src, dst, stream)
+        return dst
 
     def build_mask(self, q: Optional[torch.Tensor] = None, k: Optional[torch.Tensor] = None,
                    w_g: Optional[torch.Tensor] = None, gate: Optional[torch.Tensor] = None, stream=None):

@@ -39,7 +39,8 @@ class SaladError(RuntimeError):
 
 class salad_shape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("batch", "heads", "head_dim", "T", "H", "W", "n_pad", "block", "dtype")]
+                ("batch", "heads", "head_dim", "T", "H", "W", "n_pad", "block", "dtype",
+                 "cuboid_t", "cuboid_h", "cuboid_w")]
 
 
 class salad_mask_spec(ctypes.Structure):
@@ -60,6 +61,8 @@ _SIGS = {
     "salad_workspace_bytes": (_sz, [ctypes.POINTER(salad_shape)]),
     "salad_build_mask": (ctypes.c_int, [ctypes.POINTER(salad_shape), ctypes.POINTER(salad_mask_spec),
                                         _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "salad_token_order": (ctypes.c_int, [ctypes.POINTER(salad_shape), _vp]),
+    "salad_permute_tokens": (ctypes.c_int, [ctypes.POINTER(salad_shape), ctypes.c_int, _vp, _vp, _vp]),
     "salad_gate_from_q": (ctypes.c_int, [ctypes.POINTER(salad_shape), _vp, _vp, _vp, _vp, _sz, _vp]),
     "salad_linear_state": (ctypes.c_int, [ctypes.POINTER(salad_shape), _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "salad_attn_fwd": (ctypes.c_int, [ctypes.POINTER(salad_shape), _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -101,11 +104,12 @@ def _check(status: int, what: str):
         raise SaladError(status, f"{what}: {lib().salad_status_str(status).decode()} ({status})")
 
 
-def make_shape(batch, heads, head_dim, T, H, W, block, dtype, n_pad=None) -> salad_shape:
+def make_shape(batch, heads, head_dim, T, H, W, block, dtype, n_pad=None, cuboid=(0, 0, 0)) -> salad_shape:
     N = T * H * W
     if n_pad is None:
         n_pad = -(-N // block) * block
-    return salad_shape(batch, heads, head_dim, T, H, W, n_pad, block, dtype)
+    ct, ch, cw = (int(v) for v in cuboid)
+    return salad_shape(batch, heads, head_dim, T, H, W, n_pad, block, dtype, ct, ch, cw)
 
 
 def make_specs(specs: Sequence) -> ctypes.Array:
@@ -158,6 +162,19 @@ def salad_build_mask(shape, specs, q, k, row_ptr, col_idx, info=None, w_g=None, 
                                 col_idx.numel(), _p(info), _p(w_g), _p(gate), _p(ws),
                                 ws.numel() if ws is not None else 0, _stream(stream))
     _check(st, "salad_build_mask")
+
+
+def salad_token_order(shape: salad_shape):
+    """Host int32 numpy array [n_pad]: frame-major index of the token at each slot."""
+    import numpy as np
+    order = np.empty(shape.n_pad, dtype=np.int32)
+    _check(lib().salad_token_order(ctypes.byref(shape), order.ctypes.data), "salad_token_order")
+    return order
+
+
+def salad_permute_tokens(shape, inverse, src, dst, stream=None):
+    _check(lib().salad_permute_tokens(ctypes.byref(shape), int(inverse), _p(src), _p(dst), _stream(stream)),
+           "salad_permute_tokens")
 
 
 def salad_gate_from_q(shape, q, w_g, gate, ws, stream=None):

@@ -16,11 +16,12 @@
  *
  * Conventions shared by every entry point:
  *  - Tensors q, k, v, out are [batch, heads, n_pad, head_dim], contiguous,
- *    head_dim innermost, in the shape's dtype (fp32 or bf16).  Token n of the
- *    latent grid (T, H, W) is frame-major: t = n / (H*W), y = (n / W) % H,
- *    x = n % W.  Tokens N = T*H*W .. n_pad-1 are padding: their contents are
- *    never read into a result (any bit pattern is allowed) and output rows
- *    there are written as 0.
+ *    head_dim innermost, in the shape's dtype (fp32 or bf16), with the tokens
+ *    in the shape's storage order (see salad_shape): frame-major by default,
+ *    slot n holding the token t = n / (H*W), y = (n / W) % H, x = n % W.
+ *    Slots N = T*H*W .. n_pad-1 are padding: their contents are never read
+ *    into a result (any bit pattern is allowed) and output rows there are
+ *    written as 0.
  *  - A block mask is CSR over rows r = (b*heads + h)*nb + qb, nb = n_pad/block:
  *    row_ptr int32 [batch*heads*nb + 1], col_idx int32, key blocks ascending
  *    within a row.
@@ -69,12 +70,27 @@ typedef enum { SALAD_MASK_WINDOW = 0, SALAD_MASK_TOPK = 1, SALAD_MASK_SICS = 2 }
 
 /* Layer shape.  Requirements: batch, heads >= 1; heads <= SALAD_MAX_HEADS;
  * head_dim in {64, 128}; T, H, W >= 1; block in {64, 128};
- * n_pad == ceil(T*H*W / block) * block (so every block holds a valid token). */
+ * n_pad == ceil(T*H*W / block) * block (so every block holds a valid token).
+ *
+ * Storage order of the tokens.  cuboid_t = cuboid_h = cuboid_w = 0: frame-major,
+ * block j = the frame-major run [j*block, (j+1)*block).  Otherwise 3-D cuboid
+ * blocks (SPADE explainer, blueprint part "Der Bauplan (vDiT-SSR)": the video's
+ * block grid cut into flat, tall or mixed shapes), with cuboid_t * cuboid_h *
+ * cuboid_w == block, all >= 1.  The cuboid grid has ceil(T/cuboid_t) x
+ * ceil(H/cuboid_h) x ceil(W/cuboid_w) cells; a cell is full when it lies inside
+ * the grid, partial when it meets a far edge that its extent does not divide.
+ * Slots hold every full cell in lexicographic (t, y, x) cell order, one block
+ * each, then every partial cell in lexicographic order packed into the last
+ * blocks; tokens inside a cell frame-major.  salad_token_order lists the order
+ * and salad_permute_tokens moves tensors into and out of it.  The window mask
+ * measures distances on the stored blocks' token sets; top-k, SICS, the gate
+ * and both attention branches take the blocks as stored. */
 typedef struct {
   int32_t batch, heads, head_dim;
   int32_t T, H, W;
   int32_t n_pad, block;
   int32_t dtype; /* salad_dtype */
+  int32_t cuboid_t, cuboid_h, cuboid_w; /* 0, 0, 0 = frame-major */
 } salad_shape;
 
 /* Mask request for one head (host struct, one per head).
@@ -150,6 +166,23 @@ SALAD_API int salad_build_mask(const salad_shape* shape, const salad_mask_spec* 
                      int32_t* row_ptr, int32_t* col_idx, int64_t col_cap,
                      int32_t* info, const float* w_g, float* gate,
                      void* ws, size_t ws_bytes, void* stream);
+
+/* Storage order of the shape's tokens: order[p] = frame-major index
+ * t*H*W + y*W + x of the token stored at slot p, for p < N, and order[p] = p
+ * for the padding slots p in [N, n_pad).  order: HOST int32 [n_pad].  Pure
+ * host function (the identity for frame-major shapes). */
+SALAD_API int salad_token_order(const salad_shape* shape, int32_t* order);
+
+/* Move the token axis of a [batch, heads, n_pad, head_dim] tensor of the
+ * shape's dtype between frame-major order and the shape's storage order
+ * (order as listed by salad_token_order):
+ *   inverse = 0: dst[b, h, p, :] = src[b, h, order[p], :]  (into storage order)
+ *   inverse = 1: dst[b, h, order[p], :] = src[b, h, p, :]  (back to frame-major)
+ * Padding slots are copied unchanged.  src, dst: device, 16-byte aligned, not
+ * overlapping (SALAD_EINVAL otherwise).  A plain copy for frame-major shapes.
+ * Needs no workspace. */
+SALAD_API int salad_permute_tokens(const salad_shape* shape, int inverse, const void* src,
+                                   void* dst, void* stream);
 
 /* Gate from Q: gate[b*heads + h] = sigmoid(mean over the N valid tokens of
  * q[b, h, n, :] . w_g), the stand-in used here for the input-aware scale s of

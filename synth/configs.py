@@ -14,8 +14,8 @@ c5  long-video layer, bf16, 12 heads, d=128, grid 41x45x80 (147600 tokens
 c6  small bf16 layer with SICS heads (top key blocks by the sum of intra-block
     cosine similarities, 10%, plus the diagonal), c2's shape.
 c7  c3's shape (21x30x52, 12 heads, d=128) with SICS heads at 10%.
-c8  c3's layer with 4x4x4 cuboid blocks (tokens stored cuboid by cuboid), 10%
-    window (+-1 frame).
+c8  c3's layer with flat 1x8x8 cuboid blocks (tokens stored cuboid by cuboid),
+    10% window (+-1 frame).
 c9  small ragged cuboid layer, bf16, 4 heads, d=64, grid 5x10x14, 2x4x8 cuboids
     (partial cuboids on every axis): two window heads, one top-k, one SICS,
     gate from Q.
@@ -140,8 +140,8 @@ def _build() -> dict:
     cfgs["c8"] = LayerConfig(
         name="c8", seed=8, batch=1, heads=12, head_dim=128, T=21, H=30, W=52, block=64,
         dtype="bf16", specs=tuple(HeadSpec(WINDOW, 1, -1, 0.10) for _ in range(12)),
-        gate_kind="uniform", cuboid=(4, 4, 4),
-        description="bf16 layer, 12 heads, d=128, 21x30x52 grid (32760 tokens), 4x4x4 cuboid blocks, "
+        gate_kind="uniform", cuboid=(1, 8, 8),
+        description="bf16 layer, 12 heads, d=128, 21x30x52 grid (32760 tokens), 1x8x8 cuboid blocks, "
                     "10% window")
     cfgs["c9"] = LayerConfig(
         name="c9", seed=9, batch=1, heads=4, head_dim=64, T=5, H=10, W=14, block=64,

@@ -33,10 +33,29 @@ def inputs(name: str, canary: bool = False):
 
 
 @functools.lru_cache(maxsize=4)
+def storage_order(name: str):
+    """The oracle's storage order of the config (identity for frame-major configs)."""
+    c = CONFIGS[name]
+    return oracle.cuboid_order(c.T, c.H, c.W, c.cuboid)
+
+
+@functools.lru_cache(maxsize=4)
+def stored_inputs(name: str):
+    """(q, k, v) of the config moved into its storage order by the oracle."""
+    inp = inputs(name)
+    o = storage_order(name)
+    return tuple(oracle.permute_tokens(x, o) for x in (inp.q, inp.k, inp.v))
+
+
+@functools.lru_cache(maxsize=4)
 def oracle_csr(name: str):
     c = CONFIGS[name]
-    inp = inputs(name)
-    keep = oracle.build_masks(c.T, c.H, c.W, c.block, c.specs, c.batch, inp.q, inp.k)
+    if tuple(c.cuboid) != (0, 0, 0):
+        q, k, _ = stored_inputs(name)
+        keep = oracle.build_masks(c.T, c.H, c.W, c.block, c.specs, c.batch, q, k, order=storage_order(name))
+    else:
+        inp = inputs(name)
+        keep = oracle.build_masks(c.T, c.H, c.W, c.block, c.specs, c.batch, inp.q, inp.k)
     return oracle.csr_from_keep(keep)
 
 
@@ -67,7 +86,7 @@ def make_layer(cfg, dtype=None, specs=None):
     from block_sparse_linear_st_amd.layer import SaladLayer
     dt = S.SALAD_BF16 if (dtype or cfg.dtype) == "bf16" else S.SALAD_F32
     return SaladLayer(cfg.batch, cfg.heads, cfg.head_dim, cfg.T, cfg.H, cfg.W, cfg.block, dt,
-                      specs if specs is not None else cfg.specs)
+                      specs if specs is not None else cfg.specs, cuboid=cfg.cuboid)
 
 
 def sample_blocks(cfg, n_random=12, seed=0):

@@ -32,7 +32,7 @@ def test_exports_every_declared_function():
 def _shape(name, **over):
     c = CONFIGS[name]
     sh = S.make_shape(c.batch, c.heads, c.head_dim, c.T, c.H, c.W, c.block,
-                      S.SALAD_BF16 if c.dtype == "bf16" else S.SALAD_F32)
+                      S.SALAD_BF16 if c.dtype == "bf16" else S.SALAD_F32, cuboid=c.cuboid)
     for k, v in over.items():
         setattr(sh, k, v)
     return sh
@@ -136,3 +136,58 @@ def test_sics_specs():
     big = S.make_shape(1, 1, 128, 1, 1, 64 * 4097, 64, S.SALAD_BF16)
     one = S.make_specs([c.specs[0]])
     assert S.lib().salad_mask_nnz_max(ctypes.byref(big), one) == S.SALAD_EUNSUPPORTED
+
+
+# ------------------------------------------------------------------ cuboid storage order (host paths)
+
+ORDER_GRIDS = [
+    (21, 30, 52, 64, (4, 4, 4)), (21, 30, 52, 64, (1, 8, 8)), (21, 30, 52, 64, (2, 4, 8)),
+    (41, 45, 80, 128, (2, 8, 8)), (41, 45, 80, 128, (1, 8, 16)), (5, 10, 14, 64, (2, 4, 8)),
+    (3, 7, 5, 64, (4, 4, 4)), (7, 9, 11, 64, (64, 1, 1)), (13, 1, 1, 64, (4, 4, 4)), (6, 6, 6, 64, (4, 4, 4)),
+    (21, 30, 52, 64, (0, 0, 0)),
+]
+
+
+@pytest.mark.parametrize("grid", ORDER_GRIDS, ids=str)
+def test_token_order_matches_oracle(grid):
+    """salad_token_order (a pure host function) lists the oracle's storage order, padding slots mapped to themselves."""
+    _lib()
+    import numpy as np
+    from oracle import layout as ol
+    T, H, W, blk, cub = grid
+    sh = S.make_shape(1, 1, 64, T, H, W, blk, S.SALAD_BF16, cuboid=cub)
+    got = S.salad_token_order(sh)
+    N = T * H * W
+    np.testing.assert_array_equal(got[:N], ol.cuboid_order(T, H, W, cub))
+    np.testing.assert_array_equal(got[N:], np.arange(N, sh.n_pad))
+
+
+def test_cuboid_shape_validation():
+    _lib()
+    assert S.salad_workspace_bytes(_shape("c8")) >= S.salad_workspace_bytes(_shape("c3"))  # + box lists
+    assert S.salad_workspace_bytes(_shape("c8", cuboid_w=16)) == 0       # 1*8*16 != 64
+    assert S.salad_workspace_bytes(_shape("c8", cuboid_w=0)) == 0        # partly zero
+    assert S.salad_workspace_bytes(_shape("c8", cuboid_t=-1, cuboid_h=-8)) == 0
+    assert S.salad_workspace_bytes(_shape("c8", cuboid_t=1, cuboid_h=1, cuboid_w=64)) > 0
+    assert S.salad_workspace_bytes(_shape("c3", cuboid_t=64, cuboid_h=1, cuboid_w=1)) > 0  # taller than T
+    bad = _shape("c8", cuboid_h=2)  # 1*2*8 != 64
+    order = (ctypes.c_int32 * bad.n_pad)()
+    assert S.lib().salad_token_order(ctypes.byref(bad), order) == S.SALAD_EINVAL
+    assert S.lib().salad_token_order(ctypes.byref(_shape("c8")), None) == S.SALAD_EINVAL
+
+
+def test_permute_rejects_bad_arguments_before_launch():
+    L = _lib()
+    sh = _shape("c8")
+    nbytes = sh.batch * sh.heads * sh.n_pad * sh.head_dim * 2
+    a = ctypes.c_void_p(0x10000000)
+    b = ctypes.c_void_p(0x10000000 + nbytes)       # adjacent, not overlapping: would launch, not used here
+    over = ctypes.c_void_p(0x10000000 + nbytes - 16)
+    odd = ctypes.c_void_p(0x10000008)
+    assert L.salad_permute_tokens(ctypes.byref(sh), 0, a, over, None) == S.SALAD_EINVAL
+    assert L.salad_permute_tokens(ctypes.byref(sh), 0, over, a, None) == S.SALAD_EINVAL
+    assert L.salad_permute_tokens(ctypes.byref(sh), 0, a, a, None) == S.SALAD_EINVAL
+    assert L.salad_permute_tokens(ctypes.byref(sh), 2, a, b, None) == S.SALAD_EINVAL
+    assert L.salad_permute_tokens(ctypes.byref(sh), 0, None, b, None) == S.SALAD_EINVAL
+    assert L.salad_permute_tokens(ctypes.byref(sh), 1, odd, b, None) == S.SALAD_EINVAL
+    assert L.salad_permute_tokens(ctypes.byref(_shape("c8", cuboid_w=2)), 0, a, b, None) == S.SALAD_EINVAL  # 1*8*2
