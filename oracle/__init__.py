@@ -25,6 +25,9 @@ What it computes, and where the pages say so:
   attention; sciencestack Figure 1, ST-SWA), or key blocks ranked by the sum of
   intra-block cosine similarities (SPADE explainer, scheme generation).  The
   pages fix none of the rules; the readings used here are stated in ``masks.py``.
+* Gradients (for fine-tuning, explainer sections 2.2 and 3): dq, dk, dv, dW_lin
+  and dgate of the same forward by reverse-mode differentiation, in
+  ``backward.py``.
 * Token order: frame-major runs or 3-D cuboid blocks (SPADE explainer, the
   vDiT-SSR blueprint part); the storage rule is stated in ``layout.py``.
 
@@ -46,6 +49,7 @@ from .attention import (
     mix,
     sparse_attention,
 )
+from .backward import layer_backward
 from .layout import cuboid_order, permute_tokens, slot_coords
 from .masks import (
     InfeasibleMask,
@@ -72,6 +76,7 @@ __all__ = [
     "cuboid_order",
     "gate_from_q",
     "keep_from_csr",
+    "layer_backward",
     "layer_forward",
     "linear_attention",
     "linear_attention_from_state",
