@@ -436,4 +436,49 @@ int salad_attn_fwd_branches(const salad_shape* shape, const void* q, const void*
   return SALAD_OK;
 }
 
+size_t salad_bwd_workspace_bytes(const salad_shape* shape) {
+  Geom g;
+  if (!make_geom(shape, &g)) return 0;
+  Cuboid cu;
+  make_cuboid(shape, &cu);
+  return plan_bwd_workspace(g, cu, shape->dtype).bytes;
+}
+
+int salad_attn_bwd(const salad_shape* shape, const void* q, const void* k, const void* v,
+                   const int32_t* row_ptr, const int32_t* col_idx, const float* gate,
+                   const void* w_lin, float eps, float scale, const void* out, const void* dout,
+                   void* dq, void* dk, void* dv, float* dw_lin, float* dgate, void* ws,
+                   size_t ws_bytes, void* stream) {
+  Geom g;
+  const int st = shape_status(shape);
+  if (st != SALAD_OK) return st;
+  if (shape->dtype != SALAD_BF16) return SALAD_EUNSUPPORTED;
+  make_geom(shape, &g);
+  const void* ptrs[] = {q, k, v, out, dout, dq, dk, dv, ws, w_lin};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return SALAD_EINVAL;
+  if (!row_ptr || !col_idx || !gate || !dw_lin || !dgate) return SALAD_EINVAL;
+  if (!(eps >= 0.0f) || !std::isfinite(scale)) return SALAD_EINVAL;
+  Cuboid cu;
+  make_cuboid(shape, &cu);
+  const BwdWorkspace L = plan_bwd_workspace(g, cu, shape->dtype);
+  if (ws_bytes < L.bytes) return SALAD_ENOSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  BwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.row_ptr = row_ptr; a.col_idx = col_idx; a.gate = gate;
+  a.w_lin = w_lin; a.out = out; a.dout = dout; a.dq = dq; a.dk = dk; a.dv = dv;
+  a.dw_lin = dw_lin; a.dgate = dgate; a.eps = eps;
+  a.scale = scale > 0.0f ? scale : 1.0f / std::sqrt((float)g.D);
+  hipError_t e = launch_linear_state(g, shape->dtype, k, v, nullptr, 0.0f, w, L.fwd, s);
+  if (e == hipSuccess)
+    e = launch_linear_fold(g, shape->dtype, nullptr, nullptr, 2, 0.0f,
+                           reinterpret_cast<float*>(w + L.off_s32), reinterpret_cast<float*>(w + L.off_z),
+                           w, L.fwd, s);
+  if (e == hipSuccess) e = launch_linear_bwd(g, a, w, L, s);
+  if (e == hipSuccess) e = launch_mask_transpose(g, row_ptr, col_idx, w, L, s);
+  if (e == hipSuccess) e = launch_attn_bwd(g, a, w, L, s);
+  return hip_status(e);
+}
+
 }  // extern "C"

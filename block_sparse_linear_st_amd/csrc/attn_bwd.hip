@@ -1,0 +1,351 @@
+// attn_bwd.hip - backward of the block-sparse softmax branch on gfx950, with
+// the linear branch's dq, dk, dv terms folded into the same kernels.
+//
+// With x = scale * q.k, P = softmax over the kept keys, D_i = <dout_i, o_s,i>
+// (from linear_bwd.hip):  dS = P * (dout V^T - D),  dQ = scale dS K,
+// dK = scale dS^T Q,  dV = P^T dout.  The row statistic (log-sum-exp) is
+// recomputed here, so the forward kernel keeps nothing for training.
+//
+// k_attn_bwd_dq: one query block per workgroup, one wave per 32 queries,
+// queries in lanes (the forward's transposed orientation).  Pass 1 over the
+// kept key tiles: S^T = K Q^T and the running max / sum -> log2-sum-exp per
+// query (written for the key-side kernel).  Pass 2: S^T, P^T, dP^T = V dO^T,
+// dS^T, and dQ^T += K^T dS^T with K^T read by LDS transpose reads and dS^T
+// taken straight from the accumulators.  The epilogue adds the linear term
+// (S dU^T + z dden^T) * [q > 0] on MFMAs (S as hi + lo bf16).
+//
+// k_attn_bwd_dkdv: one key block per workgroup, one wave per 32 keys, keys in
+// lanes; K and V fragments stay in registers.  It walks the transposed mask
+// (the query blocks that keep this key block, ascending) in 64-query tiles:
+// S = Q K^T, P, dP = dO V^T, dS, then dV^T += dO^T P and dK^T += Q^T dS with
+// dO^T and Q^T by transpose reads.  The epilogue adds dS_lin^T phi(K)^T to dV
+// and (dS_lin V^T + dz) * [k > 0] to dK.
+//
+// Every tile row past the last valid token is a copy of token N-1 (finite), so
+// no NaN from padding can reach an MFMA; padded keys and queries are masked by
+// index and their output rows are written as 0.
+#include <cmath>
+
+#include "bwd_common.h"
+
+namespace salad {
+
+using namespace bwd;
+
+namespace {
+
+constexpr int kT = 64;  // keys (dq kernel) or queries (dkdv kernel) per LDS tile
+
+__device__ inline bf16x8 ld8(const __bf16* p) { return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p)); }
+
+template <int D, int BLK>
+struct BwdSmem {
+  static constexpr int TB = kT * TileLay<D>::ROW_B;
+  static constexpr int SST = D + 8;                 // staging row stride (bf16)
+  static constexpr int STAGE = BLK * SST * 2;
+  static constexpr int BYTES = 2 * TB > STAGE ? 2 * TB : STAGE;
+};
+
+// Stage a C-layout [channel][row-in-lane] result of NT tiles per wave as
+// [row][channel] bf16 in LDS and store BLK rows to dst (rows >= nvalid as 0).
+template <int D, int BLK>
+__device__ inline void store_rows(unsigned char* smem, const f32x16 (&acc)[D / 32], __bf16* dst, int nvalid,
+                                  int wave, int lane, int tid) {
+  using SM = BwdSmem<D, BLK>;
+  __bf16* st = reinterpret_cast<__bf16*>(smem);
+  const int gg = lane >> 5, m = lane & 31;
+  const int lr = wave * 32 + m;
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) st[lr * SM::SST + 32 * t + crow(i, gg)] = (__bf16)(lr < nvalid ? acc[t][i] : 0.0f);
+  __syncthreads();
+  for (int i = tid; i < BLK * D / 8; i += BLK * 2) {
+    const int r = i / (D / 8), p = i % (D / 8);
+    *reinterpret_cast<uint4*>(dst + (int64_t)r * D + p * 8) = *reinterpret_cast<const uint4*>(st + r * SM::SST + p * 8);
+  }
+  __syncthreads();
+}
+
+template <int D, int BLK>
+__global__ void __launch_bounds__(BLK * 2)
+k_attn_bwd_dq(Geom g, BwdArgs a, const float* __restrict__ Dq, const float* __restrict__ dden,
+              const __bf16* __restrict__ dU, const __bf16* __restrict__ s_hi, const __bf16* __restrict__ s_lo,
+              const float* __restrict__ z, float* __restrict__ lse_out, float c_log2) {
+  constexpr int NT = D / 32, NC = D / 16, NTH = BLK * 2;
+  using SM = BwdSmem<D, BLK>;
+  __shared__ __align__(16) unsigned char smem[SM::BYTES];
+  unsigned char* Kt = smem;
+  unsigned char* Vt = smem + SM::TB;
+  const int qb = blockIdx.x, bh = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, gg = lane >> 5, m = lane & 31;
+  const int n = qb * BLK + wave * 32 + m;
+  const bool valid = n < g.N;
+  const int nrow = min(n, g.N - 1);
+  const int64_t hb = (int64_t)bh * g.n_pad;
+  const __bf16* Q = static_cast<const __bf16*>(a.q) + hb * D;
+  const __bf16* K = static_cast<const __bf16*>(a.k) + hb * D;
+  const __bf16* V = static_cast<const __bf16*>(a.v) + hb * D;
+  const __bf16* dO = static_cast<const __bf16*>(a.dout) + hb * D;
+
+  bf16x8 qf[NC], dof[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    qf[c] = ld8(Q + (int64_t)nrow * D + 16 * c + 8 * gg);
+    dof[c] = ld8(dO + (int64_t)nrow * D + 16 * c + 8 * gg);
+  }
+  const float Dn = Dq[hb + n];
+  const int64_t r = (int64_t)bh * g.nb + qb;
+  const int e0 = a.row_ptr[r], e1 = a.row_ptr[r + 1];
+  constexpr int SUB = BLK / kT;
+
+  // pass 1: log2-sum-exp of each query over its kept keys
+  float mrun = -INFINITY, lrun = 0.0f;
+  for (int e = e0; e < e1; ++e) {
+    const int kb = a.col_idx[e];
+    for (int sub = 0; sub < SUB; ++sub) {
+      const int key0 = kb * BLK + sub * kT;
+      __syncthreads();
+      load_tile<D, kT, NTH>(Kt, K, key0, g.N - 1, tid);
+      __syncthreads();
+      f32x16 s[2];
+      zero(s[0]);
+      zero(s[1]);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        s[0] = mfma(frag_direct<D>(Kt, 0, c, lane), qf[c], s[0]);
+        s[1] = mfma(frag_direct<D>(Kt, 32, c, lane), qf[c], s[1]);
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = key0 + 32 * kt + crow(i, gg);
+          const float x = key < g.N ? s[kt][i] * c_log2 : -INFINITY;
+          s[kt][i] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = pair_max(mx);
+      const float mnew = fmaxf(mrun, mx);
+      if (mnew > -INFINITY) {
+        lrun *= __builtin_amdgcn_exp2f(mrun - mnew);
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) lrun += __builtin_amdgcn_exp2f(s[kt][i] - mnew);
+        mrun = mnew;
+      }
+    }
+  }
+  const float lt = pair_sum(lrun);
+  const float lse = (valid && lt > 0.0f) ? mrun + log2f(lt) : INFINITY;
+  if (gg == 0) lse_out[hb + n] = lse;
+
+  // pass 2: dQ^T += K^T dS^T
+  f32x16 acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) zero(acc[t]);
+  for (int e = e0; e < e1; ++e) {
+    const int kb = a.col_idx[e];
+    for (int sub = 0; sub < SUB; ++sub) {
+      const int key0 = kb * BLK + sub * kT;
+      __syncthreads();
+      load_tile<D, kT, NTH>(Kt, K, key0, g.N - 1, tid);
+      load_tile<D, kT, NTH>(Vt, V, key0, g.N - 1, tid);
+      __syncthreads();
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        f32x16 s, dp;
+        zero(s);
+        zero(dp);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          s = mfma(frag_direct<D>(Kt, 32 * kt, c, lane), qf[c], s);
+          dp = mfma(frag_direct<D>(Vt, 32 * kt, c, lane), dof[c], dp);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = key0 + 32 * kt + crow(i, gg);
+          const float p = key < g.N ? __builtin_amdgcn_exp2f(s[i] * c_log2 - lse) : 0.0f;
+          s[i] = p * (dp[i] - Dn);
+        }
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const bf16x8 b = c_to_b(s, h2);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) acc[t] = mfma(frag_tr<D>(Kt, 2 * kt + h2, t, lane), b, acc[t]);
+        }
+      }
+    }
+  }
+
+  // linear term: (S dU^T + z dden^T) * [q > 0], S rows c as hi + lo bf16
+  bf16x8 duf[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) duf[c] = ld8(dU + (hb + n) * D + 16 * c + 8 * gg);
+  const float ddn = dden[hb + n];
+  const __bf16* sh = s_hi + (int64_t)bh * D * D;
+  const __bf16* sl = s_lo + (int64_t)bh * D * D;
+  const float* zb = z + (int64_t)bh * D;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    f32x16 lt2;
+    zero(lt2);
+    const int64_t ro = (int64_t)(32 * t + m) * D + 8 * gg;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      lt2 = mfma(ld8(sh + ro + 16 * c), duf[c], lt2);
+      lt2 = mfma(ld8(sl + ro + 16 * c), duf[c], lt2);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int ch = 32 * t + crow(i, gg);
+      const float qv = (float)Q[(int64_t)nrow * D + ch];
+      const float lin = qv > 0.0f ? lt2[i] + zb[ch] * ddn : 0.0f;
+      acc[t][i] = a.scale * acc[t][i] + lin;
+    }
+  }
+  __syncthreads();
+  store_rows<D, BLK>(smem, acc, static_cast<__bf16*>(a.dq) + (hb + (int64_t)qb * BLK) * D, g.N - qb * BLK, wave,
+                     lane, tid);
+}
+
+template <int D, int BLK>
+__global__ void __launch_bounds__(BLK * 2)
+k_attn_bwd_dkdv(Geom g, BwdArgs a, const int32_t* __restrict__ colptr, const int32_t* __restrict__ rowidx,
+                const float* __restrict__ Dq, const float* __restrict__ lse, const __bf16* __restrict__ ds_hi,
+                const __bf16* __restrict__ ds_lo, const __bf16* __restrict__ dst_hi,
+                const __bf16* __restrict__ dst_lo, const float* __restrict__ dz, float c_log2) {
+  constexpr int NT = D / 32, NC = D / 16, NTH = BLK * 2;
+  using SM = BwdSmem<D, BLK>;
+  __shared__ __align__(16) unsigned char smem[SM::BYTES];
+  __shared__ float lse_s[kT], dq_s[kT];
+  unsigned char* Qt = smem;
+  unsigned char* Ot = smem + SM::TB;
+  const int kb = blockIdx.x, bh = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, gg = lane >> 5, m = lane & 31;
+  const int j = kb * BLK + wave * 32 + m;
+  const int jrow = min(j, g.N - 1);
+  const int64_t hb = (int64_t)bh * g.n_pad;
+  const __bf16* Q = static_cast<const __bf16*>(a.q) + hb * D;
+  const __bf16* K = static_cast<const __bf16*>(a.k) + hb * D;
+  const __bf16* V = static_cast<const __bf16*>(a.v) + hb * D;
+  const __bf16* dO = static_cast<const __bf16*>(a.dout) + hb * D;
+
+  bf16x8 kf[NC], vf[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    kf[c] = ld8(K + (int64_t)jrow * D + 16 * c + 8 * gg);
+    vf[c] = ld8(V + (int64_t)jrow * D + 16 * c + 8 * gg);
+  }
+  f32x16 dk[NT], dv[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    zero(dk[t]);
+    zero(dv[t]);
+  }
+  const int64_t col = (int64_t)bh * g.nb + kb;
+  const int p0 = colptr[col], p1 = colptr[col + 1];
+  constexpr int SUB = BLK / kT;
+  for (int e = p0; e < p1; ++e) {
+    const int qb = rowidx[e];
+    for (int sub = 0; sub < SUB; ++sub) {
+      const int q0 = qb * BLK + sub * kT;
+      __syncthreads();
+      load_tile<D, kT, NTH>(Qt, Q, q0, g.N - 1, tid);
+      load_tile<D, kT, NTH>(Ot, dO, q0, g.N - 1, tid);
+      if (tid < kT) {
+        lse_s[tid] = lse[hb + q0 + tid];
+        dq_s[tid] = Dq[hb + q0 + tid];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) {
+        f32x16 s, dp;
+        zero(s);
+        zero(dp);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          s = mfma(frag_direct<D>(Qt, 32 * qs, c, lane), kf[c], s);
+          dp = mfma(frag_direct<D>(Ot, 32 * qs, c, lane), vf[c], dp);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int qi = 32 * qs + crow(i, gg);
+          const float p = __builtin_amdgcn_exp2f(s[i] * c_log2 - lse_s[qi]);  // 0 for padded queries (lse = inf)
+          s[i] = p;
+          dp[i] = p * (dp[i] - dq_s[qi]);
+        }
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const bf16x8 bp = c_to_b(s, h2);
+          const bf16x8 bd = c_to_b(dp, h2);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            dv[t] = mfma(frag_tr<D>(Ot, 2 * qs + h2, t, lane), bp, dv[t]);
+            dk[t] = mfma(frag_tr<D>(Qt, 2 * qs + h2, t, lane), bd, dk[t]);
+          }
+        }
+      }
+    }
+  }
+
+  // linear terms: dv += dS_lin^T phi(K)^T; dk += (dS_lin V^T + dz) * [k > 0]
+  const int64_t mb = (int64_t)bh * D * D;
+  const float* dzb = dz + (int64_t)bh * D;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    f32x16 lv, lk;
+    zero(lv);
+    zero(lk);
+    const int64_t ro = (int64_t)(32 * t + m) * D + 8 * gg;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const bf16x8 pk = relu8(kf[c]);
+      lv = mfma(ld8(dst_hi + mb + ro + 16 * c), pk, lv);
+      lv = mfma(ld8(dst_lo + mb + ro + 16 * c), pk, lv);
+      lk = mfma(ld8(ds_hi + mb + ro + 16 * c), vf[c], lk);
+      lk = mfma(ld8(ds_lo + mb + ro + 16 * c), vf[c], lk);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int ch = 32 * t + crow(i, gg);
+      const float kv = (float)K[(int64_t)jrow * D + ch];
+      dv[t][i] += lv[i];
+      dk[t][i] = a.scale * dk[t][i] + (kv > 0.0f ? lk[i] + dzb[ch] : 0.0f);
+    }
+  }
+  const int nvalid = g.N - kb * BLK;
+  __syncthreads();
+  store_rows<D, BLK>(smem, dk, static_cast<__bf16*>(a.dk) + (hb + (int64_t)kb * BLK) * D, nvalid, wave, lane, tid);
+  store_rows<D, BLK>(smem, dv, static_cast<__bf16*>(a.dv) + (hb + (int64_t)kb * BLK) * D, nvalid, wave, lane, tid);
+}
+
+template <int D, int BLK>
+hipError_t launch_bwd_t(const Geom& g, const BwdArgs& a, char* ws, const BwdWorkspace& L, hipStream_t st) {
+  auto B16 = [&](size_t off) { return reinterpret_cast<const __bf16*>(ws + off); };
+  auto F32 = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+  const float c_log2 = a.scale * 1.4426950408889634f;
+  const dim3 grid(g.nb, g.B * g.Hh);
+  hipLaunchKernelGGL((k_attn_bwd_dq<D, BLK>), grid, dim3(BLK * 2), 0, st, g, a, F32(L.off_dq), F32(L.off_dden),
+                     B16(L.off_du), B16(L.off_s_hi), B16(L.off_s_lo), F32(L.off_z), F32(L.off_lse), c_log2);
+  hipLaunchKernelGGL((k_attn_bwd_dkdv<D, BLK>), grid, dim3(BLK * 2), 0, st, g, a,
+                     reinterpret_cast<const int32_t*>(ws + L.off_colptr),
+                     reinterpret_cast<const int32_t*>(ws + L.off_rowidx), F32(L.off_dq), F32(L.off_lse),
+                     B16(L.off_ds_hi), B16(L.off_ds_lo), B16(L.off_dst_hi), B16(L.off_dst_lo), F32(L.off_dz),
+                     c_log2);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd(const Geom& g, const BwdArgs& a, char* ws, const BwdWorkspace& L, hipStream_t st) {
+  if (g.D == 128 && g.blk == 64) return launch_bwd_t<128, 64>(g, a, ws, L, st);
+  if (g.D == 128 && g.blk == 128) return launch_bwd_t<128, 128>(g, a, ws, L, st);
+  if (g.D == 64 && g.blk == 64) return launch_bwd_t<64, 64>(g, a, ws, L, st);
+  if (g.D == 64 && g.blk == 128) return launch_bwd_t<64, 128>(g, a, ws, L, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace salad

@@ -1,0 +1,132 @@
+// bwd_common.h - LDS tile layout and MFMA fragment helpers of the backward
+// kernels (v_mfma_f32_32x32x16_bf16, fp32 accumulate).
+//
+// Operand layouts of the 32x32x16 bf16 MFMA, lane l = 32*g + m (g = l/32):
+//   A (32 x 16): lane l holds A[m][8g .. 8g+7];  B (16 x 32): B[8g .. 8g+7][m];
+//   C (32 x 32): register i of lane l holds C[8*(i/4) + 4g + i%4][m].
+// A tile of C whose column index is the lane (a query or a key) therefore
+// serves directly as the B operand of the next product when its 32 rows are
+// the contraction: for 16-row step h2 the lane's slot j carries row
+// 16*h2 + 8*(j/4) + 4g + j%4 ("slot order"); the matching A operand is read
+// from a row-major LDS tile with the transpose read ds_read_b64_tr_b16, which
+// hands lane l the column 32t + m of 4 consecutive rows.
+//
+// LDS tiles hold rows of D bf16 in 16-byte chunks, chunk p of row r stored at
+// chunk p ^ swz(r).  swz gives 16 consecutive rows 16 different chunks (direct
+// 16-byte fragment reads of one logical chunk: conflict free) and puts 4
+// consecutive rows in 4 disjoint groups of 4 chunks (transpose reads: conflict
+// free).
+#pragma once
+
+#include "internal.h"
+
+namespace salad {
+namespace bwd {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+template <int D>
+struct TileLay {
+  static constexpr int CPR = D / 8;        // 16-byte chunks per row
+  static constexpr int ROW_B = D * 2;      // bytes per row
+  static constexpr int RPB = 16 / CPR;     // rows per 256-byte bank period
+  __device__ static int swz(int r) { return 4 * ((r / RPB) % (4 / RPB)) + ((r >> 2) & 3); }
+  __device__ static int off(int r, int chunk) { return r * ROW_B + ((chunk ^ swz(r)) << 4); }
+};
+
+__device__ inline f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ inline void zero(f32x16& c) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) c[i] = 0.0f;
+}
+
+__device__ inline uint32_t pack2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+
+// Row m of a C tile, as the B operand of a product whose contraction runs over
+// the tile's rows: step h2 (rows 16*h2 .. 16*h2+15 in slot order).
+__device__ inline bf16x8 c_to_b(const f32x16& c, int h2) {
+  return __builtin_bit_cast(bf16x8, make_uint4(pack2(c[8 * h2 + 0], c[8 * h2 + 1]), pack2(c[8 * h2 + 2], c[8 * h2 + 3]),
+                                               pack2(c[8 * h2 + 4], c[8 * h2 + 5]), pack2(c[8 * h2 + 6], c[8 * h2 + 7])));
+}
+
+// Direct fragment: lane l gets tile[r0 + l%32][16*c + 8*(l/32) .. +7]
+// (A operand with rows = tile rows, or B operand with columns = tile rows;
+// contraction over the tile's columns).
+template <int D>
+__device__ inline bf16x8 frag_direct(const unsigned char* tile, int r0, int c, int lane) {
+  using TL = TileLay<D>;
+  const int r = r0 + (lane & 31);
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(tile + TL::off(r, 2 * c + (lane >> 5))));
+}
+
+// Transposed fragment: lane l gets tile[rows 16*ks + slot order][32*t + l%32]
+// (A operand whose rows are tile columns 32t .. 32t+31, contraction over the
+// tile rows 16ks .. 16ks+15 in slot order).
+template <int D>
+__device__ inline bf16x8 frag_tr(const unsigned char* tile, int ks, int t, int lane) {
+  using TL = TileLay<D>;
+  const int sl = lane & 15, dh = (lane >> 4) & 1, g = lane >> 5;
+  const int chunk = 4 * t + 2 * dh + ((sl & 3) >> 1);
+  uint2 tr[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int row = ks * 16 + 8 * h + 4 * g + (sl >> 2);
+    const unsigned char* ad = tile + TL::off(row, chunk) + (sl & 1) * 8;
+    tr[h] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                          (__attribute__((address_space(3))) s16x4*)(ad)));
+  }
+  return __builtin_bit_cast(bf16x8, make_uint4(tr[0].x, tr[0].y, tr[1].x, tr[1].y));
+}
+
+// Copy rows [row0, row0 + ROWS) of a row-major [*, D] bf16 array into an LDS
+// tile (rows clamped to `last`, so every read is in bounds).  NT threads.
+template <int D, int ROWS, int NT>
+__device__ inline void load_tile(unsigned char* tile, const __bf16* src, int row0, int last, int tid) {
+  using TL = TileLay<D>;
+  constexpr int CH = ROWS * TL::CPR;
+#pragma unroll
+  for (int i = tid; i < CH; i += NT) {
+    const int r = i / TL::CPR, p = i % TL::CPR;
+    const int gr = min(row0 + r, last);
+    const uint4 v = *reinterpret_cast<const uint4*>(src + (int64_t)gr * D + p * 8);
+    *reinterpret_cast<uint4*>(tile + TL::off(r, p)) = v;
+  }
+}
+
+// fp32 value rounded to bf16 (hi) and the bf16 of the remainder (lo).
+__device__ inline void split_hi_lo(float x, __bf16& hi, __bf16& lo) {
+  hi = (__bf16)x;
+  lo = (__bf16)(x - (float)hi);
+}
+
+__device__ inline bf16x8 relu8(bf16x8 x) {
+  uint4 u = __builtin_bit_cast(uint4, x);
+  auto r = [](uint32_t w) {
+    return ((w & 0x8000u) ? 0u : (w & 0xffffu)) | ((w & 0x80000000u) ? 0u : (w & 0xffff0000u));
+  };
+  u.x = r(u.x); u.y = r(u.y); u.z = r(u.z); u.w = r(u.w);
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+__device__ inline float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ inline float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// C-layout row index of register i for lane group g
+__device__ inline int crow(int i, int g) { return 8 * (i >> 2) + 4 * g + (i & 3); }
+
+}  // namespace bwd
+}  // namespace salad

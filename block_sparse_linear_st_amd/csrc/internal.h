@@ -77,6 +77,26 @@ struct Workspace {
   size_t mask_end, lin_end;
 };
 
+// Backward workspace: the forward layout (its linear-state partials are reused
+// to rebuild S, z) followed by the regions of the backward pass.
+struct BwdWorkspace {
+  Workspace fwd;
+  size_t bytes;
+  int red_splits, red_chunk;          // token split of the dS / dW reduction
+  size_t off_s32, off_z;              // float [BH][D][D], [BH][D]: S, z
+  size_t off_s_hi, off_s_lo;          // bf16 [BH][D][D]: S (rows c)
+  size_t off_st_hi, off_st_lo;        // bf16 [BH][D][D]: S^T (rows e)
+  size_t off_dq, off_dden, off_lse;   // float [BH][n_pad]: D_i, dden_i, (spare)
+  size_t off_du, off_ol;              // bf16 [BH][n_pad][D]: dU, o_l
+  size_t off_gpart;                   // float [BH][n_pad/32]: dgate partials
+  size_t off_dspart, off_dzpart, off_dwpart;  // float [splits][BH][D*D | D | D*D]
+  size_t off_ds_hi, off_ds_lo;        // bf16 [BH][D][D]: dS_lin (rows c)
+  size_t off_dst_hi, off_dst_lo;      // bf16 [BH][D][D]: dS_lin^T (rows e)
+  size_t off_dz;                      // float [BH][D]: dz_lin
+  size_t off_colcnt, off_colptr;      // int32 [BH*nb], [BH*nb + 1]
+  size_t off_rowidx;                  // int32 [BH*nb*nb]
+};
+
 SALAD_HIDDEN bool make_geom(const salad_shape* s, Geom* g);
 SALAD_HIDDEN void make_cuboid(const salad_shape* s, Cuboid* c);
 SALAD_HIDDEN Workspace plan_workspace(const Geom& g, const Cuboid& cu, int dtype);
@@ -122,6 +142,38 @@ SALAD_HIDDEN hipError_t launch_linear_fold(const Geom& g, int dtype, const float
                                            const void* w_lin, int mode, float drop_tau,
                                            float* S_out, float* z_out, char* ws,
                                            const Workspace& L, hipStream_t st);
+
+// ---- backward (linear_bwd.hip, attn_bwd.hip) ---------------------------------
+SALAD_HIDDEN BwdWorkspace plan_bwd_workspace(const Geom& g, const Cuboid& cu, int dtype);
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  const float* gate;
+  const void* w_lin;
+  const void* out;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dw_lin;
+  float* dgate;
+  float eps;
+  float scale;
+};
+// Linear-branch backward up to dS_lin, dz_lin, dW_lin, dgate and the per-token
+// D_i, dU, dden (needs S, z in the workspace).
+SALAD_HIDDEN hipError_t launch_linear_bwd(const Geom& g, const BwdArgs& a, char* ws,
+                                          const BwdWorkspace& L, hipStream_t st);
+// Transposed mask (CSC) of the CSR rows.
+SALAD_HIDDEN hipError_t launch_mask_transpose(const Geom& g, const int32_t* row_ptr,
+                                              const int32_t* col_idx, char* ws,
+                                              const BwdWorkspace& L, hipStream_t st);
+// Sparse-branch backward plus the linear parts of dq, dk, dv.
+SALAD_HIDDEN hipError_t launch_attn_bwd(const Geom& g, const BwdArgs& a, char* ws,
+                                        const BwdWorkspace& L, hipStream_t st);
 
 // ---- attention (attn_bf16.hip, attn_f32.hip) --------------------------------
 struct AttnArgs {

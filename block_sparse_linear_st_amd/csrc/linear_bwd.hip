@@ -1,0 +1,449 @@
+// linear_bwd.hip - backward of the ReLU linear-attention branch and of the
+// gated projection, plus the transposed (CSC) block mask the key-side sparse
+// kernel walks.
+//
+// The layer is fine-tuned ("SALAD" explainer, technical summary section 2.2:
+// the projection on the linear branch is a learnable, zero-initialised layer
+// and the scale s comes from a small learned module; section 3: the fine-tuning
+// budget), so the gradients of out = o_s + g (o_l W_lin) are needed with
+// respect to Q, K, V, W_lin and g.  With phi = ReLU, u = phi(q) S,
+// den = phi(q).z + eps, o_l = u / den, t = dout W_lin^T and r = <t, o_l>:
+//
+//   dgate  = sum_n r_n                      dW_lin = sum_heads g o_l^T dout
+//   D_n    = <dout_n, out_n> - g r_n        (= <dout_n, o_s,n>, for the softmax backward)
+//   dU_n   = g t_n / den_n                  dden_n = -g r_n / den_n
+//   dq_lin = (S dU_n + z dden_n) * [q_n > 0]
+//   dS     = sum_n phi(q_n) dU_n^T          dz = sum_n phi(q_n) dden_n
+//   dk_lin = (dS v_j + dz) * [k_j > 0]      dv_lin = dS^T phi(k_j)
+//
+// Kernels: k_lin_bwd_tok (one 64-token tile per workgroup, tokens in lanes:
+// u^T = S^T phi(q)^T and t^T = W dout^T on MFMAs, S carried as hi + lo bf16)
+// writes D, dden, dU, o_l and per-wave dgate sums; k_lin_bwd_red reduces
+// dS, dz and the per-head dW over token chunks with the token index as the MFMA
+// contraction (both operands by LDS transpose reads); the folds sum the chunks
+// in a fixed order (bitwise reproducible) and lay dS out as hi + lo bf16 in
+// both orientations.  dq_lin, dk_lin and dv_lin are formed in the sparse
+// kernels (attn_bwd.hip), which hold the needed operands in registers.
+#include <algorithm>
+
+#include "bwd_common.h"
+
+namespace salad {
+
+using namespace bwd;
+
+namespace {
+
+constexpr int kTT = 64;  // tokens per tile
+
+__device__ inline bf16x8 ld8(const __bf16* p) { return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p)); }
+
+template <int D>
+__global__ void __launch_bounds__(128)
+k_lin_bwd_tok(Geom g, const __bf16* __restrict__ Q, const __bf16* __restrict__ dO, const __bf16* __restrict__ Out,
+              const __bf16* __restrict__ st_hi, const __bf16* __restrict__ st_lo, const float* __restrict__ z,
+              const __bf16* __restrict__ W, const float* __restrict__ gate, float eps, float* __restrict__ Dq,
+              float* __restrict__ dden, __bf16* __restrict__ dU, __bf16* __restrict__ OL, float* __restrict__ gpart) {
+  constexpr int NC = D / 16, NT = D / 32, SST = D + 8;
+  __shared__ __align__(16) __bf16 stage[kTT * SST];
+  const int bh = blockIdx.y, tile = blockIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, gg = lane >> 5, m = lane & 31;
+  const int n = tile * kTT + wave * 32 + m;
+  const bool valid = n < g.N;
+  const int64_t row = ((int64_t)bh * g.n_pad + n) * D;
+  const float* zb = z + (int64_t)bh * D;
+
+  bf16x8 qf[NC], dof[NC];
+  float den_p = 0.0f, dot_p = 0.0f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int ch = 16 * c + 8 * gg;
+    qf[c] = relu8(ld8(Q + row + ch));
+    dof[c] = ld8(dO + row + ch);
+    const bf16x8 o8 = ld8(Out + row + ch);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      den_p += (float)qf[c][j] * zb[ch + j];
+      dot_p += (float)dof[c][j] * (float)o8[j];
+    }
+  }
+  const float den = pair_sum(den_p) + eps;
+  const float dot_out = pair_sum(dot_p);
+  const float inv = 1.0f / den;
+
+  f32x16 u[NT], tt[NT];
+  const __bf16* sth = st_hi + (int64_t)bh * D * D;
+  const __bf16* stl = st_lo + (int64_t)bh * D * D;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    zero(u[t]);
+    zero(tt[t]);
+    const int64_t ro = (int64_t)(32 * t + m) * D + 8 * gg;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      u[t] = mfma(ld8(sth + ro + 16 * c), qf[c], u[t]);
+      u[t] = mfma(ld8(stl + ro + 16 * c), qf[c], u[t]);
+      tt[t] = mfma(ld8(W + ro + 16 * c), dof[c], tt[t]);
+    }
+  }
+  float r = 0.0f;
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      u[t][i] *= inv;  // o_l^T
+      r += tt[t][i] * u[t][i];
+    }
+  r = pair_sum(r);
+  const float gv = gate[bh];
+  if (gg == 0) {
+    Dq[(int64_t)bh * g.n_pad + n] = valid ? dot_out - gv * r : 0.0f;
+    dden[(int64_t)bh * g.n_pad + n] = valid ? -gv * r * inv : 0.0f;
+  }
+  float rv = (valid && gg == 0) ? r : 0.0f;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) rv += __shfl_xor(rv, o, 64);
+  if (lane == 0) gpart[(int64_t)bh * (g.n_pad / 32) + tile * 2 + wave] = rv;
+
+  // dU = g t / den and o_l, staged through LDS as [token][channel] for coalesced stores
+  const int lr = wave * 32 + m;
+  const float su = valid ? gv * inv : 0.0f;
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float x = pass == 0 ? tt[t][i] * su : (valid ? u[t][i] : 0.0f);
+        stage[lr * SST + 32 * t + crow(i, gg)] = (__bf16)x;
+      }
+    __syncthreads();
+    __bf16* dst = (pass == 0 ? dU : OL) + ((int64_t)bh * g.n_pad + tile * kTT) * D;
+    for (int i = tid; i < kTT * D / 8; i += 128) {
+      const int rr = i / (D / 8), p = i % (D / 8);
+      *reinterpret_cast<uint4*>(dst + (int64_t)rr * D + p * 8) =
+          *reinterpret_cast<const uint4*>(stage + rr * SST + p * 8);
+    }
+    __syncthreads();
+  }
+}
+
+// S (fp32, rows c) -> hi + lo bf16 in both orientations.
+template <int D>
+__global__ void __launch_bounds__(256)
+k_split_state(int64_t total, const float* __restrict__ S, __bf16* s_hi, __bf16* s_lo, __bf16* st_hi,
+              __bf16* st_lo) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const int64_t bh = i / (D * D);
+  const int c = (int)(i / D % D), e = (int)(i % D);
+  __bf16 hi, lo;
+  split_hi_lo(S[i], hi, lo);
+  s_hi[i] = hi;
+  s_lo[i] = lo;
+  const int64_t j = (bh * D + e) * D + c;
+  st_hi[j] = hi;
+  st_lo[j] = lo;
+}
+
+// Zero the slots of tokens at or past `valid` in a transposed fragment (slot
+// order rows 16*ks + 8*(j/4) + 4*g + j%4 of the tile).
+__device__ inline bf16x8 mask_slots(bf16x8 f, int ks, int valid, int gg) {
+  if (16 * ks + 16 <= valid) return f;
+  uint4 u = __builtin_bit_cast(uint4, f);
+  uint32_t* w = reinterpret_cast<uint32_t*>(&u);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int tok = 16 * ks + 8 * (j >> 2) + 4 * gg + (j & 3);
+    if (tok >= valid) w[j >> 1] &= (j & 1) ? 0x0000ffffu : 0xffff0000u;
+  }
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+template <int D>
+__global__ void __launch_bounds__(256)
+k_lin_bwd_red(Geom g, int chunk, const __bf16* __restrict__ Q, const __bf16* __restrict__ dU,
+              const __bf16* __restrict__ OL, const __bf16* __restrict__ dO, const float* __restrict__ dden,
+              float* __restrict__ dspart, float* __restrict__ dzpart, float* __restrict__ dwpart) {
+  using TL = TileLay<D>;
+  constexpr int TD = D / 32, TPW = TD * TD / 4;
+  constexpr int TB = kTT * TL::ROW_B;
+  __shared__ __align__(16) unsigned char smem[4 * TB];
+  __shared__ float dd[kTT];
+  unsigned char* Qt = smem;
+  unsigned char* Ut = smem + TB;
+  unsigned char* Lt = smem + 2 * TB;
+  unsigned char* Ot = smem + 3 * TB;
+  const int split = blockIdx.x, bh = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, gg = lane >> 5, m = lane & 31;
+  const int n0 = split * chunk, n1 = min(g.N, n0 + chunk);
+  const int64_t hb = (int64_t)bh * g.n_pad;
+  const int ti = TD == 4 ? wave : wave >> 1;
+  const int tj0 = TD == 4 ? 0 : (wave & 1);
+
+  f32x16 as[TPW], aw[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    zero(as[t]);
+    zero(aw[t]);
+  }
+  float zacc = 0.0f;
+  for (int t0 = n0; t0 < n1; t0 += kTT) {
+    load_tile<D, kTT, 256>(Qt, Q + hb * D, t0, g.N - 1, tid);
+    load_tile<D, kTT, 256>(Ut, dU + hb * D, t0, g.n_pad - 1, tid);
+    load_tile<D, kTT, 256>(Lt, OL + hb * D, t0, g.n_pad - 1, tid);
+    load_tile<D, kTT, 256>(Ot, dO + hb * D, t0, g.N - 1, tid);
+    if (tid < kTT) dd[tid] = t0 + tid < n1 ? dden[hb + t0 + tid] : 0.0f;
+    __syncthreads();
+    const int valid = n1 - t0;
+#pragma unroll
+    for (int ks = 0; ks < kTT / 16; ++ks) {
+      const bf16x8 aq = mask_slots(relu8(frag_tr<D>(Qt, ks, ti, lane)), ks, valid, gg);
+      const bf16x8 al = mask_slots(frag_tr<D>(Lt, ks, ti, lane), ks, valid, gg);
+      if (tj0 == 0) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) zacc += (float)aq[j] * dd[16 * ks + 8 * (j >> 2) + 4 * gg + (j & 3)];
+      }
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        const int tj = TD == 4 ? t : tj0;
+        as[t] = mfma(aq, frag_tr<D>(Ut, ks, tj, lane), as[t]);
+        aw[t] = mfma(al, frag_tr<D>(Ot, ks, tj, lane), aw[t]);
+      }
+    }
+    __syncthreads();
+  }
+  const int64_t po = ((int64_t)split * g.B * g.Hh + bh) * D * D;
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int tj = TD == 4 ? t : tj0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = ti * 32 + crow(i, gg);
+      dspart[po + (int64_t)r * D + tj * 32 + m] = as[t][i];
+      dwpart[po + (int64_t)r * D + tj * 32 + m] = aw[t][i];
+    }
+  }
+  const float zs = pair_sum(zacc);
+  if (tj0 == 0 && gg == 0) dzpart[((int64_t)split * g.B * g.Hh + bh) * D + ti * 32 + m] = zs;
+}
+
+// dS_lin, dz_lin: split sums in order; dS as hi + lo bf16, rows c and rows e.
+template <int D>
+__global__ void __launch_bounds__(256)
+k_fold_ds(Geom g, int splits, const float* __restrict__ dspart, const float* __restrict__ dzpart,
+          __bf16* ds_hi, __bf16* ds_lo, __bf16* dst_hi, __bf16* dst_lo, float* dz) {
+  const int bh = blockIdx.y;
+  const int idx = blockIdx.x * 256 + threadIdx.x;  // c * D + e
+  const int64_t BH = (int64_t)g.B * g.Hh;
+  float s = 0.0f;
+  for (int sp = 0; sp < splits; ++sp) s += dspart[((int64_t)sp * BH + bh) * D * D + idx];
+  const int c = idx / D, e = idx % D;
+  __bf16 hi, lo;
+  split_hi_lo(s, hi, lo);
+  ds_hi[(int64_t)bh * D * D + idx] = hi;
+  ds_lo[(int64_t)bh * D * D + idx] = lo;
+  dst_hi[((int64_t)bh * D + e) * D + c] = hi;
+  dst_lo[((int64_t)bh * D + e) * D + c] = lo;
+  if (blockIdx.x == 0 && threadIdx.x < D) {
+    float zz = 0.0f;
+    for (int sp = 0; sp < splits; ++sp) zz += dzpart[((int64_t)sp * BH + bh) * D + threadIdx.x];
+    dz[(int64_t)bh * D + threadIdx.x] = zz;
+  }
+}
+
+// dW_lin = sum over heads (in order) of g * (sum over splits, in order).
+template <int D>
+__global__ void __launch_bounds__(256)
+k_fold_dw(Geom g, int splits, const float* __restrict__ dwpart, const float* __restrict__ gate,
+          float* __restrict__ dw) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  const int64_t BH = (int64_t)g.B * g.Hh;
+  float acc = 0.0f;
+  for (int64_t bh = 0; bh < BH; ++bh) {
+    float s = 0.0f;
+    for (int sp = 0; sp < splits; ++sp) s += dwpart[((int64_t)sp * BH + bh) * D * D + idx];
+    acc += gate[bh] * s;
+  }
+  dw[idx] = acc;
+}
+
+__global__ void __launch_bounds__(64)
+k_fold_dgate(Geom g, const float* __restrict__ gpart, float* __restrict__ dgate) {
+  const int bh = blockIdx.x;
+  const int parts = g.n_pad / 32;
+  if (threadIdx.x != 0) return;
+  float s = 0.0f;
+  for (int i = 0; i < parts; ++i) s += gpart[(int64_t)bh * parts + i];
+  dgate[bh] = s;
+}
+
+// ---- transposed mask ----------------------------------------------------------
+
+__device__ inline bool row_has(const int32_t* col_idx, int a, int b, int kb) {
+  while (a < b) {
+    const int mid = (a + b) >> 1;
+    const int v = col_idx[mid];
+    if (v == kb) return true;
+    if (v < kb) a = mid + 1; else b = mid;
+  }
+  return false;
+}
+
+__global__ void __launch_bounds__(256)
+k_csc_count(Geom g, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
+            int32_t* __restrict__ colcnt) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= (int64_t)g.B * g.Hh * g.nb) return;
+  const int64_t bh = i / g.nb;
+  const int kb = (int)(i % g.nb);
+  int cnt = 0;
+  for (int qb = 0; qb < g.nb; ++qb) {
+    const int64_t r = bh * g.nb + qb;
+    cnt += row_has(col_idx, row_ptr[r], row_ptr[r + 1], kb) ? 1 : 0;
+  }
+  colcnt[i] = cnt;
+}
+
+__global__ void __launch_bounds__(256)
+k_csc_fill(Geom g, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
+           const int32_t* __restrict__ colptr, int32_t* __restrict__ rowidx) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= (int64_t)g.B * g.Hh * g.nb) return;
+  const int64_t bh = i / g.nb;
+  const int kb = (int)(i % g.nb);
+  int p = colptr[i];
+  for (int qb = 0; qb < g.nb; ++qb) {
+    const int64_t r = bh * g.nb + qb;
+    if (row_has(col_idx, row_ptr[r], row_ptr[r + 1], kb)) rowidx[p++] = qb;
+  }
+}
+
+// Exclusive scan of n int32 counts into out[0..n] (out[n] = total), one workgroup.
+__global__ void __launch_bounds__(1024)
+k_scan_counts(const int32_t* __restrict__ in, int64_t n, int32_t* __restrict__ out) {
+  __shared__ int64_t part[1024];
+  const int t = threadIdx.x;
+  const int64_t per = (n + 1023) / 1024;
+  const int64_t a = min(n, t * per), b = min(n, a + per);
+  int64_t s = 0;
+  for (int64_t i = a; i < b; ++i) s += in[i];
+  part[t] = s;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {  // inclusive Hillis-Steele scan of the 1024 sums
+    const int64_t v = t >= o ? part[t - o] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  int64_t run = part[t] - s;
+  for (int64_t i = a; i < b; ++i) {
+    out[i] = (int32_t)run;
+    run += in[i];
+  }
+  if (t == 1023) out[n] = (int32_t)part[1023];
+}
+
+}  // namespace
+
+BwdWorkspace plan_bwd_workspace(const Geom& g, const Cuboid& cu, int dtype) {
+  BwdWorkspace L{};
+  L.fwd = plan_workspace(g, cu, dtype);
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t BH = (size_t)g.B * g.Hh, D = g.D, nb = g.nb, np = g.n_pad;
+  int splits = (int)std::max<size_t>(1, (512 + BH - 1) / BH);
+  splits = std::min(splits, (g.N + 63) / 64);
+  int chunk = (g.N + splits - 1) / splits;
+  chunk = (chunk + 63) / 64 * 64;
+  splits = (g.N + chunk - 1) / chunk;
+  L.red_splits = splits;
+  L.red_chunk = chunk;
+  size_t off = al(L.fwd.bytes);
+  L.off_s32 = off;    off = al(off + BH * D * D * 4);
+  L.off_z = off;      off = al(off + BH * D * 4);
+  L.off_s_hi = off;   off = al(off + BH * D * D * 2);
+  L.off_s_lo = off;   off = al(off + BH * D * D * 2);
+  L.off_st_hi = off;  off = al(off + BH * D * D * 2);
+  L.off_st_lo = off;  off = al(off + BH * D * D * 2);
+  L.off_dq = off;     off = al(off + BH * np * 4);
+  L.off_dden = off;   off = al(off + BH * np * 4);
+  L.off_lse = off;    off = al(off + BH * np * 4);
+  L.off_du = off;     off = al(off + BH * np * D * 2);
+  L.off_ol = off;     off = al(off + BH * np * D * 2);
+  L.off_gpart = off;  off = al(off + BH * (np / 32) * 4);
+  L.off_dspart = off; off = al(off + (size_t)splits * BH * D * D * 4);
+  L.off_dzpart = off; off = al(off + (size_t)splits * BH * D * 4);
+  L.off_dwpart = off; off = al(off + (size_t)splits * BH * D * D * 4);
+  L.off_ds_hi = off;  off = al(off + BH * D * D * 2);
+  L.off_ds_lo = off;  off = al(off + BH * D * D * 2);
+  L.off_dst_hi = off; off = al(off + BH * D * D * 2);
+  L.off_dst_lo = off; off = al(off + BH * D * D * 2);
+  L.off_dz = off;     off = al(off + BH * D * 4);
+  L.off_colcnt = off; off = al(off + BH * nb * 4);
+  L.off_colptr = off; off = al(off + (BH * nb + 1) * 4);
+  L.off_rowidx = off; off = al(off + BH * nb * nb * 4);
+  L.bytes = off;
+  return L;
+}
+
+hipError_t launch_linear_bwd(const Geom& g, const BwdArgs& a, char* ws, const BwdWorkspace& L,
+                             hipStream_t st) {
+  const int64_t BH = (int64_t)g.B * g.Hh;
+  auto B16 = [&](size_t off) { return reinterpret_cast<__bf16*>(ws + off); };
+  auto F32 = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+  const __bf16* Q = static_cast<const __bf16*>(a.q);
+  const __bf16* dO = static_cast<const __bf16*>(a.dout);
+  const __bf16* Out = static_cast<const __bf16*>(a.out);
+  const __bf16* W = static_cast<const __bf16*>(a.w_lin);
+  const int64_t tot = BH * g.D * g.D;
+  const dim3 tg(g.n_pad / kTT, (unsigned)BH);
+  const dim3 rg(L.red_splits, (unsigned)BH);
+  const dim3 fg(g.D * g.D / 256, (unsigned)BH);
+  if (g.D == 128) {
+    hipLaunchKernelGGL(k_split_state<128>, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, tot,
+                       F32(L.off_s32), B16(L.off_s_hi), B16(L.off_s_lo), B16(L.off_st_hi), B16(L.off_st_lo));
+    hipLaunchKernelGGL(k_lin_bwd_tok<128>, tg, dim3(128), 0, st, g, Q, dO, Out, B16(L.off_st_hi),
+                       B16(L.off_st_lo), F32(L.off_z), W, a.gate, a.eps, F32(L.off_dq), F32(L.off_dden),
+                       B16(L.off_du), B16(L.off_ol), F32(L.off_gpart));
+    hipLaunchKernelGGL(k_lin_bwd_red<128>, rg, dim3(256), 0, st, g, L.red_chunk, Q, B16(L.off_du),
+                       B16(L.off_ol), dO, F32(L.off_dden), F32(L.off_dspart), F32(L.off_dzpart),
+                       F32(L.off_dwpart));
+    hipLaunchKernelGGL(k_fold_ds<128>, fg, dim3(256), 0, st, g, L.red_splits, F32(L.off_dspart),
+                       F32(L.off_dzpart), B16(L.off_ds_hi), B16(L.off_ds_lo), B16(L.off_dst_hi),
+                       B16(L.off_dst_lo), F32(L.off_dz));
+    hipLaunchKernelGGL(k_fold_dw<128>, dim3(128 * 128 / 256), dim3(256), 0, st, g, L.red_splits,
+                       F32(L.off_dwpart), a.gate, a.dw_lin);
+  } else if (g.D == 64) {
+    hipLaunchKernelGGL(k_split_state<64>, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, tot,
+                       F32(L.off_s32), B16(L.off_s_hi), B16(L.off_s_lo), B16(L.off_st_hi), B16(L.off_st_lo));
+    hipLaunchKernelGGL(k_lin_bwd_tok<64>, tg, dim3(128), 0, st, g, Q, dO, Out, B16(L.off_st_hi),
+                       B16(L.off_st_lo), F32(L.off_z), W, a.gate, a.eps, F32(L.off_dq), F32(L.off_dden),
+                       B16(L.off_du), B16(L.off_ol), F32(L.off_gpart));
+    hipLaunchKernelGGL(k_lin_bwd_red<64>, rg, dim3(256), 0, st, g, L.red_chunk, Q, B16(L.off_du),
+                       B16(L.off_ol), dO, F32(L.off_dden), F32(L.off_dspart), F32(L.off_dzpart),
+                       F32(L.off_dwpart));
+    hipLaunchKernelGGL(k_fold_ds<64>, fg, dim3(256), 0, st, g, L.red_splits, F32(L.off_dspart),
+                       F32(L.off_dzpart), B16(L.off_ds_hi), B16(L.off_ds_lo), B16(L.off_dst_hi),
+                       B16(L.off_dst_lo), F32(L.off_dz));
+    hipLaunchKernelGGL(k_fold_dw<64>, dim3(64 * 64 / 256), dim3(256), 0, st, g, L.red_splits,
+                       F32(L.off_dwpart), a.gate, a.dw_lin);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  hipLaunchKernelGGL(k_fold_dgate, dim3((unsigned)BH), dim3(64), 0, st, g, F32(L.off_gpart), a.dgate);
+  return hipGetLastError();
+}
+
+hipError_t launch_mask_transpose(const Geom& g, const int32_t* row_ptr, const int32_t* col_idx, char* ws,
+                                 const BwdWorkspace& L, hipStream_t st) {
+  const int64_t n = (int64_t)g.B * g.Hh * g.nb;
+  int32_t* cnt = reinterpret_cast<int32_t*>(ws + L.off_colcnt);
+  int32_t* ptr = reinterpret_cast<int32_t*>(ws + L.off_colptr);
+  int32_t* idx = reinterpret_cast<int32_t*>(ws + L.off_rowidx);
+  const dim3 grid((unsigned)((n + 255) / 256));
+  hipLaunchKernelGGL(k_csc_count, grid, dim3(256), 0, st, g, row_ptr, col_idx, cnt);
+  hipLaunchKernelGGL(k_scan_counts, dim3(1), dim3(1024), 0, st, cnt, n, ptr);
+  hipLaunchKernelGGL(k_csc_fill, grid, dim3(256), 0, st, g, row_ptr, col_idx, ptr, idx);
+  return hipGetLastError();
+}
+
+}  // namespace salad

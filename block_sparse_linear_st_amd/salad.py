@@ -61,6 +61,9 @@ _SIGS = {
     "salad_workspace_bytes": (_sz, [ctypes.POINTER(salad_shape)]),
     "salad_build_mask": (ctypes.c_int, [ctypes.POINTER(salad_shape), ctypes.POINTER(salad_mask_spec),
                                         _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "salad_bwd_workspace_bytes": (_sz, [ctypes.POINTER(salad_shape)]),
+    "salad_attn_bwd": (ctypes.c_int, [ctypes.POINTER(salad_shape), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f, _f,
+                                      _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "salad_token_order": (ctypes.c_int, [ctypes.POINTER(salad_shape), _vp]),
     "salad_permute_tokens": (ctypes.c_int, [ctypes.POINTER(salad_shape), ctypes.c_int, _vp, _vp, _vp]),
     "salad_gate_from_q": (ctypes.c_int, [ctypes.POINTER(salad_shape), _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -210,3 +213,14 @@ def salad_attn_apply(shape, q, k, v, row_ptr, col_idx, gate, eps, scale, drop_ta
     _check(lib().salad_attn_apply(ctypes.byref(shape), _p(q), _p(k), _p(v), _p(row_ptr), _p(col_idx),
                                   _p(gate), eps, scale, drop_tau, _p(out), _p(ws), ws.numel(),
                                   _stream(stream)), "salad_attn_apply")
+
+
+def salad_bwd_workspace_bytes(shape: salad_shape) -> int:
+    return int(lib().salad_bwd_workspace_bytes(ctypes.byref(shape)))
+
+
+def salad_attn_bwd(shape, q, k, v, row_ptr, col_idx, gate, w_lin, eps, scale, out, dout, dq, dk, dv, dw_lin,
+                   dgate, ws, stream=None):
+    _check(lib().salad_attn_bwd(ctypes.byref(shape), _p(q), _p(k), _p(v), _p(row_ptr), _p(col_idx), _p(gate),
+                                _p(w_lin), eps, scale, _p(out), _p(dout), _p(dq), _p(dk), _p(dv), _p(dw_lin),
+                                _p(dgate), _p(ws), ws.numel(), _stream(stream)), "salad_attn_bwd")

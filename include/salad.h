@@ -250,6 +250,41 @@ SALAD_API int salad_attn_fwd_branches(const salad_shape* shape, const void* q, c
                             float eps, float scale, void* out_sparse, void* out_lin,
                             void* ws, size_t ws_bytes, void* stream);
 
+/* ---- backward (for fine-tuning) ------------------------------------------
+ * The layer is trained, not only run: the "SALAD" explainer's technical
+ * summary, section 2.2, makes the projection on the linear branch a learnable
+ * layer initialised at zero and the scale s the output of a small learned
+ * module, and section 3 reports the fine-tuning budget.  salad_attn_bwd gives
+ * the gradients of a loss L through out = o_s + g * (o_l W_lin) from dout =
+ * dL/dout. */
+
+/* Device workspace, in bytes, that salad_attn_bwd needs for this shape (it
+ * includes salad_workspace_bytes).  Pure host function; 0 on invalid shape. */
+SALAD_API size_t salad_bwd_workspace_bytes(const salad_shape* shape);
+
+/* Gradients of the fused forward (salad_attn_fwd without branch dropping) for
+ * bf16 shapes:
+ *   q, k, v, out, dout  device bf16 [batch, heads, n_pad, head_dim]: the
+ *                       forward's inputs, its output, and dL/dout (rows from N
+ *                       on are not read)
+ *   row_ptr, col_idx    the CSR mask the forward used
+ *   gate                device float [batch*heads]; w_lin device bf16
+ *                       [head_dim, head_dim]; eps, scale as in salad_attn_fwd
+ *   dq, dk, dv          device bf16, same shape as q (written; padding rows 0)
+ *   dw_lin              device float [head_dim, head_dim] (written: summed over
+ *                       every batch index and head)
+ *   dgate               device float [batch*heads] (written)
+ *   ws                  device workspace of salad_bwd_workspace_bytes(shape)
+ * Accumulation is fp32 (bf16 MFMA products), every sum in a fixed order:
+ * bitwise reproducible run to run.  The softmax statistics are recomputed, so
+ * the forward keeps nothing extra.  fp32 shapes return SALAD_EUNSUPPORTED. */
+SALAD_API int salad_attn_bwd(const salad_shape* shape, const void* q, const void* k,
+                             const void* v, const int32_t* row_ptr, const int32_t* col_idx,
+                             const float* gate, const void* w_lin, float eps, float scale,
+                             const void* out, const void* dout, void* dq, void* dk, void* dv,
+                             float* dw_lin, float* dgate, void* ws, size_t ws_bytes,
+                             void* stream);
+
 #ifdef __cplusplus
 }
 #endif

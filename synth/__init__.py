@@ -10,7 +10,7 @@ weight is involved.
 """
 
 from .configs import CONFIGS, HeadSpec, LayerConfig, get_config
-from .generate import LayerInputs, bf16_round, bf16_bits_to_f32, make_inputs
+from .generate import LayerInputs, bf16_round, bf16_bits_to_f32, make_grad_output, make_inputs
 
 __all__ = [
     "CONFIGS",
@@ -20,5 +20,6 @@ __all__ = [
     "bf16_round",
     "bf16_bits_to_f32",
     "get_config",
+    "make_grad_output",
     "make_inputs",
 ]

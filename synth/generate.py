@@ -31,6 +31,7 @@ from .configs import LayerConfig
 
 # stream ids of default_rng([seed, stream])
 _S_QK_FREQ, _S_V_FREQ, _S_QN, _S_KN, _S_VN, _S_WLIN, _S_GATE, _S_WG = 0, 1, 2, 3, 4, 5, 6, 7
+_S_DOUT = 9  # stream 8 is the c5 densities (configs.py)
 
 
 def bf16_round(x: np.ndarray) -> np.ndarray:
@@ -111,3 +112,19 @@ def make_inputs(cfg: LayerConfig, canary: bool = False) -> LayerInputs:
     elif cfg.dtype != "f32":
         raise ValueError(cfg.dtype)
     return inp
+
+
+def make_grad_output(cfg: LayerConfig, scale: float = 1.0):
+    """Upstream gradient dL/dout for a backward pass: scale * N(0, 1), [B, H, n_pad, d].
+
+    Returns (values float32, bf16 bits uint16 or None): bf16 configs round once so
+    that both sides see the same values; padding rows hold the canary 1e4, which
+    no result may read.
+    """
+    rng = np.random.default_rng([cfg.seed, _S_DOUT])
+    x = (scale * rng.standard_normal((cfg.batch, cfg.heads, cfg.n_pad, cfg.head_dim))).astype(np.float32)
+    x[:, :, cfg.N:] = 1e4
+    if cfg.dtype == "bf16":
+        bits = bf16_round(x)
+        return bf16_bits_to_f32(bits), bits
+    return x, None

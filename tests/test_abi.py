@@ -191,3 +191,30 @@ def test_permute_rejects_bad_arguments_before_launch():
     assert L.salad_permute_tokens(ctypes.byref(sh), 0, None, b, None) == S.SALAD_EINVAL
     assert L.salad_permute_tokens(ctypes.byref(sh), 1, odd, b, None) == S.SALAD_EINVAL
     assert L.salad_permute_tokens(ctypes.byref(_shape("c8", cuboid_w=2)), 0, a, b, None) == S.SALAD_EINVAL  # 1*8*2
+
+
+def test_backward_rejects_bad_arguments_before_launch():
+    L = _lib()
+    sh = _shape("c3")
+    ws_bytes = S.salad_bwd_workspace_bytes(sh)
+    assert ws_bytes > S.salad_workspace_bytes(sh)
+    assert S.salad_bwd_workspace_bytes(_shape("c3", head_dim=96)) == 0
+    fake = ctypes.c_void_p(0x100000)
+    args = [fake] * 5 + [fake, fake, 1e-6, 0.0, fake, fake, fake, fake, fake, fake, fake, fake, ws_bytes, None]
+    # q, k, v, row_ptr, col_idx, gate, w_lin, eps, scale, out, dout, dq, dk, dv, dw, dgate, ws, ws_bytes, stream
+
+    def call(shape=sh, **over):
+        a = list(args)
+        names = ["q", "k", "v", "row_ptr", "col_idx", "gate", "w_lin", "eps", "scale", "out", "dout", "dq", "dk",
+                 "dv", "dw", "dgate", "ws", "ws_bytes", "stream"]
+        for key, val in over.items():
+            a[names.index(key)] = val
+        return L.salad_attn_bwd(ctypes.byref(shape), *a)
+
+    assert call(shape=_shape("c1")) == S.SALAD_EUNSUPPORTED   # fp32 layer
+    assert call(dout=None) == S.SALAD_EINVAL
+    assert call(dgate=None) == S.SALAD_EINVAL
+    assert call(dq=ctypes.c_void_p(0x100004)) == S.SALAD_EINVAL
+    assert call(eps=-1.0) == S.SALAD_EINVAL
+    assert call(scale=float("inf")) == S.SALAD_EINVAL
+    assert call(ws_bytes=ws_bytes - 1) == S.SALAD_ENOSPACE

@@ -1,0 +1,134 @@
+"""GPU parity of the backward pass (salad_attn_bwd) against the oracle's gradients.
+
+The oracle differentiates the fp64 forward on the exact bf16 input values
+(``oracle.layer_backward``).  The kernels round P and dS to bf16 before their
+products (as the forward rounds P) and store dq, dk, dv in bf16; each rounding
+is a relative 2^-9, three of them stack on a typical element, so the bars are
+rel-L2 <= 1.5e-2 and max-abs <= 3e-2 * max|ref| per tensor (about 2.5x the
+expected error).  dW_lin and dgate are fp32 sums of bf16-rounded o_l and dU:
+rel-L2 <= 1e-2.  Padding rows of dq, dk, dv must be exactly 0, and two runs
+must agree bit for bit.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from helpers import device_tensors, inputs, make_layer, oracle_csr, storage_order, stored_inputs, to_numpy
+from synth import CONFIGS, HeadSpec, LayerConfig, make_grad_output, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+from block_sparse_linear_st_amd import salad as S  # noqa: E402
+
+REL_L2 = 1.5e-2
+MAX_REL = 3e-2
+FP32_REL_L2 = 1e-2
+
+B128 = LayerConfig(
+    name="b128", seed=21, batch=2, heads=2, head_dim=128, T=3, H=10, W=20, block=128, dtype="bf16",
+    specs=(HeadSpec(0, 1, -1, 0.5), HeadSpec(1, 0, -1, 0.4)), gate_kind="uniform",
+    description="ragged 128-token blocks, d=128, batch 2: window and top-k heads")
+
+
+def _check(got, ref, what, rel_l2=REL_L2, max_rel=MAX_REL):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite"
+    scale = float(np.max(np.abs(ref)))
+    err = float(np.max(np.abs(got - ref)))
+    rl2 = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30))
+    print(f"{what}: max-abs {err:.3e} (bar {max_rel * scale:.3e}), rel-L2 {rl2:.3e} (bar {rel_l2:g})", flush=True)
+    assert rl2 <= rel_l2, f"{what}: rel-L2 {rl2:.3e}"
+    assert err <= max_rel * scale, f"{what}: max-abs {err:.3e}"
+
+
+def _run(cfg, inp, cuboid=False):
+    layer = make_layer(cfg)
+    q, k, v, w = device_tensors(inp)
+    if cuboid:
+        qs, ks, vs = (torch.empty_like(t) for t in (q, k, v))
+        layer.to_storage(q, qs)
+        layer.to_storage(k, ks)
+        layer.to_storage(v, vs)
+        q, k, v = qs, ks, vs
+    if cfg.gate_kind == "from_q":
+        gate = torch.empty(cfg.batch * cfg.heads, dtype=torch.float32, device="cuda")
+        layer.build_mask(q, k, torch.from_numpy(inp.w_g).cuda(), gate)
+    else:
+        gate = torch.from_numpy(inp.gate).cuda()
+        layer.build_mask(q, k)
+    out = torch.empty_like(q)
+    layer.forward(q, k, v, gate, w, out, eps=cfg.eps)
+    dvals, dbits = make_grad_output(cfg)
+    dout = torch.from_numpy(dbits.view(np.int16)).view(torch.bfloat16).cuda()
+    ws = torch.empty(S.salad_bwd_workspace_bytes(layer.shape), dtype=torch.uint8, device="cuda")
+    res = []
+    for _ in range(2):
+        g = {n: torch.full_like(q, float("nan")) for n in ("dq", "dk", "dv")}
+        dw = torch.full((cfg.head_dim, cfg.head_dim), float("nan"), dtype=torch.float32, device="cuda")
+        dg = torch.full((cfg.batch * cfg.heads,), float("nan"), dtype=torch.float32, device="cuda")
+        S.salad_attn_bwd(layer.shape, q, k, v, layer.row_ptr, layer.col_idx, gate, w, cfg.eps, 0.0, out, dout,
+                         g["dq"], g["dk"], g["dv"], dw, dg, ws)
+        torch.cuda.synchronize()
+        g["dw"], g["dg"] = dw, dg
+        res.append(g)
+    for n in res[0]:
+        assert torch.equal(res[0][n], res[1][n]), f"{n} differs between two runs"
+    return layer, gate, res[0], dvals
+
+
+def _oracle(cfg, name_or_inp, gate, dvals, stored=None):
+    inp = name_or_inp
+    q, k, v = stored if stored is not None else (inp.q, inp.k, inp.v)
+    if isinstance(cfg, LayerConfig) and cfg.name in CONFIGS and CONFIGS[cfg.name] is cfg:
+        rp, ci = oracle_csr(cfg.name)
+    else:
+        keep = oracle.build_masks(cfg.T, cfg.H, cfg.W, cfg.block, cfg.specs, cfg.batch, q, k)
+        rp, ci = oracle.csr_from_keep(keep)
+    return oracle.layer_backward(q, k, v, rp, ci, gate.cpu().numpy().astype(np.float64), inp.w_lin, cfg.N,
+                                 cfg.block, cfg.eps, dvals), rp, ci
+
+
+def _compare(cfg, got, ref, tag):
+    N = cfg.N
+    for n in ("dq", "dk", "dv"):
+        t = to_numpy(got[n])
+        _check(t[:, :, :N], ref[n][:, :, :N], f"{tag} {n}")
+        assert np.all(t[:, :, N:] == 0.0), f"{tag} {n}: padding rows not zero"
+    _check(got["dw"].cpu().numpy(), ref["dw_lin"], f"{tag} dW_lin", rel_l2=FP32_REL_L2)
+    _check(got["dg"].cpu().numpy(), ref["dgate"], f"{tag} dgate", rel_l2=FP32_REL_L2)
+
+
+def test_backward_c2():
+    print("backward c2", flush=True)
+    cfg = CONFIGS["c2"]
+    inp = inputs("c2")
+    layer, gate, got, dvals = _run(cfg, inp)
+    np.testing.assert_array_equal(layer.row_ptr.cpu().numpy(), oracle_csr("c2")[0])
+    ref, _, _ = _oracle(cfg, inp, gate, dvals)
+    _compare(cfg, got, ref, "c2")
+
+
+def test_backward_b128_ragged():
+    print("backward b128", flush=True)
+    cfg = B128
+    inp = make_inputs(cfg)
+    layer, gate, got, dvals = _run(cfg, inp)
+    ref, rp, _ = _oracle(cfg, inp, gate, dvals)
+    np.testing.assert_array_equal(layer.row_ptr.cpu().numpy(), rp)
+    _compare(cfg, got, ref, "b128")
+
+
+def test_backward_c9_cuboid_mixed_masks():
+    """Ragged 5x10x14 layer in cuboid order with window, top-k and SICS heads and a gate from Q."""
+    print("backward c9", flush=True)
+    cfg = CONFIGS["c9"]
+    inp = inputs("c9")
+    layer, gate, got, dvals = _run(cfg, inp, cuboid=True)
+    stored = stored_inputs("c9")
+    ref, rp, _ = _oracle(cfg, inp, gate, dvals, stored=stored)
+    np.testing.assert_array_equal(layer.row_ptr.cpu().numpy(), rp)
+    _compare(cfg, got, ref, "c9")
