@@ -362,7 +362,7 @@ int salad_linear_prepare(const salad_shape* shape, const void* k, const void* v,
 
 int salad_attn_apply(const salad_shape* shape, const void* q, const void* k, const void* v,
                      const int32_t* row_ptr, const int32_t* col_idx, const float* gate, float eps,
-                     float scale, float drop_tau, void* out, void* ws, size_t ws_bytes,
+                     float scale, float drop_tau, void* out, float* lse, void* ws, size_t ws_bytes,
                      void* stream) {
   Geom g;
   Workspace L;
@@ -381,13 +381,15 @@ int salad_attn_apply(const salad_shape* shape, const void* q, const void* k, con
   a.gate = gate; a.drop_tau = drop_tau; a.eps = eps;
   a.scale = scale > 0.0f ? scale : 1.0f / std::sqrt((float)g.D);
   a.has_sparse = 1; a.has_lin = 1;
+  if (lse != nullptr && shape->dtype != SALAD_BF16) return SALAD_EUNSUPPORTED;
+  a.lse = lse;
   return hip_status(run_attn(g, shape->dtype, a, s));
 }
 
 int salad_attn_fwd(const salad_shape* shape, const void* q, const void* k, const void* v,
                    const int32_t* row_ptr, const int32_t* col_idx, const float* gate,
-                   const void* w_lin, float eps, float scale, float drop_tau, void* out, void* ws,
-                   size_t ws_bytes, void* stream) {
+                   const void* w_lin, float eps, float scale, float drop_tau, void* out, float* lse,
+                   void* ws, size_t ws_bytes, void* stream) {
   Geom g;
   Workspace L;
   int st = attn_common(shape, q, k, v, row_ptr, col_idx, ws, ws_bytes, &g, &L);
@@ -395,9 +397,10 @@ int salad_attn_fwd(const salad_shape* shape, const void* q, const void* k, const
   if (!gate || !w_lin || !out || !aligned16(out) || !(eps >= 0.0f) || !std::isfinite(scale) ||
       std::isnan(drop_tau))
     return SALAD_EINVAL;
+  if (lse != nullptr && shape->dtype != SALAD_BF16) return SALAD_EUNSUPPORTED;
   st = salad_linear_prepare(shape, k, v, gate, w_lin, drop_tau, ws, ws_bytes, stream);
   if (st != SALAD_OK) return st;
-  return salad_attn_apply(shape, q, k, v, row_ptr, col_idx, gate, eps, scale, drop_tau, out, ws,
+  return salad_attn_apply(shape, q, k, v, row_ptr, col_idx, gate, eps, scale, drop_tau, out, lse, ws,
                           ws_bytes, stream);
 }
 
@@ -446,9 +449,9 @@ size_t salad_bwd_workspace_bytes(const salad_shape* shape) {
 
 int salad_attn_bwd(const salad_shape* shape, const void* q, const void* k, const void* v,
                    const int32_t* row_ptr, const int32_t* col_idx, const float* gate,
-                   const void* w_lin, float eps, float scale, const void* out, const void* dout,
-                   void* dq, void* dk, void* dv, float* dw_lin, float* dgate, void* ws,
-                   size_t ws_bytes, void* stream) {
+                   const void* w_lin, float eps, float scale, const void* out, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv, float* dw_lin, float* dgate,
+                   void* ws, size_t ws_bytes, void* stream) {
   Geom g;
   const int st = shape_status(shape);
   if (st != SALAD_OK) return st;
@@ -468,7 +471,7 @@ int salad_attn_bwd(const salad_shape* shape, const void* q, const void* k, const
   BwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.row_ptr = row_ptr; a.col_idx = col_idx; a.gate = gate;
   a.w_lin = w_lin; a.out = out; a.dout = dout; a.dq = dq; a.dk = dk; a.dv = dv;
-  a.dw_lin = dw_lin; a.dgate = dgate; a.eps = eps;
+  a.dw_lin = dw_lin; a.dgate = dgate; a.lse = lse; a.eps = eps;
   a.scale = scale > 0.0f ? scale : 1.0f / std::sqrt((float)g.D);
   hipError_t e = launch_linear_state(g, shape->dtype, k, v, nullptr, 0.0f, w, L.fwd, s);
   if (e == hipSuccess)

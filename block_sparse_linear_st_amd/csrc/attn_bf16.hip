@@ -25,7 +25,8 @@
 // reads (16 consecutive rows, one chunk) and the V transpose reads (4 rows x 4
 // chunks per half-wave) spread over all banks.
 //
-// Epilogue: o_s = O / l; the linear branch ("SALAD" explainer, section 2.1)
+// Epilogue: o_s = O / l (and, when asked, each row's log2-sum-exp m + log2 l
+// for the backward pass); the linear branch ("SALAD" explainer, section 2.1)
 // and its gated projection (section 2.2) arrive pre-folded as S''^T =
 // (g S W_lin)^T in hi + lo bf16, so g*(o_l W_lin) = (S''^T ReLU(Q)^T) /
 // (ReLU(Q) z + eps) is 2*(D/32)*(D/16) more MFMAs on the Q fragments already
@@ -392,6 +393,10 @@ k_attn_bf16(Geom g, AttnArgs a, int n_items, float c_log2) {
 
   // ---- epilogue -------------------------------------------------------------
   const float inv_l = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+  // log2-sum-exp of each row's scaled scores, kept for the backward pass
+  if (a.lse != nullptr && a.has_sparse && wave_rows && g32 == 0)
+    a.lse[(int64_t)bh * g.n_pad + my_row] =
+        (my_row < g.N && l_run > 0.0f) ? m_used + __log2f(l_run) : INFINITY;
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll

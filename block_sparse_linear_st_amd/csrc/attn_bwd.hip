@@ -3,8 +3,13 @@
 //
 // With x = scale * q.k, P = softmax over the kept keys, D_i = <dout_i, o_s,i>
 // (from linear_bwd.hip):  dS = P * (dout V^T - D),  dQ = scale dS K,
-// dK = scale dS^T Q,  dV = P^T dout.  The row statistic (log-sum-exp) is
-// recomputed here, so the forward kernel keeps nothing for training.
+// dK = scale dS^T Q,  dV = P^T dout.  The row statistic (log2-sum-exp of the
+// scaled scores) comes from the forward when it kept it, else it is recomputed
+// here in a first pass.
+//
+// Both kernels stream their 64-row tiles HBM -> LDS with global_load_lds_dwordx4,
+// double buffered (the next tile's loads are issued before the current tile's
+// MFMAs).
 //
 // k_attn_bwd_dq: one query block per workgroup, one wave per 32 queries,
 // queries in lanes (the forward's transposed orientation).  Pass 1 over the
@@ -43,7 +48,7 @@ struct BwdSmem {
   static constexpr int TB = kT * TileLay<D>::ROW_B;
   static constexpr int SST = D + 8;                 // staging row stride (bf16)
   static constexpr int STAGE = BLK * SST * 2;
-  static constexpr int BYTES = 2 * TB > STAGE ? 2 * TB : STAGE;
+  static constexpr int BYTES = 4 * TB > STAGE ? 4 * TB : STAGE;  // two buffers of two tiles
 };
 
 // Stage a C-layout [channel][row-in-lane] result of NT tiles per wave as
@@ -67,7 +72,7 @@ __device__ inline void store_rows(unsigned char* smem, const f32x16 (&acc)[D / 3
   __syncthreads();
 }
 
-template <int D, int BLK>
+template <int D, int BLK, bool LSE_IN>
 __global__ void __launch_bounds__(BLK * 2)
 k_attn_bwd_dq(Geom g, BwdArgs a, const float* __restrict__ Dq, const float* __restrict__ dden,
               const __bf16* __restrict__ dU, const __bf16* __restrict__ s_hi, const __bf16* __restrict__ s_lo,
@@ -75,8 +80,6 @@ k_attn_bwd_dq(Geom g, BwdArgs a, const float* __restrict__ Dq, const float* __re
   constexpr int NT = D / 32, NC = D / 16, NTH = BLK * 2;
   using SM = BwdSmem<D, BLK>;
   __shared__ __align__(16) unsigned char smem[SM::BYTES];
-  unsigned char* Kt = smem;
-  unsigned char* Vt = smem + SM::TB;
   const int qb = blockIdx.x, bh = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, gg = lane >> 5, m = lane & 31;
   const int n = qb * BLK + wave * 32 + m;
@@ -98,16 +101,39 @@ k_attn_bwd_dq(Geom g, BwdArgs a, const float* __restrict__ Dq, const float* __re
   const int64_t r = (int64_t)bh * g.nb + qb;
   const int e0 = a.row_ptr[r], e1 = a.row_ptr[r + 1];
   constexpr int SUB = BLK / kT;
+  constexpr int NW = BLK / 32;
 
-  // pass 1: log2-sum-exp of each query over its kept keys
-  float mrun = -INFINITY, lrun = 0.0f;
-  for (int e = e0; e < e1; ++e) {
-    const int kb = a.col_idx[e];
-    for (int sub = 0; sub < SUB; ++sub) {
-      const int key0 = kb * BLK + sub * kT;
-      __syncthreads();
-      load_tile<D, kT, NTH>(Kt, K, key0, g.N - 1, tid);
-      __syncthreads();
+  // The kept key tiles are visited twice: pass 1 (tiles 0 .. T-1, K only)
+  // accumulates the log2-sum-exp, pass 2 (tiles T .. 2T-1, K and V) dQ.  Each
+  // tile's DMA is issued one tile ahead into the other buffer.
+  const int T = (e1 - e0) * SUB;
+  const uint32_t lds0 = lds_addr(smem);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  auto issue = [&](int i, int buf) __attribute__((always_inline)) {
+    const int ii = i < T ? i : i - T;
+    const int key0 = a.col_idx[e0 + ii / SUB] * BLK + (ii % SUB) * kT;
+    const uint32_t base = lds0 + buf * 2 * SM::TB;
+    dma_tile<D, NW>(base, K, key0, g.N - 1, wave_u, lane);
+    if (i >= T) dma_tile<D, NW>(base + SM::TB, V, key0, g.N - 1, wave_u, lane);
+  };
+  float mrun = -INFINITY, lrun = 0.0f, lse = INFINITY;
+  f32x16 acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) zero(acc[t]);
+  // with the forward's log2-sum-exp at hand, pass 1 is skipped
+  const int i_first = LSE_IN ? T : 0;
+  if (LSE_IN) lse = a.lse[hb + n];
+  if (T > 0) issue(i_first, i_first & 1);
+  wait_vmem();
+  __syncthreads();
+  for (int i = i_first; i < 2 * T; ++i) {
+    const int cur = i & 1;
+    if (i + 1 < 2 * T) issue(i + 1, cur ^ 1);
+    const unsigned char* Kt = smem + cur * 2 * SM::TB;
+    const unsigned char* Vt = Kt + SM::TB;
+    const int ii = i < T ? i : i - T;
+    const int key0 = a.col_idx[e0 + ii / SUB] * BLK + (ii % SUB) * kT;
+    if (i < T) {
       f32x16 s[2];
       zero(s[0]);
       zero(s[1]);
@@ -120,10 +146,10 @@ k_attn_bwd_dq(Geom g, BwdArgs a, const float* __restrict__ Dq, const float* __re
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = key0 + 32 * kt + crow(i, gg);
-          const float x = key < g.N ? s[kt][i] * c_log2 : -INFINITY;
-          s[kt][i] = x;
+        for (int j = 0; j < 16; ++j) {
+          const int key = key0 + 32 * kt + crow(j, gg);
+          const float x = key < g.N ? s[kt][j] * c_log2 : -INFINITY;
+          s[kt][j] = x;
           mx = fmaxf(mx, x);
         }
       mx = pair_max(mx);
@@ -133,27 +159,14 @@ k_attn_bwd_dq(Geom g, BwdArgs a, const float* __restrict__ Dq, const float* __re
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) lrun += __builtin_amdgcn_exp2f(s[kt][i] - mnew);
+          for (int j = 0; j < 16; ++j) lrun += __builtin_amdgcn_exp2f(s[kt][j] - mnew);
         mrun = mnew;
       }
-    }
-  }
-  const float lt = pair_sum(lrun);
-  const float lse = (valid && lt > 0.0f) ? mrun + log2f(lt) : INFINITY;
-  if (gg == 0) lse_out[hb + n] = lse;
-
-  // pass 2: dQ^T += K^T dS^T
-  f32x16 acc[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) zero(acc[t]);
-  for (int e = e0; e < e1; ++e) {
-    const int kb = a.col_idx[e];
-    for (int sub = 0; sub < SUB; ++sub) {
-      const int key0 = kb * BLK + sub * kT;
-      __syncthreads();
-      load_tile<D, kT, NTH>(Kt, K, key0, g.N - 1, tid);
-      load_tile<D, kT, NTH>(Vt, V, key0, g.N - 1, tid);
-      __syncthreads();
+    } else {
+      if (!LSE_IN && i == T) {
+        const float lt = pair_sum(lrun);
+        lse = (valid && lt > 0.0f) ? mrun + log2f(lt) : INFINITY;
+      }
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         f32x16 s, dp;
@@ -165,10 +178,10 @@ k_attn_bwd_dq(Geom g, BwdArgs a, const float* __restrict__ Dq, const float* __re
           dp = mfma(frag_direct<D>(Vt, 32 * kt, c, lane), dof[c], dp);
         }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = key0 + 32 * kt + crow(i, gg);
-          const float p = key < g.N ? __builtin_amdgcn_exp2f(s[i] * c_log2 - lse) : 0.0f;
-          s[i] = p * (dp[i] - Dn);
+        for (int j = 0; j < 16; ++j) {
+          const int key = key0 + 32 * kt + crow(j, gg);
+          const float p = key < g.N ? __builtin_amdgcn_exp2f(s[j] * c_log2 - lse) : 0.0f;
+          s[j] = p * (dp[j] - Dn);
         }
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
@@ -178,7 +191,10 @@ k_attn_bwd_dq(Geom g, BwdArgs a, const float* __restrict__ Dq, const float* __re
         }
       }
     }
+    wait_vmem();
+    __syncthreads();
   }
+  if (!LSE_IN && gg == 0) lse_out[hb + n] = lse;
 
   // linear term: (S dU^T + z dden^T) * [q > 0], S rows c as hi + lo bf16
   bf16x8 duf[NC];
@@ -220,9 +236,7 @@ k_attn_bwd_dkdv(Geom g, BwdArgs a, const int32_t* __restrict__ colptr, const int
   constexpr int NT = D / 32, NC = D / 16, NTH = BLK * 2;
   using SM = BwdSmem<D, BLK>;
   __shared__ __align__(16) unsigned char smem[SM::BYTES];
-  __shared__ float lse_s[kT], dq_s[kT];
-  unsigned char* Qt = smem;
-  unsigned char* Ot = smem + SM::TB;
+  __shared__ float lse_s[2][kT], dq_s[2][kT];
   const int kb = blockIdx.x, bh = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, gg = lane >> 5, m = lane & 31;
   const int j = kb * BLK + wave * 32 + m;
@@ -248,47 +262,70 @@ k_attn_bwd_dkdv(Geom g, BwdArgs a, const int32_t* __restrict__ colptr, const int
   const int64_t col = (int64_t)bh * g.nb + kb;
   const int p0 = colptr[col], p1 = colptr[col + 1];
   constexpr int SUB = BLK / kT;
-  for (int e = p0; e < p1; ++e) {
-    const int qb = rowidx[e];
-    for (int sub = 0; sub < SUB; ++sub) {
-      const int q0 = qb * BLK + sub * kT;
-      __syncthreads();
-      load_tile<D, kT, NTH>(Qt, Q, q0, g.N - 1, tid);
-      load_tile<D, kT, NTH>(Ot, dO, q0, g.N - 1, tid);
-      if (tid < kT) {
-        lse_s[tid] = lse[hb + q0 + tid];
-        dq_s[tid] = Dq[hb + q0 + tid];
+  constexpr int NW = BLK / 32;
+  const int T = (p1 - p0) * SUB;
+  const uint32_t lds0 = lds_addr(smem);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  auto q0_of = [&](int i) __attribute__((always_inline)) { return rowidx[p0 + i / SUB] * BLK + (i % SUB) * kT; };
+  float lse_r = 0.0f, dq_r = 0.0f;  // row statistics of the tile in flight (threads < kT)
+  auto issue = [&](int i, int buf) __attribute__((always_inline)) {
+    const int q0 = q0_of(i);
+    const uint32_t base = lds0 + buf * 2 * SM::TB;
+    dma_tile<D, NW>(base, Q, q0, g.N - 1, wave_u, lane);
+    dma_tile<D, NW>(base + SM::TB, dO, q0, g.N - 1, wave_u, lane);
+    if (tid < kT) {
+      lse_r = lse[hb + q0 + tid];
+      dq_r = Dq[hb + q0 + tid];
+    }
+  };
+  if (T > 0) {
+    issue(0, 0);
+    if (tid < kT) {
+      lse_s[0][tid] = lse_r;
+      dq_s[0][tid] = dq_r;
+    }
+  }
+  wait_vmem();
+  __syncthreads();
+  for (int i = 0; i < T; ++i) {
+    const int cur = i & 1;
+    if (i + 1 < T) issue(i + 1, cur ^ 1);
+    const unsigned char* Qt = smem + cur * 2 * SM::TB;
+    const unsigned char* Ot = Qt + SM::TB;
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      f32x16 s, dp;
+      zero(s);
+      zero(dp);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        s = mfma(frag_direct<D>(Qt, 32 * qs, c, lane), kf[c], s);
+        dp = mfma(frag_direct<D>(Ot, 32 * qs, c, lane), vf[c], dp);
       }
-      __syncthreads();
 #pragma unroll
-      for (int qs = 0; qs < 2; ++qs) {
-        f32x16 s, dp;
-        zero(s);
-        zero(dp);
+      for (int j = 0; j < 16; ++j) {
+        const int qi = 32 * qs + crow(j, gg);
+        const float p = __builtin_amdgcn_exp2f(s[j] * c_log2 - lse_s[cur][qi]);  // 0 for padded queries (lse = inf)
+        s[j] = p;
+        dp[j] = p * (dp[j] - dq_s[cur][qi]);
+      }
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          s = mfma(frag_direct<D>(Qt, 32 * qs, c, lane), kf[c], s);
-          dp = mfma(frag_direct<D>(Ot, 32 * qs, c, lane), vf[c], dp);
-        }
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const bf16x8 bp = c_to_b(s, h2);
+        const bf16x8 bd = c_to_b(dp, h2);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int qi = 32 * qs + crow(i, gg);
-          const float p = __builtin_amdgcn_exp2f(s[i] * c_log2 - lse_s[qi]);  // 0 for padded queries (lse = inf)
-          s[i] = p;
-          dp[i] = p * (dp[i] - dq_s[qi]);
-        }
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const bf16x8 bp = c_to_b(s, h2);
-          const bf16x8 bd = c_to_b(dp, h2);
-#pragma unroll
-          for (int t = 0; t < NT; ++t) {
-            dv[t] = mfma(frag_tr<D>(Ot, 2 * qs + h2, t, lane), bp, dv[t]);
-            dk[t] = mfma(frag_tr<D>(Qt, 2 * qs + h2, t, lane), bd, dk[t]);
-          }
+        for (int t = 0; t < NT; ++t) {
+          dv[t] = mfma(frag_tr<D>(Ot, 2 * qs + h2, t, lane), bp, dv[t]);
+          dk[t] = mfma(frag_tr<D>(Qt, 2 * qs + h2, t, lane), bd, dk[t]);
         }
       }
     }
+    if (i + 1 < T && tid < kT) {
+      lse_s[cur ^ 1][tid] = lse_r;
+      dq_s[cur ^ 1][tid] = dq_r;
+    }
+    wait_vmem();
+    __syncthreads();
   }
 
   // linear terms: dv += dS_lin^T phi(K)^T; dk += (dS_lin V^T + dz) * [k > 0]
@@ -328,11 +365,18 @@ hipError_t launch_bwd_t(const Geom& g, const BwdArgs& a, char* ws, const BwdWork
   auto F32 = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
   const float c_log2 = a.scale * 1.4426950408889634f;
   const dim3 grid(g.nb, g.B * g.Hh);
-  hipLaunchKernelGGL((k_attn_bwd_dq<D, BLK>), grid, dim3(BLK * 2), 0, st, g, a, F32(L.off_dq), F32(L.off_dden),
-                     B16(L.off_du), B16(L.off_s_hi), B16(L.off_s_lo), F32(L.off_z), F32(L.off_lse), c_log2);
+  if (a.lse != nullptr)
+    hipLaunchKernelGGL((k_attn_bwd_dq<D, BLK, true>), grid, dim3(BLK * 2), 0, st, g, a, F32(L.off_dq),
+                       F32(L.off_dden), B16(L.off_du), B16(L.off_s_hi), B16(L.off_s_lo), F32(L.off_z),
+                       F32(L.off_lse), c_log2);
+  else
+    hipLaunchKernelGGL((k_attn_bwd_dq<D, BLK, false>), grid, dim3(BLK * 2), 0, st, g, a, F32(L.off_dq),
+                       F32(L.off_dden), B16(L.off_du), B16(L.off_s_hi), B16(L.off_s_lo), F32(L.off_z),
+                       F32(L.off_lse), c_log2);
+  const float* lse = a.lse != nullptr ? a.lse : F32(L.off_lse);
   hipLaunchKernelGGL((k_attn_bwd_dkdv<D, BLK>), grid, dim3(BLK * 2), 0, st, g, a,
                      reinterpret_cast<const int32_t*>(ws + L.off_colptr),
-                     reinterpret_cast<const int32_t*>(ws + L.off_rowidx), F32(L.off_dq), F32(L.off_lse),
+                     reinterpret_cast<const int32_t*>(ws + L.off_rowidx), F32(L.off_dq), lse,
                      B16(L.off_ds_hi), B16(L.off_ds_lo), B16(L.off_dst_hi), B16(L.off_dst_lo), F32(L.off_dz),
                      c_log2);
   return hipGetLastError();

@@ -100,6 +100,42 @@ __device__ inline void load_tile(unsigned char* tile, const __bf16* src, int row
   }
 }
 
+// s_waitcnt vmcnt(0) as a compiler-visible instruction (gfx9 encoding: vmcnt 0,
+// expcnt 7, lgkmcnt 15).
+__device__ __attribute__((always_inline)) inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// One direct HBM -> LDS load: lane l's 16 bytes at gptr land at LDS byte
+// address m0_base + 16 l.  Inline asm with no register result, so that the
+// compiler does not hold LDS reads of the other buffer behind it; callers wait
+// with wait_vmem() before the barrier that publishes the buffer.
+__device__ __attribute__((always_inline)) inline void lds_dma16(const void* gptr, uint32_t m0_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(m0_base)
+               : "memory", "m0");
+}
+
+// Issue the DMA of rows [row0, row0 + 64) of a row-major [*, D] bf16 array
+// (rows clamped to `last`) into the swizzled LDS tile at byte address `lds`.
+// NW waves share the tile; wave w fills its 1 KiB blocks w*LOADS .. w*LOADS+LOADS-1.
+template <int D, int NW>
+__device__ __attribute__((always_inline)) inline void dma_tile(uint32_t lds, const __bf16* src, int row0, int last,
+                                                               int wave_u, int lane) {
+  using TL = TileLay<D>;
+  constexpr int LOADS = 64 * TL::ROW_B / 1024 / NW;
+  static_assert(LOADS >= 1, "tile too small for the waves");
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int blk = wave_u * LOADS + i;
+    const int P = blk * 64 + lane;
+    const int r = P / TL::CPR, p = P % TL::CPR;
+    const int gr = min(row0 + r, last);
+    lds_dma16(src + (int64_t)gr * D + ((p ^ TL::swz(r)) << 3), lds + blk * 1024);
+  }
+}
+
+__device__ inline uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)p;
+}
+
 // fp32 value rounded to bf16 (hi) and the bf16 of the remainder (lo).
 __device__ inline void split_hi_lo(float x, __bf16& hi, __bf16& lo) {
   hi = (__bf16)x;

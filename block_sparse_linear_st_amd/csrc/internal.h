@@ -93,8 +93,10 @@ struct BwdWorkspace {
   size_t off_ds_hi, off_ds_lo;        // bf16 [BH][D][D]: dS_lin (rows c)
   size_t off_dst_hi, off_dst_lo;      // bf16 [BH][D][D]: dS_lin^T (rows e)
   size_t off_dz;                      // float [BH][D]: dz_lin
+  size_t off_dwh;                     // float [BH][D][D]: g * per-head dW_lin
   size_t off_colcnt, off_colptr;      // int32 [BH*nb], [BH*nb + 1]
   size_t off_rowidx;                  // int32 [BH*nb*nb]
+  size_t off_bits;                    // uint32 [BH*nb][ceil(nb/32)]: transposed mask bitmap
 };
 
 SALAD_HIDDEN bool make_geom(const salad_shape* s, Geom* g);
@@ -160,6 +162,7 @@ struct BwdArgs {
   void* dv;
   float* dw_lin;
   float* dgate;
+  const float* lse;     // forward's log2-sum-exp [BH][n_pad], or null (recomputed)
   float eps;
   float scale;
 };
@@ -187,6 +190,7 @@ struct AttnArgs {
   const void* sft_lo;   // bf16 lo part (bf16 path only)
   const float* z;       // [BH][D]
   const float* gate;    // [BH] (branch dropping), may be null
+  float* lse;           // [BH][n_pad] log2-sum-exp of the scaled scores (bf16 path), may be null
   float drop_tau;
   float eps;
   float scale;

@@ -251,71 +251,92 @@ k_fold_ds(Geom g, int splits, const float* __restrict__ dspart, const float* __r
   }
 }
 
-// dW_lin = sum over heads (in order) of g * (sum over splits, in order).
+// dW_lin = sum over heads (in order) of g * (sum over splits, in order): first
+// the per-head split sums (one thread per head and element), then the heads.
 template <int D>
 __global__ void __launch_bounds__(256)
-k_fold_dw(Geom g, int splits, const float* __restrict__ dwpart, const float* __restrict__ gate,
-          float* __restrict__ dw) {
+k_fold_dw_heads(Geom g, int splits, const float* __restrict__ dwpart, const float* __restrict__ gate,
+                float* __restrict__ dwh) {
+  const int bh = blockIdx.y;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  const int64_t BH = (int64_t)g.B * g.Hh;
+  float s = 0.0f;
+#pragma unroll 8
+  for (int sp = 0; sp < splits; ++sp) s += dwpart[((int64_t)sp * BH + bh) * D * D + idx];
+  dwh[(int64_t)bh * D * D + idx] = gate[bh] * s;
+}
+
+template <int D>
+__global__ void __launch_bounds__(256)
+k_fold_dw(Geom g, const float* __restrict__ dwh, float* __restrict__ dw) {
   const int idx = blockIdx.x * 256 + threadIdx.x;
   const int64_t BH = (int64_t)g.B * g.Hh;
   float acc = 0.0f;
-  for (int64_t bh = 0; bh < BH; ++bh) {
-    float s = 0.0f;
-    for (int sp = 0; sp < splits; ++sp) s += dwpart[((int64_t)sp * BH + bh) * D * D + idx];
-    acc += gate[bh] * s;
-  }
+  for (int64_t bh = 0; bh < BH; ++bh) acc += dwh[bh * D * D + idx];
   dw[idx] = acc;
 }
 
-__global__ void __launch_bounds__(64)
+// dgate: the head's n_pad/32 partials, strided per thread then a fixed tree.
+__global__ void __launch_bounds__(256)
 k_fold_dgate(Geom g, const float* __restrict__ gpart, float* __restrict__ dgate) {
+  __shared__ float red[256];
   const int bh = blockIdx.x;
   const int parts = g.n_pad / 32;
-  if (threadIdx.x != 0) return;
   float s = 0.0f;
-  for (int i = 0; i < parts; ++i) s += gpart[(int64_t)bh * parts + i];
-  dgate[bh] = s;
+  for (int i = threadIdx.x; i < parts; i += 256) s += gpart[(int64_t)bh * parts + i];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) dgate[bh] = red[0];
 }
 
 // ---- transposed mask ----------------------------------------------------------
 
-__device__ inline bool row_has(const int32_t* col_idx, int a, int b, int kb) {
-  while (a < b) {
-    const int mid = (a + b) >> 1;
-    const int v = col_idx[mid];
-    if (v == kb) return true;
-    if (v < kb) a = mid + 1; else b = mid;
-  }
-  return false;
+// Transposed mask through a bitmap: one thread per CSR row sets bit qb of word
+// qb/32 in its key blocks' columns (atomicOr: order-free), then one thread per
+// column counts its bits and, after the scan, lists them in ascending order.
+__global__ void __launch_bounds__(256)
+k_csc_bits(Geom g, int words, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
+           uint32_t* __restrict__ bits) {
+  const int64_t r = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (r >= (int64_t)g.B * g.Hh * g.nb) return;
+  const int64_t base = r / g.nb * g.nb;
+  const int qb = (int)(r - base);
+  for (int e = row_ptr[r]; e < row_ptr[r + 1]; ++e)
+    atomicOr(&bits[(base + col_idx[e]) * words + (qb >> 5)], 1u << (qb & 31));
 }
 
 __global__ void __launch_bounds__(256)
-k_csc_count(Geom g, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
-            int32_t* __restrict__ colcnt) {
-  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (i >= (int64_t)g.B * g.Hh * g.nb) return;
-  const int64_t bh = i / g.nb;
-  const int kb = (int)(i % g.nb);
+k_csc_count(Geom g, int words, const uint32_t* __restrict__ bits, int32_t* __restrict__ colcnt) {
+  const int64_t c = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (c >= (int64_t)g.B * g.Hh * g.nb) return;
   int cnt = 0;
-  for (int qb = 0; qb < g.nb; ++qb) {
-    const int64_t r = bh * g.nb + qb;
-    cnt += row_has(col_idx, row_ptr[r], row_ptr[r + 1], kb) ? 1 : 0;
-  }
-  colcnt[i] = cnt;
+  for (int w = 0; w < words; ++w) cnt += __popc(bits[c * words + w]);
+  colcnt[c] = cnt;
 }
 
 __global__ void __launch_bounds__(256)
-k_csc_fill(Geom g, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
-           const int32_t* __restrict__ colptr, int32_t* __restrict__ rowidx) {
-  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (i >= (int64_t)g.B * g.Hh * g.nb) return;
-  const int64_t bh = i / g.nb;
-  const int kb = (int)(i % g.nb);
-  int p = colptr[i];
-  for (int qb = 0; qb < g.nb; ++qb) {
-    const int64_t r = bh * g.nb + qb;
-    if (row_has(col_idx, row_ptr[r], row_ptr[r + 1], kb)) rowidx[p++] = qb;
+k_csc_fill(Geom g, int words, const uint32_t* __restrict__ bits, const int32_t* __restrict__ colptr,
+           int32_t* __restrict__ rowidx) {
+  const int64_t c = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (c >= (int64_t)g.B * g.Hh * g.nb) return;
+  int p = colptr[c];
+  for (int w = 0; w < words; ++w) {
+    uint32_t b = bits[c * words + w];
+    while (b) {
+      const int i = __ffs(b) - 1;
+      rowidx[p++] = w * 32 + i;
+      b &= b - 1;
+    }
   }
+}
+
+__global__ void k_zero_u32(uint32_t* __restrict__ p, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
 }
 
 // Exclusive scan of n int32 counts into out[0..n] (out[n] = total), one workgroup.
@@ -378,9 +399,11 @@ BwdWorkspace plan_bwd_workspace(const Geom& g, const Cuboid& cu, int dtype) {
   L.off_dst_hi = off; off = al(off + BH * D * D * 2);
   L.off_dst_lo = off; off = al(off + BH * D * D * 2);
   L.off_dz = off;     off = al(off + BH * D * 4);
+  L.off_dwh = off;    off = al(off + BH * D * D * 4);
   L.off_colcnt = off; off = al(off + BH * nb * 4);
   L.off_colptr = off; off = al(off + (BH * nb + 1) * 4);
   L.off_rowidx = off; off = al(off + BH * nb * nb * 4);
+  L.off_bits = off;   off = al(off + BH * nb * ((nb + 31) / 32) * 4);
   L.bytes = off;
   return L;
 }
@@ -410,8 +433,9 @@ hipError_t launch_linear_bwd(const Geom& g, const BwdArgs& a, char* ws, const Bw
     hipLaunchKernelGGL(k_fold_ds<128>, fg, dim3(256), 0, st, g, L.red_splits, F32(L.off_dspart),
                        F32(L.off_dzpart), B16(L.off_ds_hi), B16(L.off_ds_lo), B16(L.off_dst_hi),
                        B16(L.off_dst_lo), F32(L.off_dz));
-    hipLaunchKernelGGL(k_fold_dw<128>, dim3(128 * 128 / 256), dim3(256), 0, st, g, L.red_splits,
-                       F32(L.off_dwpart), a.gate, a.dw_lin);
+    hipLaunchKernelGGL(k_fold_dw_heads<128>, fg, dim3(256), 0, st, g, L.red_splits, F32(L.off_dwpart), a.gate,
+                       F32(L.off_dwh));
+    hipLaunchKernelGGL(k_fold_dw<128>, dim3(128 * 128 / 256), dim3(256), 0, st, g, F32(L.off_dwh), a.dw_lin);
   } else if (g.D == 64) {
     hipLaunchKernelGGL(k_split_state<64>, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, tot,
                        F32(L.off_s32), B16(L.off_s_hi), B16(L.off_s_lo), B16(L.off_st_hi), B16(L.off_st_lo));
@@ -424,12 +448,13 @@ hipError_t launch_linear_bwd(const Geom& g, const BwdArgs& a, char* ws, const Bw
     hipLaunchKernelGGL(k_fold_ds<64>, fg, dim3(256), 0, st, g, L.red_splits, F32(L.off_dspart),
                        F32(L.off_dzpart), B16(L.off_ds_hi), B16(L.off_ds_lo), B16(L.off_dst_hi),
                        B16(L.off_dst_lo), F32(L.off_dz));
-    hipLaunchKernelGGL(k_fold_dw<64>, dim3(64 * 64 / 256), dim3(256), 0, st, g, L.red_splits,
-                       F32(L.off_dwpart), a.gate, a.dw_lin);
+    hipLaunchKernelGGL(k_fold_dw_heads<64>, fg, dim3(256), 0, st, g, L.red_splits, F32(L.off_dwpart), a.gate,
+                       F32(L.off_dwh));
+    hipLaunchKernelGGL(k_fold_dw<64>, dim3(64 * 64 / 256), dim3(256), 0, st, g, F32(L.off_dwh), a.dw_lin);
   } else {
     return hipErrorInvalidValue;
   }
-  hipLaunchKernelGGL(k_fold_dgate, dim3((unsigned)BH), dim3(64), 0, st, g, F32(L.off_gpart), a.dgate);
+  hipLaunchKernelGGL(k_fold_dgate, dim3((unsigned)BH), dim3(256), 0, st, g, F32(L.off_gpart), a.dgate);
   return hipGetLastError();
 }
 
@@ -439,10 +464,15 @@ hipError_t launch_mask_transpose(const Geom& g, const int32_t* row_ptr, const in
   int32_t* cnt = reinterpret_cast<int32_t*>(ws + L.off_colcnt);
   int32_t* ptr = reinterpret_cast<int32_t*>(ws + L.off_colptr);
   int32_t* idx = reinterpret_cast<int32_t*>(ws + L.off_rowidx);
+  const int words = (g.nb + 31) / 32;
+  uint32_t* bits = reinterpret_cast<uint32_t*>(ws + L.off_bits);
   const dim3 grid((unsigned)((n + 255) / 256));
-  hipLaunchKernelGGL(k_csc_count, grid, dim3(256), 0, st, g, row_ptr, col_idx, cnt);
+  hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)std::min<int64_t>((n * words + 255) / 256, 4096)), dim3(256), 0, st,
+                     bits, n * words);
+  hipLaunchKernelGGL(k_csc_bits, grid, dim3(256), 0, st, g, words, row_ptr, col_idx, bits);
+  hipLaunchKernelGGL(k_csc_count, grid, dim3(256), 0, st, g, words, bits, cnt);
   hipLaunchKernelGGL(k_scan_counts, dim3(1), dim3(1024), 0, st, cnt, n, ptr);
-  hipLaunchKernelGGL(k_csc_fill, grid, dim3(256), 0, st, g, row_ptr, col_idx, ptr, idx);
+  hipLaunchKernelGGL(k_csc_fill, grid, dim3(256), 0, st, g, words, bits, ptr, idx);
   return hipGetLastError();
 }
 

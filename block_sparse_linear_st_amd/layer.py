@@ -61,9 +61,9 @@ class SaladLayer:
         S.salad_linear_state(self.shape, k, v, S_out, z_out, self.ws, stream)
 
     def forward(self, q, k, v, gate, w_lin, out, eps: float = 1e-6, scale: float = 0.0,
-                drop_tau: float = 0.0, stream=None):
+                drop_tau: float = 0.0, stream=None, lse=None):
         S.salad_attn_fwd(self.shape, q, k, v, self.row_ptr, self.col_idx, gate, w_lin, eps, scale, drop_tau,
-                         out, self.ws, stream)
+                         out, self.ws, stream, lse=lse)
         return out
 
     def branches(self, q, k, v, out_sparse, out_lin, eps: float = 1e-6, scale: float = 0.0, stream=None):

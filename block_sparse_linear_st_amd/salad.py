@@ -63,17 +63,17 @@ _SIGS = {
                                         _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
     "salad_bwd_workspace_bytes": (_sz, [ctypes.POINTER(salad_shape)]),
     "salad_attn_bwd": (ctypes.c_int, [ctypes.POINTER(salad_shape), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f, _f,
-                                      _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+                                      _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "salad_token_order": (ctypes.c_int, [ctypes.POINTER(salad_shape), _vp]),
     "salad_permute_tokens": (ctypes.c_int, [ctypes.POINTER(salad_shape), ctypes.c_int, _vp, _vp, _vp]),
     "salad_gate_from_q": (ctypes.c_int, [ctypes.POINTER(salad_shape), _vp, _vp, _vp, _vp, _sz, _vp]),
     "salad_linear_state": (ctypes.c_int, [ctypes.POINTER(salad_shape), _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "salad_attn_fwd": (ctypes.c_int, [ctypes.POINTER(salad_shape), _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                                      _f, _f, _f, _vp, _vp, _sz, _vp]),
+                                      _f, _f, _f, _vp, _vp, _vp, _sz, _vp]),
     "salad_linear_prepare": (ctypes.c_int, [ctypes.POINTER(salad_shape), _vp, _vp, _vp, _vp, ctypes.c_float,
                                             _vp, _sz, _vp]),
     "salad_attn_apply": (ctypes.c_int, [ctypes.POINTER(salad_shape), _vp, _vp, _vp, _vp, _vp, _vp,
-                                        _f, _f, _f, _vp, _vp, _sz, _vp]),
+                                        _f, _f, _f, _vp, _vp, _vp, _sz, _vp]),
     "salad_attn_fwd_branches": (ctypes.c_int, [ctypes.POINTER(salad_shape), _vp, _vp, _vp, _vp, _vp,
                                                _f, _f, _vp, _vp, _vp, _sz, _vp]),
 }
@@ -191,9 +191,9 @@ def salad_linear_state(shape, k, v, S, z, ws, stream=None):
 
 
 def salad_attn_fwd(shape, q, k, v, row_ptr, col_idx, gate, w_lin, eps, scale, drop_tau, out, ws,
-                   stream=None):
+                   stream=None, lse=None):
     _check(lib().salad_attn_fwd(ctypes.byref(shape), _p(q), _p(k), _p(v), _p(row_ptr), _p(col_idx),
-                                _p(gate), _p(w_lin), eps, scale, drop_tau, _p(out), _p(ws), ws.numel(),
+                                _p(gate), _p(w_lin), eps, scale, drop_tau, _p(out), _p(lse), _p(ws), ws.numel(),
                                 _stream(stream)), "salad_attn_fwd")
 
 
@@ -209,9 +209,10 @@ def salad_linear_prepare(shape, k, v, gate, w_lin, ws, stream=None, drop_tau=0.0
                                       _p(ws), ws.numel(), _stream(stream)), "salad_linear_prepare")
 
 
-def salad_attn_apply(shape, q, k, v, row_ptr, col_idx, gate, eps, scale, drop_tau, out, ws, stream=None):
+def salad_attn_apply(shape, q, k, v, row_ptr, col_idx, gate, eps, scale, drop_tau, out, ws, stream=None,
+                     lse=None):
     _check(lib().salad_attn_apply(ctypes.byref(shape), _p(q), _p(k), _p(v), _p(row_ptr), _p(col_idx),
-                                  _p(gate), eps, scale, drop_tau, _p(out), _p(ws), ws.numel(),
+                                  _p(gate), eps, scale, drop_tau, _p(out), _p(lse), _p(ws), ws.numel(),
                                   _stream(stream)), "salad_attn_apply")
 
 
@@ -220,7 +221,7 @@ def salad_bwd_workspace_bytes(shape: salad_shape) -> int:
 
 
 def salad_attn_bwd(shape, q, k, v, row_ptr, col_idx, gate, w_lin, eps, scale, out, dout, dq, dk, dv, dw_lin,
-                   dgate, ws, stream=None):
+                   dgate, ws, stream=None, lse=None):
     _check(lib().salad_attn_bwd(ctypes.byref(shape), _p(q), _p(k), _p(v), _p(row_ptr), _p(col_idx), _p(gate),
-                                _p(w_lin), eps, scale, _p(out), _p(dout), _p(dq), _p(dk), _p(dv), _p(dw_lin),
-                                _p(dgate), _p(ws), ws.numel(), _stream(stream)), "salad_attn_bwd")
+                                _p(w_lin), eps, scale, _p(out), _p(lse), _p(dout), _p(dq), _p(dk), _p(dv),
+                                _p(dw_lin), _p(dgate), _p(ws), ws.numel(), _stream(stream)), "salad_attn_bwd")

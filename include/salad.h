@@ -216,11 +216,16 @@ SALAD_API int salad_linear_state(const salad_shape* shape, const void* k, const 
  *   drop_tau  branch dropping ("SALAD" explainer, section 2.3): heads whose
  *          gate < drop_tau skip the linear branch entirely: no linear state
  *          is computed for them and out = o_s; pass 0 to keep every branch
- *   out    device, shape of q */
+ *   out    device, shape of q
+ *   lse    NULL, or device float [batch*heads*n_pad] (bf16 shapes only, else
+ *          SALAD_EUNSUPPORTED): receives each row's log2-sum-exp of its scaled
+ *          scores, m + log2(sum_j 2^(x_j - m)) with x_j = scale*<q_i,k_j>*log2(e)
+ *          over the kept keys (+inf for padding rows and rows that keep no
+ *          key), for salad_attn_bwd */
 SALAD_API int salad_attn_fwd(const salad_shape* shape, const void* q, const void* k, const void* v,
                    const int32_t* row_ptr, const int32_t* col_idx,
                    const float* gate, const void* w_lin, float eps, float scale,
-                   float drop_tau, void* out, void* ws, size_t ws_bytes, void* stream);
+                   float drop_tau, void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /* salad_attn_fwd in two calls, for callers that reuse the linear state or
  * time the steps apart.  salad_linear_prepare computes S and z (as
@@ -240,7 +245,7 @@ SALAD_API int salad_linear_prepare(const salad_shape* shape, const void* k, cons
 SALAD_API int salad_attn_apply(const salad_shape* shape, const void* q, const void* k,
                                const void* v, const int32_t* row_ptr, const int32_t* col_idx,
                                const float* gate, float eps, float scale, float drop_tau,
-                               void* out, void* ws, size_t ws_bytes, void* stream);
+                               void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /* The two branches separately, for parity checks: out_sparse = o_s and
  * out_lin = o_l (before projection and gate), both shaped like q, rows >= N
@@ -267,6 +272,9 @@ SALAD_API size_t salad_bwd_workspace_bytes(const salad_shape* shape);
  *   q, k, v, out, dout  device bf16 [batch, heads, n_pad, head_dim]: the
  *                       forward's inputs, its output, and dL/dout (rows from N
  *                       on are not read)
+ *   lse                 the forward's lse output, or NULL: then the kernel
+ *                       recomputes it (one more pass of Q K^T over the kept
+ *                       blocks)
  *   row_ptr, col_idx    the CSR mask the forward used
  *   gate                device float [batch*heads]; w_lin device bf16
  *                       [head_dim, head_dim]; eps, scale as in salad_attn_fwd
@@ -281,7 +289,8 @@ SALAD_API size_t salad_bwd_workspace_bytes(const salad_shape* shape);
 SALAD_API int salad_attn_bwd(const salad_shape* shape, const void* q, const void* k,
                              const void* v, const int32_t* row_ptr, const int32_t* col_idx,
                              const float* gate, const void* w_lin, float eps, float scale,
-                             const void* out, const void* dout, void* dq, void* dk, void* dv,
+                             const void* out, const float* lse, const void* dout, void* dq,
+                             void* dk, void* dv,
                              float* dw_lin, float* dgate, void* ws, size_t ws_bytes,
                              void* stream);
 

@@ -48,6 +48,7 @@ from .attention import (
     linear_state,
     mix,
     sparse_attention,
+    sparse_lse2,
 )
 from .backward import layer_backward
 from .layout import cuboid_order, permute_tokens, slot_coords
@@ -87,6 +88,7 @@ __all__ = [
     "pooled_scores_f32",
     "slot_coords",
     "sparse_attention",
+    "sparse_lse2",
     "topk_count",
     "topk_select",
     "window_count",

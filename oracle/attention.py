@@ -106,6 +106,35 @@ def sparse_attention(q, k, v, row_ptr, col_idx, N: int, block: int, scale: Optio
     return out
 
 
+def sparse_lse2(q, k, row_ptr, col_idx, N: int, block: int, scale: Optional[float] = None) -> np.ndarray:
+    """Row statistic the forward keeps for training: log2 of sum_j exp(l_ij) over the kept keys.
+
+    l_ij = scale * <q_i, k_j> as in ``sparse_attention``; log2 because the
+    kernels work in base 2 (x = l * log2(e)).  +inf for padding rows and rows
+    that keep no valid key.  Returns fp64 [B, H, n_pad].
+    """
+    B, Hh, n_pad, d = q.shape
+    nb = n_pad // block
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+    out = np.full((B, Hh, n_pad), np.inf)
+    for b in range(B):
+        for h in range(Hh):
+            kf = np.asarray(k[b, h], np.float64)
+            for qb in range(nb):
+                rows = _rows_of(qb, block, N)
+                if rows.size == 0:
+                    continue
+                r = (b * Hh + h) * nb + qb
+                keys = np.concatenate([np.arange(kb * block, min((kb + 1) * block, N))
+                                       for kb in col_idx[row_ptr[r]:row_ptr[r + 1]]] or [np.zeros(0, np.int64)])
+                if keys.size == 0:
+                    continue
+                lg = scale * (np.asarray(q[b, h, rows], np.float64) @ kf[keys].T)
+                m = lg.max(axis=1, keepdims=True)
+                out[b, h, rows] = (m[:, 0] + np.log(np.exp(lg - m).sum(axis=1))) / np.log(2.0)
+    return out
+
+
 def linear_attention(q, k, v, N: int, eps: float, block: Optional[int] = None,
                      qblocks: Optional[Iterable[Tuple[int, int, int]]] = None):
     """Linear branch o_l in quadratic form; same return convention as ``sparse_attention``."""

@@ -95,13 +95,13 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert L.salad_build_mask(ctypes.byref(sh), topk, None, None, fake, fake, 10 ** 7, None, None, None, fake, ws_bytes, None) == S.SALAD_EINVAL
     # misaligned pointers
     odd = ctypes.c_void_p(0x100004)
-    assert L.salad_attn_fwd(ctypes.byref(sh), odd, fake, fake, fake, fake, fake, fake, 1e-6, 0.0, 0.0, fake, fake, ws_bytes, None) == S.SALAD_EINVAL
+    assert L.salad_attn_fwd(ctypes.byref(sh), odd, fake, fake, fake, fake, fake, fake, 1e-6, 0.0, 0.0, fake, None, fake, ws_bytes, None) == S.SALAD_EINVAL
     # missing gate / w_lin / out; bad eps
-    assert L.salad_attn_fwd(ctypes.byref(sh), fake, fake, fake, fake, fake, None, fake, 1e-6, 0.0, 0.0, fake, fake, ws_bytes, None) == S.SALAD_EINVAL
-    assert L.salad_attn_fwd(ctypes.byref(sh), fake, fake, fake, fake, fake, fake, None, 1e-6, 0.0, 0.0, fake, fake, ws_bytes, None) == S.SALAD_EINVAL
-    assert L.salad_attn_fwd(ctypes.byref(sh), fake, fake, fake, fake, fake, fake, fake, -1.0, 0.0, 0.0, fake, fake, ws_bytes, None) == S.SALAD_EINVAL
-    assert L.salad_attn_fwd(ctypes.byref(sh), fake, fake, fake, fake, fake, fake, fake, 1e-6, 0.0, 0.0, fake, fake, 1, None) == S.SALAD_ENOSPACE
-    assert L.salad_attn_apply(ctypes.byref(sh), fake, fake, fake, fake, fake, None, 1e-6, 0.0, 0.0, fake, fake, ws_bytes, None) == S.SALAD_EINVAL
+    assert L.salad_attn_fwd(ctypes.byref(sh), fake, fake, fake, fake, fake, None, fake, 1e-6, 0.0, 0.0, fake, None, fake, ws_bytes, None) == S.SALAD_EINVAL
+    assert L.salad_attn_fwd(ctypes.byref(sh), fake, fake, fake, fake, fake, fake, None, 1e-6, 0.0, 0.0, fake, None, fake, ws_bytes, None) == S.SALAD_EINVAL
+    assert L.salad_attn_fwd(ctypes.byref(sh), fake, fake, fake, fake, fake, fake, fake, -1.0, 0.0, 0.0, fake, None, fake, ws_bytes, None) == S.SALAD_EINVAL
+    assert L.salad_attn_fwd(ctypes.byref(sh), fake, fake, fake, fake, fake, fake, fake, 1e-6, 0.0, 0.0, fake, None, fake, 1, None) == S.SALAD_ENOSPACE
+    assert L.salad_attn_apply(ctypes.byref(sh), fake, fake, fake, fake, fake, None, 1e-6, 0.0, 0.0, fake, None, fake, ws_bytes, None) == S.SALAD_EINVAL
     assert L.salad_linear_prepare(ctypes.byref(sh), fake, fake, None, fake, 0.0, fake, ws_bytes, None) == S.SALAD_EINVAL
     assert L.salad_linear_prepare(ctypes.byref(sh), fake, fake, fake, fake, float("nan"), fake, ws_bytes, None) == S.SALAD_EINVAL
     assert L.salad_linear_state(ctypes.byref(sh), fake, None, fake, fake, fake, ws_bytes, None) == S.SALAD_EINVAL
@@ -200,13 +200,13 @@ def test_backward_rejects_bad_arguments_before_launch():
     assert ws_bytes > S.salad_workspace_bytes(sh)
     assert S.salad_bwd_workspace_bytes(_shape("c3", head_dim=96)) == 0
     fake = ctypes.c_void_p(0x100000)
-    args = [fake] * 5 + [fake, fake, 1e-6, 0.0, fake, fake, fake, fake, fake, fake, fake, fake, ws_bytes, None]
-    # q, k, v, row_ptr, col_idx, gate, w_lin, eps, scale, out, dout, dq, dk, dv, dw, dgate, ws, ws_bytes, stream
+    args = [fake] * 5 + [fake, fake, 1e-6, 0.0, fake, None, fake, fake, fake, fake, fake, fake, fake, ws_bytes, None]
+    # q, k, v, row_ptr, col_idx, gate, w_lin, eps, scale, out, lse, dout, dq, dk, dv, dw, dgate, ws, ws_bytes, stream
 
     def call(shape=sh, **over):
         a = list(args)
-        names = ["q", "k", "v", "row_ptr", "col_idx", "gate", "w_lin", "eps", "scale", "out", "dout", "dq", "dk",
-                 "dv", "dw", "dgate", "ws", "ws_bytes", "stream"]
+        names = ["q", "k", "v", "row_ptr", "col_idx", "gate", "w_lin", "eps", "scale", "out", "lse", "dout", "dq",
+                 "dk", "dv", "dw", "dgate", "ws", "ws_bytes", "stream"]
         for key, val in over.items():
             a[names.index(key)] = val
         return L.salad_attn_bwd(ctypes.byref(shape), *a)

@@ -7,7 +7,9 @@ is a relative 2^-9, three of them stack on a typical element, so the bars are
 rel-L2 <= 1.5e-2 and max-abs <= 3e-2 * max|ref| per tensor (about 2.5x the
 expected error).  dW_lin and dgate are fp32 sums of bf16-rounded o_l and dU:
 rel-L2 <= 1e-2.  Padding rows of dq, dk, dv must be exactly 0, and two runs
-must agree bit for bit.
+must agree bit for bit.  Both paths are checked: the softmax statistic kept by
+the forward (its log2-sum-exp output, itself checked against the oracle's
+definition) and the one the backward recomputes.
 """
 
 import numpy as np
@@ -61,23 +63,24 @@ def _run(cfg, inp, cuboid=False):
         gate = torch.from_numpy(inp.gate).cuda()
         layer.build_mask(q, k)
     out = torch.empty_like(q)
-    layer.forward(q, k, v, gate, w, out, eps=cfg.eps)
+    lse = torch.full((cfg.batch * cfg.heads * cfg.n_pad,), float("nan"), dtype=torch.float32, device="cuda")
+    layer.forward(q, k, v, gate, w, out, eps=cfg.eps, lse=lse)
     dvals, dbits = make_grad_output(cfg)
     dout = torch.from_numpy(dbits.view(np.int16)).view(torch.bfloat16).cuda()
     ws = torch.empty(S.salad_bwd_workspace_bytes(layer.shape), dtype=torch.uint8, device="cuda")
     res = []
-    for _ in range(2):
+    for lse_arg in (lse, lse, None):  # forward's statistic twice (determinism), then recomputed
         g = {n: torch.full_like(q, float("nan")) for n in ("dq", "dk", "dv")}
         dw = torch.full((cfg.head_dim, cfg.head_dim), float("nan"), dtype=torch.float32, device="cuda")
         dg = torch.full((cfg.batch * cfg.heads,), float("nan"), dtype=torch.float32, device="cuda")
         S.salad_attn_bwd(layer.shape, q, k, v, layer.row_ptr, layer.col_idx, gate, w, cfg.eps, 0.0, out, dout,
-                         g["dq"], g["dk"], g["dv"], dw, dg, ws)
+                         g["dq"], g["dk"], g["dv"], dw, dg, ws, lse=lse_arg)
         torch.cuda.synchronize()
         g["dw"], g["dg"] = dw, dg
         res.append(g)
     for n in res[0]:
         assert torch.equal(res[0][n], res[1][n]), f"{n} differs between two runs"
-    return layer, gate, res[0], dvals
+    return layer, gate, res, dvals, lse.view(cfg.batch, cfg.heads, cfg.n_pad).cpu().numpy(), (q, k)
 
 
 def _oracle(cfg, name_or_inp, gate, dvals, stored=None):
@@ -90,6 +93,18 @@ def _oracle(cfg, name_or_inp, gate, dvals, stored=None):
         rp, ci = oracle.csr_from_keep(keep)
     return oracle.layer_backward(q, k, v, rp, ci, gate.cpu().numpy().astype(np.float64), inp.w_lin, cfg.N,
                                  cfg.block, cfg.eps, dvals), rp, ci
+
+
+def _compare_all(cfg, res, ref, lse, stored, rp, ci, tag):
+    """Both backward paths against the oracle; the forward's log2-sum-exp against its definition."""
+    _compare(cfg, res[0], ref, f"{tag} (forward lse)")
+    _compare(cfg, res[2], ref, f"{tag} (recomputed lse)")
+    want = oracle.sparse_lse2(stored[0], stored[1], rp, ci, cfg.N, cfg.block)
+    N = cfg.N
+    assert np.all(np.isinf(lse[:, :, N:])) and np.all(np.isfinite(lse[:, :, :N]))
+    err = float(np.max(np.abs(lse[:, :, :N] - want[:, :, :N])))
+    print(f"{tag} lse: max-abs {err:.3e} (bar 2e-2)", flush=True)
+    assert err <= 2e-2  # probabilities summed after bf16 rounding (relative 2^-9): |log2(1 +- 2^-9)| = 2.8e-3
 
 
 def _compare(cfg, got, ref, tag):
@@ -106,20 +121,20 @@ def test_backward_c2():
     print("backward c2", flush=True)
     cfg = CONFIGS["c2"]
     inp = inputs("c2")
-    layer, gate, got, dvals = _run(cfg, inp)
+    layer, gate, res, dvals, lse, _ = _run(cfg, inp)
     np.testing.assert_array_equal(layer.row_ptr.cpu().numpy(), oracle_csr("c2")[0])
-    ref, _, _ = _oracle(cfg, inp, gate, dvals)
-    _compare(cfg, got, ref, "c2")
+    ref, rp, ci = _oracle(cfg, inp, gate, dvals)
+    _compare_all(cfg, res, ref, lse, (inp.q, inp.k), rp, ci, "c2")
 
 
 def test_backward_b128_ragged():
     print("backward b128", flush=True)
     cfg = B128
     inp = make_inputs(cfg)
-    layer, gate, got, dvals = _run(cfg, inp)
-    ref, rp, _ = _oracle(cfg, inp, gate, dvals)
+    layer, gate, res, dvals, lse, _ = _run(cfg, inp)
+    ref, rp, ci = _oracle(cfg, inp, gate, dvals)
     np.testing.assert_array_equal(layer.row_ptr.cpu().numpy(), rp)
-    _compare(cfg, got, ref, "b128")
+    _compare_all(cfg, res, ref, lse, (inp.q, inp.k), rp, ci, "b128")
 
 
 def test_backward_c9_cuboid_mixed_masks():
@@ -127,8 +142,8 @@ def test_backward_c9_cuboid_mixed_masks():
     print("backward c9", flush=True)
     cfg = CONFIGS["c9"]
     inp = inputs("c9")
-    layer, gate, got, dvals = _run(cfg, inp, cuboid=True)
+    layer, gate, res, dvals, lse, _ = _run(cfg, inp, cuboid=True)
     stored = stored_inputs("c9")
-    ref, rp, _ = _oracle(cfg, inp, gate, dvals, stored=stored)
+    ref, rp, ci = _oracle(cfg, inp, gate, dvals, stored=stored)
     np.testing.assert_array_equal(layer.row_ptr.cpu().numpy(), rp)
-    _compare(cfg, got, ref, "c9")
+    _compare_all(cfg, res, ref, lse, stored, rp, ci, "c9")

@@ -160,3 +160,39 @@ def test_linear_branch_chain_rule_on_the_linear_form():
             np.testing.assert_allclose(full["dq"][b, h, :N] - sparse["dq"][b, h, :N], dq, atol=1e-11)
             np.testing.assert_allclose(full["dk"][b, h, :N] - sparse["dk"][b, h, :N], dk, atol=1e-11)
             np.testing.assert_allclose(full["dv"][b, h, :N] - sparse["dv"][b, h, :N], dv, atol=1e-11)
+
+
+def test_lse2_closed_forms():
+    """Equal keys: log2 of n e^l = l log2(e) + log2(n); a two-key hand case; +inf for empty rows and padding."""
+    B, Hh, block, d = 1, 1, 4, 2
+    N = 7
+    n_pad = 8
+    q = np.zeros((B, Hh, n_pad, d))
+    k = np.zeros((B, Hh, n_pad, d))
+    q[0, 0, :, 0] = 2.0
+    k[0, 0, :, 0] = 0.5           # every logit = scale * 1.0
+    keep = np.array([[[[True, True], [False, False]]]])
+    rp, ci = oracle.csr_from_keep(keep)
+    scale = 0.7
+    got = oracle.sparse_lse2(q, k, rp, ci, N, block, scale)
+    np.testing.assert_allclose(got[0, 0, :4], scale * np.log2(np.e) + np.log2(7.0), rtol=1e-13)
+    assert np.all(np.isinf(got[0, 0, 4:]))  # rows of a block that keeps nothing, and the padding row
+    # two keys with logits 0 and ln 3: log2(1 + 3) = 2
+    q2 = np.zeros((1, 1, 2, 1)); q2[0, 0, :, 0] = 1.0
+    k2 = np.zeros((1, 1, 2, 1)); k2[0, 0, 1, 0] = np.log(3.0)
+    rp2, ci2 = oracle.csr_from_keep(np.ones((1, 1, 1, 1), dtype=bool))
+    np.testing.assert_allclose(oracle.sparse_lse2(q2, k2, rp2, ci2, 2, 2, 1.0)[0, 0], [2.0, 2.0], rtol=1e-14)
+
+
+def test_lse2_normalises_the_sparse_branch():
+    """2^(x - lse2) summed over a row's kept keys is 1 (x = scale q.k log2 e)."""
+    c = _tiny(7, empty_row=False)
+    N, block = c["N"], c["block"]
+    lse = oracle.sparse_lse2(c["q"], c["k"], c["rp"], c["ci"], N, block)
+    d = c["q"].shape[-1]
+    keep = ob._keep_matrix(c["rp"], c["ci"], 1, 2, -(-N // block))
+    for h in range(2):
+        for i in range(N):
+            keys = [j for j in range(N) if keep[0, h, i // block, j // block]]
+            x = (c["q"][0, h, i] @ c["k"][0, h, keys].T) / np.sqrt(d) * np.log2(np.e)
+            assert abs(np.sum(2.0 ** (x - lse[0, h, i])) - 1.0) < 1e-12
