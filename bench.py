@@ -42,12 +42,12 @@ ATTN_SRC = os.path.join(ROOT, "block_sparse_linear_st_amd", "csrc", "attn_bf16.h
 # HBM bytes per dispatch of the attention kernel from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE runs (KiB per dispatch), valid only for the kernel source they were
 # taken on (sha256 prefix); scaled by a plain 512 MiB copy, which reads
-# FETCH_SIZE = 262157.8 KiB and WRITE_SIZE = 524288 KiB.
+# FETCH_SIZE = 262156.8 KiB and WRITE_SIZE = 524288 KiB.
 ATTN_COUNTERS = {
-    "source_sha256": "89ed0cefb24f002b",
-    "fetch_scale": 524288.0 / 262157.8,
+    "source_sha256": "9954d48e3744c729",
+    "fetch_scale": 524288.0 / 262156.8,
     "write_scale": 1.0,
-    "c3": {"fetch_kib": 165768.2, "write_kib": 98304.0},
+    "c3": {"fetch_kib": 166185.0, "write_kib": 98304.0},
 }
 
 
@@ -71,6 +71,8 @@ def parse():
     ap.add_argument("--config", default="c3")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--backward", action="store_true",
+                    help="time a training step instead: forward (keeping its log2-sum-exp) + salad_attn_bwd")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 512 MiB device copy (torch copy_) 5 times, to scale HBM byte counters")
     return ap.parse_args()
@@ -132,6 +134,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.backward:
+        main_backward(args)
         return
     import torch
 
@@ -264,6 +269,104 @@ def main():
             inp = dataclasses.replace(inp, **{n: oracle.permute_tokens(getattr(inp, n), order)
                                               for n in ("q", "k", "v")})
         result["cpu_baseline"] = cpu_baseline(cfg, inp, row_ptr, col_idx, g, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def main_backward(args):
+    """Training step on one layer: mask, forward with its log2-sum-exp, backward (bf16 layers).
+
+    The roofline object prices the whole salad_attn_bwd call (its kernels run
+    inside one library call) at the minimal algorithmic work: five block
+    products per kept pair (S, dP, dV, dK, dQ: 10*block^2*d FLOP) plus 14*d^2
+    per valid token and head for the linear branch (u, t, dphi(q), dS, dW,
+    dphi(k), dv).  The kernels do two more products per pair, since dQ and
+    dK/dV are formed in separate passes without atomics.
+    """
+    import torch
+
+    from block_sparse_linear_st_amd import salad as S
+    from block_sparse_linear_st_amd.layer import SaladLayer
+    from synth import CONFIGS, make_grad_output, make_inputs
+
+    cfg = CONFIGS[args.config]
+    if cfg.dtype != "bf16" or tuple(cfg.cuboid) != (0, 0, 0):
+        print("--backward covers bf16 layers in frame-major order", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    inp = make_inputs(cfg)
+    layer = SaladLayer(cfg.batch, cfg.heads, cfg.head_dim, cfg.T, cfg.H, cfg.W, cfg.block, S.SALAD_BF16,
+                       cfg.specs)
+
+    def dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v, w = dev(inp.q_bits), dev(inp.k_bits), dev(inp.v_bits), dev(inp.w_lin_bits)
+    from_q = cfg.gate_kind == "from_q"
+    gate = torch.empty(cfg.batch * cfg.heads, dtype=torch.float32, device="cuda") if from_q \
+        else torch.from_numpy(inp.gate).cuda()
+    w_g = torch.from_numpy(inp.w_g).cuda() if from_q else None
+    _, dbits = make_grad_output(cfg)
+    dout = dev(dbits)
+    out = torch.empty_like(q)
+    lse = torch.empty(cfg.batch * cfg.heads * cfg.n_pad, dtype=torch.float32, device="cuda")
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    dw = torch.empty(cfg.head_dim, cfg.head_dim, dtype=torch.float32, device="cuda")
+    dg = torch.empty(cfg.batch * cfg.heads, dtype=torch.float32, device="cuda")
+    bws = torch.empty(S.salad_bwd_workspace_bytes(layer.shape), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        layer.build_mask(q, k, w_g, gate if from_q else None, stream=sp)
+        S.salad_linear_prepare(layer.shape, k, v, gate, w, layer.ws, sp, drop_tau=0.0)
+        S.salad_attn_apply(layer.shape, q, k, v, layer.row_ptr, layer.col_idx, gate, cfg.eps, 0.0, 0.0, out,
+                           layer.ws, sp, lse=lse)
+        if ev is not None:
+            ev[1].record(stream)
+        S.salad_attn_bwd(layer.shape, q, k, v, layer.row_ptr, layer.col_idx, gate, w, cfg.eps, 0.0, out, dout,
+                         dq, dk, dv, dw, dg, bws, sp, lse=lse)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    ms_fwd = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    ms_bwd = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    nnz = int(layer.row_ptr[-1].item())
+    d = cfg.head_dim
+    bwd_flop = 10.0 * cfg.block * cfg.block * d * nnz + 14.0 * d * d * cfg.N * cfg.batch * cfg.heads
+    achieved = bwd_flop / (ms_bwd * 1e-3) / 1e12
+    dense_train = 3.5 * cfg.dense_equiv_flop()  # dense attention: forward 2 products, backward 5
+    result = {
+        "metric": "dense-equiv TFLOP/s and ms per training step (forward + backward), hybrid sparse+linear attn",
+        "value": round(dense_train / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s (dense-equivalent, 3.5x the forward count)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) + smooth spatio-temporal sinusoid; dL/dout ~ N(0,1))",
+        "config": {"workload": f"{cfg.name}: {cfg.description}, forward + backward", "batch": cfg.batch,
+                   "heads": cfg.heads, "head_dim": d, "grid": f"{cfg.T}x{cfg.H}x{cfg.W}", "tokens": cfg.N,
+                   "block": cfg.block, "kept_block_pairs": nnz},
+        "ms_breakdown": {"forward": round(ms_fwd, 5), "backward": round(ms_bwd, 5)},
+        "roofline": {
+            "kernel": "salad_attn_bwd (dQ and dK/dV kernels plus the linear-branch kernels, one call)",
+            "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+            "algorithmic_flop_per_launch": bwd_flop,
+        },
+        "cpu_baseline": None,
+    }
     print(json.dumps(result), flush=True)
 
 
