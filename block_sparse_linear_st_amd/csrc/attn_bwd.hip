@@ -109,12 +109,14 @@ k_attn_bwd_dq(Geom g, BwdArgs a, const float* __restrict__ Dq, const float* __re
   const int T = (e1 - e0) * SUB;
   const uint32_t lds0 = lds_addr(smem);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  TileDma<D, NW> dma;
+  dma.init(wave_u, lane);
   auto issue = [&](int i, int buf) __attribute__((always_inline)) {
     const int ii = i < T ? i : i - T;
     const int key0 = a.col_idx[e0 + ii / SUB] * BLK + (ii % SUB) * kT;
     const uint32_t base = lds0 + buf * 2 * SM::TB;
-    dma_tile<D, NW>(base, K, key0, g.N - 1, wave_u, lane);
-    if (i >= T) dma_tile<D, NW>(base + SM::TB, V, key0, g.N - 1, wave_u, lane);
+    dma.issue(base, K, key0, g.N - 1);
+    if (i >= T) dma.issue(base + SM::TB, V, key0, g.N - 1);
   };
   float mrun = -INFINITY, lrun = 0.0f, lse = INFINITY;
   f32x16 acc[NT];
@@ -268,11 +270,13 @@ k_attn_bwd_dkdv(Geom g, BwdArgs a, const int32_t* __restrict__ colptr, const int
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   auto q0_of = [&](int i) __attribute__((always_inline)) { return rowidx[p0 + i / SUB] * BLK + (i % SUB) * kT; };
   float lse_r = 0.0f, dq_r = 0.0f;  // row statistics of the tile in flight (threads < kT)
+  TileDma<D, NW> dma;
+  dma.init(wave_u, lane);
   auto issue = [&](int i, int buf) __attribute__((always_inline)) {
     const int q0 = q0_of(i);
     const uint32_t base = lds0 + buf * 2 * SM::TB;
-    dma_tile<D, NW>(base, Q, q0, g.N - 1, wave_u, lane);
-    dma_tile<D, NW>(base + SM::TB, dO, q0, g.N - 1, wave_u, lane);
+    dma.issue(base, Q, q0, g.N - 1);
+    dma.issue(base + SM::TB, dO, q0, g.N - 1);
     if (tid < kT) {
       lse_r = lse[hb + q0 + tid];
       dq_r = Dq[hb + q0 + tid];

@@ -113,24 +113,59 @@ __device__ __attribute__((always_inline)) inline void lds_dma16(const void* gptr
                : "memory", "m0");
 }
 
-// Issue the DMA of rows [row0, row0 + 64) of a row-major [*, D] bf16 array
-// (rows clamped to `last`) into the swizzled LDS tile at byte address `lds`.
-// NW waves share the tile; wave w fills its 1 KiB blocks w*LOADS .. w*LOADS+LOADS-1.
-template <int D, int NW>
-__device__ __attribute__((always_inline)) inline void dma_tile(uint32_t lds, const __bf16* src, int row0, int last,
-                                                               int wave_u, int lane) {
-  using TL = TileLay<D>;
-  constexpr int LOADS = 64 * TL::ROW_B / 1024 / NW;
-  static_assert(LOADS >= 1, "tile too small for the waves");
-#pragma unroll
-  for (int i = 0; i < LOADS; ++i) {
-    const int blk = wave_u * LOADS + i;
-    const int P = blk * 64 + lane;
-    const int r = P / TL::CPR, p = P % TL::CPR;
-    const int gr = min(row0 + r, last);
-    lds_dma16(src + (int64_t)gr * D + ((p ^ TL::swz(r)) << 3), lds + blk * 1024);
-  }
+// The same with a wave-uniform 64-bit base in SGPRs and a 32-bit lane offset.
+__device__ __attribute__((always_inline)) inline void lds_dma16_s(uint32_t voff, const void* sbase,
+                                                                  uint32_t m0_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0_base)
+               : "memory", "m0");
 }
+
+__device__ __attribute__((always_inline)) inline const __bf16* uniform_ptr(const __bf16* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return reinterpret_cast<const __bf16*>(((uint64_t)hi << 32) | lo);
+}
+
+// DMA of a 64-row tile of a row-major [*, D] bf16 array into a swizzled LDS
+// tile.  NW waves share it; wave w fills its 1 KiB blocks w*LOADS ..
+// w*LOADS+LOADS-1.  The per-lane byte offsets inside a tile do not depend on
+// the tile: they are computed once.
+template <int D, int NW>
+struct TileDma {
+  using TL = TileLay<D>;
+  static constexpr int LOADS = 64 * TL::ROW_B / 1024 / NW;
+  static_assert(LOADS >= 1, "tile too small for the waves");
+  uint32_t off[LOADS];
+  int wave_u, lane;
+  __device__ void init(int w, int l) {
+    wave_u = w;
+    lane = l;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int P = (w * LOADS + i) * 64 + l;
+      const int r = P / TL::CPR, p = P % TL::CPR;
+      off[i] = (uint32_t)(r * TL::ROW_B + ((p ^ TL::swz(r)) << 4));
+    }
+  }
+  // rows [row0, row0 + 64) into the tile at LDS byte address lds; rows past
+  // `last` repeat row `last` (only in the tile that holds it)
+  __device__ __attribute__((always_inline)) void issue(uint32_t lds, const __bf16* src, int row0, int last) const {
+    if (row0 + 64 <= last + 1) {
+      const __bf16* base = uniform_ptr(src + (int64_t)row0 * D);
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) lds_dma16_s(off[i], base, lds + (wave_u * LOADS + i) * 1024);
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int P = (wave_u * LOADS + i) * 64 + lane;
+      const int r = P / TL::CPR, p = P % TL::CPR;
+      const int gr = min(row0 + r, last);
+      lds_dma16(src + (int64_t)gr * D + ((p ^ TL::swz(r)) << 3), lds + (wave_u * LOADS + i) * 1024);
+    }
+  }
+};
 
 __device__ inline uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)p;
