@@ -50,7 +50,7 @@ from .attention import (
     sparse_attention,
     sparse_lse2,
 )
-from .backward import layer_backward
+from .backward import layer_backward, layer_backward_sampled
 from .layout import cuboid_order, permute_tokens, slot_coords
 from .masks import (
     InfeasibleMask,
@@ -78,6 +78,7 @@ __all__ = [
     "gate_from_q",
     "keep_from_csr",
     "layer_backward",
+    "layer_backward_sampled",
     "layer_forward",
     "linear_attention",
     "linear_attention_from_state",

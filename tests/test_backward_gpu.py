@@ -147,3 +147,33 @@ def test_backward_c9_cuboid_mixed_masks():
     ref, rp, ci = _oracle(cfg, inp, gate, dvals, stored=stored)
     np.testing.assert_array_equal(layer.row_ptr.cpu().numpy(), rp)
     _compare_all(cfg, res, ref, lse, stored, rp, ci, "c9")
+
+
+@pytest.mark.parametrize("name", ["c3", "c4"])
+def test_backward_sampled_large(name):
+    """Full-size layers in the bench's launch configuration: sampled query blocks (dq) and key blocks (dk, dv)
+    against the oracle's closed-form gradients at those blocks; dW_lin and dgate in full."""
+    print(f"backward sampled {name}", flush=True)
+    from helpers import sample_blocks
+    cfg = CONFIGS[name]
+    inp = inputs(name)
+    layer, gate, res, dvals, _, _ = _run(cfg, inp)
+    rp, ci = oracle_csr(name)
+    np.testing.assert_array_equal(layer.row_ptr.cpu().numpy(), rp)
+    qbl = sample_blocks(cfg, n_random=8, seed=1)
+    kbl = sample_blocks(cfg, n_random=4, seed=2)[::2]
+    g = gate.cpu().numpy().astype(np.float64)
+    ref = oracle.layer_backward_sampled(inp.q, inp.k, inp.v, rp, ci, g, inp.w_lin, cfg.N, cfg.block, cfg.eps,
+                                        dvals, qbl, kbl)
+    blk = cfg.block
+    for which in (0, 2):  # forward's log2-sum-exp, recomputed
+        got = res[which]
+        tag = f"{name} ({'forward' if which == 0 else 'recomputed'} lse)"
+        dq = np.stack([to_numpy(got["dq"][b, h, x * blk:(x + 1) * blk]) for b, h, x in qbl])
+        dk = np.stack([to_numpy(got["dk"][b, h, x * blk:(x + 1) * blk]) for b, h, x in kbl])
+        dv = np.stack([to_numpy(got["dv"][b, h, x * blk:(x + 1) * blk]) for b, h, x in kbl])
+        _check(dq, ref["dq"], f"{tag} dq (sampled)")
+        _check(dk, ref["dk"], f"{tag} dk (sampled)")
+        _check(dv, ref["dv"], f"{tag} dv (sampled)")
+        _check(got["dw"].cpu().numpy(), ref["dw_lin"], f"{tag} dW_lin", rel_l2=FP32_REL_L2)
+        _check(got["dg"].cpu().numpy(), ref["dgate"], f"{tag} dgate", rel_l2=FP32_REL_L2)

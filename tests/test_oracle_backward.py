@@ -196,3 +196,23 @@ def test_lse2_normalises_the_sparse_branch():
             keys = [j for j in range(N) if keep[0, h, i // block, j // block]]
             x = (c["q"][0, h, i] @ c["k"][0, h, keys].T) / np.sqrt(d) * np.log2(np.e)
             assert abs(np.sum(2.0 ** (x - lse[0, h, i])) - 1.0) < 1e-12
+
+
+@pytest.mark.parametrize("seed", [0, 3])
+def test_sampled_gradients_equal_autograd(seed):
+    """The closed-form sampled gradients equal the autograd ones at every block of a small layer."""
+    c = _tiny(seed)
+    full = _grads(c)
+    B, Hh, n_pad, d = c["q"].shape
+    nb = n_pad // c["block"]
+    blocks = [(b, h, x) for b in range(B) for h in range(Hh) for x in range(nb)]
+    s = ob.layer_backward_sampled(c["q"], c["k"], c["v"], c["rp"], c["ci"], c["gate"], c["w"], c["N"], c["block"],
+                                  c["eps"], c["dout"], blocks, blocks)
+    blk = c["block"]
+    for idx, (b, h, x) in enumerate(blocks):
+        sl = slice(x * blk, (x + 1) * blk)
+        np.testing.assert_allclose(s["dq"][idx], full["dq"][b, h, sl], atol=1e-11)
+        np.testing.assert_allclose(s["dk"][idx], full["dk"][b, h, sl], atol=1e-11)
+        np.testing.assert_allclose(s["dv"][idx], full["dv"][b, h, sl], atol=1e-11)
+    np.testing.assert_allclose(s["dw_lin"], full["dw_lin"], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(s["dgate"], full["dgate"], rtol=1e-11, atol=1e-12)
