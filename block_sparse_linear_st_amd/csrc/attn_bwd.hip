@@ -171,14 +171,29 @@ k_attn_bwd_dq(Geom g, BwdArgs a, const float* __restrict__ Dq, const float* __re
       }
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
+        // every LDS fragment of a phase is read before its MFMAs, so each
+        // MFMA waits for its own operand only
+        bf16x8 ka[NC], va[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          ka[c] = frag_direct<D>(Kt, 32 * kt, c, lane);
+          va[c] = frag_direct<D>(Vt, 32 * kt, c, lane);
+        }
         f32x16 s, dp;
         zero(s);
         zero(dp);
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-          s = mfma(frag_direct<D>(Kt, 32 * kt, c, lane), qf[c], s);
-          dp = mfma(frag_direct<D>(Vt, 32 * kt, c, lane), dof[c], dp);
+          s = mfma(ka[c], qf[c], s);
+          dp = mfma(va[c], dof[c], dp);
         }
+        SG_DSREAD(2 * NC);
+        SG_MFMA(2 * NC);
+        bf16x8 kt_f[2][NT];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int tt = 0; tt < NT; ++tt) kt_f[h2][tt] = frag_tr<D>(Kt, 2 * kt + h2, tt, lane);
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int key = key0 + 32 * kt + crow(j, gg);
@@ -189,8 +204,10 @@ k_attn_bwd_dq(Geom g, BwdArgs a, const float* __restrict__ Dq, const float* __re
         for (int h2 = 0; h2 < 2; ++h2) {
           const bf16x8 b = c_to_b(s, h2);
 #pragma unroll
-          for (int t = 0; t < NT; ++t) acc[t] = mfma(frag_tr<D>(Kt, 2 * kt + h2, t, lane), b, acc[t]);
+          for (int tt = 0; tt < NT; ++tt) acc[tt] = mfma(kt_f[h2][tt], b, acc[tt]);
         }
+        SG_DSREAD(4 * NT);
+        SG_MFMA(2 * NT);
       }
     }
     wait_vmem();
@@ -205,22 +222,30 @@ k_attn_bwd_dq(Geom g, BwdArgs a, const float* __restrict__ Dq, const float* __re
   const float ddn = dden[hb + n];
   const __bf16* sh = s_hi + (int64_t)bh * D * D;
   const __bf16* sl = s_lo + (int64_t)bh * D * D;
-  const float* zb = z + (int64_t)bh * D;
+  float zr[NT][16];
+  rows_f32<D>(z + (int64_t)bh * D, gg, zr);
+  const uint64_t qpos = positive_rows<D>(Q + (int64_t)nrow * D, gg);
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     f32x16 lt2;
     zero(lt2);
     const int64_t ro = (int64_t)(32 * t + m) * D + 8 * gg;
+    bf16x8 ah[NC], al[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      lt2 = mfma(ld8(sh + ro + 16 * c), duf[c], lt2);
-      lt2 = mfma(ld8(sl + ro + 16 * c), duf[c], lt2);
+      ah[c] = ld8(sh + ro + 16 * c);
+      al[c] = ld8(sl + ro + 16 * c);
     }
 #pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      lt2 = mfma(ah[c], duf[c], lt2);
+      lt2 = mfma(al[c], duf[c], lt2);
+    }
+    SG_VMREAD(2 * NC);
+    SG_MFMA(2 * NC);
+#pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int ch = 32 * t + crow(i, gg);
-      const float qv = (float)Q[(int64_t)nrow * D + ch];
-      const float lin = qv > 0.0f ? lt2[i] + zb[ch] * ddn : 0.0f;
+      const float lin = ((qpos >> (16 * t + i)) & 1) ? lt2[i] + zr[t][i] * ddn : 0.0f;
       acc[t][i] = a.scale * acc[t][i] + lin;
     }
   }
@@ -298,14 +323,31 @@ k_attn_bwd_dkdv(Geom g, BwdArgs a, const int32_t* __restrict__ colptr, const int
     const unsigned char* Ot = Qt + SM::TB;
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
+      // every LDS fragment of a phase is read before its MFMAs
+      bf16x8 qa[NC], oa[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        qa[c] = frag_direct<D>(Qt, 32 * qs, c, lane);
+        oa[c] = frag_direct<D>(Ot, 32 * qs, c, lane);
+      }
       f32x16 s, dp;
       zero(s);
       zero(dp);
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        s = mfma(frag_direct<D>(Qt, 32 * qs, c, lane), kf[c], s);
-        dp = mfma(frag_direct<D>(Ot, 32 * qs, c, lane), vf[c], dp);
+        s = mfma(qa[c], kf[c], s);
+        dp = mfma(oa[c], vf[c], dp);
       }
+      SG_DSREAD(2 * NC);
+      SG_MFMA(2 * NC);
+      bf16x8 ot_f[2][NT], qt_f[2][NT];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+          ot_f[h2][tt] = frag_tr<D>(Ot, 2 * qs + h2, tt, lane);
+          qt_f[h2][tt] = frag_tr<D>(Qt, 2 * qs + h2, tt, lane);
+        }
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int qi = 32 * qs + crow(j, gg);
@@ -318,11 +360,13 @@ k_attn_bwd_dkdv(Geom g, BwdArgs a, const int32_t* __restrict__ colptr, const int
         const bf16x8 bp = c_to_b(s, h2);
         const bf16x8 bd = c_to_b(dp, h2);
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          dv[t] = mfma(frag_tr<D>(Ot, 2 * qs + h2, t, lane), bp, dv[t]);
-          dk[t] = mfma(frag_tr<D>(Qt, 2 * qs + h2, t, lane), bd, dk[t]);
+        for (int tt = 0; tt < NT; ++tt) {
+          dv[tt] = mfma(ot_f[h2][tt], bp, dv[tt]);
+          dk[tt] = mfma(qt_f[h2][tt], bd, dk[tt]);
         }
       }
+      SG_DSREAD(8 * NT);
+      SG_MFMA(4 * NT);
     }
     if (i + 1 < T && tid < kT) {
       lse_s[cur ^ 1][tid] = lse_r;
@@ -334,27 +378,50 @@ k_attn_bwd_dkdv(Geom g, BwdArgs a, const int32_t* __restrict__ colptr, const int
 
   // linear terms: dv += dS_lin^T phi(K)^T; dk += (dS_lin V^T + dz) * [k > 0]
   const int64_t mb = (int64_t)bh * D * D;
-  const float* dzb = dz + (int64_t)bh * D;
+  float dzr[NT][16];
+  rows_f32<D>(dz + (int64_t)bh * D, gg, dzr);
+  const uint64_t kpos = positive_rows<D>(K + (int64_t)jrow * D, gg);
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     f32x16 lv, lk;
     zero(lv);
     zero(lk);
     const int64_t ro = (int64_t)(32 * t + m) * D + 8 * gg;
+    {
+      bf16x8 a0[NC], a1[NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const bf16x8 pk = relu8(kf[c]);
-      lv = mfma(ld8(dst_hi + mb + ro + 16 * c), pk, lv);
-      lv = mfma(ld8(dst_lo + mb + ro + 16 * c), pk, lv);
-      lk = mfma(ld8(ds_hi + mb + ro + 16 * c), vf[c], lk);
-      lk = mfma(ld8(ds_lo + mb + ro + 16 * c), vf[c], lk);
+      for (int c = 0; c < NC; ++c) {
+        a0[c] = ld8(dst_hi + mb + ro + 16 * c);
+        a1[c] = ld8(dst_lo + mb + ro + 16 * c);
+      }
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const bf16x8 pk = relu8(kf[c]);
+        lv = mfma(a0[c], pk, lv);
+        lv = mfma(a1[c], pk, lv);
+      }
+      SG_VMREAD(2 * NC);
+      SG_MFMA(2 * NC);
+    }
+    {
+      bf16x8 a2[NC], a3[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        a2[c] = ld8(ds_hi + mb + ro + 16 * c);
+        a3[c] = ld8(ds_lo + mb + ro + 16 * c);
+      }
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        lk = mfma(a2[c], vf[c], lk);
+        lk = mfma(a3[c], vf[c], lk);
+      }
+      SG_VMREAD(2 * NC);
+      SG_MFMA(2 * NC);
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int ch = 32 * t + crow(i, gg);
-      const float kv = (float)K[(int64_t)jrow * D + ch];
       dv[t][i] += lv[i];
-      dk[t][i] = a.scale * dk[t][i] + (kv > 0.0f ? lk[i] + dzb[ch] : 0.0f);
+      dk[t][i] = a.scale * dk[t][i] + (((kpos >> (16 * t + i)) & 1) ? lk[i] + dzr[t][i] : 0.0f);
     }
   }
   const int nvalid = g.N - kb * BLK;

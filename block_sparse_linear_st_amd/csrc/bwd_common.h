@@ -199,5 +199,57 @@ __device__ inline float pair_max(float x) {
 // C-layout row index of register i for lane group g
 __device__ inline int crow(int i, int g) { return 8 * (i >> 2) + 4 * g + (i & 3); }
 
+// The fp32 values of `row` (global, 16-byte aligned) at the C-layout rows of this
+// lane group: out[t][i] = row[32*t + crow(i, g)] (D/8 loads of 16 bytes, all
+// issued before any is used).
+template <int D>
+__device__ inline void rows_f32(const float* row, int g, float (&out)[D / 32][16]) {
+  float4 w[D / 32][4];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) w[t][q] = *reinterpret_cast<const float4*>(row + 32 * t + 8 * q + 4 * g);
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      out[t][4 * q + 0] = w[t][q].x;
+      out[t][4 * q + 1] = w[t][q].y;
+      out[t][4 * q + 2] = w[t][q].z;
+      out[t][4 * q + 3] = w[t][q].w;
+    }
+}
+
+// Scheduling groups (same mask bits as the scheduling barrier): the next
+// `n` instructions of a kind, in program order, form a group.
+#define SG_MFMA(n) __builtin_amdgcn_sched_group_barrier(0x008, (n), 0)
+#define SG_DSREAD(n) __builtin_amdgcn_sched_group_barrier(0x100, (n), 0)
+#define SG_VMREAD(n) __builtin_amdgcn_sched_group_barrier(0x020, (n), 0)
+
+// Which of the D bf16 values of `row` (global, 16-byte aligned) at the C-layout
+// rows of this lane group are > 0: bit 16*t + i stands for row[32*t + crow(i, g)].
+// Those are D/8 runs of 4 consecutive values; all loads are issued first.
+template <int D>
+__device__ inline uint64_t positive_rows(const __bf16* row, int g) {
+  uint2 w[D / 32][4];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) w[t][q] = *reinterpret_cast<const uint2*>(row + 32 * t + 8 * q + 4 * g);
+  uint64_t m = 0;
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t v = ((r < 2 ? w[t][q].x : w[t][q].y) >> (16 * (r & 1))) & 0xffffu;
+        const uint32_t mag = v & 0x7fffu;
+        const bool pos = !(v & 0x8000u) && mag != 0u && mag <= 0x7f80u;  // > 0, not NaN
+        m |= (uint64_t)pos << (16 * t + 4 * q + r);
+      }
+  return m;
+}
+
 }  // namespace bwd
 }  // namespace salad
