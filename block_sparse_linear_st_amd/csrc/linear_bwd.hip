@@ -53,18 +53,27 @@ k_lin_bwd_tok(Geom g, const __bf16* __restrict__ Q, const __bf16* __restrict__ d
   const int64_t row = ((int64_t)bh * g.n_pad + n) * D;
   const float* zb = z + (int64_t)bh * D;
 
-  bf16x8 qf[NC], dof[NC];
-  float den_p = 0.0f, dot_p = 0.0f;
+  bf16x8 qf[NC], dof[NC], of[NC];
+  float4 zf[NC][2];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int ch = 16 * c + 8 * gg;
     qf[c] = relu8(ld8(Q + row + ch));
     dof[c] = ld8(dO + row + ch);
-    const bf16x8 o8 = ld8(Out + row + ch);
+    of[c] = ld8(Out + row + ch);
+    zf[c][0] = *reinterpret_cast<const float4*>(zb + ch);
+    zf[c][1] = *reinterpret_cast<const float4*>(zb + ch + 4);
+  }
+  SG_VMREAD(5 * NC);
+  float den_p = 0.0f, dot_p = 0.0f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const float zz[8] = {zf[c][0].x, zf[c][0].y, zf[c][0].z, zf[c][0].w,
+                         zf[c][1].x, zf[c][1].y, zf[c][1].z, zf[c][1].w};
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      den_p += (float)qf[c][j] * zb[ch + j];
-      dot_p += (float)dof[c][j] * (float)o8[j];
+      den_p += (float)qf[c][j] * zz[j];
+      dot_p += (float)dof[c][j] * (float)of[c][j];
     }
   }
   const float den = pair_sum(den_p) + eps;
@@ -79,12 +88,22 @@ k_lin_bwd_tok(Geom g, const __bf16* __restrict__ Q, const __bf16* __restrict__ d
     zero(u[t]);
     zero(tt[t]);
     const int64_t ro = (int64_t)(32 * t + m) * D + 8 * gg;
+    // all operand fragments of this row tile are requested before its MFMAs
+    bf16x8 ah[NC], al[NC], aw[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      u[t] = mfma(ld8(sth + ro + 16 * c), qf[c], u[t]);
-      u[t] = mfma(ld8(stl + ro + 16 * c), qf[c], u[t]);
-      tt[t] = mfma(ld8(W + ro + 16 * c), dof[c], tt[t]);
+      ah[c] = ld8(sth + ro + 16 * c);
+      al[c] = ld8(stl + ro + 16 * c);
+      aw[c] = ld8(W + ro + 16 * c);
     }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      u[t] = mfma(ah[c], qf[c], u[t]);
+      u[t] = mfma(al[c], qf[c], u[t]);
+      tt[t] = mfma(aw[c], dof[c], tt[t]);
+    }
+    SG_VMREAD(3 * NC);
+    SG_MFMA(3 * NC);
   }
   float r = 0.0f;
 #pragma unroll
@@ -167,12 +186,8 @@ k_lin_bwd_red(Geom g, int chunk, const __bf16* __restrict__ Q, const __bf16* __r
   using TL = TileLay<D>;
   constexpr int TD = D / 32, TPW = TD * TD / 4;
   constexpr int TB = kTT * TL::ROW_B;
-  __shared__ __align__(16) unsigned char smem[4 * TB];
-  __shared__ float dd[kTT];
-  unsigned char* Qt = smem;
-  unsigned char* Ut = smem + TB;
-  unsigned char* Lt = smem + 2 * TB;
-  unsigned char* Ot = smem + 3 * TB;
+  __shared__ __align__(16) unsigned char smem[8 * TB];
+  __shared__ float dd[2][kTT];
   const int split = blockIdx.x, bh = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, gg = lane >> 5, m = lane & 31;
   const int n0 = split * chunk, n1 = min(g.N, n0 + chunk);
@@ -187,13 +202,32 @@ k_lin_bwd_red(Geom g, int chunk, const __bf16* __restrict__ Q, const __bf16* __r
     zero(aw[t]);
   }
   float zacc = 0.0f;
+  // the four token tiles stream HBM -> LDS, double buffered
+  TileDma<D, 4> dma;
+  dma.init(__builtin_amdgcn_readfirstlane(wave), lane);
+  const uint32_t lds0 = lds_addr(smem);
+  float dd_r = 0.0f;
+  auto issue = [&](int t0, int buf) __attribute__((always_inline)) {
+    const uint32_t base = lds0 + buf * 4 * TB;
+    dma.issue(base, Q + hb * D, t0, g.N - 1);
+    dma.issue(base + TB, dU + hb * D, t0, g.n_pad - 1);
+    dma.issue(base + 2 * TB, OL + hb * D, t0, g.n_pad - 1);
+    dma.issue(base + 3 * TB, dO + hb * D, t0, g.N - 1);
+    if (tid < kTT) dd_r = t0 + tid < n1 ? dden[hb + t0 + tid] : 0.0f;
+  };
+  if (n0 < n1) {
+    issue(n0, 0);
+    if (tid < kTT) dd[0][tid] = dd_r;
+  }
+  wait_vmem();
+  __syncthreads();
+  int cur = 0;
   for (int t0 = n0; t0 < n1; t0 += kTT) {
-    load_tile<D, kTT, 256>(Qt, Q + hb * D, t0, g.N - 1, tid);
-    load_tile<D, kTT, 256>(Ut, dU + hb * D, t0, g.n_pad - 1, tid);
-    load_tile<D, kTT, 256>(Lt, OL + hb * D, t0, g.n_pad - 1, tid);
-    load_tile<D, kTT, 256>(Ot, dO + hb * D, t0, g.N - 1, tid);
-    if (tid < kTT) dd[tid] = t0 + tid < n1 ? dden[hb + t0 + tid] : 0.0f;
-    __syncthreads();
+    if (t0 + kTT < n1) issue(t0 + kTT, cur ^ 1);
+    const unsigned char* Qt = smem + cur * 4 * TB;
+    const unsigned char* Ut = Qt + TB;
+    const unsigned char* Lt = Qt + 2 * TB;
+    const unsigned char* Ot = Qt + 3 * TB;
     const int valid = n1 - t0;
 #pragma unroll
     for (int ks = 0; ks < kTT / 16; ++ks) {
@@ -201,7 +235,7 @@ k_lin_bwd_red(Geom g, int chunk, const __bf16* __restrict__ Q, const __bf16* __r
       const bf16x8 al = mask_slots(frag_tr<D>(Lt, ks, ti, lane), ks, valid, gg);
       if (tj0 == 0) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) zacc += (float)aq[j] * dd[16 * ks + 8 * (j >> 2) + 4 * gg + (j & 3)];
+        for (int j = 0; j < 8; ++j) zacc += (float)aq[j] * dd[cur][16 * ks + 8 * (j >> 2) + 4 * gg + (j & 3)];
       }
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
@@ -210,7 +244,10 @@ k_lin_bwd_red(Geom g, int chunk, const __bf16* __restrict__ Q, const __bf16* __r
         aw[t] = mfma(al, frag_tr<D>(Ot, ks, tj, lane), aw[t]);
       }
     }
+    if (t0 + kTT < n1 && tid < kTT) dd[cur ^ 1][tid] = dd_r;
+    wait_vmem();
     __syncthreads();
+    cur ^= 1;
   }
   const int64_t po = ((int64_t)split * g.B * g.Hh + bh) * D * D;
 #pragma unroll
