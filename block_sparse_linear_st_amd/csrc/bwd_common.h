@@ -85,21 +85,6 @@ __device__ inline bf16x8 frag_tr(const unsigned char* tile, int ks, int t, int l
   return __builtin_bit_cast(bf16x8, make_uint4(tr[0].x, tr[0].y, tr[1].x, tr[1].y));
 }
 
-// Copy rows [row0, row0 + ROWS) of a row-major [*, D] bf16 array into an LDS
-// tile (rows clamped to `last`, so every read is in bounds).  NT threads.
-template <int D, int ROWS, int NT>
-__device__ inline void load_tile(unsigned char* tile, const __bf16* src, int row0, int last, int tid) {
-  using TL = TileLay<D>;
-  constexpr int CH = ROWS * TL::CPR;
-#pragma unroll
-  for (int i = tid; i < CH; i += NT) {
-    const int r = i / TL::CPR, p = i % TL::CPR;
-    const int gr = min(row0 + r, last);
-    const uint4 v = *reinterpret_cast<const uint4*>(src + (int64_t)gr * D + p * 8);
-    *reinterpret_cast<uint4*>(tile + TL::off(r, p)) = v;
-  }
-}
-
 // s_waitcnt vmcnt(0) as a compiler-visible instruction (gfx9 encoding: vmcnt 0,
 // expcnt 7, lgkmcnt 15).
 __device__ __attribute__((always_inline)) inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }

@@ -408,7 +408,9 @@ BwdWorkspace plan_bwd_workspace(const Geom& g, const Cuboid& cu, int dtype) {
   L.fwd = plan_workspace(g, cu, dtype);
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
   const size_t BH = (size_t)g.B * g.Hh, D = g.D, nb = g.nb, np = g.n_pad;
-  int splits = (int)std::max<size_t>(1, (512 + BH - 1) / BH);
+  // token reduction: one resident workgroup per CU (128 KiB of LDS), at most 256
+  // in all so that it runs in one round
+  int splits = (int)std::max<size_t>(1, 256 / BH);
   splits = std::min(splits, (g.N + 63) / 64);
   int chunk = (g.N + splits - 1) / splits;
   chunk = (chunk + 63) / 64 * 64;
