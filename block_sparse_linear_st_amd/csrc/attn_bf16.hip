@@ -33,9 +33,15 @@
 // in registers.  Heads whose gate is below drop_tau skip it (section 2.3).  The
 // 128 x D bf16 result is staged through LDS for 16-byte coalesced stores.
 //
+// The per-lane LDS read offsets inside a tile are computed once; the tile loop
+// is unrolled over the two buffers, so every fragment read is that offset plus
+// an immediate.
+//
 // Work items map to workgroups so that each XCD (blockIdx % 8) gets a
 // contiguous range of (head, query group) items: neighbouring query blocks,
 // whose window lists overlap, share that XCD's L2.
+#include <type_traits>
+
 #include "internal.h"
 
 namespace salad {
@@ -172,15 +178,16 @@ __device__ __attribute__((always_inline)) inline void issue_tile(uint32_t buf, c
 }
 
 // S^T, softmax and O^T update of one wave on one tile held in `buf`.
-template <int D>
-__device__ __attribute__((always_inline)) inline void compute_tile(const unsigned char* buf, const bf16x8 (&qf)[D / 16],
+template <int D, int CUR>
+__device__ __attribute__((always_inline)) inline void compute_tile(const unsigned char* smem, const uint32_t (&ka)[D / 16],
+                                    const uint32_t (&va)[D / 32], const bf16x8 (&qf)[D / 16],
                                     f32x16 (&o)[D / 32], float& m_used, float& l_run, int key0,
                                     int N, float c_log2, int lane) {
   using LY = Lay<D>;
   constexpr int NC = D / 16, NT = D / 32;
   const int g32 = lane >> 5, l32 = lane & 31;
-  const unsigned char* Kt = buf;
-  const unsigned char* Vt = buf + LY::TILE_B;
+  const unsigned char* Kt = smem + CUR * LY::BUF_B;
+  const unsigned char* Vt = Kt + LY::TILE_B;
 
   // S^T = K Q^T: two accumulator chains (key rows 0-31 and 32-63) interleaved,
   // K fragments read two contraction steps ahead of their MFMA
@@ -190,18 +197,16 @@ __device__ __attribute__((always_inline)) inline void compute_tile(const unsigne
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[kt][i] = 0.0f;
   {
-    const unsigned char* rp0 = Kt + l32 * LY::ROW_B;
-    const unsigned char* rp1 = Kt + (32 + l32) * LY::ROW_B;
-    const int sw = LY::kswz(l32);  // equal for rows l32 and 32 + l32
-    auto kfrag = [&](const unsigned char* rp, int c) __attribute__((always_inline)) {
-      return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(rp + (((2 * c + g32) ^ sw) << 4)));
+    // ka[c]: byte offset of row l32's chunk (2c + g32) inside a K tile (row 32 + l32 has the same swizzle)
+    auto kfrag = [&](int half, int c) __attribute__((always_inline)) {
+      return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Kt + ka[c] + half * 32 * LY::ROW_B));
     };
-    bf16x8 a0 = kfrag(rp0, 0), b0 = kfrag(rp1, 0);
-    bf16x8 a1 = kfrag(rp0, 1), b1 = kfrag(rp1, 1);
+    bf16x8 a0 = kfrag(0, 0), b0 = kfrag(1, 0);
+    bf16x8 a1 = kfrag(0, 1), b1 = kfrag(1, 1);
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       bf16x8 a2 = a1, b2 = b1;
-      if (c + 2 < NC) { a2 = kfrag(rp0, c + 2); b2 = kfrag(rp1, c + 2); }
+      if (c + 2 < NC) { a2 = kfrag(0, c + 2); b2 = kfrag(1, c + 2); }
       s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[c], s[0], 0, 0, 0);
       s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, qf[c], s[1], 0, 0, 0);
       a0 = a1; b0 = b1; a1 = a2; b1 = b2;
@@ -264,15 +269,13 @@ __device__ __attribute__((always_inline)) inline void compute_tile(const unsigne
   // fragment carries in slots 4h .. 4h+3.
   // The NT output tiles are independent chains; the V fragments of the next
   // 16-key step are read while the current step's MFMAs run.
-  const int sl = lane & 15, dh = (lane >> 4) & 1;
-  const int inb = (sl & 1) * 8;
+  // va[t]: byte offset, inside a V tile, of this lane's transpose-read address for
+  // output tile t at 16-key step 0, half 0; steps and halves add whole rows
   auto vfrag = [&](int t, int ks) __attribute__((always_inline)) {
-    const int chunk = 4 * t + 2 * dh + ((sl & 3) >> 1);
     uint2 tr[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int row = ks * 16 + 8 * h + 4 * g32 + (sl >> 2);
-      const unsigned char* ad = Vt + row * LY::ROW_B + ((chunk ^ LY::vswz(row)) << 4) + inb;
+      const unsigned char* ad = Vt + va[t] + (ks * 16 + 8 * h) * LY::ROW_B;
       tr[h] = __builtin_bit_cast(
           uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(ad)));
     }
@@ -373,21 +376,44 @@ k_attn_bf16(Geom g, AttnArgs a, int n_items, float c_log2) {
     if (valid) issue_tile<D>(lds0, Kb, Vb, kb * BLK + sub * kTK, g.N, wave_u, lane, doff);
     wait_vmem();
     __syncthreads();
-    int cur = 0;
-    while (valid) {
+    // per-lane LDS read offsets inside a tile, fixed for the whole loop (kept opaque so that
+    // they stay in registers rather than being recomputed at every read)
+    uint32_t ka[NC], va[NT];
+    {
+      const int sw = LY::kswz(l32);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        ka[c] = (uint32_t)(l32 * LY::ROW_B + (((2 * c + g32) ^ sw) << 4));
+        asm volatile("" : "+v"(ka[c]));
+      }
+      const int sl = lane & 15, dh = (lane >> 4) & 1;
+      const int row = 4 * g32 + (sl >> 2);  // + 16 ks + 8 h, which leave the swizzle unchanged
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int chunk = 4 * t + 2 * dh + ((sl & 3) >> 1);
+        va[t] = (uint32_t)(row * LY::ROW_B + ((chunk ^ LY::vswz(row)) << 4) + (sl & 1) * 8);
+        asm volatile("" : "+v"(va[t]));
+      }
+    }
+    // two copies of the step, one per buffer, so that every LDS offset is an immediate
+    auto step = [&](auto cur_c) __attribute__((always_inline)) {
+      constexpr int CUR = decltype(cur_c)::value;
       int nkb, nsub, nflags;
       bool nvalid;
       advance(nkb, nsub, nflags, nvalid);
       if (nvalid)
-        issue_tile<D>(lds0 + (cur ^ 1) * LY::BUF_B, Kb, Vb, nkb * BLK + nsub * kTK, g.N, wave_u, lane,
+        issue_tile<D>(lds0 + (CUR ^ 1) * LY::BUF_B, Kb, Vb, nkb * BLK + nsub * kTK, g.N, wave_u, lane,
                       doff);
       if (wave_rows && ((flags >> qsub) & 1))
-        compute_tile<D>(smem + cur * LY::BUF_B, qf, o, m_used, l_run, kb * BLK + sub * kTK, g.N,
-                        c_log2, lane);
+        compute_tile<D, CUR>(smem, ka, va, qf, o, m_used, l_run, kb * BLK + sub * kTK, g.N, c_log2, lane);
       wait_vmem();  // the next tile has landed in LDS ...
       __syncthreads();  // ... for every wave, and nobody still reads the current one
       kb = nkb; sub = nsub; flags = nflags; valid = nvalid;
-      cur ^= 1;
+    };
+    while (valid) {
+      step(std::integral_constant<int, 0>{});
+      if (!valid) break;
+      step(std::integral_constant<int, 1>{});
     }
   }
 
