@@ -5,15 +5,19 @@
 // (from linear_bwd.hip):  dS = P * (dout V^T - D),  dQ = scale dS K,
 // dK = scale dS^T Q,  dV = P^T dout.  The row statistic (log2-sum-exp of the
 // scaled scores) comes from the forward when it kept it, else it is recomputed
-// here in a first pass.
+// by the dQ kernel in a first pass.
 //
-// Both kernels stream their 64-row tiles HBM -> LDS with global_load_lds_dwordx4,
+// All kernels stream their 64-row tiles HBM -> LDS with global_load_lds_dwordx4,
 // double buffered (the next tile's loads are issued before the current tile's
 // MFMAs).
 //
-// k_attn_bwd_dq: one query block per workgroup, one wave per 32 queries,
-// queries in lanes (the forward's transposed orientation).  Pass 1 over the
-// kept key tiles: S^T = K Q^T and the running max / sum -> log2-sum-exp per
+// k_attn_bwd_dq2 (the forward kept its statistic): the forward kernel's shape,
+// 128 queries per workgroup over the union of two query blocks' kept lists; per
+// tile S^T, P^T, dP^T, dS^T and dQ^T += K^T dS^T as below.
+//
+// k_attn_bwd_dq (statistic recomputed): one query block per workgroup, one wave
+// per 32 queries, queries in lanes (the forward's transposed orientation).
+// Pass 1 over the kept key tiles: S^T = K Q^T and the running max / sum -> log2-sum-exp per
 // query (written for the key-side kernel).  Pass 2: S^T, P^T, dP^T = V dO^T,
 // dS^T, and dQ^T += K^T dS^T with K^T read by LDS transpose reads and dS^T
 // taken straight from the accumulators.  The epilogue adds the linear term
@@ -30,6 +34,7 @@
 // no NaN from padding can reach an MFMA; padded keys and queries are masked by
 // index and their output rows are written as 0.
 #include <cmath>
+#include <type_traits>
 
 #include "bwd_common.h"
 
@@ -55,7 +60,7 @@ struct BwdSmem {
 // [row][channel] bf16 in LDS and store BLK rows to dst (rows >= nvalid as 0).
 template <int D, int BLK>
 __device__ inline void store_rows(unsigned char* smem, const f32x16 (&acc)[D / 32], __bf16* dst, int nvalid,
-                                  int wave, int lane, int tid) {
+                                  int wave, int lane, int tid, int nrows = BLK) {
   using SM = BwdSmem<D, BLK>;
   __bf16* st = reinterpret_cast<__bf16*>(smem);
   const int gg = lane >> 5, m = lane & 31;
@@ -65,14 +70,14 @@ __device__ inline void store_rows(unsigned char* smem, const f32x16 (&acc)[D / 3
 #pragma unroll
     for (int i = 0; i < 16; ++i) st[lr * SM::SST + 32 * t + crow(i, gg)] = (__bf16)(lr < nvalid ? acc[t][i] : 0.0f);
   __syncthreads();
-  for (int i = tid; i < BLK * D / 8; i += BLK * 2) {
+  for (int i = tid; i < nrows * D / 8; i += BLK * 2) {
     const int r = i / (D / 8), p = i % (D / 8);
     *reinterpret_cast<uint4*>(dst + (int64_t)r * D + p * 8) = *reinterpret_cast<const uint4*>(st + r * SM::SST + p * 8);
   }
   __syncthreads();
 }
 
-template <int D, int BLK, bool LSE_IN>
+template <int D, int BLK>
 __global__ void __launch_bounds__(BLK * 2)
 k_attn_bwd_dq(Geom g, BwdArgs a, const float* __restrict__ Dq, const float* __restrict__ dden,
               const __bf16* __restrict__ dU, const __bf16* __restrict__ s_hi, const __bf16* __restrict__ s_lo,
@@ -122,13 +127,10 @@ k_attn_bwd_dq(Geom g, BwdArgs a, const float* __restrict__ Dq, const float* __re
   f32x16 acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) zero(acc[t]);
-  // with the forward's log2-sum-exp at hand, pass 1 is skipped
-  const int i_first = LSE_IN ? T : 0;
-  if (LSE_IN) lse = a.lse[hb + n];
-  if (T > 0) issue(i_first, i_first & 1);
+  if (T > 0) issue(0, 0);
   wait_vmem();
   __syncthreads();
-  for (int i = i_first; i < 2 * T; ++i) {
+  for (int i = 0; i < 2 * T; ++i) {
     const int cur = i & 1;
     if (i + 1 < 2 * T) issue(i + 1, cur ^ 1);
     const unsigned char* Kt = smem + cur * 2 * SM::TB;
@@ -165,7 +167,7 @@ k_attn_bwd_dq(Geom g, BwdArgs a, const float* __restrict__ Dq, const float* __re
         mrun = mnew;
       }
     } else {
-      if (!LSE_IN && i == T) {
+      if (i == T) {
         const float lt = pair_sum(lrun);
         lse = (valid && lt > 0.0f) ? mrun + log2f(lt) : INFINITY;
       }
@@ -213,7 +215,7 @@ k_attn_bwd_dq(Geom g, BwdArgs a, const float* __restrict__ Dq, const float* __re
     wait_vmem();
     __syncthreads();
   }
-  if (!LSE_IN && gg == 0) lse_out[hb + n] = lse;
+  if (gg == 0) lse_out[hb + n] = lse;
 
   // linear term: (S dU^T + z dden^T) * [q > 0], S rows c as hi + lo bf16
   bf16x8 duf[NC];
@@ -252,6 +254,220 @@ k_attn_bwd_dq(Geom g, BwdArgs a, const float* __restrict__ Dq, const float* __re
   __syncthreads();
   store_rows<D, BLK>(smem, acc, static_cast<__bf16*>(a.dq) + (hb + (int64_t)qb * BLK) * D, g.N - qb * BLK, wave,
                      lane, tid);
+}
+
+// dQ with the forward's log2-sum-exp, in the forward kernel's shape: a
+// workgroup of 4 waves owns 128 query rows (two 64-token query blocks, or one
+// 128-token block) and walks the ascending union of their kept lists in
+// 64-key tiles (K and V streamed HBM -> LDS, double buffered); a wave works on
+// a tile only when its own query block keeps it.  The per-lane LDS read
+// offsets are computed once and the loop is unrolled over the two buffers.
+// Two workgroups share a CU.
+template <int D, int BLK>
+__global__ void __launch_bounds__(256, 2)
+k_attn_bwd_dq2(Geom g, BwdArgs a, int n_items, const float* __restrict__ Dq, const float* __restrict__ dden,
+               const __bf16* __restrict__ dU, const __bf16* __restrict__ s_hi, const __bf16* __restrict__ s_lo,
+               const float* __restrict__ z, float c_log2) {
+  using TL = TileLay<D>;
+  constexpr int QPW = 128 / BLK;
+  constexpr int NC = D / 16, NT = D / 32;
+  constexpr int TPB = BLK / kT;
+  constexpr int TB = kT * TL::ROW_B;      // one K or V tile
+  constexpr int BUF = 2 * TB;             // K then V
+  using SM = BwdSmem<D, 128>;
+  constexpr int SMEM = 2 * BUF > SM::STAGE ? 2 * BUF : SM::STAGE;
+  __shared__ __align__(1024) unsigned char smem[SMEM];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, gg = lane >> 5, m = lane & 31;
+  const int per_xcd = (int)(gridDim.x >> 3);
+  const int item = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if (item >= n_items) return;
+  const int qgroups = (g.nb + QPW - 1) / QPW;
+  const int bh = item / qgroups, qg = item - bh * qgroups;
+  const int qb_base = qg * QPW;
+  const int qsub = QPW == 2 ? (wave >> 1) : 0;
+  const bool wave_rows = qb_base + qsub < g.nb;
+  const int n = qb_base * BLK + wave * 32 + m;  // this lane's query (rows past n_pad only when !wave_rows)
+  const bool valid = wave_rows && n < g.N;
+  const int nrow = min(n, g.N - 1);
+  const int64_t hb = (int64_t)bh * g.n_pad;
+  const __bf16* Q = static_cast<const __bf16*>(a.q) + hb * D;
+  const __bf16* K = static_cast<const __bf16*>(a.k) + hb * D;
+  const __bf16* V = static_cast<const __bf16*>(a.v) + hb * D;
+  const __bf16* dO = static_cast<const __bf16*>(a.dout) + hb * D;
+
+  bf16x8 qf[NC], dof[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    qf[c] = ld8(Q + (int64_t)nrow * D + 16 * c + 8 * gg);
+    dof[c] = ld8(dO + (int64_t)nrow * D + 16 * c + 8 * gg);
+  }
+  const float Dn = wave_rows ? Dq[hb + n] : 0.0f;
+  const float lse = valid ? a.lse[hb + n] : INFINITY;
+  f32x16 acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) zero(acc[t]);
+
+  // kept lists of the workgroup's query blocks
+  const int64_t rbase = (int64_t)bh * g.nb + qb_base;
+  int i0 = 0, e0 = 0, i1 = 0, e1 = 0;
+  if (qb_base < g.nb) { i0 = a.row_ptr[rbase]; e0 = a.row_ptr[rbase + 1]; }
+  if (QPW == 2 && qb_base + 1 < g.nb) { i1 = e0; e1 = a.row_ptr[rbase + 2]; }
+  int c0 = i0 < e0 ? a.col_idx[i0] : INT32_MAX;
+  int c1 = i1 < e1 ? a.col_idx[i1] : INT32_MAX;
+  int kb = 0, sub = 0, flags = 0;
+  bool more = false;
+  auto advance = [&](int& nkb, int& nsub, int& nflags, bool& nmore) __attribute__((always_inline)) {
+    if (more && sub + 1 < TPB && kb * BLK + (sub + 1) * kT < g.N) {
+      nkb = kb; nsub = sub + 1; nflags = flags; nmore = true;
+      return;
+    }
+    nkb = min(c0, c1);
+    nmore = nkb != INT32_MAX;
+    nflags = (c0 == nkb ? 1 : 0) | (c1 == nkb ? 2 : 0);
+    nsub = 0;
+    if (c0 == nkb) { ++i0; c0 = i0 < e0 ? a.col_idx[i0] : INT32_MAX; }
+    if (c1 == nkb) { ++i1; c1 = i1 < e1 ? a.col_idx[i1] : INT32_MAX; }
+  };
+  advance(kb, sub, flags, more);
+  const uint32_t lds0 = lds_addr(smem);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  TileDma<D, 4> dma;
+  dma.init(wave_u, lane);
+  auto issue = [&](int key0, int buf) __attribute__((always_inline)) {
+    dma.issue(lds0 + buf * BUF, K, key0, g.N - 1);
+    dma.issue(lds0 + buf * BUF + TB, V, key0, g.N - 1);
+  };
+  if (more) issue(kb * BLK + sub * kT, 0);
+  wait_vmem();
+  __syncthreads();
+
+  // per-lane read offsets inside a tile.  The swizzle only XORs chunk bits, so
+  // one base per read kind covers every chunk: direct reads of row m (and of
+  // row 32 + m, which has the same swizzle) at chunk 2c + gg are od ^ (c << 5);
+  // transposed K reads for output tile tt are otr ^ (tt << 6), and the second
+  // 8-row half adds 8 rows with chunk bit 1 flipped.
+  uint32_t od = (uint32_t)TL::off(m, gg), otr;
+  {
+    const int sl = lane & 15, dh = (lane >> 4) & 1;
+    otr = (uint32_t)(TL::off(4 * gg + (sl >> 2), 2 * dh + ((sl & 3) >> 1)) + (sl & 1) * 8);
+  }
+  asm volatile("" : "+v"(od), "+v"(otr));
+  static_assert(TL::swz(8) == (TL::swz(0) ^ 2) && TL::swz(16) == TL::swz(0), "swizzle period assumed below");
+
+  auto compute = [&](auto cur_c, int key0) __attribute__((always_inline)) {
+    constexpr int CUR = decltype(cur_c)::value;
+    const unsigned char* Kt = smem + CUR * BUF;
+    const unsigned char* Vt = Kt + TB;
+    auto rd = [&](const unsigned char* base, int c, int kt) __attribute__((always_inline)) {
+      return __builtin_bit_cast(bf16x8,
+                                *reinterpret_cast<const uint4*>(base + (od ^ (c << 5)) + kt * 32 * TL::ROW_B));
+    };
+    auto ktr = [&](int tt, int ks) __attribute__((always_inline)) {
+      uint2 tr[2];
+      const uint32_t o0 = otr ^ (tt << 6);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        tr[h] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                              (__attribute__((address_space(3))) s16x4*)(
+                                                  Kt + (h ? (o0 ^ 32) : o0) + (16 * ks + 8 * h) * TL::ROW_B)));
+      return __builtin_bit_cast(bf16x8, make_uint4(tr[0].x, tr[0].y, tr[1].x, tr[1].y));
+    };
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      // S^T and dP^T of 32 keys: two chains, fragments read one contraction step ahead
+      f32x16 s, dp;
+      zero(s);
+      zero(dp);
+      bf16x8 ka = rd(Kt, 0, kt), va = rd(Vt, 0, kt);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        bf16x8 kn = ka, vn = va;
+        if (c + 1 < NC) { kn = rd(Kt, c + 1, kt); vn = rd(Vt, c + 1, kt); }
+        s = mfma(ka, qf[c], s);
+        dp = mfma(va, dof[c], dp);
+        ka = kn; va = vn;
+      }
+      bf16x8 kf = ktr(0, 2 * kt);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int key = key0 + 32 * kt + crow(j, gg);
+        const float p = key < g.N ? __builtin_amdgcn_exp2f(s[j] * c_log2 - lse) : 0.0f;
+        s[j] = p * (dp[j] - Dn);
+      }
+      // dQ^T += K^T dS^T over the 32 keys (two 16-key steps)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const bf16x8 b = c_to_b(s, h2);
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+          bf16x8 kn = kf;
+          if (tt + 1 < NT) kn = ktr(tt + 1, 2 * kt + h2);
+          else if (h2 == 0) kn = ktr(0, 2 * kt + 1);
+          acc[tt] = mfma(kf, b, acc[tt]);
+          kf = kn;
+        }
+      }
+    }
+  };
+  auto step = [&](auto cur_c) __attribute__((always_inline)) {
+    constexpr int CUR = decltype(cur_c)::value;
+    int nkb, nsub, nflags;
+    bool nmore;
+    advance(nkb, nsub, nflags, nmore);
+    if (nmore) issue(nkb * BLK + nsub * kT, CUR ^ 1);
+    if (wave_rows && ((flags >> qsub) & 1)) compute(cur_c, kb * BLK + sub * kT);
+    wait_vmem();
+    __syncthreads();
+    kb = nkb; sub = nsub; flags = nflags; more = nmore;
+  };
+  while (more) {
+    step(std::integral_constant<int, 0>{});
+    if (!more) break;
+    step(std::integral_constant<int, 1>{});
+  }
+
+  // linear term: (S dU^T + z dden^T) * [q > 0], S rows c as hi + lo bf16
+  if (wave_rows) {
+    bf16x8 duf[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) duf[c] = ld8(dU + (hb + n) * D + 16 * c + 8 * gg);
+    const float ddn = dden[hb + n];
+    const __bf16* sh = s_hi + (int64_t)bh * D * D;
+    const __bf16* sl = s_lo + (int64_t)bh * D * D;
+    const float* zh = z + (int64_t)bh * D;
+    const uint64_t qpos = positive_rows<D>(Q + (int64_t)nrow * D, gg);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      f32x16 lt2;
+      zero(lt2);
+      const int64_t ro = (int64_t)(32 * t + m) * D + 8 * gg;
+      bf16x8 ah[NC], al[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        ah[c] = ld8(sh + ro + 16 * c);
+        al[c] = ld8(sl + ro + 16 * c);
+      }
+      float4 zw[4];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) zw[q4] = *reinterpret_cast<const float4*>(zh + 32 * t + 8 * q4 + 4 * gg);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        lt2 = mfma(ah[c], duf[c], lt2);
+        lt2 = mfma(al[c], duf[c], lt2);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float4 w4 = zw[i >> 2];
+        const float zi = (i & 3) == 0 ? w4.x : (i & 3) == 1 ? w4.y : (i & 3) == 2 ? w4.z : w4.w;
+        const float lin = ((qpos >> (16 * t + i)) & 1) ? lt2[i] + zi * ddn : 0.0f;
+        acc[t][i] = a.scale * acc[t][i] + lin;
+      }
+    }
+  }
+  const int row0 = qb_base * BLK;
+  store_rows<D, 128>(smem, acc, static_cast<__bf16*>(a.dq) + (hb + row0) * D, g.N - row0, wave, lane, tid,
+                     min(128, g.n_pad - row0));
 }
 
 template <int D, int BLK>
@@ -436,12 +652,14 @@ hipError_t launch_bwd_t(const Geom& g, const BwdArgs& a, char* ws, const BwdWork
   auto F32 = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
   const float c_log2 = a.scale * 1.4426950408889634f;
   const dim3 grid(g.nb, g.B * g.Hh);
-  if (a.lse != nullptr)
-    hipLaunchKernelGGL((k_attn_bwd_dq<D, BLK, true>), grid, dim3(BLK * 2), 0, st, g, a, F32(L.off_dq),
-                       F32(L.off_dden), B16(L.off_du), B16(L.off_s_hi), B16(L.off_s_lo), F32(L.off_z),
-                       F32(L.off_lse), c_log2);
-  else
-    hipLaunchKernelGGL((k_attn_bwd_dq<D, BLK, false>), grid, dim3(BLK * 2), 0, st, g, a, F32(L.off_dq),
+  if (a.lse != nullptr) {
+    constexpr int QPW = 128 / BLK;
+    const int n_items = g.B * g.Hh * ((g.nb + QPW - 1) / QPW);
+    const int nwg = (n_items + 7) / 8 * 8;  // a multiple of the 8 XCDs
+    hipLaunchKernelGGL((k_attn_bwd_dq2<D, BLK>), dim3(nwg), dim3(256), 0, st, g, a, n_items, F32(L.off_dq),
+                       F32(L.off_dden), B16(L.off_du), B16(L.off_s_hi), B16(L.off_s_lo), F32(L.off_z), c_log2);
+  } else
+    hipLaunchKernelGGL((k_attn_bwd_dq<D, BLK>), grid, dim3(BLK * 2), 0, st, g, a, F32(L.off_dq),
                        F32(L.off_dden), B16(L.off_du), B16(L.off_s_hi), B16(L.off_s_lo), F32(L.off_z),
                        F32(L.off_lse), c_log2);
   const float* lse = a.lse != nullptr ? a.lse : F32(L.off_lse);

@@ -32,8 +32,8 @@ struct TileLay {
   static constexpr int CPR = D / 8;        // 16-byte chunks per row
   static constexpr int ROW_B = D * 2;      // bytes per row
   static constexpr int RPB = 16 / CPR;     // rows per 256-byte bank period
-  __device__ static int swz(int r) { return 4 * ((r / RPB) % (4 / RPB)) + ((r >> 2) & 3); }
-  __device__ static int off(int r, int chunk) { return r * ROW_B + ((chunk ^ swz(r)) << 4); }
+  __host__ __device__ static constexpr int swz(int r) { return 4 * ((r / RPB) % (4 / RPB)) + ((r >> 2) & 3); }
+  __host__ __device__ static constexpr int off(int r, int chunk) { return r * ROW_B + ((chunk ^ swz(r)) << 4); }
 };
 
 __device__ inline f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {

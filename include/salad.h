@@ -284,8 +284,9 @@ SALAD_API size_t salad_bwd_workspace_bytes(const salad_shape* shape);
  *   dgate               device float [batch*heads] (written)
  *   ws                  device workspace of salad_bwd_workspace_bytes(shape)
  * Accumulation is fp32 (bf16 MFMA products), every sum in a fixed order:
- * bitwise reproducible run to run.  The softmax statistics are recomputed, so
- * the forward keeps nothing extra.  fp32 shapes return SALAD_EUNSUPPORTED. */
+ * bitwise reproducible run to run.  Given the forward's lse, dQ runs in one
+ * pass over the kept tiles; without it a first pass recomputes the statistic.
+ * fp32 shapes return SALAD_EUNSUPPORTED. */
 SALAD_API int salad_attn_bwd(const salad_shape* shape, const void* q, const void* k,
                              const void* v, const int32_t* row_ptr, const int32_t* col_idx,
                              const float* gate, const void* w_lin, float eps, float scale,
