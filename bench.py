@@ -47,7 +47,7 @@ ATTN_COUNTERS = {
     "source_sha256": "44aaa23dd6ae582f",
     "fetch_scale": 524288.0 / 262156.8,
     "write_scale": 1.0,
-    "c3": {"fetch_kib": 173021.8, "write_kib": 98304.0},
+    "c3": {"fetch_kib": 172323.0, "write_kib": 98304.0},
 }
 
 

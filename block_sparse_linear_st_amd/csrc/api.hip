@@ -138,9 +138,10 @@ Workspace plan_workspace(const Geom& g, const Cuboid& cu, int dtype) {
   L.off_nbox = off;   off = align_up(off + boxes * 4);
   L.off_boxes = off;  off = align_up(off + boxes * (size_t)cu.box_cap * sizeof(Box));
   L.mask_end = off;
-  // linear state: at most 512 workgroups in all (two resident per CU on the
-  // 256 CUs), so that the split reduction runs in one round; 64-token chunks
-  int splits = (int)std::max<size_t>(1, 512 / BH);
+  // linear state: at most 256 workgroups in all (one resident per CU, each
+  // with a four-tile ring of 128 KiB LDS), so that the split reduction runs in
+  // one round; 64-token chunks
+  int splits = (int)std::max<size_t>(1, 256 / BH);
   splits = std::min(splits, (g.N + 63) / 64);
   int chunk = (g.N + splits - 1) / splits;
   chunk = (chunk + 63) / 64 * 64;

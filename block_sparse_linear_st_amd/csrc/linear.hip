@@ -6,7 +6,9 @@
 //
 //  1. k_lin_partial_*: grid (splits, B*H).  Each workgroup reduces one token
 //     chunk of one head into a D x D fp32 partial.  The bf16 kernel streams
-//     64-token tiles of K and V straight into LDS (double buffered) and runs
+//     64-token tiles of K and V straight into LDS through a ring of four
+//     buffers (three tiles in flight while one is reduced: one workgroup per
+//     CU keeps 96 KiB of loads outstanding against HBM latency) and runs
 //     32x32x16 bf16 MFMAs with the token index as the contraction; both
 //     operands are read with the LDS transpose read, ReLU is applied to the K
 //     fragment in registers.  Products of bf16 values are exact and the sums
@@ -89,8 +91,12 @@ __device__ __attribute__((always_inline)) inline bf16x8 tr_frag(const unsigned c
   return __builtin_bit_cast(bf16x8, make_uint4(tr[0].x, tr[0].y, tr[1].x, tr[1].y));
 }
 
+// vmcnt(n) as an s_waitcnt immediate (gfx9: low 4 bits at [3:0], high 2 at [15:14];
+// expcnt and lgkmcnt left at their maxima)
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
 template <int D>
-__global__ void __launch_bounds__(256, 2)
+__global__ void __launch_bounds__(256, 1)
 k_lin_partial_bf16(Geom g, const __bf16* __restrict__ K, const __bf16* __restrict__ V, int chunk,
                    float* __restrict__ spart, float* __restrict__ zpart, const float* __restrict__ gate,
                    float drop_tau) {
@@ -98,15 +104,16 @@ k_lin_partial_bf16(Geom g, const __bf16* __restrict__ K, const __bf16* __restric
   if (gate != nullptr && gate[blockIdx.y] < drop_tau) return;  // dropped head: no linear state
   constexpr int TD = D / 32;           // 32-wide output tiles per dimension
   constexpr int TPW = TD * TD / 4;     // output tiles per wave
-  __shared__ __align__(1024) unsigned char smem[2 * LY::BUF_B];
+  constexpr int RING = 4;              // tile buffers: three tiles in flight while one is reduced
+  constexpr int PER = 2 * LY::LOADS;   // DMA instructions per thread per tile
+  __shared__ __align__(1024) unsigned char smem[RING * LY::BUF_B];
 
   const int split = blockIdx.x, bh = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n0 = split * chunk, n1 = min(g.N, n0 + chunk);
+  const int T = (n1 - n0 + kTok - 1) / kTok;
   const __bf16* Kb = K + (int64_t)bh * g.n_pad * D;
   const __bf16* Vb = V + (int64_t)bh * g.n_pad * D;
-  // output tiles of this wave: D=128 -> row tile = wave, col tiles 0..3;
-  // D=64 -> row tile wave/2, col tile wave%2
   const int ti = TD == 4 ? wave : wave >> 1;
   const int tj0 = TD == 4 ? 0 : (wave & 1);
 
@@ -119,7 +126,8 @@ k_lin_partial_bf16(Geom g, const __bf16* __restrict__ K, const __bf16* __restric
 
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  auto issue = [&](int t0, int buf) __attribute__((always_inline)) {
+  auto issue = [&](int tt) __attribute__((always_inline)) {
+    const int t0 = n0 + tt * kTok, buf = tt % RING;
 #pragma unroll
     for (int i = 0; i < LY::LOADS; ++i) {
       const int blk1k = wave_u * LY::LOADS + i;
@@ -131,13 +139,17 @@ k_lin_partial_bf16(Geom g, const __bf16* __restrict__ K, const __bf16* __restric
       lds_dma16(Vb + (int64_t)n * D + c, lds0 + buf * LY::BUF_B + LY::TILE_B + blk1k * 1024);
     }
   };
-  issue(n0, 0);
-  wait_vmem();
-  __syncthreads();
-  int cur = 0;
-  for (int t0 = n0; t0 < n1; t0 += kTok) {
-    if (t0 + kTok < n1) issue(t0 + kTok, cur ^ 1);
-    const unsigned char* Kt = smem + cur * LY::BUF_B;
+  for (int tt = 0; tt < RING - 1 && tt < T; ++tt) issue(tt);
+  for (int tt = 0; tt < T; ++tt) {
+    // tile tt has landed once at most min(T - 1 - tt, RING - 2) later tiles are outstanding
+    const int ahead = min(T - 1 - tt, RING - 2);
+    if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * PER));
+    else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER));
+    else wait_vmem();
+    __syncthreads();  // every wave's part of tile tt is in; tile tt - 1's buffer is free
+    if (tt + RING - 1 < T) issue(tt + RING - 1);
+    const int t0 = n0 + tt * kTok;
+    const unsigned char* Kt = smem + (tt % RING) * LY::BUF_B;
     const unsigned char* Vt = Kt + LY::TILE_B;
     const int valid = n1 - t0;  // tokens of this tile inside the chunk
 #pragma unroll
@@ -163,9 +175,6 @@ k_lin_partial_bf16(Geom g, const __bf16* __restrict__ K, const __bf16* __restric
         acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, tr_frag<D>(Vt, ks, tj * 32, lane), acc[t], 0, 0, 0);
       }
     }
-    wait_vmem();
-    __syncthreads();
-    cur ^= 1;
   }
 
   // partial S: lane holds rows (i/4)*8 + (lane/32)*4 + i%4 of tile ti, column lane%32 of tile tj
