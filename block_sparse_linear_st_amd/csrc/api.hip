@@ -463,6 +463,7 @@ int salad_attn_bwd(const salad_shape* shape, const void* q, const void* k, const
   for (const void* p : ptrs)
     if (!p || !aligned16(p)) return SALAD_EINVAL;
   if (!row_ptr || !col_idx || !gate || !dw_lin || !dgate) return SALAD_EINVAL;
+  if (lse && !aligned16(lse)) return SALAD_EINVAL;  // read in 16-byte rows by the dK/dV kernel
   if (!(eps >= 0.0f) || !std::isfinite(scale)) return SALAD_EINVAL;
   Cuboid cu;
   make_cuboid(shape, &cu);

@@ -23,12 +23,13 @@
 // taken straight from the accumulators.  The epilogue adds the linear term
 // (S dU^T + z dden^T) * [q > 0] on MFMAs (S as hi + lo bf16).
 //
-// k_attn_bwd_dkdv: one key block per workgroup, one wave per 32 keys, keys in
-// lanes; K and V fragments stay in registers.  It walks the transposed mask
-// (the query blocks that keep this key block, ascending) in 64-query tiles:
-// S = Q K^T, P, dP = dO V^T, dS, then dV^T += dO^T P and dK^T += Q^T dS with
-// dO^T and Q^T by transpose reads.  The epilogue adds dS_lin^T phi(K)^T to dV
-// and (dS_lin V^T + dz) * [k > 0] to dK.
+// k_attn_bwd_dkdv_pair: one key block per workgroup, keys in lanes, each 32-key
+// group served by a pair of waves.  It walks the transposed mask (the query
+// blocks that keep this key block, ascending) in 64-query tiles: wave A forms
+// S = Q K^T, P and dV^T += dO^T P; wave B forms dP = dO V^T, takes P from A
+// through LDS, and accumulates dK^T += Q^T dS, with dO^T and Q^T by transpose
+// reads.  The linear terms dS_lin^T phi(K)^T (dV) and (dS_lin V^T + dz) * [k > 0]
+// (dK) seed the accumulators.
 //
 // Every tile row past the last valid token is a copy of token N-1 (finite), so
 // no NaN from padding can reach an MFMA; padded keys and queries are masked by
@@ -44,7 +45,7 @@ using namespace bwd;
 
 namespace {
 
-constexpr int kT = 64;  // keys (dq kernel) or queries (dkdv kernel) per LDS tile
+constexpr int kT = 64;  // keys (dQ kernels) or queries (dK/dV kernel) per LDS tile
 
 __device__ inline bf16x8 ld8(const __bf16* p) { return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p)); }
 
@@ -470,19 +471,45 @@ k_attn_bwd_dq2(Geom g, BwdArgs a, int n_items, const float* __restrict__ Dq, con
                      min(128, g.n_pad - row0));
 }
 
+// dK and dV with the work of each 32-key group split over a pair of waves, so
+// that two waves share each SIMD: wave A of pair p forms S = Q K^T and P for
+// keys 32p .. 32p+31 and accumulates dV^T += dO^T P; wave B forms dP = dO V^T
+// and accumulates dK^T += Q^T dS with dS = P (dP - D), P reaching it through
+// LDS in bf16 (the operand form A already built for its own product).  Each
+// wave runs 16 MFMAs per 32-query half, the fused kernel's 32 split in two, and
+// holds only its own 32 keys' K (A) or V (B) fragments and one accumulator set.
+// One key block per workgroup walks its CSC list in 64-query tiles: Q, dO and
+// the tile's lse and D rows stream HBM -> LDS double buffered; two barriers per
+// tile (tile landed, P written).  The linear branch's terms seed the
+// accumulators; the softmax scale is folded into dS.
 template <int D, int BLK>
-__global__ void __launch_bounds__(BLK * 2)
-k_attn_bwd_dkdv(Geom g, BwdArgs a, const int32_t* __restrict__ colptr, const int32_t* __restrict__ rowidx,
-                const float* __restrict__ Dq, const float* __restrict__ lse, const __bf16* __restrict__ ds_hi,
-                const __bf16* __restrict__ ds_lo, const __bf16* __restrict__ dst_hi,
-                const __bf16* __restrict__ dst_lo, const float* __restrict__ dz, float c_log2) {
-  constexpr int NT = D / 32, NC = D / 16, NTH = BLK * 2;
-  using SM = BwdSmem<D, BLK>;
-  __shared__ __align__(16) unsigned char smem[SM::BYTES];
-  __shared__ float lse_s[2][kT], dq_s[2][kT];
-  const int kb = blockIdx.x, bh = blockIdx.y;
+__global__ void __launch_bounds__(BLK * 4, BLK == 64 ? 2 : 1)
+k_attn_bwd_dkdv_pair(Geom g, BwdArgs a, int n_items, const int32_t* __restrict__ colptr,
+                     const int32_t* __restrict__ rowidx, const float* __restrict__ Dq, const float* __restrict__ lse,
+                     const __bf16* __restrict__ ds_hi, const __bf16* __restrict__ ds_lo,
+                     const __bf16* __restrict__ dst_hi, const __bf16* __restrict__ dst_lo,
+                     const float* __restrict__ dz, float c_log2) {
+  using TL = TileLay<D>;
+  constexpr int NP = BLK / 32;            // wave pairs
+  constexpr int NW = 2 * NP, NTH = NW * 64;
+  constexpr int NC = D / 16, NT = D / 32;
+  constexpr int TB = kT * TL::ROW_B;      // one Q or dO tile
+  constexpr int ST = 2 * kT * 4;          // the tile's lse, then D
+  constexpr int PX = NP * 2 * 2048;       // P of every pair and 32-query half, bf16 operand form
+  constexpr int OFF_ST = 4 * TB, OFF_P = OFF_ST + 2 * ST;
+  constexpr int SST = D + 8;              // output staging stride (bf16)
+  constexpr int STAGE = 2 * BLK * SST * 2;
+  constexpr int SMEM = OFF_P + PX > STAGE ? OFF_P + PX : STAGE;
+  __shared__ __align__(1024) unsigned char smem[SMEM];
+
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, gg = lane >> 5, m = lane & 31;
-  const int j = kb * BLK + wave * 32 + m;
+  const int per_xcd = (int)(gridDim.x >> 3);
+  const int item = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if (item >= n_items) return;
+  const int bh = item / g.nb, kb = item - bh * g.nb;
+  const int pair = wave >> 1;
+  const bool role_b = (wave & 1) != 0;  // uniform per wave
+  const int j = kb * BLK + pair * 32 + m;  // this lane's key
   const int jrow = min(j, g.N - 1);
   const int64_t hb = (int64_t)bh * g.n_pad;
   const __bf16* Q = static_cast<const __bf16*>(a.q) + hb * D;
@@ -490,160 +517,165 @@ k_attn_bwd_dkdv(Geom g, BwdArgs a, const int32_t* __restrict__ colptr, const int
   const __bf16* V = static_cast<const __bf16*>(a.v) + hb * D;
   const __bf16* dO = static_cast<const __bf16*>(a.dout) + hb * D;
 
-  bf16x8 kf[NC], vf[NC];
+  // A: K fragments of its keys; B: V fragments
+  bf16x8 kv[NC];
+  {
+    const __bf16* src = (role_b ? V : K) + (int64_t)jrow * D + 8 * gg;
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    kf[c] = ld8(K + (int64_t)jrow * D + 16 * c + 8 * gg);
-    vf[c] = ld8(V + (int64_t)jrow * D + 16 * c + 8 * gg);
+    for (int c = 0; c < NC; ++c) kv[c] = ld8(src + 16 * c);
   }
-  f32x16 dk[NT], dv[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    zero(dk[t]);
-    zero(dv[t]);
-  }
+
   const int64_t col = (int64_t)bh * g.nb + kb;
   const int p0 = colptr[col], p1 = colptr[col + 1];
   constexpr int SUB = BLK / kT;
-  constexpr int NW = BLK / 32;
   const int T = (p1 - p0) * SUB;
   const uint32_t lds0 = lds_addr(smem);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  auto q0_of = [&](int i) __attribute__((always_inline)) { return rowidx[p0 + i / SUB] * BLK + (i % SUB) * kT; };
-  float lse_r = 0.0f, dq_r = 0.0f;  // row statistics of the tile in flight (threads < kT)
   TileDma<D, NW> dma;
   dma.init(wave_u, lane);
+  auto q0_of = [&](int i) __attribute__((always_inline)) { return rowidx[p0 + i / SUB] * BLK + (i % SUB) * kT; };
   auto issue = [&](int i, int buf) __attribute__((always_inline)) {
     const int q0 = q0_of(i);
-    const uint32_t base = lds0 + buf * 2 * SM::TB;
-    dma.issue(base, Q, q0, g.N - 1);
-    dma.issue(base + SM::TB, dO, q0, g.N - 1);
-    if (tid < kT) {
-      lse_r = lse[hb + q0 + tid];
-      dq_r = Dq[hb + q0 + tid];
-    }
+    dma.issue(lds0 + buf * 2 * TB, Q, q0, g.N - 1);
+    dma.issue(lds0 + buf * 2 * TB + TB, dO, q0, g.N - 1);
+    // lanes 0-15 of wave 0 bring the 64 lse values, lanes 16-31 the 64 D values
+    if (wave_u == 0 && lane < 32)
+      lds_dma16(lane < 16 ? lse + hb + q0 + 4 * lane : Dq + hb + q0 + 4 * (lane - 16), lds0 + OFF_ST + buf * ST);
   };
-  if (T > 0) {
-    issue(0, 0);
-    if (tid < kT) {
-      lse_s[0][tid] = lse_r;
-      dq_s[0][tid] = dq_r;
+  if (T > 0) issue(0, 0);
+
+  // linear terms first: A: dV^T = dS_lin^T phi(K)^T; B: dK^T = (dS_lin V^T + dz) [k > 0]
+  f32x16 acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) zero(acc[t]);
+  {
+    const int64_t mb = (int64_t)bh * D * D;
+    const __bf16* mh = (role_b ? ds_hi : dst_hi) + mb;
+    const __bf16* ml = (role_b ? ds_lo : dst_lo) + mb;
+    bf16x8 bop[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) bop[c] = role_b ? kv[c] : relu8(kv[c]);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int64_t ro = (int64_t)(32 * t + m) * D + 8 * gg;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        acc[t] = mfma(ld8(mh + ro + 16 * c), bop[c], acc[t]);
+        acc[t] = mfma(ld8(ml + ro + 16 * c), bop[c], acc[t]);
+      }
+    }
+    if (role_b) {
+      const uint64_t kpos = positive_rows<D>(K + (int64_t)jrow * D, gg);
+      const float* dzh = dz + (int64_t)bh * D;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        float4 zw[4];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) zw[q4] = *reinterpret_cast<const float4*>(dzh + 32 * t + 8 * q4 + 4 * gg);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float4 w4 = zw[i >> 2];
+          const float zi = (i & 3) == 0 ? w4.x : (i & 3) == 1 ? w4.y : (i & 3) == 2 ? w4.z : w4.w;
+          acc[t][i] = ((kpos >> (16 * t + i)) & 1) ? acc[t][i] + zi : 0.0f;
+        }
+      }
     }
   }
   wait_vmem();
   __syncthreads();
+
+  const float neg_inv_c = -1.0f / c_log2;
+  const float sc = a.scale;
+  unsigned char* pslot = smem + OFF_P + pair * 2 * 2048;
   for (int i = 0; i < T; ++i) {
     const int cur = i & 1;
     if (i + 1 < T) issue(i + 1, cur ^ 1);
-    const unsigned char* Qt = smem + cur * 2 * SM::TB;
-    const unsigned char* Ot = Qt + SM::TB;
+    const unsigned char* Qt = smem + cur * 2 * TB;
+    const unsigned char* Ot = Qt + TB;
+    const float* stat = reinterpret_cast<const float*>(smem + OFF_ST + cur * ST);
+    bf16x8 pb[2][2];
+    f32x16 dp[2];
+    if (!role_b) {
+      // A: S (from -lse / c), P = exp2(c S), P to LDS in operand form
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
-      // every LDS fragment of a phase is read before its MFMAs
-      bf16x8 qa[NC], oa[NC];
+      for (int qs = 0; qs < 2; ++qs) {
+        f32x16 s;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        qa[c] = frag_direct<D>(Qt, 32 * qs, c, lane);
-        oa[c] = frag_direct<D>(Ot, 32 * qs, c, lane);
-      }
-      f32x16 s, dp;
-      zero(s);
-      zero(dp);
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        s = mfma(qa[c], kf[c], s);
-        dp = mfma(oa[c], vf[c], dp);
-      }
-      SG_DSREAD(2 * NC);
-      SG_MFMA(2 * NC);
-      bf16x8 ot_f[2][NT], qt_f[2][NT];
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
-          ot_f[h2][tt] = frag_tr<D>(Ot, 2 * qs + h2, tt, lane);
-          qt_f[h2][tt] = frag_tr<D>(Qt, 2 * qs + h2, tt, lane);
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 l4 = *reinterpret_cast<const float4*>(stat + 32 * qs + 8 * q4 + 4 * gg);
+          s[4 * q4 + 0] = l4.x * neg_inv_c; s[4 * q4 + 1] = l4.y * neg_inv_c;
+          s[4 * q4 + 2] = l4.z * neg_inv_c; s[4 * q4 + 3] = l4.w * neg_inv_c;
         }
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int qi = 32 * qs + crow(j, gg);
-        const float p = __builtin_amdgcn_exp2f(s[j] * c_log2 - lse_s[cur][qi]);  // 0 for padded queries (lse = inf)
-        s[j] = p;
-        dp[j] = p * (dp[j] - dq_s[cur][qi]);
+        for (int c = 0; c < NC; ++c) s = mfma(frag_direct<D>(Qt, 32 * qs, c, lane), kv[c], s);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[e] = __builtin_amdgcn_exp2f(s[e] * c_log2);  // 0 for padded queries
+        pb[qs][0] = c_to_b(s, 0);
+        pb[qs][1] = c_to_b(s, 1);
+        *reinterpret_cast<uint4*>(pslot + qs * 2048 + lane * 16) = __builtin_bit_cast(uint4, pb[qs][0]);
+        *reinterpret_cast<uint4*>(pslot + qs * 2048 + 1024 + lane * 16) = __builtin_bit_cast(uint4, pb[qs][1]);
       }
+    } else {
+      // B: dP - D
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const bf16x8 bp = c_to_b(s, h2);
-        const bf16x8 bd = c_to_b(dp, h2);
+      for (int qs = 0; qs < 2; ++qs) {
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
-          dv[tt] = mfma(ot_f[h2][tt], bp, dv[tt]);
-          dk[tt] = mfma(qt_f[h2][tt], bd, dk[tt]);
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 d4 = *reinterpret_cast<const float4*>(stat + kT + 32 * qs + 8 * q4 + 4 * gg);
+          dp[qs][4 * q4 + 0] = -d4.x; dp[qs][4 * q4 + 1] = -d4.y;
+          dp[qs][4 * q4 + 2] = -d4.z; dp[qs][4 * q4 + 3] = -d4.w;
         }
+#pragma unroll
+        for (int c = 0; c < NC; ++c) dp[qs] = mfma(frag_direct<D>(Ot, 32 * qs, c, lane), kv[c], dp[qs]);
       }
-      SG_DSREAD(8 * NT);
-      SG_MFMA(4 * NT);
     }
-    if (i + 1 < T && tid < kT) {
-      lse_s[cur ^ 1][tid] = lse_r;
-      dq_s[cur ^ 1][tid] = dq_r;
+    __syncthreads();  // P of this tile is in LDS
+    if (!role_b) {
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int tt = 0; tt < NT; ++tt) acc[tt] = mfma(frag_tr<D>(Ot, 2 * qs + h2, tt, lane), pb[qs][h2], acc[tt]);
+    } else {
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) {
+        f32x16 ds;
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const bf16x8 pp = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(pslot + qs * 2048 + h2 * 1024 + lane * 16));
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ds[8 * h2 + e] = (float)pp[e] * sc * dp[qs][8 * h2 + e];
+        }
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const bf16x8 bd = c_to_b(ds, h2);
+#pragma unroll
+          for (int tt = 0; tt < NT; ++tt) acc[tt] = mfma(frag_tr<D>(Qt, 2 * qs + h2, tt, lane), bd, acc[tt]);
+        }
+      }
     }
     wait_vmem();
-    __syncthreads();
+    __syncthreads();  // next tile landed; this tile's buffers and P slots are free
   }
 
-  // linear terms: dv += dS_lin^T phi(K)^T; dk += (dS_lin V^T + dz) * [k > 0]
-  const int64_t mb = (int64_t)bh * D * D;
-  float dzr[NT][16];
-  rows_f32<D>(dz + (int64_t)bh * D, gg, dzr);
-  const uint64_t kpos = positive_rows<D>(K + (int64_t)jrow * D, gg);
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    f32x16 lv, lk;
-    zero(lv);
-    zero(lk);
-    const int64_t ro = (int64_t)(32 * t + m) * D + 8 * gg;
-    {
-      bf16x8 a0[NC], a1[NC];
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        a0[c] = ld8(dst_hi + mb + ro + 16 * c);
-        a1[c] = ld8(dst_lo + mb + ro + 16 * c);
-      }
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const bf16x8 pk = relu8(kf[c]);
-        lv = mfma(a0[c], pk, lv);
-        lv = mfma(a1[c], pk, lv);
-      }
-      SG_VMREAD(2 * NC);
-      SG_MFMA(2 * NC);
-    }
-    {
-      bf16x8 a2[NC], a3[NC];
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        a2[c] = ld8(ds_hi + mb + ro + 16 * c);
-        a3[c] = ld8(ds_lo + mb + ro + 16 * c);
-      }
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        lk = mfma(a2[c], vf[c], lk);
-        lk = mfma(a3[c], vf[c], lk);
-      }
-      SG_VMREAD(2 * NC);
-      SG_MFMA(2 * NC);
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      dv[t][i] += lv[i];
-      dk[t][i] = a.scale * dk[t][i] + (((kpos >> (16 * t + i)) & 1) ? lk[i] + dzr[t][i] : 0.0f);
-    }
-  }
+  // stage dK rows [0, BLK) and dV rows [BLK, 2 BLK) as bf16, then coalesced stores
+  __bf16* st = reinterpret_cast<__bf16*>(smem);
   const int nvalid = g.N - kb * BLK;
+  const int lr = (role_b ? 0 : BLK) + pair * 32 + m;
+  const bool ok = pair * 32 + m < nvalid;
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) st[lr * SST + 32 * t + crow(e, gg)] = (__bf16)(ok ? acc[t][e] : 0.0f);
   __syncthreads();
-  store_rows<D, BLK>(smem, dk, static_cast<__bf16*>(a.dk) + (hb + (int64_t)kb * BLK) * D, nvalid, wave, lane, tid);
-  store_rows<D, BLK>(smem, dv, static_cast<__bf16*>(a.dv) + (hb + (int64_t)kb * BLK) * D, nvalid, wave, lane, tid);
+  __bf16* dkd = static_cast<__bf16*>(a.dk) + (hb + (int64_t)kb * BLK) * D;
+  __bf16* dvd = static_cast<__bf16*>(a.dv) + (hb + (int64_t)kb * BLK) * D;
+  for (int e = tid; e < 2 * BLK * D / 8; e += NTH) {
+    const int r = e / (D / 8), c8 = e % (D / 8);
+    __bf16* dst = r < BLK ? dkd + (int64_t)r * D : dvd + (int64_t)(r - BLK) * D;
+    *reinterpret_cast<uint4*>(dst + c8 * 8) = *reinterpret_cast<const uint4*>(st + r * SST + c8 * 8);
+  }
 }
 
 template <int D, int BLK>
@@ -663,8 +695,9 @@ hipError_t launch_bwd_t(const Geom& g, const BwdArgs& a, char* ws, const BwdWork
                        F32(L.off_dden), B16(L.off_du), B16(L.off_s_hi), B16(L.off_s_lo), F32(L.off_z),
                        F32(L.off_lse), c_log2);
   const float* lse = a.lse != nullptr ? a.lse : F32(L.off_lse);
-  hipLaunchKernelGGL((k_attn_bwd_dkdv<D, BLK>), grid, dim3(BLK * 2), 0, st, g, a,
-                     reinterpret_cast<const int32_t*>(ws + L.off_colptr),
+  const int k_items = g.B * g.Hh * g.nb;
+  hipLaunchKernelGGL((k_attn_bwd_dkdv_pair<D, BLK>), dim3((k_items + 7) / 8 * 8), dim3(BLK * 4), 0, st, g, a,
+                     k_items, reinterpret_cast<const int32_t*>(ws + L.off_colptr),
                      reinterpret_cast<const int32_t*>(ws + L.off_rowidx), F32(L.off_dq), lse,
                      B16(L.off_ds_hi), B16(L.off_ds_lo), B16(L.off_dst_hi), B16(L.off_dst_lo), F32(L.off_dz),
                      c_log2);

@@ -272,9 +272,9 @@ SALAD_API size_t salad_bwd_workspace_bytes(const salad_shape* shape);
  *   q, k, v, out, dout  device bf16 [batch, heads, n_pad, head_dim]: the
  *                       forward's inputs, its output, and dL/dout (rows from N
  *                       on are not read)
- *   lse                 the forward's lse output, or NULL: then the kernel
- *                       recomputes it (one more pass of Q K^T over the kept
- *                       blocks)
+ *   lse                 the forward's lse output (16-byte aligned), or NULL:
+ *                       then the kernel recomputes it (one more pass of Q K^T
+ *                       over the kept blocks)
  *   row_ptr, col_idx    the CSR mask the forward used
  *   gate                device float [batch*heads]; w_lin device bf16
  *                       [head_dim, head_dim]; eps, scale as in salad_attn_fwd

@@ -215,6 +215,7 @@ def test_backward_rejects_bad_arguments_before_launch():
     assert call(dout=None) == S.SALAD_EINVAL
     assert call(dgate=None) == S.SALAD_EINVAL
     assert call(dq=ctypes.c_void_p(0x100004)) == S.SALAD_EINVAL
+    assert call(lse=ctypes.c_void_p(0x100004)) == S.SALAD_EINVAL  # forward statistic not 16-byte aligned
     assert call(eps=-1.0) == S.SALAD_EINVAL
     assert call(scale=float("inf")) == S.SALAD_EINVAL
     assert call(ws_bytes=ws_bytes - 1) == S.SALAD_ENOSPACE

@@ -3,9 +3,9 @@
 The oracle differentiates the fp64 forward on the exact bf16 input values
 (``oracle.layer_backward``).  The kernels round P and dS to bf16 before their
 products (as the forward rounds P) and store dq, dk, dv in bf16; each rounding
-is a relative 2^-9, three of them stack on a typical element, so the bars are
-rel-L2 <= 1.5e-2 and max-abs <= 3e-2 * max|ref| per tensor (about 2.5x the
-expected error).  dW_lin and dgate are fp32 sums of bf16-rounded o_l and dU:
+is a relative 2^-9, three of them stack on a typical element (four on dK, whose
+dS is formed from the bf16-rounded P), so the bars are rel-L2 <= 1.5e-2 and
+max-abs <= 3e-2 * max|ref| per tensor (about 2.5x the expected error).  dW_lin and dgate are fp32 sums of bf16-rounded o_l and dU:
 rel-L2 <= 1e-2.  Padding rows of dq, dk, dv must be exactly 0, and two runs
 must agree bit for bit.  Both paths are checked: the softmax statistic kept by
 the forward (its log2-sum-exp output, itself checked against the oracle's
