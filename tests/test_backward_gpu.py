@@ -137,6 +137,22 @@ def test_backward_b128_ragged():
     _compare_all(cfg, res, ref, lse, (inp.q, inp.k), rp, ci, "b128")
 
 
+D64B128 = LayerConfig(
+    name="d64b128", seed=22, batch=1, heads=3, head_dim=64, T=3, H=9, W=15, block=128, dtype="bf16",
+    specs=(HeadSpec(0, 1, -1, 0.4), HeadSpec(1, 0, -1, 0.5), HeadSpec(0, 2, -1, 0.0)), gate_kind="uniform",
+    description="ragged 128-token blocks at d=64 (3 blocks per head, the last one partial): window and top-k heads")
+
+
+def test_backward_d64_b128_ragged():
+    print("backward d64b128", flush=True)
+    cfg = D64B128
+    inp = make_inputs(cfg)
+    layer, gate, res, dvals, lse, _ = _run(cfg, inp)
+    ref, rp, ci = _oracle(cfg, inp, gate, dvals)
+    np.testing.assert_array_equal(layer.row_ptr.cpu().numpy(), rp)
+    _compare_all(cfg, res, ref, lse, (inp.q, inp.k), rp, ci, "d64b128")
+
+
 def test_backward_c9_cuboid_mixed_masks():
     """Ragged 5x10x14 layer in cuboid order with window, top-k and SICS heads and a gate from Q."""
     print("backward c9", flush=True)
