@@ -16,9 +16,9 @@
 //   dS     = sum_n phi(q_n) dU_n^T          dz = sum_n phi(q_n) dden_n
 //   dk_lin = (dS v_j + dz) * [k_j > 0]      dv_lin = dS^T phi(k_j)
 //
-// Kernels: k_lin_bwd_tok (one 64-token tile per workgroup, tokens in lanes:
-// u^T = S^T phi(q)^T and t^T = W dout^T on MFMAs, S carried as hi + lo bf16)
-// writes D, dden, dU, o_l and per-wave dgate sums; k_lin_bwd_red reduces
+// Kernels: k_lin_bwd_rows (chunks of a head's rows per workgroup, tokens in
+// lanes: u^T = S^T phi(q)^T and t^T = W dout^T on MFMAs with S^T (hi + lo bf16)
+// and W in LDS) writes D, dden, dU, o_l and per-32-row dgate sums; k_lin_bwd_red reduces
 // dS, dz and the per-head dW over token chunks with the token index as the MFMA
 // contraction (both operands by LDS transpose reads); the folds sum the chunks
 // in a fixed order (bitwise reproducible) and lay dS out as hi + lo bf16 in
@@ -34,115 +34,166 @@ using namespace bwd;
 
 namespace {
 
-constexpr int kTT = 64;  // tokens per tile
+constexpr int kTT = 64;  // tokens per tile of the reduction kernel
 
 __device__ inline bf16x8 ld8(const __bf16* p) { return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p)); }
 
+// Per-token quantities of the linear branch's backward, tokens in lanes:
+// u^T = S^T phi(q)^T (S^T as hi + lo bf16) and t^T = W_lin dO^T on MFMAs, then
+// den, o_l = u / den, r = <t, o_l>, D = <dO, out> - g r, dden = -g r / den and
+// dU = g t / den, with per-32-row dgate sums.  The head's S^T (hi, lo) and
+// W_lin sit in LDS: one workgroup per CU walks a contiguous chunk of a head's
+// rows, 128 rows (four waves of 32) per iteration, and reads the three D x D
+// operands from LDS.  The next iteration's Q, dO and out rows are loaded into
+// registers while the current ones are reduced.  Rows from N to n_pad get
+// zeros (D, dden, dU, o_l).
 template <int D>
-__global__ void __launch_bounds__(128)
-k_lin_bwd_tok(Geom g, const __bf16* __restrict__ Q, const __bf16* __restrict__ dO, const __bf16* __restrict__ Out,
-              const __bf16* __restrict__ st_hi, const __bf16* __restrict__ st_lo, const float* __restrict__ z,
-              const __bf16* __restrict__ W, const float* __restrict__ gate, float eps, float* __restrict__ Dq,
-              float* __restrict__ dden, __bf16* __restrict__ dU, __bf16* __restrict__ OL, float* __restrict__ gpart) {
+__global__ void __launch_bounds__(256, 1)
+k_lin_bwd_rows(Geom g, int chunk, const __bf16* __restrict__ Q, const __bf16* __restrict__ dO,
+               const __bf16* __restrict__ Out, const __bf16* __restrict__ st_hi, const __bf16* __restrict__ st_lo,
+               const float* __restrict__ z, const __bf16* __restrict__ W, const float* __restrict__ gate, float eps,
+               float* __restrict__ Dq, float* __restrict__ dden, __bf16* __restrict__ dU, __bf16* __restrict__ OL,
+               float* __restrict__ gpart) {
+  using TL = TileLay<D>;
   constexpr int NC = D / 16, NT = D / 32, SST = D + 8;
-  __shared__ __align__(16) __bf16 stage[kTT * SST];
-  const int bh = blockIdx.y, tile = blockIdx.x;
+  constexpr int MB = D * TL::ROW_B;          // one D x D operand
+  constexpr int ROWS = 128;                  // rows per iteration
+  __shared__ __align__(1024) unsigned char smem[3 * MB + ROWS * SST * 2];
+  __bf16* stage = reinterpret_cast<__bf16*>(smem + 3 * MB);
+  const int split = blockIdx.x, bh = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, gg = lane >> 5, m = lane & 31;
-  const int n = tile * kTT + wave * 32 + m;
-  const bool valid = n < g.N;
-  const int64_t row = ((int64_t)bh * g.n_pad + n) * D;
-  const float* zb = z + (int64_t)bh * D;
-
-  bf16x8 qf[NC], dof[NC], of[NC];
-  float4 zf[NC][2];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const int ch = 16 * c + 8 * gg;
-    qf[c] = relu8(ld8(Q + row + ch));
-    dof[c] = ld8(dO + row + ch);
-    of[c] = ld8(Out + row + ch);
-    zf[c][0] = *reinterpret_cast<const float4*>(zb + ch);
-    zf[c][1] = *reinterpret_cast<const float4*>(zb + ch + 4);
-  }
-  SG_VMREAD(5 * NC);
-  float den_p = 0.0f, dot_p = 0.0f;
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const float zz[8] = {zf[c][0].x, zf[c][0].y, zf[c][0].z, zf[c][0].w,
-                         zf[c][1].x, zf[c][1].y, zf[c][1].z, zf[c][1].w};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      den_p += (float)qf[c][j] * zz[j];
-      dot_p += (float)dof[c][j] * (float)of[c][j];
-    }
-  }
-  const float den = pair_sum(den_p) + eps;
-  const float dot_out = pair_sum(dot_p);
-  const float inv = 1.0f / den;
-
-  f32x16 u[NT], tt[NT];
-  const __bf16* sth = st_hi + (int64_t)bh * D * D;
-  const __bf16* stl = st_lo + (int64_t)bh * D * D;
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    zero(u[t]);
-    zero(tt[t]);
-    const int64_t ro = (int64_t)(32 * t + m) * D + 8 * gg;
-    // all operand fragments of this row tile are requested before its MFMAs
-    bf16x8 ah[NC], al[NC], aw[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      ah[c] = ld8(sth + ro + 16 * c);
-      al[c] = ld8(stl + ro + 16 * c);
-      aw[c] = ld8(W + ro + 16 * c);
-    }
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      u[t] = mfma(ah[c], qf[c], u[t]);
-      u[t] = mfma(al[c], qf[c], u[t]);
-      tt[t] = mfma(aw[c], dof[c], tt[t]);
-    }
-    SG_VMREAD(3 * NC);
-    SG_MFMA(3 * NC);
-  }
-  float r = 0.0f;
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      u[t][i] *= inv;  // o_l^T
-      r += tt[t][i] * u[t][i];
-    }
-  r = pair_sum(r);
+  const int n0 = split * chunk, n1 = min(g.n_pad, n0 + chunk);
+  const int64_t hb = (int64_t)bh * g.n_pad;
   const float gv = gate[bh];
-  if (gg == 0) {
-    Dq[(int64_t)bh * g.n_pad + n] = valid ? dot_out - gv * r : 0.0f;
-    dden[(int64_t)bh * g.n_pad + n] = valid ? -gv * r * inv : 0.0f;
-  }
-  float rv = (valid && gg == 0) ? r : 0.0f;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) rv += __shfl_xor(rv, o, 64);
-  if (lane == 0) gpart[(int64_t)bh * (g.n_pad / 32) + tile * 2 + wave] = rv;
 
-  // dU = g t / den and o_l, staged through LDS as [token][channel] for coalesced stores
-  const int lr = wave * 32 + m;
-  const float su = valid ? gv * inv : 0.0f;
-  for (int pass = 0; pass < 2; ++pass) {
+  // S^T hi, S^T lo and W into LDS, 64 rows per DMA tile, swizzled like the K tiles
+  {
+    TileDma<D, 4> dma;
+    dma.init(__builtin_amdgcn_readfirstlane(wave), lane);
+    const uint32_t lds0 = lds_addr(smem);
+    const __bf16* src[3] = {st_hi + (int64_t)bh * D * D, st_lo + (int64_t)bh * D * D, W};
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+    for (int mtx = 0; mtx < 3; ++mtx)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float x = pass == 0 ? tt[t][i] * su : (valid ? u[t][i] : 0.0f);
-        stage[lr * SST + 32 * t + crow(i, gg)] = (__bf16)x;
-      }
-    __syncthreads();
-    __bf16* dst = (pass == 0 ? dU : OL) + ((int64_t)bh * g.n_pad + tile * kTT) * D;
-    for (int i = tid; i < kTT * D / 8; i += 128) {
-      const int rr = i / (D / 8), p = i % (D / 8);
-      *reinterpret_cast<uint4*>(dst + (int64_t)rr * D + p * 8) =
-          *reinterpret_cast<const uint4*>(stage + rr * SST + p * 8);
+      for (int r0 = 0; r0 < D; r0 += 64) dma.issue(lds0 + mtx * MB + r0 * TL::ROW_B, src[mtx], r0, D - 1);
+  }
+  float4 zf[NC][2];
+  {
+    const float* zb = z + (int64_t)bh * D;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      zf[c][0] = *reinterpret_cast<const float4*>(zb + 16 * c + 8 * gg);
+      zf[c][1] = *reinterpret_cast<const float4*>(zb + 16 * c + 8 * gg + 4);
     }
-    __syncthreads();
+  }
+  // this lane's row of an iteration starting at row i0 (clamped into the padded range)
+  bf16x8 qf[NC], dof[NC], of[NC];
+  auto load_rows = [&](int i0, bf16x8 (&q)[NC], bf16x8 (&d)[NC], bf16x8 (&o)[NC]) __attribute__((always_inline)) {
+    const int n = min(i0 + wave * 32 + m, g.n_pad - 1);
+    const int64_t row = (hb + n) * D;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int ch = 16 * c + 8 * gg;
+      q[c] = ld8(Q + row + ch);
+      d[c] = ld8(dO + row + ch);
+      o[c] = ld8(Out + row + ch);
+    }
+  };
+  if (n0 < n1) load_rows(n0, qf, dof, of);
+  wait_vmem();
+  __syncthreads();
+
+  for (int i0 = n0; i0 < n1; i0 += ROWS) {
+    bf16x8 nq[NC], nd[NC], no[NC];
+    if (i0 + ROWS < n1) load_rows(i0 + ROWS, nq, nd, no);
+    const int n = i0 + wave * 32 + m;
+    const bool active = i0 + wave * 32 < n1;  // uniform per wave
+    const bool valid = active && n < g.N;
+    float su = 0.0f;
+    f32x16 u[NT], tt[NT];
+    if (active) {
+      float den_p = 0.0f, dot_p = 0.0f;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const bf16x8 rq = relu8(qf[c]);
+        qf[c] = rq;
+        const float zz[8] = {zf[c][0].x, zf[c][0].y, zf[c][0].z, zf[c][0].w,
+                             zf[c][1].x, zf[c][1].y, zf[c][1].z, zf[c][1].w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          den_p += (float)rq[j] * zz[j];
+          dot_p += (float)dof[c][j] * (float)of[c][j];
+        }
+      }
+      const float den = pair_sum(den_p) + eps;
+      const float dot_out = pair_sum(dot_p);
+      const float inv = 1.0f / den;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        zero(u[t]);
+        zero(tt[t]);
+        const int r = 32 * t + m;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const int o = TL::off(r, 2 * c + gg);
+          const bf16x8 ah = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(smem + o));
+          const bf16x8 al = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(smem + MB + o));
+          const bf16x8 aw = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(smem + 2 * MB + o));
+          u[t] = mfma(ah, qf[c], u[t]);
+          u[t] = mfma(al, qf[c], u[t]);
+          tt[t] = mfma(aw, dof[c], tt[t]);
+        }
+      }
+      float r = 0.0f;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          u[t][e] *= inv;  // o_l^T
+          r += tt[t][e] * u[t][e];
+        }
+      r = pair_sum(r);
+      if (gg == 0) {
+        Dq[hb + n] = valid ? dot_out - gv * r : 0.0f;
+        dden[hb + n] = valid ? -gv * r * inv : 0.0f;
+      }
+      float rv = (valid && gg == 0) ? r : 0.0f;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) rv += __shfl_xor(rv, o, 64);
+      if (lane == 0) gpart[(int64_t)bh * (g.n_pad / 32) + (i0 + wave * 32) / 32] = rv;
+      su = valid ? gv * inv : 0.0f;
+    }
+    // dU = g t / den and o_l, staged through LDS as [row][channel] for coalesced stores
+    const int lr = wave * 32 + m;
+    const int nrows = min(ROWS, n1 - i0);
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      if (active) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const float x = pass == 0 ? tt[t][e] * su : (valid ? u[t][e] : 0.0f);
+            stage[lr * SST + 32 * t + crow(e, gg)] = (__bf16)x;
+          }
+      }
+      __syncthreads();
+      __bf16* dst = (pass == 0 ? dU : OL) + (hb + i0) * D;
+      for (int e = tid; e < nrows * D / 8; e += 256) {
+        const int rr = e / (D / 8), p = e % (D / 8);
+        *reinterpret_cast<uint4*>(dst + (int64_t)rr * D + p * 8) =
+            *reinterpret_cast<const uint4*>(stage + rr * SST + p * 8);
+      }
+      __syncthreads();
+    }
+    if (i0 + ROWS < n1) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        qf[c] = nq[c];
+        dof[c] = nd[c];
+        of[c] = no[c];
+      }
+    }
   }
 }
 
@@ -457,13 +508,19 @@ hipError_t launch_linear_bwd(const Geom& g, const BwdArgs& a, char* ws, const Bw
   const __bf16* Out = static_cast<const __bf16*>(a.out);
   const __bf16* W = static_cast<const __bf16*>(a.w_lin);
   const int64_t tot = BH * g.D * g.D;
-  const dim3 tg(g.n_pad / kTT, (unsigned)BH);
+  // row kernel: one workgroup per CU (S^T hi, lo and W_lin in 96 KiB of LDS), chunks of 64-row multiples
+  int row_splits = (int)std::max<int64_t>(1, 256 / BH);
+  row_splits = std::min(row_splits, g.n_pad / 64);
+  int row_chunk = (g.n_pad + row_splits - 1) / row_splits;
+  row_chunk = (row_chunk + 63) / 64 * 64;
+  row_splits = (g.n_pad + row_chunk - 1) / row_chunk;
+  const dim3 tg(row_splits, (unsigned)BH);
   const dim3 rg(L.red_splits, (unsigned)BH);
   const dim3 fg(g.D * g.D / 256, (unsigned)BH);
   if (g.D == 128) {
     hipLaunchKernelGGL(k_split_state<128>, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, tot,
                        F32(L.off_s32), B16(L.off_s_hi), B16(L.off_s_lo), B16(L.off_st_hi), B16(L.off_st_lo));
-    hipLaunchKernelGGL(k_lin_bwd_tok<128>, tg, dim3(128), 0, st, g, Q, dO, Out, B16(L.off_st_hi),
+    hipLaunchKernelGGL(k_lin_bwd_rows<128>, tg, dim3(256), 0, st, g, row_chunk, Q, dO, Out, B16(L.off_st_hi),
                        B16(L.off_st_lo), F32(L.off_z), W, a.gate, a.eps, F32(L.off_dq), F32(L.off_dden),
                        B16(L.off_du), B16(L.off_ol), F32(L.off_gpart));
     hipLaunchKernelGGL(k_lin_bwd_red<128>, rg, dim3(256), 0, st, g, L.red_chunk, Q, B16(L.off_du),
@@ -478,7 +535,7 @@ hipError_t launch_linear_bwd(const Geom& g, const BwdArgs& a, char* ws, const Bw
   } else if (g.D == 64) {
     hipLaunchKernelGGL(k_split_state<64>, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, tot,
                        F32(L.off_s32), B16(L.off_s_hi), B16(L.off_s_lo), B16(L.off_st_hi), B16(L.off_st_lo));
-    hipLaunchKernelGGL(k_lin_bwd_tok<64>, tg, dim3(128), 0, st, g, Q, dO, Out, B16(L.off_st_hi),
+    hipLaunchKernelGGL(k_lin_bwd_rows<64>, tg, dim3(256), 0, st, g, row_chunk, Q, dO, Out, B16(L.off_st_hi),
                        B16(L.off_st_lo), F32(L.off_z), W, a.gate, a.eps, F32(L.off_dq), F32(L.off_dden),
                        B16(L.off_du), B16(L.off_ol), F32(L.off_gpart));
     hipLaunchKernelGGL(k_lin_bwd_red<64>, rg, dim3(256), 0, st, g, L.red_chunk, Q, B16(L.off_du),
