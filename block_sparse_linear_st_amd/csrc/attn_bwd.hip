@@ -354,7 +354,7 @@ k_attn_bwd_dq2(Geom g, BwdArgs a, int n_items, const float* __restrict__ Dq, con
     otr = (uint32_t)(TL::off(4 * gg + (sl >> 2), 2 * dh + ((sl & 3) >> 1)) + (sl & 1) * 8);
   }
   asm volatile("" : "+v"(od), "+v"(otr));
-  static_assert(TL::swz(8) == (TL::swz(0) ^ 2) && TL::swz(16) == TL::swz(0), "swizzle period assumed below");
+  static_assert(TL::xor_rebuild_holds(), "swizzle rebuild assumed below");
 
   auto compute = [&](auto cur_c, int key0) __attribute__((always_inline)) {
     constexpr int CUR = decltype(cur_c)::value;

@@ -34,7 +34,27 @@ struct TileLay {
   static constexpr int RPB = 16 / CPR;     // rows per 256-byte bank period
   __host__ __device__ static constexpr int swz(int r) { return 4 * ((r / RPB) % (4 / RPB)) + ((r >> 2) & 3); }
   __host__ __device__ static constexpr int off(int r, int chunk) { return r * ROW_B + ((chunk ^ swz(r)) << 4); }
+  // The offset rebuild used by the dQ kernel: for every row r < 16 and chunk,
+  // rows r + 16 k (k < 4) have the same swizzle, chunk 2c + x is the chunk-x
+  // offset XOR (c << 5), chunk 4t + x is the chunk-x offset XOR (t << 6), and
+  // for r < 8 row r + 8 is row r's chunk-(x ^ 2) offset plus 8 rows.
+  static constexpr bool xor_rebuild_holds() {
+    for (int r = 0; r < 16; ++r)
+      for (int x = 0; x < CPR; ++x) {
+        for (int k = 1; k < 4; ++k)
+          if (off(r + 16 * k, x) != off(r, x) + 16 * k * ROW_B) return false;
+        for (int c = 0; 2 * c + (x & 1) < CPR; ++c)
+          if ((x & 1) == x && off(r, 2 * c + x) != (off(r, x) ^ (c << 5))) return false;
+        for (int t = 0; 4 * t + (x & 3) < CPR; ++t)
+          if (x < 4 && off(r, 4 * t + x) != (off(r, x) ^ (t << 6))) return false;
+        if (r < 8 && x < 4 && off(r + 8, x) != off(r, x ^ 2) + 8 * ROW_B) return false;
+      }
+    return true;
+  }
+  static_assert(CPR == 8 || CPR == 16, "head_dim 64 or 128");
 };
+static_assert(TileLay<64>::xor_rebuild_holds() && TileLay<128>::xor_rebuild_holds(),
+              "LDS offset rebuild by XOR does not match the swizzle");
 
 __device__ inline f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
