@@ -130,7 +130,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              f"(the layer shards by head with no communication, see DESIGN.md)", file=sys.stderr)
+              f"(the layer would shard by head, with no communication between GPUs)", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()

@@ -1,0 +1,55 @@
+"""Host-side checks of bench.py (no GPU): the one-GPU guard, the HBM traffic
+constants against the committed counter summary, and the algorithmic FLOP count
+of the attention roofline against the oracle's mask."""
+
+import os
+import re
+import subprocess
+import sys
+
+import numpy as np
+
+from helpers import oracle_csr
+from synth import CONFIGS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_traffic_constants_match_the_committed_profile():
+    """The fetch/write KiB and the copy calibration bench.py uses are the ones the profile summary reports,
+    for the attention source it was taken on."""
+    prof = open(os.path.join(ROOT, "profiles", "c3_32760tok_window_kernels.md")).read()
+    hbm = prof[prof.index("## HBM bytes"):]
+    row = re.search(r"\| k_attn_bf16<128, 64> \| ([0-9.]+) \| ([0-9.]+) \|", hbm)
+    assert row, "attention row missing from the HBM table"
+    assert float(row.group(1)) == bench.ATTN_COUNTERS["c3"]["fetch_kib"]
+    assert float(row.group(2)) == bench.ATTN_COUNTERS["c3"]["write_kib"]
+    assert "FETCH_SIZE =\n262156.8 KiB" in prof or "FETCH_SIZE = 262156.8 KiB" in prof
+    assert re.search(r"sha256\s+prefix " + bench.ATTN_COUNTERS["source_sha256"], prof)
+    got = bench.attn_traffic_bytes("c3")
+    assert got is not None, "attention source changed since the counters were taken"
+    want = 1024.0 * (172323.0 * 524288.0 / 262156.8 + 98304.0)
+    assert got == round(want)
+    assert bench.attn_traffic_bytes("c4") is None  # not measured for that layer
+
+
+def test_kept_tile_flop_count_from_the_oracle_mask():
+    """4 * block^2 * head_dim per kept block pair (two products, 2 flops per MAC), from the oracle's CSR."""
+    cfg = CONFIGS["c3"]
+    rp, ci = oracle_csr("c3")
+    nnz = int(rp[-1])
+    assert nnz == 314568
+    assert 4.0 * cfg.block * cfg.block * cfg.head_dim * nnz == 659696910336.0
+    # the dense-equivalent count the metric divides by: all N x N query-key pairs, two products
+    assert cfg.dense_equiv_flop() == 4.0 * cfg.batch * cfg.heads * float(cfg.N) ** 2 * cfg.head_dim
+    assert np.isclose(nnz / (cfg.batch * cfg.heads * cfg.nb * cfg.nb), 0.1, atol=1e-4)
