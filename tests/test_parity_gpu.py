@@ -192,6 +192,37 @@ def test_forward_c2(dtype):
         assert_close(to_numpy(o_l), ref_l, F32_MAX_ABS, 1e-4, "c2 linear fp32")
 
 
+def test_mask_and_linear_state_on_two_streams_c3():
+    """The mask pass and the linear-state pass with separate workspaces on two streams (as the bench runs them)
+    give the serial path's CSR and output bit for bit, on the 32k-token layer, and the CSR matches the oracle."""
+    print("two streams c3", flush=True)
+    cfg = CONFIGS["c3"]
+    inp = inputs("c3")
+    q, k, v, w = device_tensors(inp)
+    gate = torch.from_numpy(inp.gate).cuda()
+    outs = []
+    for concurrent in (False, True):
+        layer = make_layer(cfg)
+        ws_lin = torch.full_like(layer.ws, 0xFF) if concurrent else layer.ws
+        main = torch.cuda.current_stream()
+        side = torch.cuda.Stream() if concurrent else main
+        fork, join = torch.cuda.Event(), torch.cuda.Event()
+        fork.record(main)
+        side.wait_event(fork)
+        S.salad_linear_prepare(layer.shape, k, v, gate, w, ws_lin, side.cuda_stream, drop_tau=0.0)
+        join.record(side)
+        layer.build_mask(q, k, stream=main.cuda_stream)
+        main.wait_event(join)
+        out = torch.empty_like(q)
+        S.salad_attn_apply(layer.shape, q, k, v, layer.row_ptr, layer.col_idx, gate, cfg.eps, 0.0, 0.0, out,
+                           ws_lin, main.cuda_stream)
+        torch.cuda.synchronize()
+        outs.append((layer.row_ptr.clone(), layer.col_idx.clone(), out))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    assert torch.equal(outs[0][2], outs[1][2]), "two-stream output differs from the serial one"
+    np.testing.assert_array_equal(outs[1][0].cpu().numpy(), oracle_csr("c3")[0])
+
+
 def test_linear_branch_shifted_v_c2():
     """V + 1 makes o_l of order 1, so the linear branch is visible at the bf16 bar."""
     cfg = CONFIGS["c2"]
