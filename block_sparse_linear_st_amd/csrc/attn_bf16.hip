@@ -3,13 +3,14 @@
 // One workgroup (4 waves) owns 128 query rows: two 64-token query blocks, or
 // one 128-token block.  Each wave owns 32 rows.  The workgroup walks the
 // ascending union of its query blocks' kept key-block lists (a two-way merge of
-// the CSR rows, read through the scalar cache) in 64-key tiles; a wave computes
+// the CSR rows, read through the scalar cache) in 64-key tiles (32-key tiles
+// for 128-token blocks, see tile_keys below); a wave computes
 // a tile only when its own query block keeps that key block, so dropped blocks
 // cost nothing and key blocks kept by both query blocks are loaded once.
 //
 // Per tile, with MFMA 32x32x16 bf16 (fp32 accumulate):
 //   S^T = K Q^T      A = K tile (LDS), B = Q fragments held in registers
-//   online softmax   a row's 64 scores sit in lanes l and l^32, so the row max
+//   online softmax   a row's scores of a tile sit in lanes l and l^32, so the row max
 //                    and row sum need one v_permlane32_swap each
 //   O^T += V^T P^T   A = V^T fragments read from the row-major V tile with the
 //                    gfx950 LDS transpose read (ds_read_b64_tr_b16), B = P taken
@@ -47,25 +48,27 @@
 namespace salad {
 namespace {
 
-constexpr int kTK = 64;  // keys per LDS tile
-
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
-template <int D>
+// KT keys per LDS tile: 64, or 32 for 128-token blocks (a smaller tile leaves
+// room for three workgroups per CU).
+template <int D, int KT>
 struct Lay {
   static constexpr int CPR = D / 8;             // 16-byte chunks per row
   static constexpr int ROW_B = D * 2;           // bytes per row
-  static constexpr int TILE_B = kTK * ROW_B;    // one K or V tile
+  static constexpr int TILE_B = KT * ROW_B;     // one K or V tile
   static constexpr int BUF_B = 2 * TILE_B;      // K then V
   static constexpr int RPB = 16 / CPR;          // rows per 256-byte bank period
-  static constexpr int LOADS = kTK * CPR / 256; // 1 KiB loads per thread per tile (K or V)
+  static constexpr int LOADS = KT * CPR / 256;  // 1 KiB loads per thread per tile (K or V)
   static constexpr int OST = D + 8;             // output staging stride (bf16)
-  static_assert(128 * OST * 2 <= 2 * BUF_B, "output staging must fit");
-  static_assert(2 * D * D * 2 <= 2 * BUF_B, "folded linear state (hi + lo) must fit");
+  static constexpr int SMEM_B = 128 * OST * 2 > 2 * BUF_B ? 128 * OST * 2 : 2 * BUF_B;
+  // the folded linear state (hi, lo) goes through LDS in one pass when both fit, else one part at a time
+  static constexpr int LIN_PASSES = 2 * D * D * 2 <= SMEM_B ? 1 : 2;
+  static_assert(D * D * 2 <= SMEM_B, "one part of the folded linear state must fit");
   // 16 consecutive rows reading one logical chunk hit 16 different physical chunks
   __device__ static int kswz(int r) { return (r / RPB) % CPR; }
   // 4 consecutive rows x 4 consecutive chunks (a half-wave transpose read) are disjoint
@@ -127,13 +130,13 @@ __device__ __attribute__((always_inline)) inline const __bf16* uniform_ptr(const
   return reinterpret_cast<const __bf16*>(((uint64_t)hi << 32) | lo);
 }
 
-// Per-lane byte offsets, inside a 64-key tile, of the 16-byte chunks this lane
-// loads (row r, logical chunk p ^ swizzle(r)); they do not depend on the tile.
-template <int D>
+// Per-lane byte offsets, inside a tile, of the 16-byte chunks this lane loads
+// (row r, logical chunk p ^ swizzle(r)); they do not depend on the tile.
+template <int D, int KT>
 struct DmaOffsets {
-  uint32_t k[Lay<D>::LOADS], v[Lay<D>::LOADS];
+  uint32_t k[Lay<D, KT>::LOADS], v[Lay<D, KT>::LOADS];
   __device__ void init(int wave, int lane) {
-    using LY = Lay<D>;
+    using LY = Lay<D, KT>;
 #pragma unroll
     for (int i = 0; i < LY::LOADS; ++i) {
       const int P = (wave * LY::LOADS + i) * 64 + lane;
@@ -144,18 +147,18 @@ struct DmaOffsets {
   }
 };
 
-// Issue the loads of one 64-key K and V tile into the LDS buffer at byte
-// address `buf`.  Whole tiles use a uniform base plus the fixed lane offsets;
+// Issue the loads of one K and V tile into the LDS buffer at byte address
+// `buf`.  Whole tiles use a uniform base plus the fixed lane offsets;
 // the tile that runs past the last valid token loads row N-1 in place of the
 // missing rows (always in bounds, always finite); their scores are masked to
 // -inf, so they contribute exact zeros.
-template <int D>
+template <int D, int KT>
 __device__ __attribute__((always_inline)) inline void issue_tile(uint32_t buf, const __bf16* Kb,
                                                                  const __bf16* Vb, int key0, int N,
                                                                  int wave, int lane,
-                                                                 const DmaOffsets<D>& off) {
-  using LY = Lay<D>;
-  if (key0 + kTK <= N) {
+                                                                 const DmaOffsets<D, KT>& off) {
+  using LY = Lay<D, KT>;
+  if (key0 + KT <= N) {
     const __bf16* kbase = uniform_ptr(Kb + (int64_t)key0 * D);
     const __bf16* vbase = uniform_ptr(Vb + (int64_t)key0 * D);
 #pragma unroll
@@ -177,13 +180,14 @@ __device__ __attribute__((always_inline)) inline void issue_tile(uint32_t buf, c
   }
 }
 
-// S^T, softmax and O^T update of one wave on one tile held in `buf`.
+// S^T, softmax and O^T update of one wave on one 64-key tile held in buffer
+// CUR; ka, va are the per-lane read offsets.
 template <int D, int CUR>
-__device__ __attribute__((always_inline)) inline void compute_tile(const unsigned char* smem, const uint32_t (&ka)[D / 16],
+__device__ __attribute__((always_inline)) inline void compute_tile64(const unsigned char* smem, const uint32_t (&ka)[D / 16],
                                     const uint32_t (&va)[D / 32], const bf16x8 (&qf)[D / 16],
                                     f32x16 (&o)[D / 32], float& m_used, float& l_run, int key0,
                                     int N, float c_log2, int lane) {
-  using LY = Lay<D>;
+  using LY = Lay<D, 64>;
   constexpr int NC = D / 16, NT = D / 32;
   const int g32 = lane >> 5, l32 = lane & 31;
   const unsigned char* Kt = smem + CUR * LY::BUF_B;
@@ -213,7 +217,7 @@ __device__ __attribute__((always_inline)) inline void compute_tile(const unsigne
     }
   }
   // mask padded keys (only the tile that holds token N-1 and beyond)
-  if (key0 + kTK > N) {
+  if (key0 + 64 > N) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -297,15 +301,112 @@ __device__ __attribute__((always_inline)) inline void compute_tile(const unsigne
   }
 }
 
+// The same on one 32-key tile: one QK^T chain; kbase, vbase are the per-lane
+// read bases (chunk c of a K row is kbase ^ (c << 5), output tile t of a V
+// transpose read is vbase ^ (t << 6)).
+template <int D, int CUR>
+__device__ __attribute__((always_inline)) inline void compute_tile32(const unsigned char* smem, uint32_t kbase,
+                                    uint32_t vbase, const bf16x8 (&qf)[D / 16],
+                                    f32x16 (&o)[D / 32], float& m_used, float& l_run, int key0,
+                                    int N, float c_log2, int lane) {
+  using LY = Lay<D, 32>;
+  constexpr int NC = D / 16, NT = D / 32;
+  const int g32 = lane >> 5;
+  const unsigned char* Kt = smem + CUR * LY::BUF_B;
+  const unsigned char* Vt = Kt + LY::TILE_B;
+  // S^T = K Q^T over the tile's 32 keys: one chain, K fragments one step ahead
+  f32x16 s;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s[i] = 0.0f;
+  {
+    auto kfrag = [&](int c) __attribute__((always_inline)) {
+      return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Kt + (kbase ^ (c << 5))));
+    };
+    bf16x8 a0 = kfrag(0);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      bf16x8 a1 = a0;
+      if (c + 1 < NC) a1 = kfrag(c + 1);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[c], s, 0, 0, 0);
+      a0 = a1;
+    }
+  }
+  if (key0 + 32 > N) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = key0 + (i >> 2) * 8 + g32 * 4 + (i & 3);
+      if (key >= N) s[i] = -INFINITY;
+    }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[i]);
+  mx = pair_max(mx) * c_log2;
+  if (__ballot(mx > m_used + 8.0f)) {
+    const float m_new = fmaxf(m_used, mx);
+    const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_used - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
+    m_used = m_new;
+  }
+  const float neg_m = m_used == -INFINITY ? 0.0f : -m_used;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float rs = 0.0f;
+  bf16x8 pf[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float p[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(fmaf(s[h * 8 + j], c_log2, neg_m));
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      w[j] = pack_bf16x2(p[2 * j], p[2 * j + 1]);
+      rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[j]), ones, rs, false);
+    }
+    pf[h] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+  }
+  l_run += pair_sum(rs);
+  // O^T += V^T P^T, V^T fragments by transpose reads laid out as in the 64-key tile
+  auto vfrag = [&](int t, int ks) __attribute__((always_inline)) {
+    uint2 tr[2];
+    const uint32_t v0 = vbase ^ (t << 6);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const unsigned char* ad = Vt + v0 + (ks * 16 + 8 * h) * LY::ROW_B;
+      tr[h] = __builtin_bit_cast(
+          uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(ad)));
+    }
+    return __builtin_bit_cast(bf16x8, make_uint4(tr[0].x, tr[0].y, tr[1].x, tr[1].y));
+  };
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag(t, ks), pf[ks], o[t], 0, 0, 0);
+}
+
+// 64-key tiles for 64-token blocks (64 KiB of LDS at head_dim 128, two
+// workgroups per CU); 32-key tiles for 128-token blocks, whose workgroups walk
+// one block's list with every wave active: 35 KiB of LDS and at most 168
+// registers give three workgroups (three waves per SIMD) per CU.
+template <int BLK>
+constexpr int tile_keys() { return BLK == 128 ? 32 : 64; }
+
 template <int D, int BLK>
-__global__ void __launch_bounds__(256, 2)
+__global__ void __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(tile_keys<BLK>() == 32 ? 3 : 2, tile_keys<BLK>() == 32 ? 3 : 2)))
 k_attn_bf16(Geom g, AttnArgs a, int n_items, float c_log2) {
-  using LY = Lay<D>;
+  constexpr int KT = tile_keys<BLK>();
+  using LY = Lay<D, KT>;
   constexpr int QPW = 128 / BLK;  // query blocks per workgroup
   constexpr int NC = D / 16;
   constexpr int NT = D / 32;
-  constexpr int TPB = BLK / kTK;  // 64-key tiles per key block
-  __shared__ __align__(1024) unsigned char smem[2 * LY::BUF_B];
+  constexpr int TPB = BLK / KT;   // tiles per key block
+  __shared__ __align__(1024) unsigned char smem[LY::SMEM_B];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g32 = lane >> 5, l32 = lane & 31;
@@ -356,7 +457,7 @@ k_attn_bf16(Geom g, AttnArgs a, int n_items, float c_log2) {
     int kb = 0, sub = 0, flags = 0;
     bool valid = false;
     auto advance = [&](int& nkb, int& nsub, int& nflags, bool& nvalid) __attribute__((always_inline)) {
-      if (valid && sub + 1 < TPB && kb * BLK + (sub + 1) * kTK < g.N) {
+      if (valid && sub + 1 < TPB && kb * BLK + (sub + 1) * KT < g.N) {
         nkb = kb; nsub = sub + 1; nflags = flags; nvalid = true;
         return;
       }
@@ -371,28 +472,35 @@ k_attn_bf16(Geom g, AttnArgs a, int n_items, float c_log2) {
     // LDS byte address of the buffers (uniform); the wave index is uniform too
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    DmaOffsets<D> doff;
+    DmaOffsets<D, KT> doff;
     doff.init(wave_u, lane);
-    if (valid) issue_tile<D>(lds0, Kb, Vb, kb * BLK + sub * kTK, g.N, wave_u, lane, doff);
+    if (valid) issue_tile<D, KT>(lds0, Kb, Vb, kb * BLK + sub * KT, g.N, wave_u, lane, doff);
     wait_vmem();
     __syncthreads();
     // per-lane LDS read offsets inside a tile, fixed for the whole loop (kept opaque so that
-    // they stay in registers rather than being recomputed at every read)
-    uint32_t ka[NC], va[NT];
+    // they stay in registers rather than being recomputed at every read): all of them for
+    // 64-key tiles, one base per read kind for 32-key tiles (fewer registers)
+    uint32_t ka[NC], va[NT], kbase = 0, vbase = 0;
     {
       const int sw = LY::kswz(l32);
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        ka[c] = (uint32_t)(l32 * LY::ROW_B + (((2 * c + g32) ^ sw) << 4));
-        asm volatile("" : "+v"(ka[c]));
-      }
       const int sl = lane & 15, dh = (lane >> 4) & 1;
       const int row = 4 * g32 + (sl >> 2);  // + 16 ks + 8 h, which leave the swizzle unchanged
+      if constexpr (KT == 64) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const int chunk = 4 * t + 2 * dh + ((sl & 3) >> 1);
-        va[t] = (uint32_t)(row * LY::ROW_B + ((chunk ^ LY::vswz(row)) << 4) + (sl & 1) * 8);
-        asm volatile("" : "+v"(va[t]));
+        for (int c = 0; c < NC; ++c) {
+          ka[c] = (uint32_t)(l32 * LY::ROW_B + (((2 * c + g32) ^ sw) << 4));
+          asm volatile("" : "+v"(ka[c]));
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const int chunk = 4 * t + 2 * dh + ((sl & 3) >> 1);
+          va[t] = (uint32_t)(row * LY::ROW_B + ((chunk ^ LY::vswz(row)) << 4) + (sl & 1) * 8);
+          asm volatile("" : "+v"(va[t]));
+        }
+      } else {
+        kbase = (uint32_t)(l32 * LY::ROW_B + ((g32 ^ sw) << 4));
+        vbase = (uint32_t)(row * LY::ROW_B + (((2 * dh + ((sl & 3) >> 1)) ^ LY::vswz(row)) << 4) + (sl & 1) * 8);
+        asm volatile("" : "+v"(kbase), "+v"(vbase));
       }
     }
     // two copies of the step, one per buffer, so that every LDS offset is an immediate
@@ -402,10 +510,15 @@ k_attn_bf16(Geom g, AttnArgs a, int n_items, float c_log2) {
       bool nvalid;
       advance(nkb, nsub, nflags, nvalid);
       if (nvalid)
-        issue_tile<D>(lds0 + (CUR ^ 1) * LY::BUF_B, Kb, Vb, nkb * BLK + nsub * kTK, g.N, wave_u, lane,
-                      doff);
-      if (wave_rows && ((flags >> qsub) & 1))
-        compute_tile<D, CUR>(smem, ka, va, qf, o, m_used, l_run, kb * BLK + sub * kTK, g.N, c_log2, lane);
+        issue_tile<D, KT>(lds0 + (CUR ^ 1) * LY::BUF_B, Kb, Vb, nkb * BLK + nsub * KT, g.N, wave_u, lane,
+                          doff);
+      if (wave_rows && ((flags >> qsub) & 1)) {
+        if constexpr (KT == 64)
+          compute_tile64<D, CUR>(smem, ka, va, qf, o, m_used, l_run, kb * BLK + sub * KT, g.N, c_log2, lane);
+        else
+          compute_tile32<D, CUR>(smem, kbase, vbase, qf, o, m_used, l_run, kb * BLK + sub * KT, g.N, c_log2,
+                                 lane);
+      }
       wait_vmem();  // the next tile has landed in LDS ...
       __syncthreads();  // ... for every wave, and nobody still reads the current one
       kb = nkb; sub = nsub; flags = nflags; valid = nvalid;
@@ -431,56 +544,111 @@ k_attn_bf16(Geom g, AttnArgs a, int n_items, float c_log2) {
   bool lin = a.has_lin != 0;
   if (lin && a.gate != nullptr && a.gate[bh] < a.drop_tau) lin = false;  // uniform
   if (lin) {
-    // S''^T (hi, lo) of this head into LDS, rows swizzled like K tiles: every
-    // wave reads all of it, so one copy per workgroup instead of one per wave
-    const __bf16* hi = static_cast<const __bf16*>(a.sft_hi) + (int64_t)bh * D * D;
-    const __bf16* lo = static_cast<const __bf16*>(a.sft_lo) + (int64_t)bh * D * D;
-    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
-    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    constexpr int PER = D * LY::CPR / 256;  // 1 KiB loads per wave per matrix
-    __syncthreads();  // the tile buffers are free
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int blk1k = wave_u * PER + i;
-      const int P = blk1k * 64 + lane;
-      const int r = P / LY::CPR, p = P % LY::CPR;
-      lds_dma16(hi + r * D + (p ^ LY::kswz(r)) * 8, lds0 + blk1k * 1024);
-      lds_dma16(lo + r * D + (p ^ LY::kswz(r)) * 8, lds0 + D * D * 2 + blk1k * 1024);
-    }
-    const float* z = a.z + (int64_t)bh * D;
-    bf16x8 rq[NC];
-    float den = 0.0f;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      rq[c] = relu8(qf[c]);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) den += (float)rq[c][j] * z[c * 16 + g32 * 8 + j];
-    }
-    den = pair_sum(den);
-    const float inv_den = 1.0f / (den + a.eps);
-    wait_vmem();
-    __syncthreads();
-    if (wave_rows) {
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const int row = t * 32 + l32;
-        const unsigned char* rh = smem + row * LY::ROW_B;
-        const unsigned char* rl = rh + D * D * 2;
-        const int sw = LY::kswz(row);
-        f32x16 la;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) la[i] = 0.0f;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const int off = ((2 * c + g32) ^ sw) << 4;
-          la = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(rh + off)), rq[c], la, 0, 0, 0);
-          la = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(rl + off)), rq[c], la, 0, 0, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[t][i] += la[i] * inv_den;
+    if constexpr (LY::LIN_PASSES == 1) {
+      // S''^T (hi, lo) of this head into LDS, rows swizzled like K tiles: every
+      // wave reads all of it, so one copy per workgroup instead of one per wave
+      const __bf16* hi = static_cast<const __bf16*>(a.sft_hi) + (int64_t)bh * D * D;
+      const __bf16* lo = static_cast<const __bf16*>(a.sft_lo) + (int64_t)bh * D * D;
+      const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
+      const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+      constexpr int PER = D * LY::CPR / 256;  // 1 KiB loads per wave per matrix
+      __syncthreads();  // the tile buffers are free
+  #pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int blk1k = wave_u * PER + i;
+        const int P = blk1k * 64 + lane;
+        const int r = P / LY::CPR, p = P % LY::CPR;
+        lds_dma16(hi + r * D + (p ^ LY::kswz(r)) * 8, lds0 + blk1k * 1024);
+        lds_dma16(lo + r * D + (p ^ LY::kswz(r)) * 8, lds0 + D * D * 2 + blk1k * 1024);
       }
+      const float* z = a.z + (int64_t)bh * D;
+      bf16x8 rq[NC];
+      float den = 0.0f;
+  #pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        rq[c] = relu8(qf[c]);
+  #pragma unroll
+        for (int j = 0; j < 8; ++j) den += (float)rq[c][j] * z[c * 16 + g32 * 8 + j];
+      }
+      den = pair_sum(den);
+      const float inv_den = 1.0f / (den + a.eps);
+      wait_vmem();
+      __syncthreads();
+      if (wave_rows) {
+  #pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const int row = t * 32 + l32;
+          const unsigned char* rh = smem + row * LY::ROW_B;
+          const unsigned char* rl = rh + D * D * 2;
+          const int sw = LY::kswz(row);
+          f32x16 la;
+  #pragma unroll
+          for (int i = 0; i < 16; ++i) la[i] = 0.0f;
+  #pragma unroll
+          for (int c = 0; c < NC; ++c) {
+            const int off = ((2 * c + g32) ^ sw) << 4;
+            la = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(rh + off)), rq[c], la, 0, 0, 0);
+            la = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(rl + off)), rq[c], la, 0, 0, 0);
+          }
+  #pragma unroll
+          for (int i = 0; i < 16; ++i) o[t][i] += la[i] * inv_den;
+        }
+      }
+  
+    } else {
+      // S''^T hi, then lo, through LDS one part at a time; the linear term goes
+      // straight into O: o = (o_s den + S''^T relu(q)) / den
+      const __bf16* part[2] = {static_cast<const __bf16*>(a.sft_hi) + (int64_t)bh * D * D,
+                               static_cast<const __bf16*>(a.sft_lo) + (int64_t)bh * D * D};
+      const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
+      const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+      constexpr int PER = D * LY::CPR / 256;  // 1 KiB loads per wave per matrix
+      const float* z = a.z + (int64_t)bh * D;
+      bf16x8 rq[NC];
+      float den = 0.0f;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        rq[c] = relu8(qf[c]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) den += (float)rq[c][j] * z[c * 16 + g32 * 8 + j];
+      }
+      den = pair_sum(den) + a.eps;
+      const float inv_den = 1.0f / den;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[t][i] *= den;
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        __syncthreads();  // the buffers are free
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+          const int blk1k = wave_u * PER + i;
+          const int P = blk1k * 64 + lane;
+          const int r = P / LY::CPR, p = P % LY::CPR;
+          lds_dma16(part[pp] + r * D + (p ^ LY::kswz(r)) * 8, lds0 + blk1k * 1024);
+        }
+        wait_vmem();
+        __syncthreads();
+        if (wave_rows) {
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            const unsigned char* rh = smem + (t * 32 + l32) * LY::ROW_B;
+            const int sw = LY::kswz(t * 32 + l32);
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+              o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(rh + (((2 * c + g32) ^ sw) << 4))),
+                  rq[c], o[t], 0, 0, 0);
+          }
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[t][i] *= inv_den;
     }
   }
 

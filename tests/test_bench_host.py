@@ -34,11 +34,14 @@ def test_traffic_constants_match_the_committed_profile():
     assert row, "attention row missing from the HBM table"
     assert float(row.group(1)) == bench.ATTN_COUNTERS["c3"]["fetch_kib"]
     assert float(row.group(2)) == bench.ATTN_COUNTERS["c3"]["write_kib"]
-    assert "FETCH_SIZE =\n262156.8 KiB" in prof or "FETCH_SIZE = 262156.8 KiB" in prof
+    cal = re.search(r"reads FETCH_SIZE =\s+([0-9.]+) KiB and WRITE_SIZE = ([0-9.]+) KiB", prof)
+    assert cal, "copy calibration missing"
+    assert bench.ATTN_COUNTERS["fetch_scale"] == 524288.0 / float(cal.group(1))
+    assert bench.ATTN_COUNTERS["write_scale"] == 524288.0 / float(cal.group(2))
     assert re.search(r"sha256\s+prefix " + bench.ATTN_COUNTERS["source_sha256"], prof)
     got = bench.attn_traffic_bytes("c3")
     assert got is not None, "attention source changed since the counters were taken"
-    want = 1024.0 * (172323.0 * 524288.0 / 262156.8 + 98304.0)
+    want = 1024.0 * (float(row.group(1)) * 524288.0 / float(cal.group(1)) + float(row.group(2)))
     assert got == round(want)
     assert bench.attn_traffic_bytes("c4") is None  # not measured for that layer
 
