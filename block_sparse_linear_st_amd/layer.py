@@ -69,3 +69,56 @@ class SaladLayer:
     def branches(self, q, k, v, out_sparse, out_lin, eps: float = 1e-6, scale: float = 0.0, stream=None):
         S.salad_attn_fwd_branches(self.shape, q, k, v, self.row_ptr, self.col_idx, eps, scale, out_sparse,
                                   out_lin, self.ws, stream)
+
+    def backward(self, q, k, v, gate, w_lin, out, dout, dq, dk, dv, dw_lin, dgate, eps: float = 1e-6,
+                 scale: float = 0.0, lse=None, stream=None):
+        """Gradients of the layer (salad_attn_bwd) into caller buffers; the backward workspace is owned here."""
+        ws = self.backward_workspace()
+        S.salad_attn_bwd(self.shape, q, k, v, self.row_ptr, self.col_idx, gate, w_lin, eps, scale, out, dout,
+                         dq, dk, dv, dw_lin, dgate, ws, stream, lse=lse)
+
+    def backward_workspace(self) -> torch.Tensor:
+        if getattr(self, "_bwd_ws", None) is None:
+            n = S.salad_bwd_workspace_bytes(self.shape)
+            if n == 0:
+                raise S.SaladError(S.SALAD_EINVAL, "invalid or unsupported layer shape")
+            self._bwd_ws = torch.empty(n, dtype=torch.uint8, device=self.device)
+        return self._bwd_ws
+
+    def attention(self, q, k, v, gate, w_lin, eps: float = 1e-6, scale: float = 0.0):
+        """out = layer(q, k, v, gate, w_lin) as a differentiable torch op (bf16 layers) over the mask the last
+        build_mask call made; the backward gives dq, dk, dv, dgate and dW_lin (cast to W_lin's dtype)."""
+        return _SaladAttention.apply(self, q, k, v, gate, w_lin, eps, scale)
+
+
+class _SaladAttention(torch.autograd.Function):
+    """Forward through salad_attn_fwd keeping each row's log2-sum-exp, backward through salad_attn_bwd.
+    Marshalling only: outputs and gradient buffers are allocated here, every step runs in libsalad."""
+
+    @staticmethod
+    def forward(ctx, layer, q, k, v, gate, w_lin, eps, scale):
+        if layer.torch_dtype != torch.bfloat16:
+            raise S.SaladError(S.SALAD_EUNSUPPORTED, "the differentiable layer needs a bf16 shape")
+        q, k, v, w_lin = (t.contiguous() for t in (q, k, v, w_lin))
+        gate = gate.contiguous()
+        out = torch.empty_like(q)
+        s = layer.shape
+        lse = torch.empty(s.batch * s.heads * s.n_pad, dtype=torch.float32, device=q.device)
+        layer.forward(q, k, v, gate, w_lin, out, eps=eps, scale=scale, lse=lse,
+                      stream=torch.cuda.current_stream().cuda_stream)
+        ctx.save_for_backward(q, k, v, gate, w_lin, out, lse)
+        ctx.layer, ctx.eps, ctx.scale = layer, eps, scale
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, gate, w_lin, out, lse = ctx.saved_tensors
+        layer = ctx.layer
+        dout = dout.to(torch.bfloat16).contiguous()
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        d = layer.shape.head_dim
+        dw = torch.empty((d, d), dtype=torch.float32, device=q.device)
+        dg = torch.empty(gate.numel(), dtype=torch.float32, device=q.device)
+        layer.backward(q, k, v, gate, w_lin, out, dout, dq, dk, dv, dw, dg, eps=ctx.eps, scale=ctx.scale,
+                       lse=lse, stream=torch.cuda.current_stream().cuda_stream)
+        return None, dq, dk, dv, dg.view_as(gate).to(gate.dtype), dw.to(w_lin.dtype), None, None

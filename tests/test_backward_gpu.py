@@ -193,3 +193,42 @@ def test_backward_sampled_large(name):
         _check(dv, ref["dv"], f"{tag} dv (sampled)")
         _check(got["dw"].cpu().numpy(), ref["dw_lin"], f"{tag} dW_lin", rel_l2=FP32_REL_L2)
         _check(got["dg"].cpu().numpy(), ref["dgate"], f"{tag} dgate", rel_l2=FP32_REL_L2)
+
+
+def test_differentiable_layer_op_c2():
+    """layer.attention(...) under torch autograd gives the entry points' output and gradients bit for bit, and
+    its gradients meet the oracle's bars."""
+    print("autograd op c2", flush=True)
+    cfg = CONFIGS["c2"]
+    inp = inputs("c2")
+    layer = make_layer(cfg)
+    q, k, v, w = device_tensors(inp)
+    layer.build_mask(q, k)
+    gate = torch.from_numpy(inp.gate).cuda()
+    dvals, dbits = make_grad_output(cfg)
+    dout = torch.from_numpy(dbits.view(np.int16)).view(torch.bfloat16).cuda()
+
+    leaves = [t.clone().requires_grad_(True) for t in (q, k, v, gate, w)]
+    out = layer.attention(*leaves, eps=cfg.eps)
+    out.backward(dout)
+    torch.cuda.synchronize()
+
+    ref_out = torch.empty_like(q)
+    lse = torch.empty(cfg.batch * cfg.heads * cfg.n_pad, dtype=torch.float32, device="cuda")
+    layer.forward(q, k, v, gate, w, ref_out, eps=cfg.eps, lse=lse)
+    g = {n: torch.empty_like(q) for n in ("dq", "dk", "dv")}
+    dw = torch.empty((cfg.head_dim, cfg.head_dim), dtype=torch.float32, device="cuda")
+    dg = torch.empty(cfg.batch * cfg.heads, dtype=torch.float32, device="cuda")
+    layer.backward(q, k, v, gate, w, ref_out, dout, g["dq"], g["dk"], g["dv"], dw, dg, eps=cfg.eps, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.equal(out.detach(), ref_out)
+    for leaf, want in zip(leaves[:3], (g["dq"], g["dk"], g["dv"])):
+        assert torch.equal(leaf.grad, want)
+    assert torch.equal(leaves[3].grad, dg)
+    assert torch.equal(leaves[4].grad, dw.to(torch.bfloat16))
+
+    ref, _, _ = _oracle(cfg, inp, gate, dvals)
+    N = cfg.N
+    for n, leaf in zip(("dq", "dk", "dv"), leaves[:3]):
+        _check(to_numpy(leaf.grad)[:, :, :N], ref[n][:, :, :N], f"autograd c2 {n}")
+    _check(leaves[3].grad.cpu().numpy(), ref["dgate"], "autograd c2 dgate", rel_l2=FP32_REL_L2)
