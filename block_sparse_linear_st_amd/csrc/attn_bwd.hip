@@ -83,7 +83,7 @@ __global__ void __launch_bounds__(BLK * 2)
 k_attn_bwd_dq(Geom g, BwdArgs a, const float* __restrict__ Dq, const float* __restrict__ dden,
               const __bf16* __restrict__ dU, const __bf16* __restrict__ s_hi, const __bf16* __restrict__ s_lo,
               const float* __restrict__ z, float* __restrict__ lse_out, float c_log2) {
-  constexpr int NT = D / 32, NC = D / 16, NTH = BLK * 2;
+  constexpr int NT = D / 32, NC = D / 16;
   using SM = BwdSmem<D, BLK>;
   __shared__ __align__(16) unsigned char smem[SM::BYTES];
   const int qb = blockIdx.x, bh = blockIdx.y;

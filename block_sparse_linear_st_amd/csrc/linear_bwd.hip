@@ -375,7 +375,7 @@ k_fold_dgate(Geom g, const float* __restrict__ gpart, float* __restrict__ dgate)
   red[threadIdx.x] = s;
   __syncthreads();
   for (int o = 128; o > 0; o >>= 1) {
-    if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
     __syncthreads();
   }
   if (threadIdx.x == 0) dgate[bh] = red[0];
