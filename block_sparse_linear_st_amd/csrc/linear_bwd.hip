@@ -389,12 +389,15 @@ k_fold_dgate(Geom g, const float* __restrict__ gpart, float* __restrict__ dgate)
 __global__ void __launch_bounds__(256)
 k_csc_bits(Geom g, int words, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
            uint32_t* __restrict__ bits) {
-  const int64_t r = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (r >= (int64_t)g.B * g.Hh * g.nb) return;
+  // one wave per CSR row, its lanes over the row's entries
+  const int64_t r = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) >> 6;
+  const int lane = threadIdx.x & 63;
+  if (r >= (int64_t)g.B * g.Hh * g.nb) return;  // uniform per wave
   const int64_t base = r / g.nb * g.nb;
   const int qb = (int)(r - base);
-  for (int e = row_ptr[r]; e < row_ptr[r + 1]; ++e)
-    atomicOr(&bits[(base + col_idx[e]) * words + (qb >> 5)], 1u << (qb & 31));
+  const uint32_t bit = 1u << (qb & 31);
+  for (int e = row_ptr[r] + lane; e < row_ptr[r + 1]; e += 64)
+    atomicOr(&bits[(base + col_idx[e]) * words + (qb >> 5)], bit);
 }
 
 __global__ void __launch_bounds__(256)
@@ -409,16 +412,28 @@ k_csc_count(Geom g, int words, const uint32_t* __restrict__ bits, int32_t* __res
 __global__ void __launch_bounds__(256)
 k_csc_fill(Geom g, int words, const uint32_t* __restrict__ bits, const int32_t* __restrict__ colptr,
            int32_t* __restrict__ rowidx) {
-  const int64_t c = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (c >= (int64_t)g.B * g.Hh * g.nb) return;
+  // one wave per column: lanes take 64 words at a time, an exclusive scan of their
+  // popcounts gives each lane its output position, bits are emitted in ascending order
+  const int64_t c = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) >> 6;
+  const int lane = threadIdx.x & 63;
+  if (c >= (int64_t)g.B * g.Hh * g.nb) return;  // uniform per wave
   int p = colptr[c];
-  for (int w = 0; w < words; ++w) {
-    uint32_t b = bits[c * words + w];
+  for (int w0 = 0; w0 < words; w0 += 64) {
+    const int w = w0 + lane;
+    uint32_t b = w < words ? bits[c * words + w] : 0u;
+    const int cnt = __popc(b);
+    int incl = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
+    }
+    int pos = p + incl - cnt;
     while (b) {
-      const int i = __ffs(b) - 1;
-      rowidx[p++] = w * 32 + i;
+      rowidx[pos++] = w * 32 + (__ffs(b) - 1);
       b &= b - 1;
     }
+    p += __shfl(incl, 63, 64);
   }
 }
 
@@ -565,10 +580,11 @@ hipError_t launch_mask_transpose(const Geom& g, const int32_t* row_ptr, const in
   const dim3 grid((unsigned)((n + 255) / 256));
   hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)std::min<int64_t>((n * words + 255) / 256, 4096)), dim3(256), 0, st,
                      bits, n * words);
-  hipLaunchKernelGGL(k_csc_bits, grid, dim3(256), 0, st, g, words, row_ptr, col_idx, bits);
+  const dim3 wave_grid((unsigned)((n * 64 + 255) / 256));  // one wave per row (bits) or column (fill)
+  hipLaunchKernelGGL(k_csc_bits, wave_grid, dim3(256), 0, st, g, words, row_ptr, col_idx, bits);
   hipLaunchKernelGGL(k_csc_count, grid, dim3(256), 0, st, g, words, bits, cnt);
   hipLaunchKernelGGL(k_scan_counts, dim3(1), dim3(1024), 0, st, cnt, n, ptr);
-  hipLaunchKernelGGL(k_csc_fill, grid, dim3(256), 0, st, g, words, bits, ptr, idx);
+  hipLaunchKernelGGL(k_csc_fill, wave_grid, dim3(256), 0, st, g, words, bits, ptr, idx);
   return hipGetLastError();
 }
 
