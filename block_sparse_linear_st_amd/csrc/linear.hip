@@ -13,7 +13,7 @@
 //     operands are read with the LDS transpose read, ReLU is applied to the K
 //     fragment in registers.  Products of bf16 values are exact and the sums
 //     are fp32.  The fp32 kernel does the same with VALU FMAs.
-//  2. k_lin_fold: grid (B*H, D/8).  Sums the partials over the splits in a fixed
+//  2. k_lin_fold: grid (B*H, D/2).  Sums the partials over the splits in a fixed
 //     order (bitwise reproducible; loads batched 8 splits deep), then, for the
 //     fused forward, folds gate and
 //     projection into the state:  S'' = g * S * W_lin, so that the attention
