@@ -155,6 +155,7 @@ Workspace plan_workspace(const Geom& g, const Cuboid& cu, int dtype) {
   const size_t esz = dtype == SALAD_BF16 ? 2 : 4;
   L.off_sft_hi = off; off = align_up(off + BH * D * D * esz);
   L.off_sft_lo = off; off = align_up(off + (dtype == SALAD_BF16 ? BH * D * D * 2 : 0));
+  L.off_split = off;  off = align_up(off + 9 * 4);
   L.lin_end = off;
   L.bytes = std::max(L.mask_end, L.lin_end);
   return L;
@@ -379,6 +380,7 @@ int salad_attn_apply(const salad_shape* shape, const void* q, const void* k, con
   a.q = q; a.k = k; a.v = v; a.out = out;
   a.row_ptr = row_ptr; a.col_idx = col_idx;
   a.sft_hi = w + L.off_sft_hi; a.sft_lo = w + L.off_sft_lo;
+  a.split = reinterpret_cast<int32_t*>(w + L.off_split);
   a.z = reinterpret_cast<const float*>(w + L.off_z);
   a.gate = gate; a.drop_tau = drop_tau; a.eps = eps;
   a.scale = scale > 0.0f ? scale : 1.0f / std::sqrt((float)g.D);
@@ -423,6 +425,7 @@ int salad_attn_fwd_branches(const salad_shape* shape, const void* q, const void*
   a.q = q; a.k = k; a.v = v;
   a.row_ptr = row_ptr; a.col_idx = col_idx;
   a.sft_hi = w + L.off_sft_hi; a.sft_lo = w + L.off_sft_lo;
+  a.split = reinterpret_cast<int32_t*>(w + L.off_split);
   a.z = reinterpret_cast<const float*>(w + L.off_z);
   a.gate = nullptr; a.drop_tau = 0.0f; a.eps = eps;
   a.scale = scale > 0.0f ? scale : 1.0f / std::sqrt((float)g.D);

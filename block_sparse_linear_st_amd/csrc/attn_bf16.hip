@@ -40,7 +40,9 @@
 //
 // Work items map to workgroups so that each XCD (blockIdx % 8) gets a
 // contiguous range of (head, query group) items: neighbouring query blocks,
-// whose window lists overlap, share that XCD's L2.
+// whose window lists overlap, share that XCD's L2.  The ranges are cut by
+// estimated work (sched.hip) rather than by count, so that heads of different
+// density do not leave some XCDs idle at the end.
 #include <type_traits>
 
 #include "internal.h"
@@ -411,11 +413,12 @@ k_attn_bf16(Geom g, AttnArgs a, int n_items, float c_log2) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g32 = lane >> 5, l32 = lane & 31;
 
-  // XCD-aware item order: workgroup w runs on XCD w % 8; each XCD gets a
-  // contiguous range of items.
-  const int per_xcd = (int)(gridDim.x >> 3);
-  const int item = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
-  if (item >= n_items) return;
+  // XCD-aware item order: workgroup w runs on XCD w % 8, which takes its own
+  // contiguous run of items, cut by estimated work before the launch.
+  const const_i32_ptr cuts = (const_i32_ptr)a.split;
+  const int xcd = (int)(blockIdx.x & 7);
+  const int item = cuts[xcd] + (int)(blockIdx.x >> 3);
+  if (item >= cuts[xcd + 1] || item >= n_items) return;
   const int qgroups = (g.nb + QPW - 1) / QPW;
   const int bh = item / qgroups, qg = item - bh * qgroups;
   const int qb_base = qg * QPW;
@@ -683,7 +686,13 @@ hipError_t launch(const Geom& g, const AttnArgs& a, hipStream_t st) {
   constexpr int QPW = 128 / BLK;
   const int qgroups = (g.nb + QPW - 1) / QPW;
   const int n_items = g.B * g.Hh * qgroups;
-  const int grid = (n_items + 7) / 8 * 8;
+  // work per item in tile steps: kept key blocks times tiles per block, plus
+  // about three 64-key steps for the item's own loads and epilogue
+  constexpr int TPB = BLK / tile_keys<BLK>();
+  const ItemSplit job{a.row_ptr, a.split, g.B * g.Hh, g.nb, QPW, TPB, 3 * 64 / tile_keys<BLK>()};
+  hipError_t e = launch_item_splits(&job, 1, st);
+  if (e != hipSuccess) return e;
+  const int grid = 8 * xcd_items_cap(n_items);
   const float c_log2 = a.scale * 1.4426950408889634f;
   hipLaunchKernelGGL((k_attn_bf16<D, BLK>), dim3(grid), dim3(256), 0, st, g, a, n_items, c_log2);
   return hipGetLastError();

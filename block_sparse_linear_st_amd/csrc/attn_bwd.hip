@@ -266,7 +266,8 @@ k_attn_bwd_dq(Geom g, BwdArgs a, const float* __restrict__ Dq, const float* __re
 // Two workgroups share a CU.
 template <int D, int BLK>
 __global__ void __launch_bounds__(256, 2)
-k_attn_bwd_dq2(Geom g, BwdArgs a, int n_items, const float* __restrict__ Dq, const float* __restrict__ dden,
+k_attn_bwd_dq2(Geom g, BwdArgs a, int n_items, const int32_t* __restrict__ cuts, const float* __restrict__ Dq,
+               const float* __restrict__ dden,
                const __bf16* __restrict__ dU, const __bf16* __restrict__ s_hi, const __bf16* __restrict__ s_lo,
                const float* __restrict__ z, float c_log2) {
   using TL = TileLay<D>;
@@ -280,9 +281,10 @@ k_attn_bwd_dq2(Geom g, BwdArgs a, int n_items, const float* __restrict__ Dq, con
   __shared__ __align__(1024) unsigned char smem[SMEM];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, gg = lane >> 5, m = lane & 31;
-  const int per_xcd = (int)(gridDim.x >> 3);
-  const int item = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
-  if (item >= n_items) return;
+  // workgroup w runs on XCD w % 8, which takes its own contiguous run of items
+  const int xcd = (int)(blockIdx.x & 7);
+  const int item = cuts[xcd] + (int)(blockIdx.x >> 3);
+  if (item >= cuts[xcd + 1] || item >= n_items) return;
   const int qgroups = (g.nb + QPW - 1) / QPW;
   const int bh = item / qgroups, qg = item - bh * qgroups;
   const int qb_base = qg * QPW;
@@ -484,7 +486,8 @@ k_attn_bwd_dq2(Geom g, BwdArgs a, int n_items, const float* __restrict__ Dq, con
 // accumulators; the softmax scale is folded into dS.
 template <int D, int BLK>
 __global__ void __launch_bounds__(BLK * 4, BLK == 64 ? 2 : 1)
-k_attn_bwd_dkdv_pair(Geom g, BwdArgs a, int n_items, const int32_t* __restrict__ colptr,
+k_attn_bwd_dkdv_pair(Geom g, BwdArgs a, int n_items, const int32_t* __restrict__ cuts,
+                     const int32_t* __restrict__ colptr,
                      const int32_t* __restrict__ rowidx, const float* __restrict__ Dq, const float* __restrict__ lse,
                      const __bf16* __restrict__ ds_hi, const __bf16* __restrict__ ds_lo,
                      const __bf16* __restrict__ dst_hi, const __bf16* __restrict__ dst_lo,
@@ -503,9 +506,10 @@ k_attn_bwd_dkdv_pair(Geom g, BwdArgs a, int n_items, const int32_t* __restrict__
   __shared__ __align__(1024) unsigned char smem[SMEM];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, gg = lane >> 5, m = lane & 31;
-  const int per_xcd = (int)(gridDim.x >> 3);
-  const int item = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
-  if (item >= n_items) return;
+  // workgroup w runs on XCD w % 8, which takes its own contiguous run of items
+  const int xcd = (int)(blockIdx.x & 7);
+  const int item = cuts[xcd] + (int)(blockIdx.x >> 3);
+  if (item >= cuts[xcd + 1] || item >= n_items) return;
   const int bh = item / g.nb, kb = item - bh * g.nb;
   const int pair = wave >> 1;
   const bool role_b = (wave & 1) != 0;  // uniform per wave
@@ -684,20 +688,30 @@ hipError_t launch_bwd_t(const Geom& g, const BwdArgs& a, char* ws, const BwdWork
   auto F32 = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
   const float c_log2 = a.scale * 1.4426950408889634f;
   const dim3 grid(g.nb, g.B * g.Hh);
+  // XCD runs of both kernels' items, from one launch: query-block groups over
+  // the CSR rows (the one-pass dQ kernel), key blocks over the CSC columns
+  constexpr int QPW = 128 / BLK;
+  const int32_t* colptr = reinterpret_cast<const int32_t*>(ws + L.off_colptr);
+  int32_t* qcuts = reinterpret_cast<int32_t*>(ws + L.off_split_q);
+  int32_t* kcuts = reinterpret_cast<int32_t*>(ws + L.off_split_k);
+  const ItemSplit jobs[2] = {{colptr, kcuts, g.B * g.Hh, g.nb, 1, BLK / kT, 2 * 64 / kT},
+                             {a.row_ptr, qcuts, g.B * g.Hh, g.nb, QPW, BLK / kT, 3 * 64 / kT}};
+  hipError_t e = launch_item_splits(jobs, a.lse != nullptr ? 2 : 1, st);
+  if (e != hipSuccess) return e;
   if (a.lse != nullptr) {
-    constexpr int QPW = 128 / BLK;
     const int n_items = g.B * g.Hh * ((g.nb + QPW - 1) / QPW);
-    const int nwg = (n_items + 7) / 8 * 8;  // a multiple of the 8 XCDs
-    hipLaunchKernelGGL((k_attn_bwd_dq2<D, BLK>), dim3(nwg), dim3(256), 0, st, g, a, n_items, F32(L.off_dq),
-                       F32(L.off_dden), B16(L.off_du), B16(L.off_s_hi), B16(L.off_s_lo), F32(L.off_z), c_log2);
+    hipLaunchKernelGGL((k_attn_bwd_dq2<D, BLK>), dim3(8 * xcd_items_cap(n_items)), dim3(256), 0, st, g, a,
+                       n_items, qcuts, F32(L.off_dq), F32(L.off_dden), B16(L.off_du), B16(L.off_s_hi),
+                       B16(L.off_s_lo), F32(L.off_z), c_log2);
   } else
     hipLaunchKernelGGL((k_attn_bwd_dq<D, BLK>), grid, dim3(BLK * 2), 0, st, g, a, F32(L.off_dq),
                        F32(L.off_dden), B16(L.off_du), B16(L.off_s_hi), B16(L.off_s_lo), F32(L.off_z),
                        F32(L.off_lse), c_log2);
   const float* lse = a.lse != nullptr ? a.lse : F32(L.off_lse);
+  // key-block items: the query blocks that keep a key block (its CSC column) are its work
   const int k_items = g.B * g.Hh * g.nb;
-  hipLaunchKernelGGL((k_attn_bwd_dkdv_pair<D, BLK>), dim3((k_items + 7) / 8 * 8), dim3(BLK * 4), 0, st, g, a,
-                     k_items, reinterpret_cast<const int32_t*>(ws + L.off_colptr),
+  hipLaunchKernelGGL((k_attn_bwd_dkdv_pair<D, BLK>), dim3(8 * xcd_items_cap(k_items)), dim3(BLK * 4), 0, st, g,
+                     a, k_items, kcuts, colptr,
                      reinterpret_cast<const int32_t*>(ws + L.off_rowidx), F32(L.off_dq), lse,
                      B16(L.off_ds_hi), B16(L.off_ds_lo), B16(L.off_dst_hi), B16(L.off_dst_lo), F32(L.off_dz),
                      c_log2);

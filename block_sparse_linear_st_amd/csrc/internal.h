@@ -74,6 +74,7 @@ struct Workspace {
   size_t off_spart, off_zpart;     // float [splits][B*H][D*D], [splits][B*H][D]
   size_t off_z;                    // float [B*H][D]
   size_t off_sft_hi, off_sft_lo;   // folded state, transposed: bf16 or f32 [B*H][D*D]
+  size_t off_split;                // int32 [9]: attention items per XCD
   size_t mask_end, lin_end;
 };
 
@@ -97,7 +98,24 @@ struct BwdWorkspace {
   size_t off_colcnt, off_colptr;      // int32 [BH*nb], [BH*nb + 1]
   size_t off_rowidx;                  // int32 [BH*nb*nb]
   size_t off_bits;                    // uint32 [BH*nb][ceil(nb/32)]: transposed mask bitmap
+  size_t off_split_q, off_split_k;    // int32 [9] each: dQ and dK/dV items per XCD
 };
+
+// ---- XCD assignment of attention items (sched.hip) ----------------------------
+// Item i of a job covers `per` consecutive rows of one of n_seq sequences of
+// nrows rows (the last item of a sequence may be short); ptr is the CSR or CSC
+// pointer array over the n_seq*nrows rows.  split[x] .. split[x+1]-1 are the
+// items XCD x runs, cut by estimated work (kept blocks * tpb + ovh per item),
+// each run at most xcd_items_cap(n_items) long: the consumer launches 8 times
+// that many workgroups.
+__host__ __device__ inline int xcd_items_cap(int n_items) { return (n_items + 7) / 8 + (n_items + 31) / 32; }
+struct ItemSplit {
+  const int32_t* ptr;  // pointer array over n_seq * nrows rows
+  int32_t* split;      // [9] output
+  int n_seq, nrows, per, tpb, ovh;
+};
+// One workgroup per job (one or two jobs per launch).
+SALAD_HIDDEN hipError_t launch_item_splits(const ItemSplit* jobs, int n_jobs, hipStream_t st);
 
 SALAD_HIDDEN bool make_geom(const salad_shape* s, Geom* g);
 SALAD_HIDDEN void make_cuboid(const salad_shape* s, Cuboid* c);
@@ -191,6 +209,7 @@ struct AttnArgs {
   const float* z;       // [BH][D]
   const float* gate;    // [BH] (branch dropping), may be null
   float* lse;           // [BH][n_pad] log2-sum-exp of the scaled scores (bf16 path), may be null
+  int32_t* split;       // [9] cuts of the item sequence per XCD (bf16 path; written before the launch)
   float drop_tau;
   float eps;
   float scale;

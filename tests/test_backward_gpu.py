@@ -232,3 +232,47 @@ def test_differentiable_layer_op_c2():
     for n, leaf in zip(("dq", "dk", "dv"), leaves[:3]):
         _check(to_numpy(leaf.grad)[:, :, :N], ref[n][:, :, :N], f"autograd c2 {n}")
     _check(leaves[3].grad.cpu().numpy(), ref["dgate"], "autograd c2 dgate", rel_l2=FP32_REL_L2)
+
+
+def test_skewed_heads_hand_built_mask():
+    """One dense head beside eleven diagonal-only heads, so that the run of work items each XCD takes is cut far
+    from equal counts and clamped at its longest: forward, its log2-sum-exp and both backward paths against the
+    oracle."""
+    print("skewed heads", flush=True)
+    from helpers import BF16_MAX_ABS, BF16_REL_L2, assert_close
+    cfg = LayerConfig(name="skew", seed=31, batch=1, heads=12, head_dim=64, T=8, H=16, W=16, block=64,
+                      dtype="bf16", specs=(HeadSpec(0, 1, -1, 0.0),) * 12, gate_kind="uniform")
+    nb = cfg.nb
+    keep = np.zeros((1, cfg.heads, nb, nb), bool)
+    keep[0, 0] = True
+    keep[0, 1:, np.arange(nb), np.arange(nb)] = True
+    rp, ci = oracle.csr_from_keep(keep)
+    inp = make_inputs(cfg)
+    layer = make_layer(cfg)
+    q, k, v, w = device_tensors(inp)
+    row_ptr = torch.from_numpy(rp).cuda()
+    col_idx = torch.from_numpy(ci).cuda()
+    gate = torch.from_numpy(inp.gate).cuda()
+    out = torch.empty_like(q)
+    lse = torch.full((cfg.heads * cfg.n_pad,), float("nan"), dtype=torch.float32, device="cuda")
+    S.salad_attn_fwd(layer.shape, q, k, v, row_ptr, col_idx, gate, w, cfg.eps, 0.0, 0.0, out, layer.ws, lse=lse)
+    torch.cuda.synchronize()
+    ref_out, _, _ = oracle.layer_forward(inp.q, inp.k, inp.v, rp, ci, inp.gate, inp.w_lin, cfg.N, cfg.block,
+                                         cfg.eps)
+    assert_close(to_numpy(out), ref_out, BF16_MAX_ABS, BF16_REL_L2, "skewed forward")
+    want = oracle.sparse_lse2(inp.q, inp.k, rp, ci, cfg.N, cfg.block)
+    got_lse = lse.view(1, cfg.heads, cfg.n_pad).cpu().numpy()
+    assert float(np.max(np.abs(got_lse[:, :, :cfg.N] - want[:, :, :cfg.N]))) <= 2e-2
+    dvals, dbits = make_grad_output(cfg)
+    dout = torch.from_numpy(dbits.view(np.int16)).view(torch.bfloat16).cuda()
+    ws = torch.empty(S.salad_bwd_workspace_bytes(layer.shape), dtype=torch.uint8, device="cuda")
+    ref = oracle.layer_backward(inp.q, inp.k, inp.v, rp, ci, inp.gate.astype(np.float64), inp.w_lin, cfg.N,
+                                cfg.block, cfg.eps, dvals)
+    for lse_arg, tag in ((lse, "forward lse"), (None, "recomputed lse")):
+        g = {n: torch.full_like(q, float("nan")) for n in ("dq", "dk", "dv")}
+        g["dw"] = torch.full((cfg.head_dim, cfg.head_dim), float("nan"), dtype=torch.float32, device="cuda")
+        g["dg"] = torch.full((cfg.heads,), float("nan"), dtype=torch.float32, device="cuda")
+        S.salad_attn_bwd(layer.shape, q, k, v, row_ptr, col_idx, gate, w, cfg.eps, 0.0, out, dout, g["dq"],
+                         g["dk"], g["dv"], g["dw"], g["dg"], ws, lse=lse_arg)
+        torch.cuda.synchronize()
+        _compare(cfg, g, ref, f"skewed ({tag})")
