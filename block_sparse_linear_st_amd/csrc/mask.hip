@@ -122,6 +122,68 @@ k_window_rstar_boxes(Geom g, int cap, const int32_t* __restrict__ nbox, const Bo
   }
 }
 
+// r* of one block pair in cuboid order, both box lists read from memory.
+__device__ inline int rstar_boxes_pair(int cap, const int32_t* __restrict__ nbox, const Box* __restrict__ boxes,
+                                       int qb, int kb, int tw) {
+  const int nq = nbox[qb], nk = nbox[kb];
+  int best = kRstarInf;
+  for (int j = 0; j < nk; ++j) {
+    const Box kx = boxes[(int64_t)kb * cap + j];
+    for (int i = 0; i < nq; ++i) {
+      const Box qx = boxes[(int64_t)qb * cap + i];
+      const int tgap = max(0, max(kx.ty.x - qx.ty.y, qx.ty.x - kx.ty.y));
+      if (tgap > tw) continue;
+      const int ygap = max(0, max(kx.ty.z - qx.ty.w, qx.ty.z - kx.ty.w));
+      const int xgap = max(0, max(kx.x.x - qx.x.y, qx.x.x - kx.x.y));
+      best = min(best, max(ygap, xgap));
+    }
+  }
+  return best;
+}
+
+// The same table, one workgroup per block offset d = kb - qb >= 0, in either
+// token order.  r* is symmetric in (qb, kb), so each pair is computed once and
+// written to both halves of the table; all pairs of one offset fall in the
+// rank bins 1 + r*·nb + d (bin 0 for d = 0), so the workgroup counts them per
+// r* in LDS and writes its column of the histogram with plain stores: every
+// bin is written, and no clearing pass or global atomics are needed.  Tables
+// whose r* range exceeds kMaxRankR use the kernels above.
+constexpr int kMaxRankR = 4096;
+
+template <bool BOXES>
+__global__ void __launch_bounds__(256)
+k_window_rstar_sym(Geom g, int tw, int rmax, uint16_t* rt, int32_t* hist, int cap, const int32_t* nbox,
+                   const Box* boxes) {
+  __shared__ int cnt[kMaxRankR];
+  const int d = blockIdx.x, t = threadIdx.x;
+  const int RB = max(g.H, g.W);  // r* < max(H, W)
+  if (hist)
+    for (int r = t; r < RB; r += blockDim.x) cnt[r] = 0;
+  __syncthreads();
+  for (int qb = t; qb + d < g.nb; qb += blockDim.x) {
+    const int kb = qb + d;
+    const int r = BOXES ? rstar_boxes_pair(cap, nbox, boxes, qb, kb, tw) : rstar_pair(g, qb, kb, tw);
+    const bool cand = window_candidate(r, rmax);
+    const uint16_t v = cand ? (uint16_t)r : kNoCand;
+    rt[(int64_t)qb * g.nb + kb] = v;
+    if (d > 0) rt[(int64_t)kb * g.nb + qb] = v;
+    if (cand && hist) atomicAdd(&cnt[r], d == 0 ? 1 : 2);
+  }
+  if (!hist) return;
+  __syncthreads();
+  if (d == 0) {
+    // diagonal pairs rank first (bin 0); bins 1 + r*·nb hold nothing
+    if (t == 0) {
+      int all = 0;
+      for (int r = 0; r < RB; ++r) all += cnt[r];
+      hist[0] = all;
+    }
+    for (int r = t; r < RB; r += blockDim.x) hist[1 + (int64_t)r * g.nb] = 0;
+  } else {
+    for (int r = t; r < RB; r += blockDim.x) hist[1 + (int64_t)r * g.nb + d] = cnt[r];
+  }
+}
+
 // Block-wide exclusive scan of one int64 per thread (kScanThreads threads):
 // shuffle scan inside each wave, then one wave scans the 16 wave totals.
 __device__ int64_t block_exclusive_scan(int64_t v, int64_t* tmp, int64_t* total) {
@@ -808,8 +870,17 @@ hipError_t launch_build_mask(const Geom& g, const Cuboid& cu, int dtype, const H
   const int32_t* nbox = reinterpret_cast<const int32_t*>(ws + L.off_nbox);
   const Box* boxes = reinterpret_cast<const Box*>(ws + L.off_boxes);
   if (cu.ct != 0 && cu.box_cap > kMaxBoxCap) return hipErrorInvalidValue;
+  // tables of moderate r* range come from the symmetric kernels, which also
+  // write every histogram bin (no clearing pass)
+  const bool sym = std::max(g.H, g.W) <= kMaxRankR;
   auto rstar = [&](int gi, int32_t* h) {
-    if (cu.ct == 0)
+    if (sym && cu.ct == 0)
+      hipLaunchKernelGGL(k_window_rstar_sym<false>, dim3(g.nb), dim3(256), 0, st, g, grp_tw[gi], grp_rmax[gi],
+                         rt, h, 0, nullptr, nullptr);
+    else if (sym)
+      hipLaunchKernelGGL(k_window_rstar_sym<true>, dim3(g.nb), dim3(256), 0, st, g, grp_tw[gi], grp_rmax[gi],
+                         rt, h, cu.box_cap, nbox, boxes);
+    else if (cu.ct == 0)
       hipLaunchKernelGGL(k_window_rstar, dim3(g.nb), dim3(256), 0, st, g, grp_tw[gi], grp_rmax[gi], rt, h);
     else
       hipLaunchKernelGGL(k_window_rstar_boxes, dim3(g.nb), dim3(256), 0, st, g, cu.box_cap, nbox, boxes,
@@ -823,8 +894,9 @@ hipError_t launch_build_mask(const Geom& g, const Cuboid& cu, int dtype, const H
   for (int gi = 0; gi < n_groups; ++gi) {
     int32_t* h_ptr = nullptr;
     if (grp_ranked[gi]) {
-      hipLaunchKernelGGL(k_fill_i32, dim3((unsigned)std::min<size_t>((L.hist_bins + 255) / 256, 4096)),
-                         dim3(256), 0, st, hist, (int64_t)L.hist_bins, 0);
+      if (!sym)
+        hipLaunchKernelGGL(k_fill_i32, dim3((unsigned)std::min<size_t>((L.hist_bins + 255) / 256, 4096)),
+                           dim3(256), 0, st, hist, (int64_t)L.hist_bins, 0);
       h_ptr = hist;
     }
     rstar(gi, h_ptr);
