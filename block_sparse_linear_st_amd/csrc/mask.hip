@@ -324,31 +324,33 @@ k_row_counts(Geom g, HeadTable ht, int grp, int topk, const uint16_t* rt, const 
 }
 
 // One workgroup: row_ptr = exclusive scan of the row counts; info = number of
-// infeasible window heads.
+// infeasible window heads (the head flags are read one per thread, beside the
+// row counts).
 __global__ void __launch_bounds__(kScanThreads)
 k_scan_rows(const int32_t* rowcnt, int64_t rows, int32_t* row_ptr, HeadTable ht,
             const int32_t* flags, int32_t* info) {
   __shared__ int64_t tmp[2 * kScanThreads / 64];
+  __shared__ int s_inf;
   const int t = threadIdx.x;
+  if (t == 0) s_inf = 0;
+  int inf = 0;
+  if (info && t < ht.n_heads && ht.kind[t] == SALAD_MASK_WINDOW) inf = flags[t];
   const int64_t seg = (rows + kScanThreads - 1) / kScanThreads;
   const int64_t lo = min((int64_t)t * seg, rows), hi = min(lo + seg, rows);
   int64_t local = 0;
 #pragma unroll 8
   for (int64_t r = lo; r < hi; ++r) local += rowcnt[r];
+  __syncthreads();  // s_inf is cleared
+  if (inf) atomicAdd(&s_inf, inf);
   int64_t total;
-  int64_t run = block_exclusive_scan(local, tmp, &total);
+  int64_t run = block_exclusive_scan(local, tmp, &total);  // its barriers also publish s_inf
   for (int64_t r = lo; r < hi; ++r) {
     row_ptr[r] = (int32_t)run;
     run += rowcnt[r];
   }
   if (t == 0) {
     row_ptr[rows] = (int32_t)total;
-    if (info) {
-      int n = 0;
-      for (int h = 0; h < ht.n_heads; ++h)
-        if (ht.kind[h] == SALAD_MASK_WINDOW) n += flags[h];
-      info[0] = n;
-    }
+    if (info) info[0] = s_inf;
   }
 }
 
