@@ -34,8 +34,8 @@ __global__ void __launch_bounds__(kSplitThreads) k_item_split(ItemSplit j0, Item
     return (int64_t)s * J.nrows + (int64_t)(i - s * groups) * J.per;
   };
   if (t < 8) s_cut[t] = n_items;
-  const int32_t p0 = J.ptr[0];
-  const int64_t total = (int64_t)(J.ptr[(int64_t)J.n_seq * J.nrows] - p0) * J.tpb + (int64_t)J.ovh * n_items;
+  const int64_t p0 = J.ptr[0];
+  const int64_t total = ((int64_t)J.ptr[(int64_t)J.n_seq * J.nrows] - p0) * J.tpb + (int64_t)J.ovh * n_items;
   __syncthreads();
   for (int base = 0; base <= n_items; base += kSplitBatch * kSplitThreads) {
     int32_t pc[kSplitBatch], pp[kSplitBatch];
@@ -49,8 +49,8 @@ __global__ void __launch_bounds__(kSplitThreads) k_item_split(ItemSplit j0, Item
     for (int k = 0; k < kSplitBatch; ++k) {
       const int i = base + k * kSplitThreads + t;
       if (i > n_items) break;
-      const int64_t c = (int64_t)(pc[k] - p0) * J.tpb + (int64_t)J.ovh * i;
-      const int64_t prev = i == 0 ? -1 : (int64_t)(pp[k] - p0) * J.tpb + (int64_t)J.ovh * (i - 1);
+      const int64_t c = ((int64_t)pc[k] - p0) * J.tpb + (int64_t)J.ovh * i;
+      const int64_t prev = i == 0 ? -1 : ((int64_t)pp[k] - p0) * J.tpb + (int64_t)J.ovh * (i - 1);
 #pragma unroll
       for (int x = 1; x < 8; ++x) {
         const int64_t target = total * x / 8;
