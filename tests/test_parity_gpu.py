@@ -409,3 +409,25 @@ def test_empty_and_hand_built_rows(dt):
     assert_close(to_numpy(o_s), ref_s, *tol, f"holes sparse {dt}")
     assert torch.count_nonzero(o_s[0, 0, 64:128]).item() == 0
     assert torch.count_nonzero(o_s[0, 1, :128]).item() == 0
+
+
+@pytest.mark.parametrize("cuboid", [(0, 0, 0), (1, 2, 32)], ids=["runs", "cuboids"])
+def test_window_mask_grid_wider_than_rank_range(cuboid):
+    """max(H, W) above 4096, beyond the symmetric r* kernel's rank range: the table and its histogram come from
+    the one-workgroup-per-query-block kernels instead (a cleared histogram and global atomics). Window heads only,
+    so the CSR depends on the geometry alone; bit-exact against the oracle in frame-major and cuboid order."""
+    print(f"wide grid {cuboid}", flush=True)
+    T, H, W, blk = 2, 2, 4200, 64
+    specs = (HeadSpec(0, 1, -1, 0.2), HeadSpec(0, 0, 40, 0.0))
+    cfg = LayerConfig(name="wide", seed=13, batch=1, heads=2, head_dim=64, T=T, H=H, W=W, block=blk, dtype="bf16",
+                      specs=specs, gate_kind="uniform", cuboid=cuboid)
+    layer = make_layer(cfg)
+    x = torch.zeros((1, 2, cfg.n_pad, 64), dtype=torch.bfloat16, device="cuda")
+    layer.build_mask(x, x)
+    torch.cuda.synchronize()
+    z = np.zeros((1, 2, cfg.N, 64))
+    order = None if cuboid == (0, 0, 0) else oracle.cuboid_order(T, H, W, cuboid)
+    rp, ci = oracle.csr_from_keep(oracle.build_masks(T, H, W, blk, specs, 1, z, z, order=order))
+    np.testing.assert_array_equal(layer.row_ptr.cpu().numpy(), rp)
+    np.testing.assert_array_equal(layer.col_idx[:rp[-1]].cpu().numpy(), ci)
+    assert int(layer.info.item()) == 0
