@@ -392,10 +392,12 @@ k_attn_bwd_dq2(Geom g, BwdArgs a, int n_items, const int32_t* __restrict__ cuts,
         ka = kn; va = vn;
       }
       bf16x8 kf = ktr(0, 2 * kt);
+      // key = key0 + 32 kt + crow(j, gg) < N, with the lane's part moved to the
+      // right-hand side so that each test compares a constant
+      const int klim = g.N - key0 - 32 * kt - 4 * gg;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const int key = key0 + 32 * kt + crow(j, gg);
-        const float p = key < g.N ? __builtin_amdgcn_exp2f(s[j] * c_log2 - lse) : 0.0f;
+        const float p = 8 * (j >> 2) + (j & 3) < klim ? __builtin_amdgcn_exp2f(s[j] * c_log2 - lse) : 0.0f;
         s[j] = p * (dp[j] - Dn);
       }
       // dQ^T += K^T dS^T over the 32 keys (two 16-key steps)
