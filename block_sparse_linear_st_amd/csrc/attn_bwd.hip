@@ -197,10 +197,11 @@ k_attn_bwd_dq(Geom g, BwdArgs a, const float* __restrict__ Dq, const float* __re
         for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
           for (int tt = 0; tt < NT; ++tt) kt_f[h2][tt] = frag_tr<D>(Kt, 2 * kt + h2, tt, lane);
+        // key0 + 32 kt + crow(j, gg) < N, tested against a per-lane limit
+        const int klim = g.N - key0 - 32 * kt - 4 * gg;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const int key = key0 + 32 * kt + crow(j, gg);
-          const float p = key < g.N ? __builtin_amdgcn_exp2f(s[j] * c_log2 - lse) : 0.0f;
+          const float p = 8 * (j >> 2) + (j & 3) < klim ? __builtin_amdgcn_exp2f(s[j] * c_log2 - lse) : 0.0f;
           s[j] = p * (dp[j] - Dn);
         }
 #pragma unroll
