@@ -57,15 +57,51 @@ int spec_status(const salad_shape* s, const salad_mask_spec* specs) {
   return SALAD_OK;
 }
 
-// K for a window head: floor(density * nb * nb + 0.5), -1 = keep every candidate.
-int64_t window_count(float density, int64_t nb) {
-  if (density <= 0.0f) return -1;
-  return (int64_t)std::floor((double)density * (double)nb * (double)nb + 0.5);
+int64_t topk_count(float density, int64_t nb) {
+  const double k = std::floor((double)density * (double)nb + 0.5);
+  if (!(k >= 1.0)) return 1;
+  return k >= (double)nb ? nb : (int64_t)k;
 }
 
-int64_t topk_count(float density, int64_t nb) {
-  int64_t k = (int64_t)std::floor((double)density * (double)nb + 0.5);
-  return std::min<int64_t>(std::max<int64_t>(k, 1), nb);
+// Per-head entry counts of one (b, h) (host).  count[h] receives the window K
+// (-1 = keep every candidate) or the top-k / SICS k; per[h] the CSR entries of
+// one (b, h): exact for window and top-k heads, the upper bound (m + 1) * nb for
+// SICS heads.  SALAD_EINFEASIBLE when a window head asks for more pairs than it
+// has candidates.
+int head_counts(const salad_shape* s, const salad_mask_spec* specs, int64_t* count, int64_t* per) {
+  Geom g;
+  make_geom(s, &g);
+  Cuboid cu;
+  make_cuboid(s, &cu);
+  const int64_t nb = g.nb;
+  // window heads sharing (t_window, r_max) share one candidate count
+  int64_t cand[SALAD_MAX_HEADS];
+  for (int h = 0; h < s->heads; ++h) {
+    const salad_mask_spec& sp = specs[h];
+    if (sp.kind == SALAD_MASK_WINDOW) {
+      cand[h] = -1;
+      for (int j = 0; j < h; ++j)
+        if (specs[j].kind == SALAD_MASK_WINDOW && specs[j].t_window == sp.t_window &&
+            specs[j].r_max == sp.r_max) {
+          cand[h] = cand[j];
+          break;
+        }
+      if (cand[h] < 0) cand[h] = window_candidates(g, cu, sp.t_window, sp.r_max);
+      if (sp.density <= 0.0f) {
+        count[h] = -1;
+        per[h] = cand[h];
+      } else {
+        // K = floor(density * nb^2 + 0.5), compared in double before any cast
+        const double K = std::floor((double)sp.density * (double)nb * (double)nb + 0.5);
+        if (K > (double)cand[h]) return SALAD_EINFEASIBLE;
+        count[h] = per[h] = (int64_t)K;
+      }
+    } else {
+      count[h] = topk_count(sp.density, nb);
+      per[h] = (sp.kind == SALAD_MASK_TOPK ? count[h] : std::min<int64_t>(count[h] + 1, nb)) * nb;
+    }
+  }
+  return SALAD_OK;
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? SALAD_OK : SALAD_EHIP; }
@@ -127,7 +163,6 @@ Workspace plan_workspace(const Geom& g, const Cuboid& cu, int dtype) {
   L.off_rt = off;     off = align_up(off + nb * nb * 2);
   L.off_hist = off;   off = align_up(off + L.hist_bins * 4);
   L.off_thr = off;    off = align_up(off + (size_t)g.Hh * 8);
-  L.off_flags = off;  off = align_up(off + (size_t)g.Hh * 4);
   L.off_rowcnt = off; off = align_up(off + BH * nb * 4);
   L.off_psum_q = off; off = align_up(off + BH * nb * D * 4);
   L.off_psum_k = off; off = align_up(off + BH * nb * D * 4);
@@ -191,26 +226,16 @@ const char* salad_status_str(int status) {
   }
 }
 
-int64_t salad_mask_nnz_max(const salad_shape* shape, const salad_mask_spec* specs) {
+int64_t salad_mask_nnz(const salad_shape* shape, const salad_mask_spec* specs) {
   int st = shape_status(shape);
   if (st != SALAD_OK) return st;
   st = spec_status(shape, specs);
   if (st != SALAD_OK) return st;
-  const int64_t nb = shape->n_pad / shape->block;
+  int64_t count[SALAD_MAX_HEADS], per[SALAD_MAX_HEADS];
+  st = head_counts(shape, specs, count, per);
+  if (st != SALAD_OK) return st;
   int64_t total = 0;
-  for (int h = 0; h < shape->heads; ++h) {
-    const salad_mask_spec& sp = specs[h];
-    int64_t per;
-    if (sp.kind == SALAD_MASK_WINDOW) {
-      const int64_t K = window_count(sp.density, nb);
-      per = K < 0 ? nb * nb : std::min(K, nb * nb);
-    } else if (sp.kind == SALAD_MASK_TOPK) {
-      per = topk_count(sp.density, nb) * nb;
-    } else {  // SICS: m kept blocks plus the diagonal when it is not among them
-      per = std::min<int64_t>(topk_count(sp.density, nb) + 1, nb) * nb;
-    }
-    total += per * shape->batch;
-  }
+  for (int h = 0; h < shape->heads; ++h) total += per[h] * shape->batch;
   return total;
 }
 
@@ -222,8 +247,7 @@ size_t salad_workspace_bytes(const salad_shape* shape) {
 
 int salad_build_mask(const salad_shape* shape, const salad_mask_spec* specs, const void* q,
                      const void* k, int32_t* row_ptr, int32_t* col_idx, int64_t col_cap,
-                     int32_t* info, const float* w_g, float* gate, void* ws, size_t ws_bytes,
-                     void* stream) {
+                     const float* w_g, float* gate, void* ws, size_t ws_bytes, void* stream) {
   Geom g;
   int st = shape_status(shape);
   if (st != SALAD_OK) return st;
@@ -243,8 +267,12 @@ int salad_build_mask(const salad_shape* shape, const salad_mask_spec* specs, con
   if (!aligned16(ws)) return SALAD_EINVAL;
   const Workspace L = plan_for(shape, g);
   if (ws_bytes < L.bytes) return SALAD_ENOSPACE;
-  const int64_t need = salad_mask_nnz_max(shape, specs);
-  if (need < 0) return (int)need;
+  int64_t count[SALAD_MAX_HEADS], per[SALAD_MAX_HEADS];
+  st = head_counts(shape, specs, count, per);
+  if (st != SALAD_OK) return st;
+  int64_t need = 0;
+  for (int h = 0; h < g.Hh; ++h) need += per[h] * g.B;
+  if (need > INT32_MAX) return SALAD_EUNSUPPORTED;  // row_ptr is int32
   if (col_cap < need) return SALAD_ENOSPACE;
   HeadTable ht{};
   ht.n_heads = g.Hh;
@@ -252,14 +280,23 @@ int salad_build_mask(const salad_shape* shape, const salad_mask_spec* specs, con
     ht.kind[h] = specs[h].kind;
     ht.t_window[h] = specs[h].t_window;
     ht.r_max[h] = specs[h].r_max;
-    ht.count[h] = (int)(specs[h].kind == SALAD_MASK_WINDOW ? window_count(specs[h].density, g.nb)
-                                                           : topk_count(specs[h].density, g.nb));
+    ht.count[h] = (int)count[h];  // <= nb * nb < 2^31, or -1
   }
   Cuboid cu;
   make_cuboid(shape, &cu);
-  return hip_status(launch_build_mask(g, cu, shape->dtype, ht, q, k, row_ptr, col_idx, col_cap, info,
-                                      w_g, gate, static_cast<char*>(ws), L,
+  return hip_status(launch_build_mask(g, cu, shape->dtype, ht, q, k, row_ptr, col_idx, col_cap, w_g,
+                                      gate, static_cast<char*>(ws), L,
                                       static_cast<hipStream_t>(stream)));
+}
+
+int salad_check_mask(const salad_shape* shape, const int32_t* row_ptr, const int32_t* col_idx,
+                     int64_t col_cap, int32_t* result, void* stream) {
+  Geom g;
+  const int st = shape_status(shape);
+  if (st != SALAD_OK) return st;
+  if (!row_ptr || !result || col_cap < 0 || (col_cap > 0 && !col_idx)) return SALAD_EINVAL;
+  make_geom(shape, &g);
+  return hip_status(launch_check_mask(g, row_ptr, col_idx, col_cap, result, static_cast<hipStream_t>(stream)));
 }
 
 int salad_token_order(const salad_shape* shape, int32_t* order) {

@@ -63,7 +63,6 @@ struct Workspace {
   size_t off_rt;                   // uint16 [nb][nb]: r* of one window group (0xffff = no candidate)
   size_t off_hist, hist_bins;      // int32 [hist_bins]: that group's candidates per rank bin
   size_t off_thr;                  // int64 [heads] threshold keys
-  size_t off_flags;                // int32 [heads] infeasible flags
   size_t off_rowcnt;               // int32 [B*H*nb]
   size_t off_psum_q, off_psum_k;   // float [B*H*nb*D]
   size_t off_scores;               // float [heads per batch][nb][nb] (top-k scores)
@@ -133,9 +132,15 @@ SALAD_HIDDEN hipError_t launch_block_boxes(const Geom& g, const Cuboid& cu, char
 SALAD_HIDDEN hipError_t launch_build_mask(const Geom& g, const Cuboid& cu, int dtype,
                                           const HeadTable& ht,
                                           const void* q, const void* k, int32_t* row_ptr,
-                                          int32_t* col_idx, int64_t col_cap, int32_t* info,
+                                          int32_t* col_idx, int64_t col_cap,
                                           const float* w_g, float* gate, char* ws,
                                           const Workspace& L, hipStream_t st);
+// Number of candidate (qb, kb) pairs of a window head with this t_window and
+// r_max (window_count.hip, host only).
+SALAD_HIDDEN int64_t window_candidates(const Geom& g, const Cuboid& cu, int t_window, int r_max);
+// CSR structure check (check.hip): writes the SALAD_MASK_BAD_* bits to out[0].
+SALAD_HIDDEN hipError_t launch_check_mask(const Geom& g, const int32_t* row_ptr, const int32_t* col_idx,
+                                          int64_t col_cap, int32_t* out, hipStream_t st);
 SALAD_HIDDEN hipError_t launch_gate_from_q(const Geom& g, int dtype, const void* q,
                                            const float* w_g, float* gate, char* ws,
                                            const Workspace& L, hipStream_t st);

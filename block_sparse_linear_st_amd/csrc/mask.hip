@@ -222,18 +222,18 @@ __device__ inline int64_t rt_key(const uint16_t* rt, const Geom& g, int qb, int 
 // group `grp` (its r* table and histogram are current).
 __global__ void __launch_bounds__(kScanThreads)
 k_window_threshold(Geom g, HeadTable ht, int grp, const uint16_t* rt, const int32_t* hist,
-                   int64_t hist_bins, int64_t* thr, int32_t* flags) {
+                   int64_t hist_bins, int64_t* thr) {
   __shared__ int64_t tmp[2 * kScanThreads / 64];
   __shared__ int64_t s_bin, s_need;
   const int h = blockIdx.x, t = threadIdx.x;
   if (ht.kind[h] != SALAD_MASK_WINDOW || ht.group[h] != grp) return;
   const int64_t K = ht.count[h];
   if (K < 0) {  // keep every candidate
-    if (t == 0) { thr[h] = INT64_MAX; flags[h] = 0; }
+    if (t == 0) thr[h] = INT64_MAX;
     return;
   }
   if (K == 0) {
-    if (t == 0) { thr[h] = -1; flags[h] = 0; }
+    if (t == 0) thr[h] = -1;
     return;
   }
   // 1) the bin that holds the K-th pair (segments of whole int4s, loads batched)
@@ -244,8 +244,8 @@ k_window_threshold(Geom g, HeadTable ht, int grp, const uint16_t* rt, const int3
   for (int64_t b = lo; b < hi; ++b) local += hist[b];
   int64_t total;
   const int64_t excl = block_exclusive_scan(local, tmp, &total);
-  if (total < K) {  // infeasible: keep all candidates and report it
-    if (t == 0) { thr[h] = INT64_MAX; flags[h] = 1; }
+  if (total < K) {  // not reached: the host rejects K above the candidate count
+    if (t == 0) thr[h] = INT64_MAX;
     return;
   }
   if (excl < K && K <= excl + local) {
@@ -284,7 +284,6 @@ k_window_threshold(Geom g, HeadTable ht, int grp, const uint16_t* rt, const int3
         else if (rem == 1) kb = lo_in ? qb - dd : qb + dd;
         else kb = qb + dd;
         thr[h] = pair_key(bin, qb, kb, g.nb);
-        flags[h] = 0;
         break;
       }
       cum += c;
@@ -323,35 +322,23 @@ k_row_counts(Geom g, HeadTable ht, int grp, int topk, const uint16_t* rt, const 
     for (int b = 0; b < g.B; ++b) rowcnt[((int64_t)b * g.Hh + h) * g.nb + qb] = cnt;
 }
 
-// One workgroup: row_ptr = exclusive scan of the row counts; info = number of
-// infeasible window heads (the head flags are read one per thread, beside the
-// row counts).
+// One workgroup: row_ptr = exclusive scan of the row counts.
 __global__ void __launch_bounds__(kScanThreads)
-k_scan_rows(const int32_t* rowcnt, int64_t rows, int32_t* row_ptr, HeadTable ht,
-            const int32_t* flags, int32_t* info) {
+k_scan_rows(const int32_t* rowcnt, int64_t rows, int32_t* row_ptr) {
   __shared__ int64_t tmp[2 * kScanThreads / 64];
-  __shared__ int s_inf;
   const int t = threadIdx.x;
-  if (t == 0) s_inf = 0;
-  int inf = 0;
-  if (info && t < ht.n_heads && ht.kind[t] == SALAD_MASK_WINDOW) inf = flags[t];
   const int64_t seg = (rows + kScanThreads - 1) / kScanThreads;
   const int64_t lo = min((int64_t)t * seg, rows), hi = min(lo + seg, rows);
   int64_t local = 0;
 #pragma unroll 8
   for (int64_t r = lo; r < hi; ++r) local += rowcnt[r];
-  __syncthreads();  // s_inf is cleared
-  if (inf) atomicAdd(&s_inf, inf);
   int64_t total;
-  int64_t run = block_exclusive_scan(local, tmp, &total);  // its barriers also publish s_inf
+  int64_t run = block_exclusive_scan(local, tmp, &total);
   for (int64_t r = lo; r < hi; ++r) {
     row_ptr[r] = (int32_t)run;
     run += rowcnt[r];
   }
-  if (t == 0) {
-    row_ptr[rows] = (int32_t)total;
-    if (info) info[0] = s_inf;
-  }
+  if (t == 0) row_ptr[rows] = (int32_t)total;
 }
 
 // grid (nb, heads), one wave: kept key blocks of the window rows of group `grp`, ascending.
@@ -826,7 +813,7 @@ hipError_t launch_topk(const Geom& g, const HeadTable& ht, const float* pq, cons
 hipError_t launch_build_mask(const Geom& g, const Cuboid& cu, int dtype, const HeadTable& ht0,
                              const void* q,
                              const void* k, int32_t* row_ptr, int32_t* col_idx, int64_t col_cap,
-                             int32_t* info, const float* w_g, float* gate, char* ws,
+                             const float* w_g, float* gate, char* ws,
                              const Workspace& L, hipStream_t st) {
   HeadTable ht = ht0;
   bool any_topk = false, any_sics = false;
@@ -859,7 +846,6 @@ hipError_t launch_build_mask(const Geom& g, const Cuboid& cu, int dtype, const H
   uint16_t* rt = reinterpret_cast<uint16_t*>(ws + L.off_rt);
   int32_t* hist = reinterpret_cast<int32_t*>(ws + L.off_hist);
   int64_t* thr = reinterpret_cast<int64_t*>(ws + L.off_thr);
-  int32_t* flags = reinterpret_cast<int32_t*>(ws + L.off_flags);
   int32_t* rowcnt = reinterpret_cast<int32_t*>(ws + L.off_rowcnt);
   float* psq = reinterpret_cast<float*>(ws + L.off_psum_q);
   float* psk = reinterpret_cast<float*>(ws + L.off_psum_k);
@@ -903,7 +889,7 @@ hipError_t launch_build_mask(const Geom& g, const Cuboid& cu, int dtype, const H
     }
     rstar(gi, h_ptr);
     hipLaunchKernelGGL(k_window_threshold, dim3(g.Hh), dim3(kScanThreads), 0, st, g, ht, gi, rt, hist,
-                       (int64_t)L.hist_bins, thr, flags);
+                       (int64_t)L.hist_bins, thr);
     hipLaunchKernelGGL(k_row_counts, dim3(g.nb, g.Hh), dim3(64), 0, st, g, ht, gi,
                        (int)(any_topk && gi == 0), rt, thr, rowcnt);
   }
@@ -924,8 +910,7 @@ hipError_t launch_build_mask(const Geom& g, const Cuboid& cu, int dtype, const H
     hipLaunchKernelGGL(k_sics_counts, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, g, ht, pack,
                        rowcnt);
   }
-  hipLaunchKernelGGL(k_scan_rows, dim3(1), dim3(kScanThreads), 0, st, rowcnt, rows, row_ptr, ht, flags,
-                     info);
+  hipLaunchKernelGGL(k_scan_rows, dim3(1), dim3(kScanThreads), 0, st, rowcnt, rows, row_ptr);
   if (any_sics)
     hipLaunchKernelGGL(k_sics_emit, dim3(g.nb, g.B * g.Hh), dim3(64), 0, st, g, ht, pack, row_ptr, col_idx,
                        col_cap);

@@ -31,9 +31,8 @@ class SaladLayer:
             raise S.SaladError(S.SALAD_EINVAL, "invalid or unsupported layer shape")
         self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=self.device)
         self.row_ptr = torch.empty(batch * heads * self.nb + 1, dtype=torch.int32, device=self.device)
-        self.col_idx = torch.empty(max(1, S.salad_mask_nnz_max(self.shape, self.specs)), dtype=torch.int32,
+        self.col_idx = torch.empty(max(1, S.salad_mask_nnz(self.shape, self.specs)), dtype=torch.int32,
                                    device=self.device)
-        self.info = torch.zeros(1, dtype=torch.int32, device=self.device)
 
     def tensor_shape(self):
         s = self.shape
@@ -51,8 +50,7 @@ class SaladLayer:
 
     def build_mask(self, q: Optional[torch.Tensor] = None, k: Optional[torch.Tensor] = None,
                    w_g: Optional[torch.Tensor] = None, gate: Optional[torch.Tensor] = None, stream=None):
-        S.salad_build_mask(self.shape, self.specs, q, k, self.row_ptr, self.col_idx, self.info, w_g, gate,
-                           self.ws, stream)
+        S.salad_build_mask(self.shape, self.specs, q, k, self.row_ptr, self.col_idx, w_g, gate, self.ws, stream)
 
     def gate_from_q(self, q, w_g, gate, stream=None):
         S.salad_gate_from_q(self.shape, q, w_g, gate, self.ws, stream)
@@ -71,10 +69,13 @@ class SaladLayer:
                                   out_lin, self.ws, stream)
 
     def backward(self, q, k, v, gate, w_lin, out, dout, dq, dk, dv, dw_lin, dgate, eps: float = 1e-6,
-                 scale: float = 0.0, lse=None, stream=None):
-        """Gradients of the layer (salad_attn_bwd) into caller buffers; the backward workspace is owned here."""
+                 scale: float = 0.0, lse=None, stream=None, row_ptr=None, col_idx=None):
+        """Gradients of the layer (salad_attn_bwd) into caller buffers; the backward workspace is owned here.
+        The mask is the layer's current one unless the forward's (row_ptr, col_idx) are given."""
         ws = self.backward_workspace()
-        S.salad_attn_bwd(self.shape, q, k, v, self.row_ptr, self.col_idx, gate, w_lin, eps, scale, out, dout,
+        rp = self.row_ptr if row_ptr is None else row_ptr
+        ci = self.col_idx if col_idx is None else col_idx
+        S.salad_attn_bwd(self.shape, q, k, v, rp, ci, gate, w_lin, eps, scale, out, dout,
                          dq, dk, dv, dw_lin, dgate, ws, stream, lse=lse)
 
     def backward_workspace(self) -> torch.Tensor:
@@ -87,7 +88,8 @@ class SaladLayer:
 
     def attention(self, q, k, v, gate, w_lin, eps: float = 1e-6, scale: float = 0.0):
         """out = layer(q, k, v, gate, w_lin) as a differentiable torch op (bf16 layers) over the mask the last
-        build_mask call made; the backward gives dq, dk, dv, dgate and dW_lin (cast to W_lin's dtype)."""
+        build_mask call made; the backward gives dq, dk, dv, dgate and dW_lin (cast to W_lin's dtype) over that
+        same mask, even if build_mask runs again before the backward (the op keeps a copy of the CSR)."""
         return _SaladAttention.apply(self, q, k, v, gate, w_lin, eps, scale)
 
 
@@ -106,13 +108,16 @@ class _SaladAttention(torch.autograd.Function):
         lse = torch.empty(s.batch * s.heads * s.n_pad, dtype=torch.float32, device=q.device)
         layer.forward(q, k, v, gate, w_lin, out, eps=eps, scale=scale, lse=lse,
                       stream=torch.cuda.current_stream().cuda_stream)
-        ctx.save_for_backward(q, k, v, gate, w_lin, out, lse)
+        # the mask this forward used: a later build_mask on the layer must not change the backward's
+        nnz = layer.col_idx.numel()
+        row_ptr, col_idx = layer.row_ptr.clone(), layer.col_idx[:nnz].clone()
+        ctx.save_for_backward(q, k, v, gate, w_lin, out, lse, row_ptr, col_idx)
         ctx.layer, ctx.eps, ctx.scale = layer, eps, scale
         return out
 
     @staticmethod
     def backward(ctx, dout):
-        q, k, v, gate, w_lin, out, lse = ctx.saved_tensors
+        q, k, v, gate, w_lin, out, lse, row_ptr, col_idx = ctx.saved_tensors
         layer = ctx.layer
         dout = dout.to(torch.bfloat16).contiguous()
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -120,5 +125,5 @@ class _SaladAttention(torch.autograd.Function):
         dw = torch.empty((d, d), dtype=torch.float32, device=q.device)
         dg = torch.empty(gate.numel(), dtype=torch.float32, device=q.device)
         layer.backward(q, k, v, gate, w_lin, out, dout, dq, dk, dv, dw, dg, eps=ctx.eps, scale=ctx.scale,
-                       lse=lse, stream=torch.cuda.current_stream().cuda_stream)
+                       lse=lse, stream=torch.cuda.current_stream().cuda_stream, row_ptr=row_ptr, col_idx=col_idx)
         return None, dq, dk, dv, dg.view_as(gate).to(gate.dtype), dw.to(w_lin.dtype), None, None

@@ -29,6 +29,10 @@ SALAD_BF16 = 1
 SALAD_MASK_WINDOW = 0
 SALAD_MASK_TOPK = 1
 SALAD_MASK_SICS = 2
+SALAD_MASK_BAD_START = 1
+SALAD_MASK_BAD_ROW_PTR = 2
+SALAD_MASK_BAD_COL = 4
+SALAD_MASK_BAD_ORDER = 8
 
 
 class SaladError(RuntimeError):
@@ -57,14 +61,15 @@ _f = ctypes.c_float
 _SIGS = {
     "salad_version": (ctypes.c_int, []),
     "salad_status_str": (ctypes.c_char_p, [ctypes.c_int]),
-    "salad_mask_nnz_max": (_i64, [ctypes.POINTER(salad_shape), ctypes.POINTER(salad_mask_spec)]),
+    "salad_mask_nnz": (_i64, [ctypes.POINTER(salad_shape), ctypes.POINTER(salad_mask_spec)]),
     "salad_workspace_bytes": (_sz, [ctypes.POINTER(salad_shape)]),
     "salad_build_mask": (ctypes.c_int, [ctypes.POINTER(salad_shape), ctypes.POINTER(salad_mask_spec),
-                                        _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
+                                        _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
     "salad_bwd_workspace_bytes": (_sz, [ctypes.POINTER(salad_shape)]),
     "salad_attn_bwd": (ctypes.c_int, [ctypes.POINTER(salad_shape), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f, _f,
                                       _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "salad_token_order": (ctypes.c_int, [ctypes.POINTER(salad_shape), _vp]),
+    "salad_check_mask": (ctypes.c_int, [ctypes.POINTER(salad_shape), _vp, _vp, _i64, _vp, _vp]),
     "salad_permute_tokens": (ctypes.c_int, [ctypes.POINTER(salad_shape), ctypes.c_int, _vp, _vp, _vp]),
     "salad_gate_from_q": (ctypes.c_int, [ctypes.POINTER(salad_shape), _vp, _vp, _vp, _vp, _sz, _vp]),
     "salad_linear_state": (ctypes.c_int, [ctypes.POINTER(salad_shape), _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -131,6 +136,38 @@ def _p(t) -> Optional[int]:
     return t.data_ptr()
 
 
+def _torch_dtype(code):
+    import torch
+    return {"f32": torch.float32, "bf16": torch.bfloat16, "i32": torch.int32, "u8": torch.uint8}[code]
+
+
+def _t(t, dtype, numel, what: str, optional: bool = False) -> Optional[int]:
+    """Data pointer of a contiguous device tensor after checking its dtype and element count.
+
+    dtype: "f32", "bf16", "i32", "u8", or a salad_dtype code (the layer's dtype); numel: the exact count
+    the C function reads or writes, or (lo,) for a lower bound."""
+    if t is None:
+        if optional:
+            return None
+        raise SaladError(SALAD_EINVAL, f"{what}: a tensor is required")
+    want = _torch_dtype(("f32", "bf16")[dtype] if isinstance(dtype, int) else dtype)
+    if t.dtype != want:
+        raise SaladError(SALAD_EINVAL, f"{what}: dtype {t.dtype}, expected {want}")
+    n = t.numel()
+    if isinstance(numel, tuple):
+        if n < numel[0]:
+            raise SaladError(SALAD_EINVAL, f"{what}: {n} elements, at least {numel[0]} needed")
+    elif n != numel:
+        raise SaladError(SALAD_EINVAL, f"{what}: {n} elements, expected {numel}")
+    return _p(t)
+
+
+def _sizes(shape: salad_shape):
+    """(elements of a [B, H, n_pad, d] tensor, B*H, rows of the CSR + 1, d*d)."""
+    bh = shape.batch * shape.heads
+    return bh * shape.n_pad * shape.head_dim, bh, bh * (shape.n_pad // shape.block) + 1, shape.head_dim ** 2
+
+
 def _stream(stream) -> Optional[int]:
     if stream is not None:
         return stream
@@ -148,10 +185,10 @@ def salad_status_str(status: int) -> str:
     return lib().salad_status_str(status).decode()
 
 
-def salad_mask_nnz_max(shape: salad_shape, specs) -> int:
-    n = lib().salad_mask_nnz_max(ctypes.byref(shape), specs)
+def salad_mask_nnz(shape: salad_shape, specs) -> int:
+    n = lib().salad_mask_nnz(ctypes.byref(shape), specs)
     if n < 0:
-        _check(int(n), "salad_mask_nnz_max")
+        _check(int(n), "salad_mask_nnz")
     return int(n)
 
 
@@ -159,12 +196,23 @@ def salad_workspace_bytes(shape: salad_shape) -> int:
     return int(lib().salad_workspace_bytes(ctypes.byref(shape)))
 
 
-def salad_build_mask(shape, specs, q, k, row_ptr, col_idx, info=None, w_g=None, gate=None,
-                     ws=None, stream=None):
-    st = lib().salad_build_mask(ctypes.byref(shape), specs, _p(q), _p(k), _p(row_ptr), _p(col_idx),
-                                col_idx.numel(), _p(info), _p(w_g), _p(gate), _p(ws),
-                                ws.numel() if ws is not None else 0, _stream(stream))
+def salad_build_mask(shape, specs, q, k, row_ptr, col_idx, w_g=None, gate=None, ws=None, stream=None):
+    nt, bh, nrp, _ = _sizes(shape)
+    dt = shape.dtype
+    st = lib().salad_build_mask(ctypes.byref(shape), specs, _t(q, dt, nt, "q", True), _t(k, dt, nt, "k", True),
+                                _t(row_ptr, "i32", nrp, "row_ptr"), _t(col_idx, "i32", (1,), "col_idx"),
+                                col_idx.numel(), _t(w_g, "f32", shape.head_dim, "w_g", True),
+                                _t(gate, "f32", bh, "gate", True), _t(ws, "u8", (1,), "ws"),
+                                ws.numel(), _stream(stream))
     _check(st, "salad_build_mask")
+
+
+def salad_check_mask(shape, row_ptr, col_idx, result, stream=None):
+    """Enqueue the CSR check; result (device int32 [1]) receives 0 or the SALAD_MASK_BAD_* bits."""
+    nrp = _sizes(shape)[2]
+    _check(lib().salad_check_mask(ctypes.byref(shape), _t(row_ptr, "i32", nrp, "row_ptr"),
+                                  _t(col_idx, "i32", (0,), "col_idx"), col_idx.numel(),
+                                  _t(result, "i32", 1, "result"), _stream(stream)), "salad_check_mask")
 
 
 def salad_token_order(shape: salad_shape):
@@ -176,44 +224,65 @@ def salad_token_order(shape: salad_shape):
 
 
 def salad_permute_tokens(shape, inverse, src, dst, stream=None):
-    _check(lib().salad_permute_tokens(ctypes.byref(shape), int(inverse), _p(src), _p(dst), _stream(stream)),
-           "salad_permute_tokens")
+    nt = _sizes(shape)[0]
+    _check(lib().salad_permute_tokens(ctypes.byref(shape), int(inverse), _t(src, shape.dtype, nt, "src"),
+                                      _t(dst, shape.dtype, nt, "dst"), _stream(stream)), "salad_permute_tokens")
 
 
 def salad_gate_from_q(shape, q, w_g, gate, ws, stream=None):
-    _check(lib().salad_gate_from_q(ctypes.byref(shape), _p(q), _p(w_g), _p(gate), _p(ws), ws.numel(),
-                                   _stream(stream)), "salad_gate_from_q")
+    nt, bh, _, _ = _sizes(shape)
+    _check(lib().salad_gate_from_q(ctypes.byref(shape), _t(q, shape.dtype, nt, "q"),
+                                   _t(w_g, "f32", shape.head_dim, "w_g"), _t(gate, "f32", bh, "gate"),
+                                   _t(ws, "u8", (1,), "ws"), ws.numel(), _stream(stream)), "salad_gate_from_q")
 
 
 def salad_linear_state(shape, k, v, S, z, ws, stream=None):
-    _check(lib().salad_linear_state(ctypes.byref(shape), _p(k), _p(v), _p(S), _p(z), _p(ws), ws.numel(),
-                                    _stream(stream)), "salad_linear_state")
+    nt, bh, _, dd = _sizes(shape)
+    _check(lib().salad_linear_state(ctypes.byref(shape), _t(k, shape.dtype, nt, "k"), _t(v, shape.dtype, nt, "v"),
+                                    _t(S, "f32", bh * dd, "S"), _t(z, "f32", bh * shape.head_dim, "z"),
+                                    _t(ws, "u8", (1,), "ws"), ws.numel(), _stream(stream)), "salad_linear_state")
+
+
+def _qkv_csr(shape, q, k, v, row_ptr, col_idx):
+    nt, _, nrp, _ = _sizes(shape)
+    dt = shape.dtype
+    return (_t(q, dt, nt, "q"), _t(k, dt, nt, "k"), _t(v, dt, nt, "v"), _t(row_ptr, "i32", nrp, "row_ptr"),
+            _t(col_idx, "i32", (1,), "col_idx"))
 
 
 def salad_attn_fwd(shape, q, k, v, row_ptr, col_idx, gate, w_lin, eps, scale, drop_tau, out, ws,
                    stream=None, lse=None):
-    _check(lib().salad_attn_fwd(ctypes.byref(shape), _p(q), _p(k), _p(v), _p(row_ptr), _p(col_idx),
-                                _p(gate), _p(w_lin), eps, scale, drop_tau, _p(out), _p(lse), _p(ws), ws.numel(),
-                                _stream(stream)), "salad_attn_fwd")
+    nt, bh, _, dd = _sizes(shape)
+    _check(lib().salad_attn_fwd(ctypes.byref(shape), *_qkv_csr(shape, q, k, v, row_ptr, col_idx),
+                                _t(gate, "f32", bh, "gate"), _t(w_lin, shape.dtype, dd, "w_lin"), eps, scale,
+                                drop_tau, _t(out, shape.dtype, nt, "out"),
+                                _t(lse, "f32", bh * shape.n_pad, "lse", True), _t(ws, "u8", (1,), "ws"),
+                                ws.numel(), _stream(stream)), "salad_attn_fwd")
 
 
 def salad_attn_fwd_branches(shape, q, k, v, row_ptr, col_idx, eps, scale, out_sparse, out_lin, ws,
                             stream=None):
-    _check(lib().salad_attn_fwd_branches(ctypes.byref(shape), _p(q), _p(k), _p(v), _p(row_ptr),
-                                         _p(col_idx), eps, scale, _p(out_sparse), _p(out_lin), _p(ws),
+    nt = _sizes(shape)[0]
+    _check(lib().salad_attn_fwd_branches(ctypes.byref(shape), *_qkv_csr(shape, q, k, v, row_ptr, col_idx), eps,
+                                         scale, _t(out_sparse, shape.dtype, nt, "out_sparse", True),
+                                         _t(out_lin, shape.dtype, nt, "out_lin", True), _t(ws, "u8", (1,), "ws"),
                                          ws.numel(), _stream(stream)), "salad_attn_fwd_branches")
 
 
 def salad_linear_prepare(shape, k, v, gate, w_lin, ws, stream=None, drop_tau=0.0):
-    _check(lib().salad_linear_prepare(ctypes.byref(shape), _p(k), _p(v), _p(gate), _p(w_lin), drop_tau,
-                                      _p(ws), ws.numel(), _stream(stream)), "salad_linear_prepare")
+    nt, bh, _, dd = _sizes(shape)
+    _check(lib().salad_linear_prepare(ctypes.byref(shape), _t(k, shape.dtype, nt, "k"), _t(v, shape.dtype, nt, "v"),
+                                      _t(gate, "f32", bh, "gate"), _t(w_lin, shape.dtype, dd, "w_lin"), drop_tau,
+                                      _t(ws, "u8", (1,), "ws"), ws.numel(), _stream(stream)), "salad_linear_prepare")
 
 
 def salad_attn_apply(shape, q, k, v, row_ptr, col_idx, gate, eps, scale, drop_tau, out, ws, stream=None,
                      lse=None):
-    _check(lib().salad_attn_apply(ctypes.byref(shape), _p(q), _p(k), _p(v), _p(row_ptr), _p(col_idx),
-                                  _p(gate), eps, scale, drop_tau, _p(out), _p(lse), _p(ws), ws.numel(),
-                                  _stream(stream)), "salad_attn_apply")
+    nt, bh, _, _ = _sizes(shape)
+    _check(lib().salad_attn_apply(ctypes.byref(shape), *_qkv_csr(shape, q, k, v, row_ptr, col_idx),
+                                  _t(gate, "f32", bh, "gate"), eps, scale, drop_tau, _t(out, shape.dtype, nt, "out"),
+                                  _t(lse, "f32", bh * shape.n_pad, "lse", True), _t(ws, "u8", (1,), "ws"),
+                                  ws.numel(), _stream(stream)), "salad_attn_apply")
 
 
 def salad_bwd_workspace_bytes(shape: salad_shape) -> int:
@@ -222,6 +291,11 @@ def salad_bwd_workspace_bytes(shape: salad_shape) -> int:
 
 def salad_attn_bwd(shape, q, k, v, row_ptr, col_idx, gate, w_lin, eps, scale, out, dout, dq, dk, dv, dw_lin,
                    dgate, ws, stream=None, lse=None):
-    _check(lib().salad_attn_bwd(ctypes.byref(shape), _p(q), _p(k), _p(v), _p(row_ptr), _p(col_idx), _p(gate),
-                                _p(w_lin), eps, scale, _p(out), _p(lse), _p(dout), _p(dq), _p(dk), _p(dv),
-                                _p(dw_lin), _p(dgate), _p(ws), ws.numel(), _stream(stream)), "salad_attn_bwd")
+    nt, bh, _, dd = _sizes(shape)
+    dt = shape.dtype
+    _check(lib().salad_attn_bwd(ctypes.byref(shape), *_qkv_csr(shape, q, k, v, row_ptr, col_idx),
+                                _t(gate, "f32", bh, "gate"), _t(w_lin, dt, dd, "w_lin"), eps, scale,
+                                _t(out, dt, nt, "out"), _t(lse, "f32", bh * shape.n_pad, "lse", True),
+                                _t(dout, dt, nt, "dout"), _t(dq, dt, nt, "dq"), _t(dk, dt, nt, "dk"),
+                                _t(dv, dt, nt, "dv"), _t(dw_lin, "f32", dd, "dw_lin"), _t(dgate, "f32", bh, "dgate"),
+                                _t(ws, "u8", (1,), "ws"), ws.numel(), _stream(stream)), "salad_attn_bwd")

@@ -60,7 +60,7 @@ typedef enum {
   SALAD_EINVAL = -1,        /* bad argument (null pointer, inconsistent shape) */
   SALAD_EUNSUPPORTED = -2,  /* valid but not built: head_dim not 64/128, block not 64/128, heads > 128 */
   SALAD_ENOSPACE = -3,      /* workspace or col_idx capacity too small */
-  SALAD_EINFEASIBLE = -4,   /* (reported through `info`, see salad_build_mask) */
+  SALAD_EINFEASIBLE = -4,   /* a window head asks for more block pairs than it has candidates */
   SALAD_EHIP = -5           /* a HIP launch failed */
 } salad_status;
 
@@ -132,11 +132,19 @@ SALAD_API int salad_version(void);
 /* Static description of a status code; never NULL. */
 SALAD_API const char* salad_status_str(int status);
 
-/* Upper bound on the number of col_idx entries salad_build_mask writes for this
- * shape and these specs (exact unless a window head has density <= 0, where the
- * bound is nb*nb per (b, h), or a head is SICS, bounded by (m + 1) * nb).  Pure host function.  Negative salad_status on
- * invalid arguments. */
-SALAD_API int64_t salad_mask_nnz_max(const salad_shape* shape, const salad_mask_spec* specs);
+/* Number of col_idx entries salad_build_mask writes for this shape and these
+ * specs (pure host function, no device work).  Exact for window heads (K when
+ * density > 0, else the number of candidate pairs) and top-k heads (k * nb per
+ * (b, h)); for SICS heads it is the upper bound (m + 1) * nb per (b, h), since
+ * whether the diagonal block is among a head's m chosen blocks depends on K.
+ * Negative salad_status on invalid arguments, and SALAD_EINFEASIBLE when a
+ * window head with density > 0 asks for K block pairs but has fewer candidate
+ * pairs (the "SALAD" explainer, section 5, names static sliding-window masks;
+ * the window rule is given with salad_mask_spec).  The candidate count depends
+ * on the shape and the spec only; it takes O(nb log nb) host time without a
+ * spatial cap (r_max < 0) in frame-major order, otherwise time proportional to
+ * nb times the blocks of the frames a block's window spans. */
+SALAD_API int64_t salad_mask_nnz(const salad_shape* shape, const salad_mask_spec* specs);
 
 /* Device workspace, in bytes, that salad_build_mask, salad_gate_from_q,
  * salad_linear_state, salad_attn_fwd and salad_attn_fwd_branches need for this
@@ -145,16 +153,17 @@ SALAD_API int64_t salad_mask_nnz_max(const salad_shape* shape, const salad_mask_
 SALAD_API size_t salad_workspace_bytes(const salad_shape* shape);
 
 /* Build the CSR block mask for every (b, h) from the per-head specs.
+ * Validation (before any launch) includes the window feasibility of
+ * salad_mask_nnz: SALAD_EINFEASIBLE when a window head asks for more pairs
+ * than it has candidates, SALAD_EUNSUPPORTED when the mask would hold more
+ * than INT32_MAX entries (row_ptr is int32).
  *   specs    host array [heads]
  *   q, k     device tensors; q is read when some head is SALAD_MASK_TOPK or a
  *            gate is requested, k when some head is SALAD_MASK_TOPK or
  *            SALAD_MASK_SICS (either may be NULL when not read)
  *   row_ptr  device int32 [batch*heads*nb + 1], written
  *   col_idx  device int32 [col_cap], written in [0, row_ptr[last])
- *   col_cap  must be >= salad_mask_nnz_max(shape, specs), else SALAD_ENOSPACE
- *   info     device int32 [1] or NULL: receives the number of window heads that
- *            asked for more pairs than they have candidates (those heads keep
- *            all their candidates); 0 means every request was met
+ *   col_cap  must be >= salad_mask_nnz(shape, specs), else SALAD_ENOSPACE
  *   w_g, gate  optional (both NULL, or both device pointers): also compute
  *            the gate of salad_gate_from_q from the same pass over Q that pools
  *            the query blocks, saving a second read of Q
@@ -164,8 +173,32 @@ SALAD_API size_t salad_workspace_bytes(const salad_shape* shape);
 SALAD_API int salad_build_mask(const salad_shape* shape, const salad_mask_spec* specs,
                      const void* q, const void* k,
                      int32_t* row_ptr, int32_t* col_idx, int64_t col_cap,
-                     int32_t* info, const float* w_g, float* gate,
+                     const float* w_g, float* gate,
                      void* ws, size_t ws_bytes, void* stream);
+
+/* Bits of the result of salad_check_mask. */
+#define SALAD_MASK_BAD_START 1   /* row_ptr[0] != 0 */
+#define SALAD_MASK_BAD_ROW_PTR 2 /* row_ptr decreases, is negative, or passes col_cap */
+#define SALAD_MASK_BAD_COL 4     /* a col_idx entry outside [0, nb) */
+#define SALAD_MASK_BAD_ORDER 8   /* a row's key blocks not strictly ascending */
+
+/* Check a CSR block mask against what salad_attn_fwd, salad_attn_apply,
+ * salad_attn_fwd_branches and salad_attn_bwd assume of it (they index the key
+ * and value tensors with col_idx unchecked and walk each row in order):
+ * row_ptr[0] == 0, row_ptr non-decreasing with row_ptr[rows] <= col_cap,
+ * every entry in [0, nb), each row strictly ascending.  Masks made by
+ * salad_build_mask always pass; a caller that builds its own (a hand-made or
+ * learned block mask in place of the window or Top-K rules of the "SALAD"
+ * explainer, section 5) can check it first.
+ *   row_ptr  device int32 [batch*heads*nb + 1]
+ *   col_idx  device int32 [col_cap]: col_cap is the number of elements the
+ *            allocation holds; the check reads no entry at or beyond it, nor
+ *            the entries of a row whose row_ptr bounds are bad
+ *   result   device int32 [1], written: 0 for a valid mask, else the OR of
+ *            the SALAD_MASK_BAD_* bits found
+ * One small kernel on `stream`; no workspace. */
+SALAD_API int salad_check_mask(const salad_shape* shape, const int32_t* row_ptr, const int32_t* col_idx,
+                               int64_t col_cap, int32_t* result, void* stream);
 
 /* Storage order of the shape's tokens: order[p] = frame-major index
  * t*H*W + y*W + x of the token stored at slot p, for p < N, and order[p] = p
@@ -206,6 +239,11 @@ SALAD_API int salad_linear_state(const salad_shape* shape, const void* k, const 
  * o_s: softmax attention of query i over the keys (< N) of the key blocks its
  *   query block keeps in (row_ptr, col_idx), logits scale*<q_i,k_j>; a row
  *   keeping no block gives 0.
+ * Precondition on the mask (here and in salad_attn_apply,
+ *   salad_attn_fwd_branches and salad_attn_bwd): it is a valid CSR as
+ *   salad_check_mask defines it.  Entries are used as key-block indices
+ *   without a check, so an entry >= nb reads outside k and v; masks from
+ *   salad_build_mask always hold, others can be checked with salad_check_mask.
  * o_l: ReLU(q_i)^T S / (ReLU(q_i)^T z + eps) with S, z as salad_linear_state.
  *   gate   device float [batch*heads], values in (0,1) by the method's design
  *          (any finite value is accepted)

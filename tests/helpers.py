@@ -59,6 +59,18 @@ def oracle_csr(name: str):
     return oracle.csr_from_keep(keep)
 
 
+def oracle_gate(cfg, inp, device_gate=None):
+    """The gate the oracle references use: the config's drawn gate, or (gate from Q) the oracle's own
+    gate_from_q, never the device's.  When the device gate is given, it is checked against it (rtol 1e-5)."""
+    if cfg.gate_kind == "from_q":
+        g = oracle.gate_from_q(inp.q, inp.w_g, cfg.N)
+    else:
+        g = np.asarray(inp.gate, dtype=np.float64)
+    if device_gate is not None:
+        np.testing.assert_allclose(device_gate.cpu().numpy(), g, rtol=1e-5, atol=1e-6)
+    return g
+
+
 def device_tensors(inp, dtype=None):
     """q, k, v, w_lin as torch device tensors in the config's dtype (or the given one)."""
     import torch

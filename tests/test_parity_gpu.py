@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import oracle
-from helpers import (BF16_MAX_ABS, BF16_REL_L2, F32_MAX_ABS, assert_close, device_tensors, inputs,
+from helpers import (BF16_MAX_ABS, BF16_REL_L2, F32_MAX_ABS, assert_close, device_tensors, inputs, oracle_gate,
                      make_layer, oracle_csr, sample_blocks, to_numpy)
 from synth import CONFIGS, HeadSpec, LayerConfig, make_inputs
 
@@ -55,7 +55,6 @@ def test_mask_csr_bit_exact(name):
     np.testing.assert_array_equal(got_rp, rp)
     got_ci = layer.col_idx[:rp[-1]].cpu().numpy()
     np.testing.assert_array_equal(got_ci, ci)
-    assert int(layer.info.item()) == 0
 
 
 def test_sics_mask_forward_c6():
@@ -103,15 +102,26 @@ def test_gate_from_q_c4():
     np.testing.assert_array_equal(gate_fused.cpu().numpy(), gate2.cpu().numpy())
 
 
-def test_window_infeasible_reported():
+def test_window_at_and_past_the_candidate_count():
+    """c1's +-1-frame window has 10 candidate pairs per head.  Asking for exactly 10 (K = every candidate) gives
+    the oracle's CSR bit for bit; asking for 11 is refused on the host (SALAD_EINFEASIBLE, as the oracle raises
+    InfeasibleMask) before anything is allocated or launched."""
     cfg = CONFIGS["c1"]
-    specs = [HeadSpec(0, 1, -1, 0.9), HeadSpec(0, 1, -1, 0.5)]  # 14.4 and 8 pairs; 10 candidates
-    layer = make_layer(cfg, specs=specs)
+    at = [HeadSpec(0, 1, -1, 9.75 / 16), HeadSpec(0, 1, -1, 0.5)]  # K = 10 (all candidates) and 8
+    assert oracle.window_count(at[0].density, cfg.nb, cfg.nb) == 10
+    layer = make_layer(cfg, specs=at)
     layer.build_mask()
     torch.cuda.synchronize()
-    assert int(layer.info.item()) == 1
-    rp = layer.row_ptr.cpu().numpy()
-    assert rp[4] == 10 and rp[8] - rp[4] == 8  # head 0 keeps its 10 candidates, head 1 its 8
+    keep = oracle.build_masks(cfg.T, cfg.H, cfg.W, cfg.block, at, cfg.batch)
+    rp, ci = oracle.csr_from_keep(keep)
+    np.testing.assert_array_equal(layer.row_ptr.cpu().numpy(), rp)
+    np.testing.assert_array_equal(layer.col_idx[:rp[-1]].cpu().numpy(), ci)
+    past = [HeadSpec(0, 1, -1, 10.75 / 16), HeadSpec(0, 1, -1, 0.5)]  # K = 11 > 10 candidates
+    with pytest.raises(oracle.InfeasibleMask):
+        oracle.build_masks(cfg.T, cfg.H, cfg.W, cfg.block, past, cfg.batch)
+    with pytest.raises(S.SaladError) as err:
+        make_layer(cfg, specs=past)
+    assert err.value.status == S.SALAD_EINFEASIBLE
 
 
 # ------------------------------------------------------------------ linear state
@@ -309,9 +319,7 @@ def test_forward_sampled_large(name):
     orp, oci = oracle_csr(name)
     np.testing.assert_array_equal(rp, orp)
     np.testing.assert_array_equal(ci, oci)
-    g = gate.cpu().numpy().astype(np.float64)
-    if cfg.gate_kind == "from_q":
-        np.testing.assert_allclose(g, oracle.gate_from_q(inp.q, inp.w_g, cfg.N), rtol=1e-5, atol=1e-6)
+    g = oracle_gate(cfg, inp, gate)  # the device gate is checked, the reference uses the oracle's
     picks = sample_blocks(cfg)
     ref, ref_s, ref_l = oracle.layer_forward(inp.q, inp.k, inp.v, orp, oci, g, inp.w_lin, cfg.N, cfg.block,
                                              cfg.eps, qblocks=picks)
@@ -430,4 +438,3 @@ def test_window_mask_grid_wider_than_rank_range(cuboid):
     rp, ci = oracle.csr_from_keep(oracle.build_masks(T, H, W, blk, specs, 1, z, z, order=order))
     np.testing.assert_array_equal(layer.row_ptr.cpu().numpy(), rp)
     np.testing.assert_array_equal(layer.col_idx[:rp[-1]].cpu().numpy(), ci)
-    assert int(layer.info.item()) == 0
