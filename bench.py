@@ -38,24 +38,34 @@ if ROOT not in sys.path:
 
 METRIC = "dense-equiv TFLOP/s and ms/layer, hybrid sparse+linear attn at 90% sparsity"
 PEAK_BF16_TFLOPS = 2500.0
-ATTN_SRC = os.path.join(ROOT, "block_sparse_linear_st_amd", "csrc", "attn_bf16.hip")
+# the dominant kernel's sources (its counters below are valid only for them)
+ATTN_SOURCES = [os.path.join(ROOT, "block_sparse_linear_st_amd", "csrc", f) for f in ("attn_bf16.hip", "attn_common.h")]
+ATTN_KERNEL = "k_attn_bf16 (block-sparse flash attention + linear epilogue)"
 # HBM bytes per dispatch of the attention kernel from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE runs (KiB per dispatch), valid only for the kernel source they were
 # taken on (sha256 prefix); scaled by a plain 512 MiB copy, which reads
-# FETCH_SIZE = 262156.7 KiB and WRITE_SIZE = 524288 KiB.
+# FETCH_SIZE = 262157.8 KiB and WRITE_SIZE = 524288 KiB.
 ATTN_COUNTERS = {
-    "source_sha256": "cc260356f526118f",
-    "fetch_scale": 524288.0 / 262156.7,
+    "source_sha256": "14d58dbb344972a3",
+    "fetch_scale": 524288.0 / 262157.8,
     "write_scale": 1.0,
-    "c3": {"fetch_kib": 171218.9, "write_kib": 98304.0},
+    "c3": {"fetch_kib": 201170.7, "write_kib": 98304.0},
 }
+
+
+def attn_source_sha() -> str:
+    """sha256 prefix of the attention kernel's sources, concatenated in ATTN_SOURCES order."""
+    import hashlib
+    h = hashlib.sha256()
+    for p in ATTN_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def attn_traffic_bytes(config: str):
     """Measured HBM bytes per attention launch, or None if not measured for this source."""
-    import hashlib
-    with open(ATTN_SRC, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()[:16]
+    sha = attn_source_sha()
     rec = ATTN_COUNTERS.get(config)
     if rec is None or sha != ATTN_COUNTERS["source_sha256"]:
         return None
@@ -70,7 +80,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="c3")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=25.0)
     ap.add_argument("--backward", action="store_true",
                     help="time a training step instead: forward (keeping its log2-sum-exp) + salad_attn_bwd")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -90,40 +100,134 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}), flush=True)
 
 
-def cpu_baseline(cfg, inp, row_ptr, col_idx, gate, budget_s):
-    """Time the oracle forward on query blocks spread over heads until the budget is spent."""
+# The CPU oracle runs in worker processes forked before the GPU is touched, so
+# they inherit the layer's inputs and mask without copying and share no GPU
+# state; each uses one BLAS thread.
+_POOL_STATE = {}
+
+
+def _cpu_worker_init():
+    os.environ["OMP_NUM_THREADS"] = "1"
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:  # noqa: BLE001
+        pass
+
+
+def _cpu_worker_run(blocks):
     import oracle
+    st = _POOL_STATE
+    t0 = time.perf_counter()
+    oracle.layer_forward(st["q"], st["k"], st["v"], st["row_ptr"], st["col_idx"], st["gate"], st["w_lin"],
+                         st["N"], st["block"], st["eps"], qblocks=blocks)
+    return len(blocks), time.perf_counter() - t0
+
+
+def host_cpus():
+    """(CPUs this process may run on, BLAS threads of this process)."""
+    n_aff = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # noqa: BLE001
-        cores = 1
-    order = []
+        blas = 1
+    return n_aff, int(blas)
+
+
+def start_cpu_pool(cfg, inp, row_ptr, col_idx, gate):
+    """Fork the oracle's worker processes (before any GPU call): one per host CPU, at most OMP_NUM_THREADS."""
+    import multiprocessing as mp
+    n_aff, _ = host_cpus()
+    workers = max(1, min(n_aff, int(os.environ.get("OMP_NUM_THREADS", n_aff))))
+    _POOL_STATE.update(q=inp.q, k=inp.k, v=inp.v, w_lin=inp.w_lin, row_ptr=row_ptr, col_idx=col_idx,
+                       gate=np.asarray(gate, np.float64), N=cfg.N, block=cfg.block, eps=cfg.eps)
+    return mp.get_context("fork").Pool(workers, initializer=_cpu_worker_init), workers
+
+
+def cpu_baseline(cfg, pool, workers, budget_s):
+    """The oracle forward over the layer's query blocks on `workers` processes, in a fixed random order,
+    until every block is done or the budget is spent (the blocks already submitted still finish)."""
+    n_aff, blas = host_cpus()
     rng = np.random.default_rng(1234)
-    for i in range(cfg.batch * cfg.heads * cfg.nb):
-        order.append((int(rng.integers(cfg.batch)), int(rng.integers(cfg.heads)), int(rng.integers(cfg.nb))))
-    done = []
+    allb = [(b, h, qb) for b in range(cfg.batch) for h in range(cfg.heads) for qb in range(cfg.nb)]
+    order = [allb[i] for i in rng.permutation(len(allb))]
+    chunk = 8
+    chunks = [order[i:i + chunk] for i in range(0, len(order), chunk)]
     t0 = time.perf_counter()
-    for blkid in order:
-        oracle.layer_forward(inp.q, inp.k, inp.v, row_ptr, col_idx, gate, inp.w_lin, cfg.N, cfg.block,
-                             cfg.eps, qblocks=[blkid])
-        done.append(blkid)
-        if time.perf_counter() - t0 >= budget_s and len(done) >= 2:
+    pending, done_blocks, busy = [], 0, 0.0
+    it = iter(chunks)
+    exhausted = False
+    while True:
+        while not exhausted and len(pending) < 2 * workers and time.perf_counter() - t0 < budget_s:
+            c = next(it, None)
+            if c is None:
+                exhausted = True
+                break
+            pending.append((c, pool.apply_async(_cpu_worker_run, (c,))))
+        if not pending:
+            break
+        c, r = pending.pop(0)
+        n, dt = r.get()
+        done_blocks += n
+        busy += dt
+        if exhausted and not pending:
+            break
+        if time.perf_counter() - t0 >= budget_s and not exhausted:
+            for c2, r2 in pending:
+                n2, dt2 = r2.get()
+                done_blocks += n2
+                busy += dt2
+            pending = []
             break
     t = time.perf_counter() - t0
-    rows = sum(max(0, min(cfg.block, cfg.N - qb * cfg.block)) for _, _, qb in done)
+    pool.close()
+    pool.join()
+    rows = 0
+    # the blocks finished are the first done_blocks of the submission order
+    for b, h, qb in order[:done_blocks]:
+        rows += max(0, min(cfg.block, cfg.N - qb * cfg.block))
     dense_flop = 4.0 * rows * cfg.N * cfg.head_dim
-    total_blocks = cfg.batch * cfg.heads * cfg.nb
+    full = done_blocks == len(order)
+    frac = done_blocks / len(order)
     return {
         "value": dense_flop / t / 1e12,
         "unit": "TFLOP/s (dense-equivalent)",
-        "cores": int(cores),
+        "cores": workers,
         "kind": "oracle",
-        "sample": f"{len(done)} of {total_blocks} query blocks ({rows} query rows) of the same layer, "
-                  f"fp64 dense masked softmax + quadratic ReLU linear branch + mix, in {t:.1f} s; "
-                  f"projected full layer {t * total_blocks / len(done):.1f} s",
-        "ms_per_layer_projected": t * total_blocks / len(done) * 1e3,
+        "sample": (f"the full layer ({len(order)} query blocks) in {t:.1f} s" if full else
+                   f"{done_blocks} of {len(order)} query blocks ({100 * frac:.1f}% of the layer, {rows} query rows, "
+                   f"random order) in {t:.1f} s; the full layer projects to {t / frac:.1f} s") +
+                  f"; fp64 dense masked softmax + quadratic ReLU linear branch + mix; {workers} worker processes "
+                  f"with one BLAS thread each",
+        "host_cpus": n_aff,
+        "blas_threads_main": blas,
+        "full_layer": full,
+        "ms_per_layer": t * 1e3 if full else None,
+        "ms_per_layer_projected": t / frac * 1e3,
     }
+
+
+HBM_PEAK_GBS = 8000.0
+
+
+def pct(xs, q):
+    return float(np.percentile(np.asarray(xs, np.float64), q))
+
+
+def oracle_inputs_for_cpu(cfg, inp):
+    """The oracle's own CSR and gate for the layer, and its inputs in storage order (CPU only)."""
+    import dataclasses
+
+    import oracle
+    order = None
+    if tuple(cfg.cuboid) != (0, 0, 0):
+        order = oracle.cuboid_order(cfg.T, cfg.H, cfg.W, cfg.cuboid)
+        inp = dataclasses.replace(inp, **{n: oracle.permute_tokens(getattr(inp, n), order) for n in ("q", "k", "v")})
+    keep = oracle.build_masks(cfg.T, cfg.H, cfg.W, cfg.block, cfg.specs, cfg.batch, inp.q, inp.k, order=order)
+    rp, ci = oracle.csr_from_keep(keep)
+    gate = oracle.gate_from_q(inp.q, inp.w_g, cfg.N) if cfg.gate_kind == "from_q" else inp.gate
+    return inp, rp, ci, gate
 
 
 def main():
@@ -138,15 +242,21 @@ def main():
     if args.backward:
         main_backward(args)
         return
+    from synth import CONFIGS, make_inputs
+    cfg = CONFIGS[args.config]
+    inp = make_inputs(cfg)
+    pool = None
+    if not args.no_cpu:
+        # forked before the first GPU call; the workers wait until the GPU part is done
+        cinp, crp, cci, cgate = oracle_inputs_for_cpu(cfg, inp)
+        pool, workers = start_cpu_pool(cfg, cinp, crp, cci, cgate)
+
     import torch
 
     from block_sparse_linear_st_amd import salad as S
     from block_sparse_linear_st_amd.layer import SaladLayer
-    from synth import CONFIGS, make_inputs
 
-    cfg = CONFIGS[args.config]
     torch.cuda.set_device(0)
-    inp = make_inputs(cfg)
     bf = cfg.dtype == "bf16"
     cub = tuple(cfg.cuboid) != (0, 0, 0)
     layer = SaladLayer(cfg.batch, cfg.heads, cfg.head_dim, cfg.T, cfg.H, cfg.W, cfg.block,
@@ -208,19 +318,53 @@ def main():
     torch.cuda.synchronize()
     ms_total = t_start.elapsed_time(t_end)
     ms_step = ms_total / args.steps
-    ms_perm = float(np.mean([e[0].elapsed_time(e[1]) + e[4].elapsed_time(e[5]) for e in evs]))
-    ms_mask = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    ms_lin = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
-    ms_attn = float(np.mean([e[3].elapsed_time(e[4]) for e in evs]))
+    per_step = [e[0].elapsed_time(e[5]) for e in evs]
+    perm = [e[0].elapsed_time(e[1]) + e[4].elapsed_time(e[5]) for e in evs]
+    mask = [e[1].elapsed_time(e[2]) for e in evs]
+    lin = [e[2].elapsed_time(e[3]) for e in evs]
+    attn = [e[3].elapsed_time(e[4]) for e in evs]
+    ms_mask, ms_lin, ms_attn = float(np.median(mask)), float(np.median(lin)), float(np.median(attn))
 
     row_ptr = layer.row_ptr.cpu().numpy()
     nnz = int(row_ptr[-1])
-    col_idx = layer.col_idx[:nnz].cpu().numpy()
     dense_flop = cfg.dense_equiv_flop()
     value = dense_flop / (ms_step * 1e-3) / 1e12
     kept_flop = 4.0 * cfg.block * cfg.block * cfg.head_dim * nnz
     achieved = kept_flop / (ms_attn * 1e-3) / 1e12
     density = nnz / float(cfg.batch * cfg.heads * cfg.nb * cfg.nb)
+    esz = 2 if bf else 4
+    tensor_b = cfg.batch * cfg.heads * cfg.n_pad * cfg.head_dim * esz
+    BH, d = cfg.batch * cfg.heads, cfg.head_dim
+    # phases and their algorithmic work (see the design doc for the derivations)
+    topk_heads = sum(1 for sp_ in cfg.specs if sp_.kind == 1)
+    sics_heads = sum(1 for sp_ in cfg.specs if sp_.kind == 2)
+    per_head_b = cfg.batch * cfg.n_pad * cfg.head_dim * esz
+    # Q and K of top-k heads, K of SICS heads, and (gate from Q) Q of the heads not pooled already
+    mask_bytes = per_head_b * (2 * topk_heads + sics_heads + ((cfg.heads - topk_heads) if from_q else 0))
+    lin_bytes = 2 * tensor_b + BH * (d * d + d) * 4
+    attn_bytes = 4 * tensor_b
+    phases = {
+        "mask": {"ms": round(ms_mask, 5), "bound": "hbm" if mask_bytes else "latency",
+                 "algorithmic_bytes": mask_bytes,
+                 "gbs": round(mask_bytes / (ms_mask * 1e-3) / 1e9, 1) if mask_bytes else None,
+                 "frac": round(mask_bytes / (ms_mask * 1e-3) / 1e9 / HBM_PEAK_GBS, 4) if mask_bytes else None,
+                 "bound_ms": round(mask_bytes / (HBM_PEAK_GBS * 1e9) * 1e3, 5),
+                 "share_of_attention": round(ms_mask / ms_attn, 4)},
+        "linear_prepare": {"ms": round(ms_lin, 5), "bound": "hbm", "algorithmic_bytes": lin_bytes,
+                           "gbs": round(lin_bytes / (ms_lin * 1e-3) / 1e9, 1),
+                           "frac": round(lin_bytes / (ms_lin * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                           "bound_ms": round(lin_bytes / (HBM_PEAK_GBS * 1e9) * 1e3, 5)},
+        "attention": {"ms": round(ms_attn, 5), "bound": "mfma", "algorithmic_flop": kept_flop,
+                      "tflops": round(achieved, 2), "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                      "bound_ms": round(kept_flop / (PEAK_BF16_TFLOPS * 1e12) * 1e3, 5),
+                      "hbm_bytes": attn_bytes},
+    }
+    if cub:
+        phases["permute"] = {"ms": round(float(np.median(perm)), 5), "bound": "hbm",
+                             "algorithmic_bytes": 8 * tensor_b,
+                             "frac": round(8 * tensor_b / (float(np.median(perm)) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                             "bound_ms": round(8 * tensor_b / (HBM_PEAK_GBS * 1e9) * 1e3, 5)}
+    layer_bound = sum(ph["bound_ms"] for ph in phases.values())
 
     result = {
         "metric": METRIC,
@@ -242,10 +386,15 @@ def main():
             "kept_block_pairs": nnz, "block_density": round(density, 6),
             "block_shape": "x".join(str(c) for c in cfg.cuboid) if cub else "frame-major runs",
         },
+        "step_ms": {"mean": round(ms_step, 5), "median": round(pct(per_step, 50), 5),
+                    "p10": round(pct(per_step, 10), 5), "p90": round(pct(per_step, 90), 5)},
         "ms_breakdown": {"mask": round(ms_mask, 5), "linear_prepare": round(ms_lin, 5),
                          "attn_kernel": round(ms_attn, 5)},
+        "phases": phases,
+        "layer_roofline": {"bound_ms": round(layer_bound, 5), "frac": round(layer_bound / ms_step, 4),
+                           "note": "sum of the phases' bounds (they run one after another) over ms_per_step"},
         "roofline": {
-            "kernel": "k_attn_bf16 (block-sparse flash attention + linear epilogue)",
+            "kernel": ATTN_KERNEL,
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS,
@@ -254,21 +403,12 @@ def main():
             "traffic": attn_traffic_bytes(cfg.name),
             "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "algorithmic_flop_per_launch": kept_flop,
+            "timing": "median of HIP events around salad_attn_apply (item split + attention kernel) on its stream",
         },
         "cpu_baseline": None,
     }
-    if cub:
-        result["ms_breakdown"]["permute_in_out"] = round(ms_perm, 5)
-    if not args.no_cpu:
-        g = gate.cpu().numpy().astype(np.float64)
-        if cub:  # the oracle runs on the same stored token order as the kernels
-            import dataclasses
-
-            import oracle
-            order = oracle.cuboid_order(cfg.T, cfg.H, cfg.W, cfg.cuboid)
-            inp = dataclasses.replace(inp, **{n: oracle.permute_tokens(getattr(inp, n), order)
-                                              for n in ("q", "k", "v")})
-        result["cpu_baseline"] = cpu_baseline(cfg, inp, row_ptr, col_idx, g, args.cpu_seconds)
+    if pool is not None:
+        result["cpu_baseline"] = cpu_baseline(cfg, pool, workers, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 

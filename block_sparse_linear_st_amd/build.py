@@ -24,7 +24,7 @@ LIB = os.path.join(PKG, "libsalad.so")
 
 ARCH = "gfx950"
 COMMON = [
-    "-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}",
+    "-std=c++20", "-O3", "-fPIC", f"--offload-arch={ARCH}",
     "-fvisibility=hidden",
     # keep the compiler from emitting packed fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

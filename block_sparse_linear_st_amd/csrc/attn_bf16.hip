@@ -16,7 +16,10 @@
 //                    gfx950 LDS transpose read (ds_read_b64_tr_b16), B = P taken
 //                    straight from the S^T accumulators, converted to bf16
 // The transposed orientation keeps every per-query quantity (max, sum, scale)
-// in the lane that owns the query.  The softmax rescale is lazy: the running
+// in the lane that owns the query.  With 64-key tiles the loop is software
+// pipelined inside each wave (pipe_step): the QK^T of tile u runs beside the
+// exponentials of tile u-1 and the PV of tile u-1 beside the row max of tile u,
+// K tiles travelling one step ahead of V tiles.  The softmax rescale is lazy: the running
 // max used for the exponentials only moves when a row's max grows by more than
 // 2^8, so most tiles skip rescaling O; the final O/l is exact either way.
 //
@@ -45,265 +48,15 @@
 // density do not leave some XCDs idle at the end.
 #include <type_traits>
 
-#include "internal.h"
+#include "attn_common.h"
 
 namespace salad {
 namespace {
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
-typedef __attribute__((address_space(3))) void* lds_ptr;
+using namespace fwd;
 
-// KT keys per LDS tile: 64, or 32 for 128-token blocks (a smaller tile leaves
-// room for three workgroups per CU).
-template <int D, int KT>
-struct Lay {
-  static constexpr int CPR = D / 8;             // 16-byte chunks per row
-  static constexpr int ROW_B = D * 2;           // bytes per row
-  static constexpr int TILE_B = KT * ROW_B;     // one K or V tile
-  static constexpr int BUF_B = 2 * TILE_B;      // K then V
-  static constexpr int RPB = 16 / CPR;          // rows per 256-byte bank period
-  static constexpr int LOADS = KT * CPR / 256;  // 1 KiB loads per thread per tile (K or V)
-  static constexpr int OST = D + 8;             // output staging stride (bf16)
-  static constexpr int SMEM_B = 128 * OST * 2 > 2 * BUF_B ? 128 * OST * 2 : 2 * BUF_B;
-  // the folded linear state (hi, lo) goes through LDS in one pass when both fit, else one part at a time
-  static constexpr int LIN_PASSES = 2 * D * D * 2 <= SMEM_B ? 1 : 2;
-  static_assert(D * D * 2 <= SMEM_B, "one part of the folded linear state must fit");
-  // 16 consecutive rows reading one logical chunk hit 16 different physical chunks
-  __device__ static int kswz(int r) { return (r / RPB) % CPR; }
-  // 4 consecutive rows x 4 consecutive chunks (a half-wave transpose read) are disjoint
-  __device__ static int vswz(int r) { return 4 * ((r / RPB) % (CPR / 4)); }
-};
-
-__device__ inline bf16x8 load_bf16x8(const __bf16* p) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
-}
-
-__device__ inline bf16x8 relu8(bf16x8 x) {
-  uint4 u = __builtin_bit_cast(uint4, x);
-  auto r = [](uint32_t w) {
-    return ((w & 0x8000u) ? 0u : (w & 0xffffu)) | ((w & 0x80000000u) ? 0u : (w & 0xffff0000u));
-  };
-  u.x = r(u.x); u.y = r(u.y); u.z = r(u.z); u.w = r(u.w);
-  return __builtin_bit_cast(bf16x8, u);
-}
-
-__device__ inline uint32_t pack_bf16x2(float a, float b) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
-}
-
-// the own value combined with the one of lane l ^ 32 (max or sum), bit-identical in both lanes
-__device__ inline float pair_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ inline float pair_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// s_waitcnt vmcnt(0) as a compiler-visible instruction (gfx9 encoding: vmcnt 0,
-// expcnt 7, lgkmcnt 15), so the compiler knows every vector load has landed.
-__device__ __attribute__((always_inline)) inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-// One direct HBM -> LDS load: every lane's 16 bytes at gptr land at LDS byte
-// address m0_base + 16 * lane.  Written as inline asm so that the compiler,
-// which cannot tell the two LDS buffers apart, does not stall every LDS read
-// until this load lands; the kernel waits for it explicitly (vmcnt) before the
-// barrier that publishes the buffer.  The instruction has no register result.
-// M0 is set inside the asm; the compiler uses M0 nowhere in these kernels.
-__device__ __attribute__((always_inline)) inline void lds_dma16(const void* gptr, uint32_t m0_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(m0_base)
-               : "memory", "m0");
-}
-// The same with a wave-uniform 64-bit base in SGPRs and a 32-bit lane offset.
-__device__ __attribute__((always_inline)) inline void lds_dma16_s(uint32_t voff, const void* sbase,
-                                                                  uint32_t m0_base) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0_base)
-               : "memory", "m0");
-}
-
-__device__ __attribute__((always_inline)) inline const __bf16* uniform_ptr(const __bf16* p) {
-  const uint64_t u = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
-  return reinterpret_cast<const __bf16*>(((uint64_t)hi << 32) | lo);
-}
-
-// Per-lane byte offsets, inside a tile, of the 16-byte chunks this lane loads
-// (row r, logical chunk p ^ swizzle(r)); they do not depend on the tile.
-template <int D, int KT>
-struct DmaOffsets {
-  uint32_t k[Lay<D, KT>::LOADS], v[Lay<D, KT>::LOADS];
-  __device__ void init(int wave, int lane) {
-    using LY = Lay<D, KT>;
-#pragma unroll
-    for (int i = 0; i < LY::LOADS; ++i) {
-      const int P = (wave * LY::LOADS + i) * 64 + lane;
-      const int r = P / LY::CPR, p = P % LY::CPR;
-      k[i] = (uint32_t)(r * LY::ROW_B + ((p ^ LY::kswz(r)) << 4));
-      v[i] = (uint32_t)(r * LY::ROW_B + ((p ^ LY::vswz(r)) << 4));
-    }
-  }
-};
-
-// Issue the loads of one K and V tile into the LDS buffer at byte address
-// `buf`.  Whole tiles use a uniform base plus the fixed lane offsets;
-// the tile that runs past the last valid token loads row N-1 in place of the
-// missing rows (always in bounds, always finite); their scores are masked to
-// -inf, so they contribute exact zeros.
-template <int D, int KT>
-__device__ __attribute__((always_inline)) inline void issue_tile(uint32_t buf, const __bf16* Kb,
-                                                                 const __bf16* Vb, int key0, int N,
-                                                                 int wave, int lane,
-                                                                 const DmaOffsets<D, KT>& off) {
-  using LY = Lay<D, KT>;
-  if (key0 + KT <= N) {
-    const __bf16* kbase = uniform_ptr(Kb + (int64_t)key0 * D);
-    const __bf16* vbase = uniform_ptr(Vb + (int64_t)key0 * D);
-#pragma unroll
-    for (int i = 0; i < LY::LOADS; ++i) {
-      const uint32_t m0 = buf + (wave * LY::LOADS + i) * 1024;
-      lds_dma16_s(off.k[i], kbase, m0);
-      lds_dma16_s(off.v[i], vbase, m0 + LY::TILE_B);
-    }
-    return;
-  }
-#pragma unroll
-  for (int i = 0; i < LY::LOADS; ++i) {
-    const int blk1k = wave * LY::LOADS + i;  // which 1 KiB of the tile this instruction fills
-    const int P = blk1k * 64 + lane;         // physical 16-byte chunk in the tile
-    const int r = P / LY::CPR, p = P % LY::CPR;
-    const int n = min(max(key0 + r, 0), N - 1);
-    lds_dma16(Kb + (int64_t)n * D + (p ^ LY::kswz(r)) * 8, buf + blk1k * 1024);
-    lds_dma16(Vb + (int64_t)n * D + (p ^ LY::vswz(r)) * 8, buf + LY::TILE_B + blk1k * 1024);
-  }
-}
-
-// S^T, softmax and O^T update of one wave on one 64-key tile held in buffer
-// CUR; ka, va are the per-lane read offsets.
-template <int D, int CUR>
-__device__ __attribute__((always_inline)) inline void compute_tile64(const unsigned char* smem, const uint32_t (&ka)[D / 16],
-                                    const uint32_t (&va)[D / 32], const bf16x8 (&qf)[D / 16],
-                                    f32x16 (&o)[D / 32], float& m_used, float& l_run, int key0,
-                                    int N, float c_log2, int lane) {
-  using LY = Lay<D, 64>;
-  constexpr int NC = D / 16, NT = D / 32;
-  const int g32 = lane >> 5, l32 = lane & 31;
-  const unsigned char* Kt = smem + CUR * LY::BUF_B;
-  const unsigned char* Vt = Kt + LY::TILE_B;
-
-  // S^T = K Q^T: two accumulator chains (key rows 0-31 and 32-63) interleaved,
-  // K fragments read two contraction steps ahead of their MFMA
-  f32x16 s[2];
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) s[kt][i] = 0.0f;
-  {
-    // ka[c]: byte offset of row l32's chunk (2c + g32) inside a K tile (row 32 + l32 has the same swizzle)
-    auto kfrag = [&](int half, int c) __attribute__((always_inline)) {
-      return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Kt + ka[c] + half * 32 * LY::ROW_B));
-    };
-    bf16x8 a0 = kfrag(0, 0), b0 = kfrag(1, 0);
-    bf16x8 a1 = kfrag(0, 1), b1 = kfrag(1, 1);
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      bf16x8 a2 = a1, b2 = b1;
-      if (c + 2 < NC) { a2 = kfrag(0, c + 2); b2 = kfrag(1, c + 2); }
-      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[c], s[0], 0, 0, 0);
-      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, qf[c], s[1], 0, 0, 0);
-      a0 = a1; b0 = b1; a1 = a2; b1 = b2;
-    }
-  }
-  // mask padded keys (only the tile that holds token N-1 and beyond)
-  if (key0 + 64 > N) {
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = key0 + kt * 32 + (i >> 2) * 8 + g32 * 4 + (i & 3);
-        if (key >= N) s[kt][i] = -INFINITY;
-      }
-  }
-  float mx = -INFINITY;
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
-  mx = pair_max(mx) * c_log2;
-  // lazy rescale: move the reference max only when some row grew by more than 2^8
-  if (__ballot(mx > m_used + 8.0f)) {
-    const float m_new = fmaxf(m_used, mx);
-    const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_used - m_new);
-    l_run *= alpha;
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
-    m_used = m_new;
-  }
-  const float neg_m = m_used == -INFINITY ? 0.0f : -m_used;
-  // P in bf16; the row sum adds the same rounded values the PV product uses
-  // (v_dot2 with (1, 1) sums a packed pair in fp32)
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  float rs = 0.0f;
-  bf16x8 pf[4];
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      float p[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(fmaf(s[kt][h * 8 + j], c_log2, neg_m));
-      uint32_t w[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        w[j] = pack_bf16x2(p[2 * j], p[2 * j + 1]);
-        rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[j]), ones, rs, false);
-      }
-      pf[kt * 2 + h] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
-    }
-  l_run += pair_sum(rs);
-
-  // O^T += V^T P^T.  For 16-key step ks and half h, lane (group a = lane/16,
-  // s = lane%16) points the transpose read at key ks*16 + 8h + 4*g32 + s/4 and
-  // channels t*32 + 16*(a%2) + 4*(s%4) .. +3; lane i of the group then holds
-  // channel t*32 + 16*(a%2) + i of those 4 keys, which are the keys its P
-  // fragment carries in slots 4h .. 4h+3.
-  // The NT output tiles are independent chains; the V fragments of the next
-  // 16-key step are read while the current step's MFMAs run.
-  // va[t]: byte offset, inside a V tile, of this lane's transpose-read address for
-  // output tile t at 16-key step 0, half 0; steps and halves add whole rows
-  auto vfrag = [&](int t, int ks) __attribute__((always_inline)) {
-    uint2 tr[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const unsigned char* ad = Vt + va[t] + (ks * 16 + 8 * h) * LY::ROW_B;
-      tr[h] = __builtin_bit_cast(
-          uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(ad)));
-    }
-    return __builtin_bit_cast(bf16x8, make_uint4(tr[0].x, tr[0].y, tr[1].x, tr[1].y));
-  };
-  bf16x8 vf[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) vf[t] = vfrag(t, 0);
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    bf16x8 vn[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) vn[t] = ks + 1 < 4 ? vfrag(t, ks + 1) : vf[t];
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-      o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t], pf[ks], o[t], 0, 0, 0);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) vf[t] = vn[t];
-  }
-}
-
-// The same on one 32-key tile: one QK^T chain; kbase, vbase are the per-lane
+// S^T, softmax and O^T update of one wave on one 32-key tile held in buffer
+// CUR (a tile's steps in order, one QK^T chain); kbase, vbase are the per-lane
 // read bases (chunk c of a K row is kbase ^ (c << 5), output tile t of a V
 // transpose read is vbase ^ (t << 6)).
 template <int D, int CUR>
@@ -391,24 +144,182 @@ __device__ __attribute__((always_inline)) inline void compute_tile32(const unsig
       o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag(t, ks), pf[ks], o[t], 0, 0, 0);
 }
 
+// ---- software-pipelined 64-key tiles ------------------------------------------
+// Within one wave the steps of a tile are serial (QK^T -> softmax -> PV).  The
+// pipelined loop overlaps two tiles instead: in step u a wave runs
+//   phase A: S_u = K_u Q^T (MFMA) beside the exponentials of S_{u-1} (VALU),
+//   phase B: O^T += V_{u-1}^T P_{u-1}^T (MFMA) beside the row max of S_u (VALU),
+// then decides whether tile u moves the reference max.  K tiles are loaded one
+// step ahead of V tiles (tile u's K and V share LDS slot u % 2), so step u reads
+// K_u and V_{u-1}.  Scheduling groups pin the MFMA/VALU interleave.
+
+// Exponentials of chunk c (of NC) of the 32 scores a lane holds for one tile:
+// score v = 16 kt + 8 h + j sits in s[kt][8 h + j]; p = 2^(s * c_log2 - m),
+// packed to bf16 pairs (word v / 2) and summed (the sum adds the rounded values).
+template <int NC>
+__device__ __attribute__((always_inline)) inline void exp_chunk(int c, const f32x16 (&s)[2], float c_log2,
+                                                                float neg_m, uint32_t (&w)[16], float& rs) {
+  constexpr int PER = 32 / NC;  // scores per chunk (4 or 8)
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int q = 0; q < PER / 2; ++q) {
+    const int v = c * PER + 2 * q;
+    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[v / 16][v % 16], c_log2, neg_m));
+    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[(v + 1) / 16][(v + 1) % 16], c_log2, neg_m));
+    w[v / 2] = pack_bf16x2(p0, p1);
+    rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[v / 2]), ones, rs, false);
+  }
+}
+
+__device__ __attribute__((always_inline)) inline void words_to_frags(const uint32_t (&w)[16], bf16x8 (&pf)[4]) {
+#pragma unroll
+  for (int g4 = 0; g4 < 4; ++g4)
+    pf[g4] = __builtin_bit_cast(bf16x8, make_uint4(w[4 * g4], w[4 * g4 + 1], w[4 * g4 + 2], w[4 * g4 + 3]));
+}
+
+// One pipelined step of a wave.  QK: the wave keeps tile u (sn receives its
+// scores); PV: it kept tile u-1 (sp holds those scores).  Returns nothing; o,
+// m_used, l_run are updated.  CUR = u % 2.
+template <int D, int CUR, bool QK, bool PV>
+__device__ __attribute__((always_inline)) inline void pipe_step(
+    const unsigned char* smem, const uint32_t (&ka)[D / 16], const uint32_t (&va)[D / 32],
+    const bf16x8 (&qf)[D / 16], f32x16 (&o)[D / 32], const f32x16 (&sp)[2], f32x16 (&sn)[2], float& m_used,
+    float& l_run, int key0, int N, float c_log2, int lane) {
+  using LY = Lay<D, 64>;
+  constexpr int NC = D / 16, NT = D / 32;
+  constexpr int VPC = 3 * (32 / NC);  // VALU instructions per exponential chunk
+  const int g32 = lane >> 5;
+  const unsigned char* Kt = smem + CUR * LY::BUF_B;                      // K of tile u
+  const unsigned char* Vt = smem + (CUR ^ 1) * LY::BUF_B + LY::TILE_B;   // V of tile u-1
+  auto kfrag = [&](int half, int c) __attribute__((always_inline)) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Kt + ka[c] + half * 32 * LY::ROW_B));
+  };
+  auto vfrag = [&](int t, int ks) __attribute__((always_inline)) {
+    uint2 tr[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const unsigned char* ad = Vt + va[t] + (ks * 16 + 8 * h) * LY::ROW_B;
+      tr[h] = __builtin_bit_cast(
+          uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(ad)));
+    }
+    return __builtin_bit_cast(bf16x8, make_uint4(tr[0].x, tr[0].y, tr[1].x, tr[1].y));
+  };
+
+  // ---- phase A
+  uint32_t w[16];
+  float rs = 0.0f;
+  const float neg_m = m_used == -INFINITY ? 0.0f : -m_used;
+  if constexpr (QK) {
+    bf16x8 a0 = kfrag(0, 0), b0 = kfrag(1, 0);
+    bf16x8 a1 = kfrag(0, 1), b1 = kfrag(1, 1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      bf16x8 a2 = a1, b2 = b1;
+      if (c + 2 < NC) { a2 = kfrag(0, c + 2); b2 = kfrag(1, c + 2); }
+      sn[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[c], c == 0 ? f32x16{} : sn[0], 0, 0, 0);
+      sn[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, qf[c], c == 0 ? f32x16{} : sn[1], 0, 0, 0);
+      if constexpr (PV) exp_chunk<NC>(c, sp, c_log2, neg_m, w, rs);
+      a0 = a1; b0 = b1; a1 = a2; b1 = b2;
+      if (c + 2 < NC) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if constexpr (PV) __builtin_amdgcn_sched_group_barrier(0x002, VPC / 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if constexpr (PV) __builtin_amdgcn_sched_group_barrier(0x002, VPC - VPC / 2, 0);
+    }
+  } else if constexpr (PV) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) exp_chunk<NC>(c, sp, c_log2, neg_m, w, rs);
+  }
+  if constexpr (PV) l_run += pair_sum(rs);
+
+  // scores of keys past N (only the tile holding token N-1 and beyond)
+  if constexpr (QK) {
+    if (key0 + 64 > N) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = key0 + kt * 32 + (i >> 2) * 8 + g32 * 4 + (i & 3);
+          if (key >= N) sn[kt][i] = -INFINITY;
+        }
+    }
+  }
+
+  // ---- phase B
+  float mx = -INFINITY;
+  if constexpr (PV) {
+    bf16x8 pf[4];
+    words_to_frags(w, pf);
+    constexpr int NOPS = 4 * NT;  // (ks, t) in order
+    constexpr int MPO = 32 / NOPS;  // max3 inputs pairs per op: 16 pairs over NOPS ops
+    bf16x8 vf0 = vfrag(0, 0), vf1 = vfrag(1 % NT, (1 / NT) % 4);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < NOPS; ++i) {
+      const int ks = i / NT, t = i % NT;
+      bf16x8 vf2 = vf1;
+      if (i + 2 < NOPS) vf2 = vfrag((i + 2) % NT, (i + 2) / NT);
+      o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf0, pf[ks], o[t], 0, 0, 0);
+      if constexpr (QK) {
+#pragma unroll
+        for (int q = 0; q < MPO; ++q) {
+          const int v = i * MPO + q;
+          mx = fmaxf(mx, sn[v / 16][v % 16]);
+        }
+      }
+      vf0 = vf1; vf1 = vf2;
+      if (i + 2 < NOPS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if constexpr (QK) __builtin_amdgcn_sched_group_barrier(0x002, MPO / 2, 0);
+    }
+  } else if constexpr (QK) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sn[kt][i]);
+  }
+  if constexpr (QK) {
+    // tile u moves the reference max only when some row grew by more than 2^8
+    mx = pair_max(mx) * c_log2;
+    if (__ballot(mx > m_used + 8.0f)) {
+      const float m_new = fmaxf(m_used, mx);
+      const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_used - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
+      m_used = m_new;
+    }
+  }
+}
+
 // 64-key tiles for 64-token blocks (64 KiB of LDS at head_dim 128, two
-// workgroups per CU); 32-key tiles for 128-token blocks, whose workgroups walk
-// one block's list with every wave active: 35 KiB of LDS and at most 168
-// registers give three workgroups (three waves per SIMD) per CU.
+// workgroups per CU, software-pipelined); 32-key tiles for 128-token blocks,
+// whose workgroups walk one block's list with every wave active: 35 KiB of LDS
+// and at most 168 registers give three workgroups (three waves per SIMD) per CU.
 template <int BLK>
-constexpr int tile_keys() { return BLK == 128 ? 32 : 64; }
+constexpr int tile_keys() { return BLK == 64 ? 64 : 32; }
 
 template <int D, int BLK>
 __global__ void __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(tile_keys<BLK>() == 32 ? 3 : 2, tile_keys<BLK>() == 32 ? 3 : 2)))
+__attribute__((amdgpu_waves_per_eu(BLK == 128 ? 3 : 2, BLK == 128 ? 3 : 2)))
 k_attn_bf16(Geom g, AttnArgs a, int n_items, float c_log2) {
+  constexpr int NW = 4;             // waves per workgroup
   constexpr int KT = tile_keys<BLK>();
-  using LY = Lay<D, KT>;
-  constexpr int QPW = 128 / BLK;  // query blocks per workgroup
+  using LY = Lay<D, KT, NW>;
+  constexpr int ROWS = NW * 32;     // query rows per workgroup
+  constexpr int QPW = ROWS / BLK;   // query blocks per workgroup
   constexpr int NC = D / 16;
   constexpr int NT = D / 32;
   constexpr int TPB = BLK / KT;   // tiles per key block
-  __shared__ __align__(1024) unsigned char smem[LY::SMEM_B];
+  constexpr int SMEM_B = ROWS * LY::OST * 2 > 2 * LY::BUF_B ? ROWS * LY::OST * 2 : 2 * LY::BUF_B;
+  // the folded linear state (hi, lo) goes through LDS in one pass when both fit, else one part at a time
+  constexpr int LIN_PASSES = 2 * D * D * 2 <= SMEM_B ? 1 : 2;
+  static_assert(D * D * 2 <= SMEM_B, "one part of the folded linear state must fit");
+  constexpr int THREADS = NW * 64;
+  __shared__ __align__(1024) unsigned char smem[SMEM_B];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g32 = lane >> 5, l32 = lane & 31;
@@ -475,9 +386,13 @@ k_attn_bf16(Geom g, AttnArgs a, int n_items, float c_log2) {
     // LDS byte address of the buffers (uniform); the wave index is uniform too
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    DmaOffsets<D, KT> doff;
+    DmaOffsets<D, KT, NW> doff;
     doff.init(wave_u, lane);
-    if (valid) issue_tile<D, KT>(lds0, Kb, Vb, kb * BLK + sub * KT, g.N, wave_u, lane, doff);
+    constexpr bool PIPE = KT == 64;  // 64-key tiles: the software-pipelined loop
+    if (valid) {
+      if constexpr (PIPE) issue_half<D, KT, NW, true>(lds0, Kb, kb * BLK + sub * KT, g.N, wave_u, lane, doff);
+      else issue_tile<D, KT, NW>(lds0, Kb, Vb, kb * BLK + sub * KT, g.N, wave_u, lane, doff);
+    }
     wait_vmem();
     __syncthreads();
     // per-lane LDS read offsets inside a tile, fixed for the whole loop (kept opaque so that
@@ -513,23 +428,58 @@ k_attn_bf16(Geom g, AttnArgs a, int n_items, float c_log2) {
       bool nvalid;
       advance(nkb, nsub, nflags, nvalid);
       if (nvalid)
-        issue_tile<D, KT>(lds0 + (CUR ^ 1) * LY::BUF_B, Kb, Vb, nkb * BLK + nsub * KT, g.N, wave_u, lane,
+        issue_tile<D, KT, NW>(lds0 + (CUR ^ 1) * LY::BUF_B, Kb, Vb, nkb * BLK + nsub * KT, g.N, wave_u, lane,
                           doff);
-      if (wave_rows && ((flags >> qsub) & 1)) {
-        if constexpr (KT == 64)
-          compute_tile64<D, CUR>(smem, ka, va, qf, o, m_used, l_run, kb * BLK + sub * KT, g.N, c_log2, lane);
-        else
-          compute_tile32<D, CUR>(smem, kbase, vbase, qf, o, m_used, l_run, kb * BLK + sub * KT, g.N, c_log2,
-                                 lane);
-      }
+      if (wave_rows && ((flags >> qsub) & 1))
+        compute_tile32<D, CUR>(smem, kbase, vbase, qf, o, m_used, l_run, kb * BLK + sub * KT, g.N, c_log2, lane);
       wait_vmem();  // the next tile has landed in LDS ...
       __syncthreads();  // ... for every wave, and nobody still reads the current one
       kb = nkb; sub = nsub; flags = nflags; valid = nvalid;
     };
-    while (valid) {
-      step(std::integral_constant<int, 0>{});
-      if (!valid) break;
-      step(std::integral_constant<int, 1>{});
+    if constexpr (PIPE) {
+      // step u: tile u is (kb, sub, flags, valid), tile u-1 (pflags, pvalid); scores of
+      // alternate tiles in sA / sB; one more step after the last tile finishes it
+      f32x16 sA[2], sB[2];
+      int pflags = 0;
+      bool pvalid = false;
+      auto pstep = [&](auto cur_c) __attribute__((always_inline)) {
+        constexpr int CUR = decltype(cur_c)::value;
+        int nkb, nsub, nflags;
+        bool nvalid;
+        advance(nkb, nsub, nflags, nvalid);
+        if (nvalid)
+          issue_half<D, KT, NW, true>(lds0 + (CUR ^ 1) * LY::BUF_B, Kb, nkb * BLK + nsub * KT, g.N, wave_u, lane,
+                                      doff);
+        if (valid)
+          issue_half<D, KT, NW, false>(lds0 + CUR * LY::BUF_B + LY::TILE_B, Vb, kb * BLK + sub * KT, g.N, wave_u,
+                                       lane, doff);
+        const bool kc = valid && wave_rows && ((flags >> qsub) & 1);
+        const bool kp = pvalid && wave_rows && ((pflags >> qsub) & 1);
+        f32x16(&sp)[2] = CUR ? sA : sB;
+        f32x16(&sn)[2] = CUR ? sB : sA;
+        const int key0 = kb * BLK + sub * KT;
+        if (kc && kp)
+          pipe_step<D, CUR, true, true>(smem, ka, va, qf, o, sp, sn, m_used, l_run, key0, g.N, c_log2, lane);
+        else if (kc)
+          pipe_step<D, CUR, true, false>(smem, ka, va, qf, o, sp, sn, m_used, l_run, key0, g.N, c_log2, lane);
+        else if (kp)
+          pipe_step<D, CUR, false, true>(smem, ka, va, qf, o, sp, sn, m_used, l_run, key0, g.N, c_log2, lane);
+        wait_vmem();      // K of tile u+1 and V of tile u have landed ...
+        __syncthreads();  // ... for every wave, and nobody still reads K_u or V_{u-1}
+        pflags = flags; pvalid = valid;
+        kb = nkb; sub = nsub; flags = nflags; valid = nvalid;
+      };
+      while (valid || pvalid) {
+        pstep(std::integral_constant<int, 0>{});
+        if (!(valid || pvalid)) break;
+        pstep(std::integral_constant<int, 1>{});
+      }
+    } else {
+      while (valid) {
+        step(std::integral_constant<int, 0>{});
+        if (!valid) break;
+        step(std::integral_constant<int, 1>{});
+      }
     }
   }
 
@@ -547,14 +497,14 @@ k_attn_bf16(Geom g, AttnArgs a, int n_items, float c_log2) {
   bool lin = a.has_lin != 0;
   if (lin && a.gate != nullptr && a.gate[bh] < a.drop_tau) lin = false;  // uniform
   if (lin) {
-    if constexpr (LY::LIN_PASSES == 1) {
+    if constexpr (LIN_PASSES == 1) {
       // S''^T (hi, lo) of this head into LDS, rows swizzled like K tiles: every
       // wave reads all of it, so one copy per workgroup instead of one per wave
       const __bf16* hi = static_cast<const __bf16*>(a.sft_hi) + (int64_t)bh * D * D;
       const __bf16* lo = static_cast<const __bf16*>(a.sft_lo) + (int64_t)bh * D * D;
       const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
       const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-      constexpr int PER = D * LY::CPR / 256;  // 1 KiB loads per wave per matrix
+      constexpr int PER = D * LY::CPR / THREADS;  // 1 KiB loads per wave per matrix
       __syncthreads();  // the tile buffers are free
   #pragma unroll
       for (int i = 0; i < PER; ++i) {
@@ -607,7 +557,7 @@ k_attn_bf16(Geom g, AttnArgs a, int n_items, float c_log2) {
                                static_cast<const __bf16*>(a.sft_lo) + (int64_t)bh * D * D};
       const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
       const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-      constexpr int PER = D * LY::CPR / 256;  // 1 KiB loads per wave per matrix
+      constexpr int PER = D * LY::CPR / THREADS;  // 1 KiB loads per wave per matrix
       const float* z = a.z + (int64_t)bh * D;
       bf16x8 rq[NC];
       float den = 0.0f;
@@ -655,7 +605,7 @@ k_attn_bf16(Geom g, AttnArgs a, int n_items, float c_log2) {
     }
   }
 
-  // stage [128 rows][D] bf16 through LDS, then 16-byte coalesced stores
+  // stage [ROWS][D] bf16 through LDS, then 16-byte coalesced stores
   __syncthreads();
   __bf16* ost = reinterpret_cast<__bf16*>(smem);
   const bool row_ok = wave_rows && my_row < g.N;
@@ -672,7 +622,7 @@ k_attn_bf16(Geom g, AttnArgs a, int n_items, float c_log2) {
   __syncthreads();
   __bf16* Ob = static_cast<__bf16*>(a.out) + (int64_t)bh * g.n_pad * D;
   constexpr int CPR = D / 8;
-  for (int ch = tid; ch < 128 * CPR; ch += 256) {
+  for (int ch = tid; ch < ROWS * CPR; ch += THREADS) {
     const int r = ch / CPR, dc = ch % CPR;
     const int row = qb_base * BLK + r;
     if (row < g.n_pad)
@@ -686,10 +636,11 @@ hipError_t launch(const Geom& g, const AttnArgs& a, hipStream_t st) {
   constexpr int QPW = 128 / BLK;
   const int qgroups = (g.nb + QPW - 1) / QPW;
   const int n_items = g.B * g.Hh * qgroups;
-  // work per item in tile steps: kept key blocks times tiles per block, plus
+  // work per item in tile steps: kept blocks times tiles per block, plus
   // about three 64-key steps for the item's own loads and epilogue
-  constexpr int TPB = BLK / tile_keys<BLK>();
-  const ItemSplit job{a.row_ptr, a.split, g.B * g.Hh, g.nb, QPW, TPB, 3 * 64 / tile_keys<BLK>()};
+  constexpr int KT = tile_keys<BLK>();
+  constexpr int TPB = BLK / KT;
+  const ItemSplit job{a.row_ptr, a.split, g.B * g.Hh, g.nb, QPW, TPB, 3 * 64 / KT};
   hipError_t e = launch_item_splits(&job, 1, st);
   if (e != hipSuccess) return e;
   const int grid = 8 * xcd_items_cap(n_items);

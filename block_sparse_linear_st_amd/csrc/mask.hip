@@ -334,7 +334,19 @@ k_scan_rows(const int32_t* rowcnt, int64_t rows, int32_t* row_ptr) {
   for (int64_t r = lo; r < hi; ++r) local += rowcnt[r];
   int64_t total;
   int64_t run = block_exclusive_scan(local, tmp, &total);
-  for (int64_t r = lo; r < hi; ++r) {
+  // the segment's counts again, 8 loads in flight before their stores
+  int64_t r = lo;
+  for (; r + 8 <= hi; r += 8) {
+    int32_t c[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) c[u] = rowcnt[r + u];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      row_ptr[r + u] = (int32_t)run;
+      run += c[u];
+    }
+  }
+  for (; r < hi; ++r) {
     row_ptr[r] = (int32_t)run;
     run += rowcnt[r];
   }

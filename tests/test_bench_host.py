@@ -56,3 +56,34 @@ def test_kept_tile_flop_count_from_the_oracle_mask():
     # the dense-equivalent count the metric divides by: all N x N query-key pairs, two products
     assert cfg.dense_equiv_flop() == 4.0 * cfg.batch * cfg.heads * float(cfg.N) ** 2 * cfg.head_dim
     assert np.isclose(nnz / (cfg.batch * cfg.heads * cfg.nb * cfg.nb), 0.1, atol=1e-4)
+
+
+def test_phase_work_constants():
+    """The algorithmic work bench.py prices each phase at, for the headline layer: the linear pass reads K and
+    V once and writes S and z; the attention kernel reads Q, K, V and writes out; a window mask reads nothing."""
+    cfg = CONFIGS["c3"]
+    tensor = cfg.batch * cfg.heads * cfg.n_pad * cfg.head_dim * 2
+    assert tensor == 100663296
+    BH, d = cfg.batch * cfg.heads, cfg.head_dim
+    assert 2 * tensor + BH * (d * d + d) * 4 == 202119168  # the "linear_prepare" algorithmic_bytes
+    assert 202119168 / 8e12 * 1e3 == 0.025264896            # its bound at 8 TB/s, in ms
+    assert abs(659696910336.0 / 2.5e15 * 1e3 - 0.2638787641344) < 1e-12  # the attention bound at 2.5 PFLOP/s, in ms
+    # a top-k layer pools Q and K of every head (and the gate rides on the same pass over Q)
+    c4 = CONFIGS["c4"]
+    per_head = c4.batch * c4.n_pad * c4.head_dim * 2
+    assert per_head * 2 * c4.heads == 671088640
+
+
+def test_cpu_pool_is_forked_before_the_gpu_and_reports_its_cores():
+    """The oracle's worker count is the host's CPUs capped by OMP_NUM_THREADS, and cpu_baseline labels a full
+    layer as such (a tiny layer finishes within any budget)."""
+    from synth import make_inputs
+    cfg = CONFIGS["c1"]
+    inp = make_inputs(cfg)
+    cinp, rp, ci, gate = bench.oracle_inputs_for_cpu(cfg, inp)
+    pool, workers = bench.start_cpu_pool(cfg, cinp, rp, ci, gate)
+    n_aff, _ = bench.host_cpus()
+    assert 1 <= workers <= n_aff
+    r = bench.cpu_baseline(cfg, pool, workers, 30.0)
+    assert r["full_layer"] and r["cores"] == workers and r["host_cpus"] == n_aff
+    assert r["kind"] == "oracle" and "full layer" in r["sample"]
