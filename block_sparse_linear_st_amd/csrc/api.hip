@@ -2,9 +2,18 @@
 // argument validation, workspace planning and the launch sequence of each call.
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "cuboid.h"
 #include "internal.h"
+
+// The allocation-free forward's scratch (salad_attn_fwd_noalloc): one static
+// device array per GPU; each device that loads the library holds its own copy
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// not the device address: the address comes from hipGetSymbolAddress, once per
+// device, with that device current (scratch_of_current_device).
+static constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace salad {
 
@@ -105,6 +114,26 @@ int head_counts(const salad_shape* s, const salad_mask_spec* specs, int64_t* cou
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? SALAD_OK : SALAD_EHIP; }
+
+// Device address of `scratch` on the current device, looked up on the first
+// call on each device and kept (write-once per device, under a lock).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_of_current_device(char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return SALAD_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return SALAD_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return SALAD_EHIP;
+    g_scratch_ptr[dev] = static_cast<char*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return SALAD_OK;
+}
 
 }  // namespace
 
@@ -378,6 +407,40 @@ hipError_t run_attn(const Geom& g, int dtype, const AttnArgs& a, hipStream_t s) 
   return dtype == SALAD_BF16 ? launch_attn_bf16(g, a, s) : launch_attn_f32(g, a, s);
 }
 
+// Arguments of the fused forward beyond q, k, v and the mask.
+int fwd_args_status(const salad_shape* shape, const float* gate, const void* w_lin, float eps, float scale,
+                    float drop_tau, void* out, float* lse) {
+  if (!gate || !w_lin || !out || !aligned16(out) || !(eps >= 0.0f) || !std::isfinite(scale) ||
+      std::isnan(drop_tau))
+    return SALAD_EINVAL;
+  if (lse != nullptr && shape->dtype != SALAD_BF16) return SALAD_EUNSUPPORTED;
+  return SALAD_OK;
+}
+
+// The fused forward's launches (validated arguments): linear-state partials,
+// fold, attention with the linear epilogue.  Only the linear-phase part of the
+// workspace layout (up to L.lin_end) is touched.
+int fwd_run(const salad_shape* shape, const Geom& g, const Workspace& L, const void* q, const void* k,
+            const void* v, const int32_t* row_ptr, const int32_t* col_idx, const float* gate,
+            const void* w_lin, float eps, float scale, float drop_tau, void* out, float* lse, char* w,
+            hipStream_t s) {
+  hipError_t e = launch_linear_state(g, shape->dtype, k, v, gate, drop_tau, w, L, s);
+  if (e == hipSuccess)
+    e = launch_linear_fold(g, shape->dtype, gate, w_lin, 0, drop_tau, nullptr, nullptr, w, L, s);
+  if (e != hipSuccess) return SALAD_EHIP;
+  AttnArgs a{};
+  a.q = q; a.k = k; a.v = v; a.out = out;
+  a.row_ptr = row_ptr; a.col_idx = col_idx;
+  a.sft_hi = w + L.off_sft_hi; a.sft_lo = w + L.off_sft_lo;
+  a.split = reinterpret_cast<int32_t*>(w + L.off_split);
+  a.z = reinterpret_cast<const float*>(w + L.off_z);
+  a.gate = gate; a.drop_tau = drop_tau; a.eps = eps;
+  a.scale = scale > 0.0f ? scale : 1.0f / std::sqrt((float)g.D);
+  a.has_sparse = 1; a.has_lin = 1;
+  a.lse = lse;
+  return hip_status(run_attn(g, shape->dtype, a, s));
+}
+
 }  // namespace
 
 int salad_linear_prepare(const salad_shape* shape, const void* k, const void* v,
@@ -435,14 +498,31 @@ int salad_attn_fwd(const salad_shape* shape, const void* q, const void* k, const
   Workspace L;
   int st = attn_common(shape, q, k, v, row_ptr, col_idx, ws, ws_bytes, &g, &L);
   if (st != SALAD_OK) return st;
-  if (!gate || !w_lin || !out || !aligned16(out) || !(eps >= 0.0f) || !std::isfinite(scale) ||
-      std::isnan(drop_tau))
-    return SALAD_EINVAL;
-  if (lse != nullptr && shape->dtype != SALAD_BF16) return SALAD_EUNSUPPORTED;
-  st = salad_linear_prepare(shape, k, v, gate, w_lin, drop_tau, ws, ws_bytes, stream);
+  st = fwd_args_status(shape, gate, w_lin, eps, scale, drop_tau, out, lse);
   if (st != SALAD_OK) return st;
-  return salad_attn_apply(shape, q, k, v, row_ptr, col_idx, gate, eps, scale, drop_tau, out, lse, ws,
-                          ws_bytes, stream);
+  return fwd_run(shape, g, L, q, k, v, row_ptr, col_idx, gate, w_lin, eps, scale, drop_tau, out, lse,
+                 static_cast<char*>(ws), static_cast<hipStream_t>(stream));
+}
+
+int salad_attn_fwd_noalloc(const salad_shape* shape, const void* q, const void* k, const void* v,
+                           const int32_t* row_ptr, const int32_t* col_idx, const float* gate,
+                           const void* w_lin, float eps, float scale, float drop_tau, void* out,
+                           float* lse, void* stream) {
+  Geom g;
+  int st = shape_status(shape);
+  if (st != SALAD_OK) return st;
+  make_geom(shape, &g);
+  if (!q || !k || !v || !row_ptr || !col_idx) return SALAD_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return SALAD_EINVAL;
+  st = fwd_args_status(shape, gate, w_lin, eps, scale, drop_tau, out, lse);
+  if (st != SALAD_OK) return st;
+  const Workspace L = plan_for(shape, g);
+  if (L.lin_end > kScratchBytes) return SALAD_ENOSPACE;  // the forward uses the linear-phase part only
+  char* w = nullptr;
+  st = scratch_of_current_device(&w);
+  if (st != SALAD_OK) return st;
+  return fwd_run(shape, g, L, q, k, v, row_ptr, col_idx, gate, w_lin, eps, scale, drop_tau, out, lse, w,
+                 static_cast<hipStream_t>(stream));
 }
 
 int salad_attn_fwd_branches(const salad_shape* shape, const void* q, const void* k, const void* v,

@@ -75,6 +75,8 @@ _SIGS = {
     "salad_linear_state": (ctypes.c_int, [ctypes.POINTER(salad_shape), _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "salad_attn_fwd": (ctypes.c_int, [ctypes.POINTER(salad_shape), _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                       _f, _f, _f, _vp, _vp, _vp, _sz, _vp]),
+    "salad_attn_fwd_noalloc": (ctypes.c_int, [ctypes.POINTER(salad_shape), _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                              _f, _f, _f, _vp, _vp, _vp]),
     "salad_linear_prepare": (ctypes.c_int, [ctypes.POINTER(salad_shape), _vp, _vp, _vp, _vp, ctypes.c_float,
                                             _vp, _sz, _vp]),
     "salad_attn_apply": (ctypes.c_int, [ctypes.POINTER(salad_shape), _vp, _vp, _vp, _vp, _vp, _vp,
@@ -258,6 +260,17 @@ def salad_attn_fwd(shape, q, k, v, row_ptr, col_idx, gate, w_lin, eps, scale, dr
                                 drop_tau, _t(out, shape.dtype, nt, "out"),
                                 _t(lse, "f32", bh * shape.n_pad, "lse", True), _t(ws, "u8", (1,), "ws"),
                                 ws.numel(), _stream(stream)), "salad_attn_fwd")
+
+
+def salad_attn_fwd_noalloc(shape, q, k, v, row_ptr, col_idx, gate, w_lin, eps, scale, drop_tau, out, stream=None,
+                           lse=None):
+    """salad_attn_fwd on the library's static scratch: no workspace argument, nothing allocated."""
+    nt, bh, _, dd = _sizes(shape)
+    _check(lib().salad_attn_fwd_noalloc(ctypes.byref(shape), *_qkv_csr(shape, q, k, v, row_ptr, col_idx),
+                                        _t(gate, "f32", bh, "gate"), _t(w_lin, shape.dtype, dd, "w_lin"), eps,
+                                        scale, drop_tau, _t(out, shape.dtype, nt, "out"),
+                                        _t(lse, "f32", bh * shape.n_pad, "lse", True), _stream(stream)),
+           "salad_attn_fwd_noalloc")
 
 
 def salad_attn_fwd_branches(shape, q, k, v, row_ptr, col_idx, eps, scale, out_sparse, out_lin, ws,

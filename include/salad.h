@@ -265,6 +265,24 @@ SALAD_API int salad_attn_fwd(const salad_shape* shape, const void* q, const void
                    const float* gate, const void* w_lin, float eps, float scale,
                    float drop_tau, void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
+/* salad_attn_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same launches and the same results, with the workspace taken from a
+ * static device array inside the library (32 MiB on each GPU that loads the
+ * library, held until the process ends) instead of a caller buffer.  The
+ * call itself allocates nothing.  Only the linear-state part of the
+ * workspace layout is used; SALAD_ENOSPACE when it exceeds 32 MiB (at
+ * head_dim 128 about batch*heads > 240).  Every call on one GPU shares that
+ * GPU's array: calls that overlap in time on one GPU (two streams, two host
+ * threads without ordering) race and give wrong results; calls ordered on one
+ * stream are safe.  Nothing in the array needs to start at zero.  The first
+ * call on each device looks up the array's address (hipGetSymbolAddress) with
+ * that device current; `stream` must belong to the current device. */
+SALAD_API int salad_attn_fwd_noalloc(const salad_shape* shape, const void* q, const void* k, const void* v,
+                                     const int32_t* row_ptr, const int32_t* col_idx, const float* gate,
+                                     const void* w_lin, float eps, float scale, float drop_tau, void* out,
+                                     float* lse, void* stream);
+
 /* salad_attn_fwd in two calls, for callers that reuse the linear state or
  * time the steps apart.  salad_linear_prepare computes S and z (as
  * salad_linear_state) and keeps, in the workspace, the state with gate and

@@ -318,3 +318,22 @@ def test_check_mask_rejects_bad_arguments_before_launch():
     assert L.salad_check_mask(ctypes.byref(sh), fake, fake, -1, fake, None) == S.SALAD_EINVAL
     assert L.salad_check_mask(ctypes.byref(_shape("c2", head_dim=96)), fake, fake, 10, fake, None) == \
         S.SALAD_EUNSUPPORTED
+
+
+def test_noalloc_forward_refuses_layers_beyond_its_scratch():
+    """salad_attn_fwd_noalloc checks its arguments and the 32 MiB scratch limit before any HIP call."""
+    L = _lib()
+    fake = ctypes.c_void_p(0x100000)
+    big = S.make_shape(2, 128, 128, 21, 30, 52, 64, S.SALAD_BF16)  # 256 (b, h): linear state over 32 MiB
+    args = [fake] * 7 + [1e-6, 0.0, 0.0, fake, None, None]
+    assert L.salad_attn_fwd_noalloc(ctypes.byref(big), *args) == S.SALAD_ENOSPACE
+    sh = _shape("c3")
+    assert L.salad_attn_fwd_noalloc(None, *args) == S.SALAD_EINVAL
+    bad = list(args)
+    bad[5] = None  # gate
+    assert L.salad_attn_fwd_noalloc(ctypes.byref(sh), *bad) == S.SALAD_EINVAL
+    bad = list(args)
+    bad[0] = ctypes.c_void_p(0x100004)  # misaligned q
+    assert L.salad_attn_fwd_noalloc(ctypes.byref(sh), *bad) == S.SALAD_EINVAL
+    assert L.salad_attn_fwd_noalloc(ctypes.byref(_shape("c1")), *(args[:11] + [fake, None])) == \
+        S.SALAD_EUNSUPPORTED  # lse on an fp32 layer
