@@ -410,8 +410,8 @@ hipError_t run_attn(const Geom& g, int dtype, const AttnArgs& a, hipStream_t s) 
 // Arguments of the fused forward beyond q, k, v and the mask.
 int fwd_args_status(const salad_shape* shape, const float* gate, const void* w_lin, float eps, float scale,
                     float drop_tau, void* out, float* lse) {
-  if (!gate || !w_lin || !out || !aligned16(out) || !(eps >= 0.0f) || !std::isfinite(scale) ||
-      std::isnan(drop_tau))
+  if (!gate || !w_lin || !aligned16(w_lin) || !out || !aligned16(out) || !(eps >= 0.0f) ||
+      !std::isfinite(scale) || std::isnan(drop_tau))
     return SALAD_EINVAL;
   if (lse != nullptr && shape->dtype != SALAD_BF16) return SALAD_EUNSUPPORTED;
   return SALAD_OK;
@@ -451,7 +451,7 @@ int salad_linear_prepare(const salad_shape* shape, const void* k, const void* v,
   if (st != SALAD_OK) return st;
   make_geom(shape, &g);
   if (!k || !v || !gate || !w_lin || !ws || !aligned16(k) || !aligned16(v) || !aligned16(ws) ||
-      std::isnan(drop_tau))
+      !aligned16(w_lin) || std::isnan(drop_tau))
     return SALAD_EINVAL;
   const Workspace L = plan_for(shape, g);
   if (ws_bytes < L.bytes) return SALAD_ENOSPACE;

@@ -182,6 +182,9 @@ def test_entry_points_reject_bad_arguments_before_launch():
     # misaligned pointers
     odd = ctypes.c_void_p(0x100004)
     assert L.salad_attn_fwd(ctypes.byref(sh), odd, fake, fake, fake, fake, fake, fake, 1e-6, 0.0, 0.0, fake, None, fake, ws_bytes, None) == S.SALAD_EINVAL
+    # w_lin is staged in 16-byte chunks
+    assert L.salad_attn_fwd(ctypes.byref(sh), fake, fake, fake, fake, fake, fake, odd, 1e-6, 0.0, 0.0, fake, None, fake, ws_bytes, None) == S.SALAD_EINVAL
+    assert L.salad_linear_prepare(ctypes.byref(sh), fake, fake, fake, odd, 0.0, fake, ws_bytes, None) == S.SALAD_EINVAL
     # missing gate / w_lin / out; bad eps
     assert L.salad_attn_fwd(ctypes.byref(sh), fake, fake, fake, fake, fake, None, fake, 1e-6, 0.0, 0.0, fake, None, fake, ws_bytes, None) == S.SALAD_EINVAL
     assert L.salad_attn_fwd(ctypes.byref(sh), fake, fake, fake, fake, fake, fake, None, 1e-6, 0.0, 0.0, fake, None, fake, ws_bytes, None) == S.SALAD_EINVAL
