@@ -306,18 +306,24 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # timed region: K whole steps
+    # timed region: K whole steps, nothing else recorded on the stream
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start.record(stream)
     for i in range(args.steps):
-        step(evs[i])
+        step()
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_total = t_start.elapsed_time(t_end)
     ms_step = ms_total / args.steps
+    # phase breakdown and per-step spread: K more steps after the timed region,
+    # with HIP events between the phases (they cost ~1% of a step, so they stay
+    # out of the timed region)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
     per_step = [e[0].elapsed_time(e[5]) for e in evs]
     perm = [e[0].elapsed_time(e[1]) + e[4].elapsed_time(e[5]) for e in evs]
     mask = [e[1].elapsed_time(e[2]) for e in evs]
@@ -387,7 +393,8 @@ def main():
             "block_shape": "x".join(str(c) for c in cfg.cuboid) if cub else "frame-major runs",
         },
         "step_ms": {"mean": round(ms_step, 5), "median": round(pct(per_step, 50), 5),
-                    "p10": round(pct(per_step, 10), 5), "p90": round(pct(per_step, 90), 5)},
+                    "p10": round(pct(per_step, 10), 5), "p90": round(pct(per_step, 90), 5),
+                    "note": "mean over the timed region; median and percentiles of the event-timed steps that follow it"},
         "ms_breakdown": {"mask": round(ms_mask, 5), "linear_prepare": round(ms_lin, 5),
                          "attn_kernel": round(ms_attn, 5)},
         "phases": phases,
@@ -474,13 +481,17 @@ def main_backward(args):
     torch.cuda.synchronize()
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t_start.record(stream)
     for i in range(args.steps):
-        step(evs[i])
+        step()
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / args.steps
+    # forward / backward split: K more steps with events, after the timed region
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
     ms_fwd = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     ms_bwd = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     nnz = int(layer.row_ptr[-1].item())
