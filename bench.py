@@ -341,7 +341,8 @@ def main():
     esz = 2 if bf else 4
     tensor_b = cfg.batch * cfg.heads * cfg.n_pad * cfg.head_dim * esz
     BH, d = cfg.batch * cfg.heads, cfg.head_dim
-    # phases and their algorithmic work (see the design doc for the derivations)
+    # phases and their algorithmic work: bytes each phase must move at least (mask: the pooled inputs;
+    # linear: K and V once plus the state; attention: Q, K, V and out once), FLOP on the kept tiles
     topk_heads = sum(1 for sp_ in cfg.specs if sp_.kind == 1)
     sics_heads = sum(1 for sp_ in cfg.specs if sp_.kind == 2)
     per_head_b = cfg.batch * cfg.n_pad * cfg.head_dim * esz
