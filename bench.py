@@ -278,7 +278,7 @@ def main():
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
 
-    def step(ev=None):
+    def step(ev=None, ev_attn=None):
         if ev is not None:
             ev[0].record(stream)
         if cub:
@@ -293,8 +293,12 @@ def main():
         S.salad_linear_prepare(layer.shape, ks, vs, gate, w, layer.ws, sp, drop_tau=0.0)
         if ev is not None:
             ev[3].record(stream)
+        if ev_attn is not None:
+            ev_attn[0].record(stream)
         S.salad_attn_apply(layer.shape, qs, ks, vs, layer.row_ptr, layer.col_idx, gate, cfg.eps, 0.0, 0.0,
                            outs, layer.ws, sp)
+        if ev_attn is not None:
+            ev_attn[1].record(stream)
         if ev is not None:
             ev[4].record(stream)
         if cub:
@@ -306,20 +310,23 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # timed region: K whole steps, nothing else recorded on the stream
+    # timed region: K whole steps; the only other records on the stream are the
+    # HIP events around the attention call, whose mean is the roofline's kernel time
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
+    evs_attn = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start.record(stream)
     for i in range(args.steps):
-        step()
+        step(ev_attn=evs_attn[i])
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_total = t_start.elapsed_time(t_end)
     ms_step = ms_total / args.steps
-    # phase breakdown and per-step spread: K more steps after the timed region,
-    # with HIP events between the phases (they cost ~1% of a step, so they stay
-    # out of the timed region)
+    attn_timed = [e[0].elapsed_time(e[1]) for e in evs_attn]
+    # the other phases and the per-step spread: K more steps after the timed
+    # region, with HIP events between all the phases (six records per step cost
+    # about 1% of a step, so they stay out of the timed region)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     for i in range(args.steps):
         step(evs[i])
@@ -328,8 +335,8 @@ def main():
     perm = [e[0].elapsed_time(e[1]) + e[4].elapsed_time(e[5]) for e in evs]
     mask = [e[1].elapsed_time(e[2]) for e in evs]
     lin = [e[2].elapsed_time(e[3]) for e in evs]
-    attn = [e[3].elapsed_time(e[4]) for e in evs]
-    ms_mask, ms_lin, ms_attn = float(np.median(mask)), float(np.median(lin)), float(np.median(attn))
+    ms_mask, ms_lin = float(np.median(mask)), float(np.median(lin))
+    ms_attn = float(np.mean(attn_timed))  # average launch duration over the timed region
 
     row_ptr = layer.row_ptr.cpu().numpy()
     nnz = int(row_ptr[-1])
@@ -411,7 +418,9 @@ def main():
             "traffic": attn_traffic_bytes(cfg.name),
             "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "algorithmic_flop_per_launch": kept_flop,
-            "timing": "median of HIP events around salad_attn_apply (item split + attention kernel) on its stream",
+            "timing": "mean of HIP events around salad_attn_apply (item split + attention kernel) on its stream, "
+                      "over the timed region",
+            "kernel_ms": {"mean": round(ms_attn, 5), "median": round(float(np.median(attn_timed)), 5)},
         },
         "cpu_baseline": None,
     }
@@ -482,17 +491,15 @@ def main_backward(args):
     torch.cuda.synchronize()
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
+    # three HIP events per step in the timed region (the forward / backward split
+    # and the backward call's time for the roofline; ~0.1% of a training step)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t_start.record(stream)
     for i in range(args.steps):
-        step()
+        step(evs[i])
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / args.steps
-    # forward / backward split: K more steps with events, after the timed region
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
     ms_fwd = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     ms_bwd = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     nnz = int(layer.row_ptr[-1].item())
