@@ -49,7 +49,7 @@ ATTN_COUNTERS = {
     "source_sha256": "14d58dbb344972a3",
     "fetch_scale": 524288.0 / 262157.8,
     "write_scale": 1.0,
-    "c3": {"fetch_kib": 201170.7, "write_kib": 98304.0},
+    "c3": {"fetch_kib": 201862.3, "write_kib": 98304.0},
 }
 
 
