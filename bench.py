@@ -44,12 +44,12 @@ ATTN_KERNEL = "k_attn_bf16 (block-sparse flash attention + linear epilogue)"
 # HBM bytes per dispatch of the attention kernel from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE runs (KiB per dispatch), valid only for the kernel source they were
 # taken on (sha256 prefix); scaled by a plain 512 MiB copy, which reads
-# FETCH_SIZE = 262157.8 KiB and WRITE_SIZE = 524288 KiB.
+# FETCH_SIZE = 262157.9 KiB and WRITE_SIZE = 524288 KiB.
 ATTN_COUNTERS = {
-    "source_sha256": "14d58dbb344972a3",
-    "fetch_scale": 524288.0 / 262157.8,
+    "source_sha256": "5d5ed860335f9a3f",
+    "fetch_scale": 524288.0 / 262157.9,
     "write_scale": 1.0,
-    "c3": {"fetch_kib": 201862.3, "write_kib": 98304.0},
+    "c3": {"fetch_kib": 203247.8, "write_kib": 98304.0},
 }
 
 

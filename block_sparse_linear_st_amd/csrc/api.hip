@@ -219,7 +219,7 @@ Workspace plan_workspace(const Geom& g, const Cuboid& cu, int dtype) {
   const size_t esz = dtype == SALAD_BF16 ? 2 : 4;
   L.off_sft_hi = off; off = align_up(off + BH * D * D * esz);
   L.off_sft_lo = off; off = align_up(off + (dtype == SALAD_BF16 ? BH * D * D * 2 : 0));
-  L.off_split = off;  off = align_up(off + 9 * 4);
+  L.off_split = off;  off = align_up(off + (9 + kPairModeSlots) * 4);
   L.lin_end = off;
   L.bytes = std::max(L.mask_end, L.lin_end);
   return L;

@@ -87,11 +87,10 @@ __device__ __attribute__((always_inline)) inline void compute_tile32(const unsig
     }
   }
   if (key0 + 32 > N) {
+    // keys past N get -inf added (bit patterns, no per-key compare masks)
+    const int rem = N - key0 - g32 * 4;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = key0 + (i >> 2) * 8 + g32 * 4 + (i & 3);
-      if (key >= N) s[i] = -INFINITY;
-    }
+    for (int i = 0; i < 16; ++i) s[i] += past_n_bias(rem, (i >> 2) * 8 + (i & 3));
   }
   float mx = -INFINITY;
 #pragma unroll
@@ -236,13 +235,11 @@ __device__ __attribute__((always_inline)) inline void pipe_step(
   // scores of keys past N (only the tile holding token N-1 and beyond)
   if constexpr (QK) {
     if (key0 + 64 > N) {
+      const int rem = N - key0 - g32 * 4;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = key0 + kt * 32 + (i >> 2) * 8 + g32 * 4 + (i & 3);
-          if (key >= N) sn[kt][i] = -INFINITY;
-        }
+        for (int i = 0; i < 16; ++i) sn[kt][i] += past_n_bias(rem, kt * 32 + (i >> 2) * 8 + (i & 3));
     }
   }
 
@@ -365,6 +362,10 @@ k_attn_bf16(Geom g, AttnArgs a, int n_items, float c_log2) {
     int i0 = 0, e0 = 0, i1 = 0, e1 = 0;
     if (qb_base < g.nb) { i0 = rptr[rbase]; e0 = rptr[rbase + 1]; }
     if (QPW == 2 && qb_base + 1 < g.nb) { i1 = e0; e1 = rptr[rbase + 2]; }
+    // this head's layout (64-key tiles only): 0 walks the union of the two
+    // lists, 1 gives each wave pair its own block's list
+    const bool own_lists = KT == 64 && cuts[9 + (bh < kPairModeSlots ? bh : bh % g.Hh)] != 0;
+    const int i0s = i0, e0s = e0, i1s = i1, e1s = e1;
     int c0 = i0 < e0 ? col[i0] : INT32_MAX;
     int c1 = i1 < e1 ? col[i1] : INT32_MAX;
     // current tile
@@ -389,7 +390,7 @@ k_attn_bf16(Geom g, AttnArgs a, int n_items, float c_log2) {
     DmaOffsets<D, KT, NW> doff;
     doff.init(wave_u, lane);
     constexpr bool PIPE = KT == 64;  // 64-key tiles: the software-pipelined loop
-    if (valid) {
+    if (valid && !own_lists) {
       if constexpr (PIPE) issue_half<D, KT, NW, true>(lds0, Kb, kb * BLK + sub * KT, g.N, wave_u, lane, doff);
       else issue_tile<D, KT, NW>(lds0, Kb, Vb, kb * BLK + sub * KT, g.N, wave_u, lane, doff);
     }
@@ -436,7 +437,60 @@ k_attn_bf16(Geom g, AttnArgs a, int n_items, float c_log2) {
       __syncthreads();  // ... for every wave, and nobody still reads the current one
       kb = nkb; sub = nsub; flags = nflags; valid = nvalid;
     };
-    if constexpr (PIPE) {
+    if (PIPE && own_lists) {
+      // Each wave pair walks its own block's list in 32-key tiles through its
+      // own half of the LDS (two buffers), the pairs in step: max(L0, L1) * 2
+      // steps, a pair whose list is done idles at the barriers.
+      using LP = Lay<D, 32, 2>;
+      const int wp = wave_u & 1, qs = wave_u >> 1;
+      const uint32_t pbase = lds0 + qs * 2 * LP::BUF_B;
+      const unsigned char* psmem = smem + qs * 2 * LP::BUF_B;
+      DmaOffsets<D, 32, 2> poff;
+      poff.init(wp, lane);
+      uint32_t kb32, vb32;
+      {
+        const int sw = LP::kswz(l32), sl = lane & 15, dh = (lane >> 4) & 1;
+        const int row = 4 * g32 + (sl >> 2);
+        kb32 = (uint32_t)(l32 * LP::ROW_B + ((g32 ^ sw) << 4));
+        vb32 = (uint32_t)(row * LP::ROW_B + (((2 * dh + ((sl & 3) >> 1)) ^ LP::vswz(row)) << 4) + (sl & 1) * 8);
+        asm volatile("" : "+v"(kb32), "+v"(vb32));
+      }
+      constexpr int TP = BLK / 32;  // 32-key tiles per key block
+      const int ib = qs == 0 ? i0s : i1s;
+      const int len = qs == 0 ? e0s - i0s : e1s - i1s;
+      const int nsteps = max(e0s - i0s, e1s - i1s) * TP;
+      // tile of step s: sub-tile s % TP of list entry s / TP, if it holds a key below N
+      auto tile_at = [&](int s_, int& kb_) __attribute__((always_inline)) -> bool {
+        const int e = s_ / TP;
+        if (e >= len) return false;
+        kb_ = col[ib + e];
+        return kb_ * BLK + (s_ % TP) * 32 < g.N;
+      };
+      int s = 0, kb_c = 0;
+      bool v_c = nsteps > 0 && tile_at(0, kb_c);
+      if (v_c) issue_tile<D, 32, 2>(pbase, Kb, Vb, kb_c * BLK, g.N, wp, lane, poff);
+      wait_vmem();
+      __syncthreads();
+      auto ostep = [&](auto cur_c) __attribute__((always_inline)) {
+        constexpr int CUR = decltype(cur_c)::value;
+        int kb_n = 0;
+        const bool v_n = s + 1 < nsteps && tile_at(s + 1, kb_n);
+        if (v_n)
+          issue_tile<D, 32, 2>(pbase + (CUR ^ 1) * LP::BUF_B, Kb, Vb, kb_n * BLK + ((s + 1) % TP) * 32, g.N, wp,
+                               lane, poff);
+        if (wave_rows && v_c)
+          compute_tile32<D, CUR>(psmem, kb32, vb32, qf, o, m_used, l_run, kb_c * BLK + (s % TP) * 32, g.N, c_log2,
+                                 lane);
+        wait_vmem();      // the next tile has landed in LDS ...
+        __syncthreads();  // ... for both waves of the pair, and nobody still reads the current one
+        kb_c = kb_n; v_c = v_n; ++s;
+      };
+      while (s < nsteps) {
+        ostep(std::integral_constant<int, 0>{});
+        if (s >= nsteps) break;
+        ostep(std::integral_constant<int, 1>{});
+      }
+    } else if constexpr (PIPE) {
       // step u: tile u is (kb, sub, flags, valid), tile u-1 (pflags, pvalid); scores of
       // alternate tiles in sA / sB; one more step after the last tile finishes it
       f32x16 sA[2], sB[2];
@@ -640,7 +694,11 @@ hipError_t launch(const Geom& g, const AttnArgs& a, hipStream_t st) {
   // about three 64-key steps for the item's own loads and epilogue
   constexpr int KT = tile_keys<BLK>();
   constexpr int TPB = BLK / KT;
-  const ItemSplit job{a.row_ptr, a.split, g.B * g.Hh, g.nb, QPW, TPB, 3 * 64 / KT};
+  ItemSplit job{a.row_ptr, a.split, g.B * g.Hh, g.nb, QPW, TPB, 3 * 64 / KT};
+  if (KT == 64 && QPW == 2) {
+    job.col = a.col_idx;
+    job.mode_heads = g.Hh;
+  }
   hipError_t e = launch_item_splits(&job, 1, st);
   if (e != hipSuccess) return e;
   const int grid = 8 * xcd_items_cap(n_items);

@@ -61,6 +61,13 @@ __device__ inline float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// 0 for a key at offset kofs < rem inside its tile, -inf past it (rem = keys of
+// the tile below N, for this lane): an arithmetic select, so that masking a
+// tile's 16 or 32 scores keeps no compare masks alive in scalar registers.
+__device__ __attribute__((always_inline)) inline float past_n_bias(int rem, int kofs) {
+  return __int_as_float((int)(((uint32_t)((rem - 1 - kofs) >> 31)) & 0xff800000u));
+}
+
 // s_waitcnt vmcnt(0) as a compiler-visible instruction (gfx9 encoding: vmcnt 0,
 // expcnt 7, lgkmcnt 15), so the compiler knows every vector load has landed.
 __device__ __attribute__((always_inline)) inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }

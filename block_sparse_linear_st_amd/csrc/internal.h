@@ -18,6 +18,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kRstarInf = 1 << 30;
+// int32 words after the 9 per-XCD cuts of the forward item split: one layout
+// mode per head (sched.hip)
+constexpr int kPairModeSlots = SALAD_MAX_HEADS;
 
 // Geometry of the latent grid and its blocking, as kernels see it.
 struct Geom {
@@ -73,7 +76,7 @@ struct Workspace {
   size_t off_spart, off_zpart;     // float [splits][B*H][D*D], [splits][B*H][D]
   size_t off_z;                    // float [B*H][D]
   size_t off_sft_hi, off_sft_lo;   // folded state, transposed: bf16 or f32 [B*H][D*D]
-  size_t off_split;                // int32 [9]: attention items per XCD
+  size_t off_split;                // int32 [9 + kPairModeSlots]: attention items per XCD, layout modes
   size_t mask_end, lin_end;
 };
 
@@ -107,11 +110,24 @@ struct BwdWorkspace {
 // items XCD x runs, cut by estimated work (kept blocks * tpb + ovh per item),
 // each run at most xcd_items_cap(n_items) long: the consumer launches 8 times
 // that many workgroups.
+//
+// With mode_heads > 0 (forward kernels whose workgroups own two neighbouring
+// query blocks, per = 2), the same launch also chooses, per head, how those
+// workgroups walk the kept lists: mode 0, the union of both blocks' lists with
+// all four waves (tiles kept by both blocks are loaded once); mode 1, each wave
+// pair its own block's list (no wave sits out a tile its block does not keep).
+// Mode 1 is chosen when sampled neighbouring lists of the head (batch 0)
+// overlap little: their union is more than 5/4 of the longer list.  Word
+// split[9 + x] receives the mode of sequence x (head x % mode_heads) for every
+// x < min(n_seq, kPairModeSlots).  Both modes compute the same attention, up
+// to the order of floating-point sums.
 __host__ __device__ inline int xcd_items_cap(int n_items) { return (n_items + 7) / 8 + (n_items + 31) / 32; }
 struct ItemSplit {
   const int32_t* ptr;  // pointer array over n_seq * nrows rows
-  int32_t* split;      // [9] output
+  int32_t* split;      // [9] output, then [mode_heads] modes when mode_heads > 0
   int n_seq, nrows, per, tpb, ovh;
+  const int32_t* col = nullptr;  // the rows' entries (needed for the modes)
+  int mode_heads = 0;            // 0: no modes; else heads <= kPairModeSlots
 };
 // One workgroup per job (one or two jobs per launch).
 SALAD_HIDDEN hipError_t launch_item_splits(const ItemSplit* jobs, int n_jobs, hipStream_t st);

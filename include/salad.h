@@ -245,6 +245,11 @@ SALAD_API int salad_linear_state(const salad_shape* shape, const void* k, const 
  *   without a check, so an entry >= nb reads outside k and v; masks from
  *   salad_build_mask always hold, others can be checked with salad_check_mask.
  * o_l: ReLU(q_i)^T S / (ReLU(q_i)^T z + eps) with S, z as salad_linear_state.
+ * Equal inputs give bitwise equal outputs.  For bf16 shapes with 64-token
+ *   blocks the kernel walks each head's kept lists in one of two orders,
+ *   chosen on the device from how much neighbouring query blocks' lists
+ *   overlap (a function of the mask alone); the choice changes only the
+ *   order of floating-point sums.
  *   gate   device float [batch*heads], values in (0,1) by the method's design
  *          (any finite value is accepted)
  *   w_lin  device [head_dim*head_dim] in the shape's dtype, row-major, applied

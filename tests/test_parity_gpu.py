@@ -419,6 +419,36 @@ def test_empty_and_hand_built_rows(dt):
     assert torch.count_nonzero(o_s[0, 1, :128]).item() == 0
 
 
+def test_union_and_own_list_layouts_in_one_launch():
+    """Heads whose neighbouring query blocks keep nearly the same key blocks (walked as the union of the two
+    lists) beside heads whose neighbours share few or none (each wave pair walks its own block's list), two
+    batches, 630 tokens (a 54-token tail block), against the oracle on every output row."""
+    cfg = LayerConfig(name="layouts", seed=21, batch=2, heads=4, head_dim=128, T=3, H=10, W=21, block=64,
+                      dtype="bf16", specs=(HeadSpec(0, 1, -1, 0.0),) * 4, gate_kind="uniform")
+    inp = make_inputs(cfg)
+    layer = make_layer(cfg)
+    q, k, v, w = device_tensors(inp)
+    nb = cfg.nb
+    rng = np.random.default_rng(5)
+    keep = np.zeros((2, 4, nb, nb), dtype=bool)
+    for b in range(2):
+        keep[b, 0] = rng.random((nb, nb)) < 0.35                        # scattered: little overlap
+        for qb in range(nb):                                            # a band: neighbours nearly equal
+            keep[b, 1, qb, max(0, qb - 2):qb + 3] = True
+        for qb in range(nb):                                            # neighbours disjoint
+            keep[b, 2, qb, (qb % 2)::2] = True
+        keep[b, 3, 0::2, :] = True                                      # every other row full, the rest empty
+    rp, ci = oracle.csr_from_keep(keep)
+    layer.row_ptr.copy_(torch.from_numpy(rp))
+    layer.col_idx[:len(ci)].copy_(torch.from_numpy(ci))
+    gate = torch.from_numpy(inp.gate).cuda()
+    out = torch.empty_like(q)
+    layer.forward(q, k, v, gate, w, out, eps=cfg.eps)
+    torch.cuda.synchronize()
+    ref, _, _ = oracle.layer_forward(inp.q, inp.k, inp.v, rp, ci, inp.gate, inp.w_lin, cfg.N, cfg.block, cfg.eps)
+    assert_close(to_numpy(out), ref, BF16_MAX_ABS, BF16_REL_L2, "layouts")
+
+
 @pytest.mark.parametrize("cuboid", [(0, 0, 0), (1, 2, 32)], ids=["runs", "cuboids"])
 def test_window_mask_grid_wider_than_rank_range(cuboid):
     """max(H, W) above 4096, beyond the symmetric r* kernel's rank range: the table and its histogram come from
