@@ -317,6 +317,10 @@ k_attn_bwd_dq2(Geom g, BwdArgs a, int n_items, const int32_t* __restrict__ cuts,
   int i0 = 0, e0 = 0, i1 = 0, e1 = 0;
   if (qb_base < g.nb) { i0 = a.row_ptr[rbase]; e0 = a.row_ptr[rbase + 1]; }
   if (QPW == 2 && qb_base + 1 < g.nb) { i1 = e0; e1 = a.row_ptr[rbase + 2]; }
+  // this head's layout (as the forward kernel's): 0 walks the union of the two
+  // lists, 1 gives each wave pair its own block's list
+  const bool own_lists = QPW == 2 && cuts[9 + (bh < kPairModeSlots ? bh : bh % g.Hh)] != 0;
+  const int i0s = i0, e0s = e0, i1s = i1, e1s = e1;
   int c0 = i0 < e0 ? a.col_idx[i0] : INT32_MAX;
   int c1 = i1 < e1 ? a.col_idx[i1] : INT32_MAX;
   int kb = 0, sub = 0, flags = 0;
@@ -342,7 +346,7 @@ k_attn_bwd_dq2(Geom g, BwdArgs a, int n_items, const int32_t* __restrict__ cuts,
     dma.issue(lds0 + buf * BUF, K, key0, g.N - 1);
     dma.issue(lds0 + buf * BUF + TB, V, key0, g.N - 1);
   };
-  if (more) issue(kb * BLK + sub * kT, 0);
+  if (more && !own_lists) issue(kb * BLK + sub * kT, 0);
   wait_vmem();
   __syncthreads();
 
@@ -359,10 +363,10 @@ k_attn_bwd_dq2(Geom g, BwdArgs a, int n_items, const int32_t* __restrict__ cuts,
   asm volatile("" : "+v"(od), "+v"(otr));
   static_assert(TL::xor_rebuild_holds(), "swizzle rebuild assumed below");
 
-  auto compute = [&](auto cur_c, int key0) __attribute__((always_inline)) {
-    constexpr int CUR = decltype(cur_c)::value;
-    const unsigned char* Kt = smem + CUR * BUF;
-    const unsigned char* Vt = Kt + TB;
+  // the products of one K/V tile of KH 32-key halves at Kt, Vt
+  auto compute_at = [&](const unsigned char* Kt, const unsigned char* Vt, auto kh_c, int key0)
+                        __attribute__((always_inline)) {
+    constexpr int KH = decltype(kh_c)::value;
     auto rd = [&](const unsigned char* base, int c, int kt) __attribute__((always_inline)) {
       return __builtin_bit_cast(bf16x8,
                                 *reinterpret_cast<const uint4*>(base + (od ^ (c << 5)) + kt * 32 * TL::ROW_B));
@@ -378,7 +382,7 @@ k_attn_bwd_dq2(Geom g, BwdArgs a, int n_items, const int32_t* __restrict__ cuts,
       return __builtin_bit_cast(bf16x8, make_uint4(tr[0].x, tr[0].y, tr[1].x, tr[1].y));
     };
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < KH; ++kt) {
       // S^T and dP^T of 32 keys: two chains, fragments read one contraction step ahead
       f32x16 s, dp;
       zero(s);
@@ -416,6 +420,10 @@ k_attn_bwd_dq2(Geom g, BwdArgs a, int n_items, const int32_t* __restrict__ cuts,
       }
     }
   };
+  auto compute = [&](auto cur_c, int key0) __attribute__((always_inline)) {
+    constexpr int CUR = decltype(cur_c)::value;
+    compute_at(smem + CUR * BUF, smem + CUR * BUF + TB, std::integral_constant<int, 2>{}, key0);
+  };
   auto step = [&](auto cur_c) __attribute__((always_inline)) {
     constexpr int CUR = decltype(cur_c)::value;
     int nkb, nsub, nflags;
@@ -427,10 +435,57 @@ k_attn_bwd_dq2(Geom g, BwdArgs a, int n_items, const int32_t* __restrict__ cuts,
     __syncthreads();
     kb = nkb; sub = nsub; flags = nflags; more = nmore;
   };
-  while (more) {
-    step(std::integral_constant<int, 0>{});
-    if (!more) break;
-    step(std::integral_constant<int, 1>{});
+  if (own_lists) {
+    // each wave pair walks its own block's list in 32-key tiles through its
+    // own half of the LDS (two buffers of K then V), the pairs in step
+    constexpr int TB32 = 32 * TL::ROW_B, BUF32 = 2 * TB32;
+    const int wp = wave_u & 1, qs = wave_u >> 1;
+    const uint32_t pbase = lds0 + qs * 2 * BUF32;
+    const unsigned char* psmem = smem + qs * 2 * BUF32;
+    TileDma<D, 2, 32> pdma;
+    pdma.init(wp, lane);
+    constexpr int TP = BLK / 32;  // 32-key tiles per key block
+    const int ib = qs == 0 ? i0s : i1s;
+    const int len = qs == 0 ? e0s - i0s : e1s - i1s;
+    const int nsteps = max(e0s - i0s, e1s - i1s) * TP;
+    auto tile_at = [&](int s_, int& kb_) __attribute__((always_inline)) -> bool {
+      const int e = s_ / TP;
+      if (e >= len) return false;
+      kb_ = a.col_idx[ib + e];
+      return kb_ * BLK + (s_ % TP) * 32 < g.N;
+    };
+    auto pissue = [&](int key0, int buf) __attribute__((always_inline)) {
+      pdma.issue(pbase + buf * BUF32, K, key0, g.N - 1);
+      pdma.issue(pbase + buf * BUF32 + TB32, V, key0, g.N - 1);
+    };
+    int s = 0, kb_c = 0;
+    bool v_c = nsteps > 0 && tile_at(0, kb_c);
+    if (v_c) pissue(kb_c * BLK, 0);
+    wait_vmem();
+    __syncthreads();
+    auto ostep = [&](auto cur_c) __attribute__((always_inline)) {
+      constexpr int CUR = decltype(cur_c)::value;
+      int kb_n = 0;
+      const bool v_n = s + 1 < nsteps && tile_at(s + 1, kb_n);
+      if (v_n) pissue(kb_n * BLK + ((s + 1) % TP) * 32, CUR ^ 1);
+      if (wave_rows && v_c)
+        compute_at(psmem + CUR * BUF32, psmem + CUR * BUF32 + TB32, std::integral_constant<int, 1>{},
+                   kb_c * BLK + (s % TP) * 32);
+      wait_vmem();      // the next tile has landed in LDS ...
+      __syncthreads();  // ... for both waves of the pair, and nobody still reads the current one
+      kb_c = kb_n; v_c = v_n; ++s;
+    };
+    while (s < nsteps) {
+      ostep(std::integral_constant<int, 0>{});
+      if (s >= nsteps) break;
+      ostep(std::integral_constant<int, 1>{});
+    }
+  } else {
+    while (more) {
+      step(std::integral_constant<int, 0>{});
+      if (!more) break;
+      step(std::integral_constant<int, 1>{});
+    }
   }
 
   // linear term: (S dU^T + z dden^T) * [q > 0], S rows c as hi + lo bf16
@@ -697,8 +752,12 @@ hipError_t launch_bwd_t(const Geom& g, const BwdArgs& a, char* ws, const BwdWork
   const int32_t* colptr = reinterpret_cast<const int32_t*>(ws + L.off_colptr);
   int32_t* qcuts = reinterpret_cast<int32_t*>(ws + L.off_split_q);
   int32_t* kcuts = reinterpret_cast<int32_t*>(ws + L.off_split_k);
-  const ItemSplit jobs[2] = {{colptr, kcuts, g.B * g.Hh, g.nb, 1, BLK / kT, 2 * 64 / kT},
-                             {a.row_ptr, qcuts, g.B * g.Hh, g.nb, QPW, BLK / kT, 3 * 64 / kT}};
+  ItemSplit jobs[2] = {{colptr, kcuts, g.B * g.Hh, g.nb, 1, BLK / kT, 2 * 64 / kT},
+                       {a.row_ptr, qcuts, g.B * g.Hh, g.nb, QPW, BLK / kT, 3 * 64 / kT}};
+  if (QPW == 2) {  // the dQ kernel's per-head list layout, as in the forward
+    jobs[1].col = a.col_idx;
+    jobs[1].mode_heads = g.Hh;
+  }
   hipError_t e = launch_item_splits(jobs, a.lse != nullptr ? 2 : 1, st);
   if (e != hipSuccess) return e;
   if (a.lse != nullptr) {

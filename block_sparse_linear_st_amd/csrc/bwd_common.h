@@ -132,14 +132,14 @@ __device__ __attribute__((always_inline)) inline const __bf16* uniform_ptr(const
   return reinterpret_cast<const __bf16*>(((uint64_t)hi << 32) | lo);
 }
 
-// DMA of a 64-row tile of a row-major [*, D] bf16 array into a swizzled LDS
-// tile.  NW waves share it; wave w fills its 1 KiB blocks w*LOADS ..
-// w*LOADS+LOADS-1.  The per-lane byte offsets inside a tile do not depend on
-// the tile: they are computed once.
-template <int D, int NW>
+// DMA of a ROWS-row tile (64, or 32) of a row-major [*, D] bf16 array into a
+// swizzled LDS tile.  NW waves share it; wave w fills its 1 KiB blocks
+// w*LOADS .. w*LOADS+LOADS-1.  The per-lane byte offsets inside a tile do not
+// depend on the tile: they are computed once.
+template <int D, int NW, int ROWS = 64>
 struct TileDma {
   using TL = TileLay<D>;
-  static constexpr int LOADS = 64 * TL::ROW_B / 1024 / NW;
+  static constexpr int LOADS = ROWS * TL::ROW_B / 1024 / NW;
   static_assert(LOADS >= 1, "tile too small for the waves");
   uint32_t off[LOADS];
   int wave_u, lane;
@@ -153,10 +153,10 @@ struct TileDma {
       off[i] = (uint32_t)(r * TL::ROW_B + ((p ^ TL::swz(r)) << 4));
     }
   }
-  // rows [row0, row0 + 64) into the tile at LDS byte address lds; rows past
+  // rows [row0, row0 + ROWS) into the tile at LDS byte address lds; rows past
   // `last` repeat row `last` (only in the tile that holds it)
   __device__ __attribute__((always_inline)) void issue(uint32_t lds, const __bf16* src, int row0, int last) const {
-    if (row0 + 64 <= last + 1) {
+    if (row0 + ROWS <= last + 1) {
       const __bf16* base = uniform_ptr(src + (int64_t)row0 * D);
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) lds_dma16_s(off[i], base, lds + (wave_u * LOADS + i) * 1024);

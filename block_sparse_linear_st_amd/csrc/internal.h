@@ -100,7 +100,8 @@ struct BwdWorkspace {
   size_t off_colcnt, off_colptr;      // int32 [BH*nb], [BH*nb + 1]
   size_t off_rowidx;                  // int32 [BH*nb*nb]
   size_t off_bits;                    // uint32 [BH*nb][ceil(nb/32)]: transposed mask bitmap
-  size_t off_split_q, off_split_k;    // int32 [9] each: dQ and dK/dV items per XCD
+  size_t off_split_q, off_split_k;    // int32 [9 + kPairModeSlots], [9]: dQ items per XCD and layout modes,
+                                      // dK/dV items per XCD
 };
 
 // ---- XCD assignment of attention items (sched.hip) ----------------------------

@@ -509,7 +509,7 @@ BwdWorkspace plan_bwd_workspace(const Geom& g, const Cuboid& cu, int dtype) {
   L.off_colptr = off; off = al(off + (BH * nb + 1) * 4);
   L.off_rowidx = off; off = al(off + BH * nb * nb * 4);
   L.off_bits = off;   off = al(off + BH * nb * ((nb + 31) / 32) * 4);
-  L.off_split_q = off; off = al(off + 9 * 4);
+  L.off_split_q = off; off = al(off + (9 + kPairModeSlots) * 4);
   L.off_split_k = off; off = al(off + 9 * 4);
   L.bytes = off;
   return L;

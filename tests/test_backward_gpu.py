@@ -306,3 +306,54 @@ def test_skewed_heads_hand_built_mask():
                          g["dk"], g["dv"], g["dw"], g["dg"], ws, lse=lse_arg)
         torch.cuda.synchronize()
         _compare(cfg, g, ref, f"skewed ({tag})")
+
+
+def test_union_and_own_list_layouts_backward():
+    """The mixed-overlap mask of the forward layout test (scattered, banded, disjoint-neighbour and half-empty
+    heads; two batches; a 54-token tail block): the dQ kernel walks the union of paired lists for some heads and
+    each block's own list for others; forward, its log2-sum-exp and both backward paths against the oracle."""
+    print("list layouts backward", flush=True)
+    from helpers import BF16_MAX_ABS, BF16_REL_L2, assert_close
+    cfg = LayerConfig(name="layouts", seed=21, batch=2, heads=4, head_dim=128, T=3, H=10, W=21, block=64,
+                      dtype="bf16", specs=(HeadSpec(0, 1, -1, 0.0),) * 4, gate_kind="uniform")
+    nb = cfg.nb
+    rng = np.random.default_rng(5)
+    keep = np.zeros((2, 4, nb, nb), dtype=bool)
+    for b in range(2):
+        keep[b, 0] = rng.random((nb, nb)) < 0.35
+        for qb in range(nb):
+            keep[b, 1, qb, max(0, qb - 2):qb + 3] = True
+            keep[b, 2, qb, (qb % 2)::2] = True
+        keep[b, 3, 0::2, :] = True
+    rp, ci = oracle.csr_from_keep(keep)
+    inp = make_inputs(cfg)
+    layer = make_layer(cfg)
+    q, k, v, w = device_tensors(inp)
+    row_ptr = torch.from_numpy(rp).cuda()
+    col_idx = torch.from_numpy(ci).cuda()
+    gate = torch.from_numpy(inp.gate).cuda()
+    out = torch.empty_like(q)
+    lse = torch.full((cfg.batch * cfg.heads * cfg.n_pad,), float("nan"), dtype=torch.float32, device="cuda")
+    S.salad_attn_fwd(layer.shape, q, k, v, row_ptr, col_idx, gate, w, cfg.eps, 0.0, 0.0, out, layer.ws, lse=lse)
+    torch.cuda.synchronize()
+    ref_out, _, _ = oracle.layer_forward(inp.q, inp.k, inp.v, rp, ci, inp.gate, inp.w_lin, cfg.N, cfg.block,
+                                         cfg.eps)
+    assert_close(to_numpy(out), ref_out, BF16_MAX_ABS, BF16_REL_L2, "layouts forward")
+    want = oracle.sparse_lse2(inp.q, inp.k, rp, ci, cfg.N, cfg.block)[:, :, :cfg.N]
+    got_lse = lse.view(cfg.batch, cfg.heads, cfg.n_pad).cpu().numpy()[:, :, :cfg.N]
+    kept = np.isfinite(want)  # rows of head 3's empty query blocks keep no key: +inf on both sides
+    assert np.array_equal(np.isfinite(got_lse), kept) and np.all(got_lse[~kept] == np.inf)
+    assert float(np.max(np.abs(got_lse[kept] - want[kept]))) <= 2e-2
+    dvals, dbits = make_grad_output(cfg)
+    dout = torch.from_numpy(dbits.view(np.int16)).view(torch.bfloat16).cuda()
+    ws = torch.empty(S.salad_bwd_workspace_bytes(layer.shape), dtype=torch.uint8, device="cuda")
+    ref = oracle.layer_backward(inp.q, inp.k, inp.v, rp, ci, inp.gate.astype(np.float64), inp.w_lin, cfg.N,
+                                cfg.block, cfg.eps, dvals)
+    for lse_arg, tag in ((lse, "forward lse"), (None, "recomputed lse")):
+        g = {n: torch.full_like(q, float("nan")) for n in ("dq", "dk", "dv")}
+        g["dw"] = torch.full((cfg.head_dim, cfg.head_dim), float("nan"), dtype=torch.float32, device="cuda")
+        g["dg"] = torch.full((cfg.batch * cfg.heads,), float("nan"), dtype=torch.float32, device="cuda")
+        S.salad_attn_bwd(layer.shape, q, k, v, row_ptr, col_idx, gate, w, cfg.eps, 0.0, out, dout, g["dq"],
+                         g["dk"], g["dv"], g["dw"], g["dg"], ws, lse=lse_arg)
+        torch.cuda.synchronize()
+        _compare(cfg, g, ref, f"layouts ({tag})")
