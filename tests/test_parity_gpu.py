@@ -360,6 +360,9 @@ RAGGED = [
     (1, 3, 128, 3, 6, 37, 64, "f32", [HeadSpec(0, 1, 3, 0.0), HeadSpec(1, 0, -1, 0.1), HeadSpec(0, 1, -1, 0.15)]),
     (2, 2, 64, 4, 8, 9, 128, "f32", [HeadSpec(1, 0, -1, 0.5), HeadSpec(0, 1, -1, 0.5)]),
     (1, 128, 64, 1, 4, 40, 64, "bf16", [HeadSpec(h % 2, 1, -1, 0.5) for h in range(128)]),
+    # one key block (no neighbouring pair to sample), and 192 sequences (per-head layout words past 128)
+    (1, 2, 128, 1, 5, 9, 64, "bf16", [HeadSpec(0, 1, -1, 0.0), HeadSpec(1, 0, -1, 1.0)]),
+    (2, 96, 64, 1, 4, 40, 64, "bf16", [HeadSpec(h % 2, 1, -1, 0.5) for h in range(96)]),
 ]
 
 
