@@ -264,19 +264,17 @@ k_lin_fold(Geom g, int splits, const float* __restrict__ spart, const float* __r
     const int e = v * 4;  // element offset inside the row block
     const float* src = spart + (int64_t)bh * D * D + (int64_t)r0 * D + e;
     const int64_t stride = BH * D * D;
-    int sp = s0;
-    for (; sp + 8 <= s1; sp += 8) {
+    // up to 8 loads in flight, added in split order
+    for (int sp = s0; sp < s1; sp += 8) {
       float4 x[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) x[u] = *reinterpret_cast<const float4*>(src + (sp + u) * stride);
+      for (int u = 0; u < 8; ++u)
+        if (sp + u < s1) x[u] = *reinterpret_cast<const float4*>(src + (sp + u) * stride);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        acc.x += x[u].x; acc.y += x[u].y; acc.z += x[u].z; acc.w += x[u].w;
-      }
-    }
-    for (; sp < s1; ++sp) {
-      const float4 x = *reinterpret_cast<const float4*>(src + sp * stride);
-      acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
+      for (int u = 0; u < 8; ++u)
+        if (sp + u < s1) {
+          acc.x += x[u].x; acc.y += x[u].y; acc.z += x[u].z; acc.w += x[u].w;
+        }
     }
     parts[tid] = acc;
   }
@@ -296,22 +294,25 @@ k_lin_fold(Geom g, int splits, const float* __restrict__ spart, const float* __r
       const float* zp = zpart + (int64_t)bh * D + c;
       const int64_t zstride = BH * D;
       float s = 0.0f;
-      int sp = 0;
-      for (; sp + 8 <= splits; sp += 8) {
+      for (int sp = 0; sp < splits; sp += 8) {
         float v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = zp[(sp + u) * zstride];
+        for (int u = 0; u < 8; ++u)
+          if (sp + u < splits) v[u] = zp[(sp + u) * zstride];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) s += v[u];
+        for (int u = 0; u < 8; ++u)
+          if (sp + u < splits) s += v[u];
       }
-      for (; sp < splits; ++sp) s += zp[sp * zstride];
       z_ws[(int64_t)bh * D + c] = s;
       if (z_out) z_out[(int64_t)bh * D + c] = s;
     }
   }
   if (mode == 2) return;
   if (mode == 0) {
-    for (int i = tid; i < D * D; i += 256) Ws[i] = w[i];
+    // 16-byte copies (w_lin is 16-byte aligned)
+    constexpr int PER16 = 16 / (int)sizeof(WT);
+    for (int i = tid; i < D * D / PER16; i += 256)
+      reinterpret_cast<uint4*>(Ws)[i] = reinterpret_cast<const uint4*>(w)[i];
   }
   __syncthreads();
   const float gv = mode == 0 ? gate[bh] : 1.0f;
