@@ -450,6 +450,14 @@ def test_union_and_own_list_layouts_in_one_launch():
     torch.cuda.synchronize()
     ref, _, _ = oracle.layer_forward(inp.q, inp.k, inp.v, rp, ci, inp.gate, inp.w_lin, cfg.N, cfg.block, cfg.eps)
     assert_close(to_numpy(out), ref, BF16_MAX_ABS, BF16_REL_L2, "layouts")
+    # branch dropping across both layouts: heads whose gate is below the median keep o_s only
+    tau = float(np.median(inp.gate))
+    out2 = torch.full_like(q, float("nan"))
+    layer.forward(q, k, v, gate, w, out2, eps=cfg.eps, drop_tau=tau)
+    torch.cuda.synchronize()
+    ref2, _, _ = oracle.layer_forward(inp.q, inp.k, inp.v, rp, ci, inp.gate, inp.w_lin, cfg.N, cfg.block, cfg.eps,
+                                      drop_tau=tau)
+    assert_close(to_numpy(out2), ref2, BF16_MAX_ABS, BF16_REL_L2, "layouts, branch dropping")
 
 
 @pytest.mark.parametrize("cuboid", [(0, 0, 0), (1, 2, 32)], ids=["runs", "cuboids"])
