@@ -101,7 +101,6 @@ k_lin_partial_bf16(Geom g, const __bf16* __restrict__ K, const __bf16* __restric
                    float* __restrict__ spart, float* __restrict__ zpart, const float* __restrict__ gate,
                    float drop_tau) {
   using LY = LinLay<D>;
-  if (gate != nullptr && gate[blockIdx.y] < drop_tau) return;  // dropped head: no linear state
   constexpr int TD = D / 32;           // 32-wide output tiles per dimension
   constexpr int TPW = TD * TD / 4;     // output tiles per wave
   constexpr int RING = 4;              // tile buffers: three tiles in flight while one is reduced
@@ -140,6 +139,12 @@ k_lin_partial_bf16(Geom g, const __bf16* __restrict__ K, const __bf16* __restric
     }
   };
   for (int tt = 0; tt < RING - 1 && tt < T; ++tt) issue(tt);
+  // the gate is read once the first tiles are on their way, so that its latency
+  // does not delay them
+  if (gate != nullptr && gate[bh] < drop_tau) {  // dropped head: no linear state
+    wait_vmem();
+    return;
+  }
   for (int tt = 0; tt < T; ++tt) {
     // tile tt has landed once at most min(T - 1 - tt, RING - 2) later tiles are outstanding
     const int ahead = min(T - 1 - tt, RING - 2);
@@ -235,9 +240,22 @@ k_lin_partial_f32(Geom g, const float* __restrict__ K, const float* __restrict__
   if (c0 == 0) zpart[((int64_t)split * g.B * g.Hh + bh) * D + r] = zacc;
 }
 
-// grid (B*H, D/2), 256 threads: reduce 2 rows of S over the splits (in
-// ordered parts), then fold.  mode 0: S'' = g*S*W; 1: S'' = S; 2: state only.  In mode
-// 0 heads with g < drop_tau are skipped (their partials were never written).
+// dst[256 u + tid] = src[256 u + tid] for u < N: every load issued before the
+// first store
+template <int N>
+__device__ __attribute__((always_inline)) inline void stage16(const uint4* __restrict__ src,
+                                                             uint4* __restrict__ dst, int tid) {
+  uint4 x[N];
+#pragma unroll
+  for (int u = 0; u < N; ++u) x[u] = src[256 * u + tid];
+#pragma unroll
+  for (int u = 0; u < N; ++u) dst[256 * u + tid] = x[u];
+}
+
+// grid (B*H, D/2), 256 threads: reduce 2 rows of S and the same 2 channels of z
+// over the splits (in ordered parts), then fold.  mode 0: S'' = g*S*W; 1: S'' = S;
+// 2: state only.  In mode 0 heads with g < drop_tau are skipped (their partials
+// were never written).
 template <typename WT, bool BF16OUT>
 __global__ void __launch_bounds__(256)
 k_lin_fold(Geom g, int splits, const float* __restrict__ spart, const float* __restrict__ zpart,
@@ -247,10 +265,21 @@ k_lin_fold(Geom g, int splits, const float* __restrict__ spart, const float* __r
   constexpr int FR = 2;  // rows of S per workgroup
   __shared__ float Srows[FR][128];
   __shared__ float4 parts[256];
+  __shared__ float zsp[FR][256];  // z of channels r0, r0 + 1: one entry per split (splits <= 256)
   __shared__ WT Ws[128 * 128];  // W_lin, staged once per workgroup (mode 0)
   const int D = g.D, bh = blockIdx.x, r0 = blockIdx.y * FR, tid = threadIdx.x;
-  if (mode == 0 && gate[bh] < drop_tau) return;
   const int64_t BH = (int64_t)g.B * g.Hh;
+  if (mode == 0 && gate[bh] < drop_tau) return;
+  // this workgroup's z entries (channel r0 + i / splits, split i % splits), loaded
+  // beside the partial rows so that both take one round trip
+  // (indices past the last entry reload it: straight-line loads, none waited on here)
+  float zv[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int i = min(tid + 256 * u, FR * splits - 1);
+    const int rr = i / splits, sp = i - rr * splits;
+    zv[u] = zpart[(int64_t)sp * BH * D + (int64_t)bh * D + r0 + rr];
+  }
   const int nvec = FR * D / 4;  // float4s in this row block (64 or 32)
   const int np = 256 / nvec;    // threads per float4 (4 or 8)
   // np threads per float4: part p sums splits [p * len, (p + 1) * len) in
@@ -278,6 +307,14 @@ k_lin_fold(Geom g, int splits, const float* __restrict__ spart, const float* __r
     }
     parts[tid] = acc;
   }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int i = tid + 256 * u;
+    if (i < FR * splits) {
+      const int rr = i / splits;
+      zsp[rr][i - rr * splits] = zv[u];
+    }
+  }
   __syncthreads();
   if (part == 0) {
     for (int p = 1; p < np; ++p) {
@@ -288,31 +325,21 @@ k_lin_fold(Geom g, int splits, const float* __restrict__ spart, const float* __r
     Srows[rr][c] = acc.x; Srows[rr][c + 1] = acc.y; Srows[rr][c + 2] = acc.z; Srows[rr][c + 3] = acc.w;
     if (S_out) *reinterpret_cast<float4*>(S_out + (int64_t)bh * D * D + (int64_t)r0 * D + e) = acc;
   }
-  if (blockIdx.y == 0) {
-    for (int c = tid; c < D; c += 256) {
-      // the same split order as above, loads batched 8 deep
-      const float* zp = zpart + (int64_t)bh * D + c;
-      const int64_t zstride = BH * D;
-      float s = 0.0f;
-      for (int sp = 0; sp < splits; sp += 8) {
-        float v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          if (sp + u < splits) v[u] = zp[(sp + u) * zstride];
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          if (sp + u < splits) s += v[u];
-      }
-      z_ws[(int64_t)bh * D + c] = s;
-      if (z_out) z_out[(int64_t)bh * D + c] = s;
-    }
+  if (tid < FR) {
+    // z summed over the splits in split order
+    float z = 0.0f;
+    for (int sp = 0; sp < splits; ++sp) z += zsp[tid][sp];
+    z_ws[(int64_t)bh * D + r0 + tid] = z;
+    if (z_out) z_out[(int64_t)bh * D + r0 + tid] = z;
   }
   if (mode == 2) return;
   if (mode == 0) {
-    // 16-byte copies (w_lin is 16-byte aligned)
+    // 16-byte copies (w_lin is 16-byte aligned), all of a thread's loads in flight at once
     constexpr int PER16 = 16 / (int)sizeof(WT);
-    for (int i = tid; i < D * D / PER16; i += 256)
-      reinterpret_cast<uint4*>(Ws)[i] = reinterpret_cast<const uint4*>(w)[i];
+    const uint4* src = reinterpret_cast<const uint4*>(w);
+    uint4* dst = reinterpret_cast<uint4*>(Ws);
+    if (D == 128) stage16<128 * 128 / PER16 / 256>(src, dst, tid);
+    else stage16<64 * 64 / PER16 / 256>(src, dst, tid);
   }
   __syncthreads();
   const float gv = mode == 0 ? gate[bh] : 1.0f;
