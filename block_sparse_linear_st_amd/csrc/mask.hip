@@ -236,12 +236,33 @@ k_window_threshold(Geom g, HeadTable ht, int grp, const uint16_t* rt, const int3
     if (t == 0) thr[h] = -1;
     return;
   }
-  // 1) the bin that holds the K-th pair (segments of whole int4s, loads batched)
+  // 1) the bin that holds the K-th pair.  Thread t owns the bins [t*seg, t*seg + seg)
+  //    (seg a multiple of 4, so each int4 is aligned; the workspace rounds the
+  //    histogram up to 256 bytes, and entries past hist_bins count as 0), read
+  //    kVec int4s at a time with every load of a batch in flight.
+  constexpr int kVec = 8;
   const int64_t seg = (hist_bins + 4 * kScanThreads - 1) / (4 * kScanThreads) * 4;
   const int64_t lo = min((int64_t)t * seg, hist_bins), hi = min(lo + seg, hist_bins);
+  auto load_bins = [&](int64_t b0, int4* x) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kVec; ++u) {
+      const int64_t b = min(b0 + 4 * u, (hist_bins - 1) / 4 * 4);  // in bounds, masked below
+      x[u] = *reinterpret_cast<const int4*>(hist + b);
+    }
+  };
+  auto bin_at = [&](const int4* x, int64_t b0, int i) __attribute__((always_inline)) -> int {
+    const int4 v = x[i >> 2];
+    const int e = i & 3;
+    const int c = e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
+    return b0 + i < hi ? c : 0;
+  };
   int64_t local = 0;
-#pragma unroll 8
-  for (int64_t b = lo; b < hi; ++b) local += hist[b];
+  for (int64_t b0 = lo; b0 < hi; b0 += 4 * kVec) {
+    int4 x[kVec];
+    load_bins(b0, x);
+#pragma unroll
+    for (int i = 0; i < 4 * kVec; ++i) local += bin_at(x, b0, i);
+  }
   int64_t total;
   const int64_t excl = block_exclusive_scan(local, tmp, &total);
   if (total < K) {  // not reached: the host rejects K above the candidate count
@@ -250,32 +271,53 @@ k_window_threshold(Geom g, HeadTable ht, int grp, const uint16_t* rt, const int3
   }
   if (excl < K && K <= excl + local) {
     int64_t cum = excl;
-    for (int64_t b = lo; b < hi; ++b) {
-      if (cum + hist[b] >= K) { s_bin = b; s_need = K - cum; break; }
-      cum += hist[b];
+    bool found = false;
+    for (int64_t b0 = lo; b0 < hi && !found; b0 += 4 * kVec) {
+      int4 x[kVec];
+      load_bins(b0, x);
+#pragma unroll
+      for (int i = 0; i < 4 * kVec; ++i) {
+        const int c = bin_at(x, b0, i);
+        if (!found && b0 + i < hi) {
+          if (cum + c >= K) {
+            s_bin = b0 + i;
+            s_need = K - cum;
+            found = true;
+          } else {
+            cum += c;
+          }
+        }
+      }
     }
   }
   __syncthreads();
   const int64_t bin = s_bin, need = s_need;
-  // 2) inside that bin, pairs run in (qb, kb) order with at most two per qb
+  // 2) inside that bin, pairs run in (qb, kb) order with at most two per qb:
+  //    (qb, qb - dd) and (qb, qb + dd), or the diagonal alone when dd = 0.  Both
+  //    table entries of a qb are read before either is used.
   const int dd = bin == 0 ? 0 : (int)((bin - 1) % g.nb);
-  auto in_bin = [&](int qb, int kb) -> bool {
-    if (kb < 0 || kb >= g.nb) return false;
-    bool cand;
-    const int64_t key = rt_key(rt, g, qb, kb, &cand);
-    return cand && key / ((int64_t)g.nb * g.nb) == bin;
+  auto pair_in = [&](int qb, bool* lo_in, bool* hi_in) __attribute__((always_inline)) {
+    const int kl = qb - dd, kh = qb + dd;
+    const bool vl = kl >= 0, vh = dd != 0 && kh < g.nb;
+    const uint16_t* row = rt + (int64_t)qb * g.nb;
+    const uint16_t rl = row[vl ? kl : qb], rh = row[vh ? kh : qb];
+    *lo_in = vl && rl != kNoCand && pair_bin(qb, kl, rl, g.nb) == bin;
+    *hi_in = vh && rh != kNoCand && pair_bin(qb, kh, rh, g.nb) == bin;
   };
   const int qseg = (g.nb + kScanThreads - 1) / kScanThreads;
   const int qlo = min(t * qseg, g.nb), qhi = min(qlo + qseg, g.nb);
   int64_t qlocal = 0;
-  for (int qb = qlo; qb < qhi; ++qb)
-    qlocal += dd == 0 ? (int)in_bin(qb, qb) : (int)in_bin(qb, qb - dd) + (int)in_bin(qb, qb + dd);
+  for (int qb = qlo; qb < qhi; ++qb) {
+    bool a, b;
+    pair_in(qb, &a, &b);
+    qlocal += (int)a + (int)b;
+  }
   const int64_t qexcl = block_exclusive_scan(qlocal, tmp, nullptr);
   if (qexcl < need && need <= qexcl + qlocal) {
     int64_t cum = qexcl;
     for (int qb = qlo; qb < qhi; ++qb) {
-      const bool lo_in = dd == 0 ? in_bin(qb, qb) : in_bin(qb, qb - dd);
-      const bool hi_in = dd == 0 ? false : in_bin(qb, qb + dd);
+      bool lo_in, hi_in;
+      pair_in(qb, &lo_in, &hi_in);
       const int c = (int)lo_in + (int)hi_in;
       if (cum + c >= need) {
         const int64_t rem = need - cum;
