@@ -383,7 +383,7 @@ int salad_linear_state(const salad_shape* shape, const void* k, const void* v, f
   if (ws_bytes < L.bytes) return SALAD_ENOSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(ws);
-  hipError_t e = launch_linear_state(g, shape->dtype, k, v, nullptr, 0.0f, w, L, s);
+  hipError_t e = launch_linear_state(g, shape->dtype, k, v, nullptr, 0.0f, nullptr, w, L, s);
   if (e != hipSuccess) return SALAD_EHIP;
   return hip_status(launch_linear_fold(g, shape->dtype, nullptr, nullptr, 2, 0.0f, S, z, w, L, s));
 }
@@ -424,7 +424,7 @@ int fwd_run(const salad_shape* shape, const Geom& g, const Workspace& L, const v
             const void* v, const int32_t* row_ptr, const int32_t* col_idx, const float* gate,
             const void* w_lin, float eps, float scale, float drop_tau, void* out, float* lse, char* w,
             hipStream_t s) {
-  hipError_t e = launch_linear_state(g, shape->dtype, k, v, gate, drop_tau, w, L, s);
+  hipError_t e = launch_linear_state(g, shape->dtype, k, v, gate, drop_tau, w_lin, w, L, s);
   if (e == hipSuccess)
     e = launch_linear_fold(g, shape->dtype, gate, w_lin, 0, drop_tau, nullptr, nullptr, w, L, s);
   if (e != hipSuccess) return SALAD_EHIP;
@@ -457,7 +457,7 @@ int salad_linear_prepare(const salad_shape* shape, const void* k, const void* v,
   if (ws_bytes < L.bytes) return SALAD_ENOSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(ws);
-  hipError_t e = launch_linear_state(g, shape->dtype, k, v, gate, drop_tau, w, L, s);
+  hipError_t e = launch_linear_state(g, shape->dtype, k, v, gate, drop_tau, w_lin, w, L, s);
   if (e == hipSuccess)
     e = launch_linear_fold(g, shape->dtype, gate, w_lin, 0, drop_tau, nullptr, nullptr, w, L, s);
   return hip_status(e);
@@ -551,7 +551,7 @@ int salad_attn_fwd_branches(const salad_shape* shape, const void* q, const void*
     if (run_attn(g, shape->dtype, a, s) != hipSuccess) return SALAD_EHIP;
   }
   if (out_lin) {
-    hipError_t e = launch_linear_state(g, shape->dtype, k, v, nullptr, 0.0f, w, L, s);
+    hipError_t e = launch_linear_state(g, shape->dtype, k, v, nullptr, 0.0f, nullptr, w, L, s);
     if (e == hipSuccess)
       e = launch_linear_fold(g, shape->dtype, nullptr, nullptr, 1, 0.0f, nullptr, nullptr, w, L, s);
     if (e != hipSuccess) return SALAD_EHIP;
@@ -596,7 +596,7 @@ int salad_attn_bwd(const salad_shape* shape, const void* q, const void* k, const
   a.w_lin = w_lin; a.out = out; a.dout = dout; a.dq = dq; a.dk = dk; a.dv = dv;
   a.dw_lin = dw_lin; a.dgate = dgate; a.lse = lse; a.eps = eps;
   a.scale = scale > 0.0f ? scale : 1.0f / std::sqrt((float)g.D);
-  hipError_t e = launch_linear_state(g, shape->dtype, k, v, nullptr, 0.0f, w, L.fwd, s);
+  hipError_t e = launch_linear_state(g, shape->dtype, k, v, nullptr, 0.0f, nullptr, w, L.fwd, s);
   if (e == hipSuccess)
     e = launch_linear_fold(g, shape->dtype, nullptr, nullptr, 2, 0.0f,
                            reinterpret_cast<float*>(w + L.off_s32), reinterpret_cast<float*>(w + L.off_z),

@@ -172,14 +172,18 @@ inline int topk_heads_per_batch(const Geom& g) {
 
 // ---- linear state (linear.hip) ----------------------------------------------
 // Split partials of S and z.  With a gate, heads whose gate < drop_tau are
-// skipped (nothing written for them).
+// skipped (nothing written for them).  For bf16, a non-null w_lin makes the
+// partials S_c W_lin (the fused forward: pass it exactly when the fold runs in
+// mode 0); the fp32 kernel ignores it.
 SALAD_HIDDEN hipError_t launch_linear_state(const Geom& g, int dtype, const void* k,
                                             const void* v, const float* gate, float drop_tau,
-                                            char* ws, const Workspace& L, hipStream_t st);
+                                            const void* w_lin, char* ws, const Workspace& L,
+                                            hipStream_t st);
 // Reduce the split partials and fold.  mode 0: folded state g*S*W_lin (fused
-// forward; heads with g < drop_tau skipped); 1: S itself (linear branch
-// alone); 2: reduce only.  S_out / z_out (may be null) receive the fp32
-// state; z always lands in the workspace.
+// forward; heads with g < drop_tau skipped; for bf16 the product with W_lin
+// was taken by the partial kernel); 1: S itself (linear branch alone); 2:
+// reduce only.  S_out / z_out (may be null) receive the fp32 state in modes 1
+// and 2; z always lands in the workspace.
 SALAD_HIDDEN hipError_t launch_linear_fold(const Geom& g, int dtype, const float* gate,
                                            const void* w_lin, int mode, float drop_tau,
                                            float* S_out, float* z_out, char* ws,

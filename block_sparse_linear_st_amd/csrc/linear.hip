@@ -13,6 +13,10 @@
 //     operands are read with the LDS transpose read, ReLU is applied to the K
 //     fragment in registers.  Products of bf16 values are exact and the sums
 //     are fp32.  The fp32 kernel does the same with VALU FMAs.
+//     For the fused bf16 forward the workgroup multiplies its partial by W_lin
+//     before storing it (the partial S_c W_lin of chunk c, by linearity), with
+//     W_lin staged in LDS beside the ring and the fp32 partial split into
+//     hi + lo bf16 MFMA operands, so that the fold needs no W_lin.
 //  2. k_lin_fold: grid (B*H, D/2).  Sums the partials over the splits in a fixed
 //     order (bitwise reproducible; loads batched 8 splits deep), then, for the
 //     fused forward, folds gate and
@@ -95,17 +99,24 @@ __device__ __attribute__((always_inline)) inline bf16x8 tr_frag(const unsigned c
 // expcnt and lgkmcnt left at their maxima)
 constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
-template <int D>
+// PREMUL: the workgroup's partial is stored as S_c W_lin instead of S_c.  The
+// MFMA operands are then swapped so that the accumulators hold S_c^T (a lane
+// owns one K channel, its registers run over V channels): split into hi + lo
+// bf16 they are the A operand of S_c W_lin directly, contracted over the V
+// channel, with W_lin read from LDS by the same transpose read as a V tile.
+template <int D, bool PREMUL>
 __global__ void __launch_bounds__(256, 1)
 k_lin_partial_bf16(Geom g, const __bf16* __restrict__ K, const __bf16* __restrict__ V, int chunk,
                    float* __restrict__ spart, float* __restrict__ zpart, const float* __restrict__ gate,
-                   float drop_tau) {
+                   float drop_tau, const __bf16* __restrict__ W) {
   using LY = LinLay<D>;
   constexpr int TD = D / 32;           // 32-wide output tiles per dimension
   constexpr int TPW = TD * TD / 4;     // output tiles per wave
   constexpr int RING = 4;              // tile buffers: three tiles in flight while one is reduced
   constexpr int PER = 2 * LY::LOADS;   // DMA instructions per thread per tile
-  __shared__ __align__(1024) unsigned char smem[RING * LY::BUF_B];
+  constexpr int W_B = PREMUL ? D * LY::ROW_B : 0;  // W_lin, rows laid out like a V tile's
+  // 160 KiB at D = 128: the whole of a gfx950 CU's LDS
+  __shared__ __align__(1024) unsigned char smem[RING * LY::BUF_B + W_B];
 
   const int split = blockIdx.x, bh = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -138,6 +149,18 @@ k_lin_partial_bf16(Geom g, const __bf16* __restrict__ K, const __bf16* __restric
       lds_dma16(Vb + (int64_t)n * D + c, lds0 + buf * LY::BUF_B + LY::TILE_B + blk1k * 1024);
     }
   };
+  if constexpr (PREMUL) {
+    // W_lin (L2-resident after the first workgroups) goes in first: loads
+    // complete in order, so the wait for tile 0 covers it too
+    constexpr int WL = D * LY::CPR / 256;  // 16-byte pieces per thread
+#pragma unroll
+    for (int i = 0; i < WL; ++i) {
+      const int blk1k = wave_u * WL + i;
+      const int P = blk1k * 64 + lane;
+      const int r = P / LY::CPR, p = P % LY::CPR;
+      lds_dma16(W + r * D + (p ^ LY::swz(r)) * 8, lds0 + RING * LY::BUF_B + blk1k * 1024);
+    }
+  }
   for (int tt = 0; tt < RING - 1 && tt < T; ++tt) issue(tt);
   // the gate is read once the first tiles are on their way, so that its latency
   // does not delay them
@@ -177,21 +200,88 @@ k_lin_partial_bf16(Geom g, const __bf16* __restrict__ K, const __bf16* __restric
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
         const int tj = TD == 4 ? t : tj0;
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, tr_frag<D>(Vt, ks, tj * 32, lane), acc[t], 0, 0, 0);
+        const bf16x8 vf = tr_frag<D>(Vt, ks, tj * 32, lane);
+        if constexpr (PREMUL)
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, af, acc[t], 0, 0, 0);  // S^T tile (tj, ti)
+        else
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, vf, acc[t], 0, 0, 0);  // S tile (ti, tj)
       }
     }
   }
 
-  // partial S: lane holds rows (i/4)*8 + (lane/32)*4 + i%4 of tile ti, column lane%32 of tile tj
+  // partial S (or S W_lin): lane holds rows (i/4)*8 + (lane/32)*4 + i%4 of row
+  // tile ti, column lane%32 of column tile tj
   const int g32 = lane >> 5, l32 = lane & 31;
   float* sp = spart + ((int64_t)split * g.B * g.Hh + bh) * D * D;
+  if constexpr (PREMUL) {
+    if (T == 0) {  // no tile step waited for W_lin
+      wait_vmem();
+      __syncthreads();
+    }
+    // C[dk][j] = sum_dv S[dk][dv] W[dv][j] for this wave's dk tile ti.  acc[t][8 s + e]
+    // is S^T[dv][dk] at dv = 32 t + 16 s + 8 (e / 4) + 4 g32 + e % 4, which is the
+    // V-channel slot order the transpose read gives W's rows for step 2 t + s.
+    constexpr int JT = TD;  // output column tiles
+    const unsigned char* Ws = smem + RING * LY::BUF_B;
+    f32x16 out[JT];
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    const int tj = TD == 4 ? t : tj0;
+    for (int jt = 0; jt < JT; ++jt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = ti * 32 + (i >> 2) * 8 + g32 * 4 + (i & 3);
-      sp[r * D + tj * 32 + l32] = acc[t][i];
+      for (int i = 0; i < 16; ++i) out[jt][i] = 0.0f;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const int tj = TD == 4 ? t : tj0;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        bf16x8 ah, al;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = acc[t][8 * s + e];
+          ah[e] = (__bf16)x;
+          al[e] = (__bf16)(x - (float)ah[e]);
+        }
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt) {
+          const bf16x8 wf = tr_frag<D>(Ws, 2 * tj + s, jt * 32, lane);
+          out[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, wf, out[jt], 0, 0, 0);
+          out[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, wf, out[jt], 0, 0, 0);
+        }
+      }
+    }
+    if constexpr (TD == 2) {
+      // D = 64: waves 2 ti and 2 ti + 1 hold the two V-channel halves of row
+      // tile ti; the second passes its sums through ring slot T % RING (free:
+      // every wave is past the step that last read it) and the first adds them
+      float* xb = reinterpret_cast<float*>(smem + (T % RING) * LY::BUF_B) + ti * (JT * 16 * 64);
+      if (tj0 == 1) {
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) xb[(jt * 16 + i) * 64 + lane] = out[jt][i];
+      }
+      __syncthreads();
+      if (tj0 == 1) return;
+#pragma unroll
+      for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) out[jt][i] += xb[(jt * 16 + i) * 64 + lane];
+    }
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = ti * 32 + (i >> 2) * 8 + g32 * 4 + (i & 3);
+        sp[r * D + jt * 32 + l32] = out[jt][i];
+      }
+  } else {
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const int tj = TD == 4 ? t : tj0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = ti * 32 + (i >> 2) * 8 + g32 * 4 + (i & 3);
+        sp[r * D + tj * 32 + l32] = acc[t][i];
+      }
     }
   }
   // z: the lane pair (l, l^32) covers all tokens of channel ti*32 + l%32
@@ -253,10 +343,11 @@ __device__ __attribute__((always_inline)) inline void stage16(const uint4* __res
 }
 
 // grid (B*H, D/2), 256 threads: reduce 2 rows of S and the same 2 channels of z
-// over the splits (in ordered parts), then fold.  mode 0: S'' = g*S*W; 1: S'' = S;
-// 2: state only.  In mode 0 heads with g < drop_tau are skipped (their partials
-// were never written).
-template <typename WT, bool BF16OUT>
+// over the splits (in ordered parts), then fold.  mode 0: S'' = g*S*W (WITH_W);
+// 1: S'' = S; 2: state only; 3: S'' = g*S, the partials already carrying W_lin.
+// In modes 0 and 3 heads with g < drop_tau are skipped (their partials were
+// never written).
+template <typename WT, bool BF16OUT, bool WITH_W>
 __global__ void __launch_bounds__(256)
 k_lin_fold(Geom g, int splits, const float* __restrict__ spart, const float* __restrict__ zpart,
            const float* __restrict__ gate, const WT* __restrict__ w, int mode, float drop_tau,
@@ -266,10 +357,10 @@ k_lin_fold(Geom g, int splits, const float* __restrict__ spart, const float* __r
   __shared__ float Srows[FR][128];
   __shared__ float4 parts[256];
   __shared__ float zsp[FR][256];  // z of channels r0, r0 + 1: one entry per split (splits <= 256)
-  __shared__ WT Ws[128 * 128];  // W_lin, staged once per workgroup (mode 0)
+  __shared__ WT Ws[WITH_W ? 128 * 128 : 1];  // W_lin, staged once per workgroup (mode 0)
   const int D = g.D, bh = blockIdx.x, r0 = blockIdx.y * FR, tid = threadIdx.x;
   const int64_t BH = (int64_t)g.B * g.Hh;
-  if (mode == 0 && gate[bh] < drop_tau) return;
+  if ((mode == 0 || mode == 3) && gate[bh] < drop_tau) return;
   // this workgroup's z entries (channel r0 + i / splits, split i % splits), loaded
   // beside the partial rows so that both take one round trip
   // (indices past the last entry reload it: straight-line loads, none waited on here)
@@ -333,7 +424,7 @@ k_lin_fold(Geom g, int splits, const float* __restrict__ spart, const float* __r
     if (z_out) z_out[(int64_t)bh * D + r0 + tid] = z;
   }
   if (mode == 2) return;
-  if (mode == 0) {
+  if constexpr (WITH_W) {
     // 16-byte copies (w_lin is 16-byte aligned), all of a thread's loads in flight at once
     constexpr int PER16 = 16 / (int)sizeof(WT);
     const uint4* src = reinterpret_cast<const uint4*>(w);
@@ -342,17 +433,17 @@ k_lin_fold(Geom g, int splits, const float* __restrict__ spart, const float* __r
     else stage16<64 * 64 / PER16 / 256>(src, dst, tid);
   }
   __syncthreads();
-  const float gv = mode == 0 ? gate[bh] : 1.0f;
+  const float gv = mode == 0 || mode == 3 ? gate[bh] : 1.0f;
   // S''[r0+rr][j] for column j, stored transposed at [j][r0+rr]
   for (int i = tid; i < FR * D; i += 256) {
     const int j = i / FR, rr = i % FR;
     float v;
-    if (mode == 0) {
+    if (WITH_W) {
       float s = 0.0f;
       for (int kk = 0; kk < D; ++kk) s = fmaf(Srows[rr][kk], (float)Ws[kk * D + j], s);
       v = gv * s;
     } else {
-      v = Srows[rr][j];
+      v = gv * Srows[rr][j];
     }
     const int64_t o = (int64_t)bh * D * D + (int64_t)j * D + r0 + rr;
     if (BF16OUT) {
@@ -369,20 +460,30 @@ k_lin_fold(Geom g, int splits, const float* __restrict__ spart, const float* __r
 }  // namespace
 
 hipError_t launch_linear_state(const Geom& g, int dtype, const void* k, const void* v,
-                               const float* gate, float drop_tau, char* ws, const Workspace& L,
-                               hipStream_t st) {
+                               const float* gate, float drop_tau, const void* w_lin, char* ws,
+                               const Workspace& L, hipStream_t st) {
   float* spart = reinterpret_cast<float*>(ws + L.off_spart);
   float* zpart = reinterpret_cast<float*>(ws + L.off_zpart);
   dim3 grid(L.lin_splits, g.B * g.Hh);
   if (dtype == SALAD_BF16) {
-    if (g.D == 128)
-      hipLaunchKernelGGL(k_lin_partial_bf16<128>, grid, dim3(256), 0, st, g,
-                         static_cast<const __bf16*>(k), static_cast<const __bf16*>(v), L.lin_chunk,
-                         spart, zpart, gate, drop_tau);
-    else
-      hipLaunchKernelGGL(k_lin_partial_bf16<64>, grid, dim3(256), 0, st, g,
-                         static_cast<const __bf16*>(k), static_cast<const __bf16*>(v), L.lin_chunk,
-                         spart, zpart, gate, drop_tau);
+    const __bf16* kb = static_cast<const __bf16*>(k);
+    const __bf16* vb = static_cast<const __bf16*>(v);
+    const __bf16* wb = static_cast<const __bf16*>(w_lin);
+    if (g.D == 128) {
+      if (wb)
+        hipLaunchKernelGGL((k_lin_partial_bf16<128, true>), grid, dim3(256), 0, st, g, kb, vb, L.lin_chunk,
+                           spart, zpart, gate, drop_tau, wb);
+      else
+        hipLaunchKernelGGL((k_lin_partial_bf16<128, false>), grid, dim3(256), 0, st, g, kb, vb, L.lin_chunk,
+                           spart, zpart, gate, drop_tau, wb);
+    } else {
+      if (wb)
+        hipLaunchKernelGGL((k_lin_partial_bf16<64, true>), grid, dim3(256), 0, st, g, kb, vb, L.lin_chunk,
+                           spart, zpart, gate, drop_tau, wb);
+      else
+        hipLaunchKernelGGL((k_lin_partial_bf16<64, false>), grid, dim3(256), 0, st, g, kb, vb, L.lin_chunk,
+                           spart, zpart, gate, drop_tau, wb);
+    }
   } else {
     if (g.D == 128)
       hipLaunchKernelGGL(k_lin_partial_f32<128>, grid, dim3(256), 0, st, g,
@@ -405,14 +506,18 @@ hipError_t launch_linear_fold(const Geom& g, int dtype, const float* gate, const
   void* hi = ws + L.off_sft_hi;
   void* lo = ws + L.off_sft_lo;
   dim3 grid(g.B * g.Hh, g.D / 2);
-  if (dtype == SALAD_BF16)
-    hipLaunchKernelGGL((k_lin_fold<__bf16, true>), grid, dim3(256), 0, st, g, L.lin_splits, spart,
-                       zpart, gate, static_cast<const __bf16*>(w_lin), mode, drop_tau, S_out, z_out, z_ws,
-                       hi, lo);
-  else
-    hipLaunchKernelGGL((k_lin_fold<float, false>), grid, dim3(256), 0, st, g, L.lin_splits, spart,
+  if (dtype == SALAD_BF16)  // mode 0: the bf16 partials already carry W_lin
+    hipLaunchKernelGGL((k_lin_fold<__bf16, true, false>), grid, dim3(256), 0, st, g, L.lin_splits, spart,
+                       zpart, gate, static_cast<const __bf16*>(nullptr), mode == 0 ? 3 : mode, drop_tau, S_out,
+                       z_out, z_ws, hi, lo);
+  else if (mode == 0)
+    hipLaunchKernelGGL((k_lin_fold<float, false, true>), grid, dim3(256), 0, st, g, L.lin_splits, spart,
                        zpart, gate, static_cast<const float*>(w_lin), mode, drop_tau, S_out, z_out, z_ws, hi,
                        lo);
+  else
+    hipLaunchKernelGGL((k_lin_fold<float, false, false>), grid, dim3(256), 0, st, g, L.lin_splits, spart,
+                       zpart, gate, static_cast<const float*>(nullptr), mode, drop_tau, S_out, z_out, z_ws,
+                       hi, lo);
   return hipGetLastError();
 }
 
