@@ -565,7 +565,9 @@ k_topk_scores(Geom g, HeadTable ht, const float* __restrict__ pmean_q, const flo
 // the k-th largest order-preserving 32-bit key by a bitwise radix search whose
 // counts are ballot popcounts over keys held in registers (MAXK per lane),
 // keeps every larger key and the first remaining equal keys in kb order, and
-// emits the kept kb's ascending.
+// emits the kept kb's ascending.  The search ends at the first bit at which the
+// candidates still tied on the bits above are exactly the keys still to take
+// (about 15 of 32 bits on 512-block rows of pooled scores).
 template <int MAXK>
 __global__ void __launch_bounds__(256)
 k_topk_select(Geom g, HeadTable ht, const float* __restrict__ scores, int bh0,
@@ -587,16 +589,26 @@ k_topk_select(Geom g, HeadTable ht, const float* __restrict__ scores, int bh0,
       key[m] = kb < nb ? ordered_bits(srow[kb]) : 0u;  // real keys are never 0
     }
   }
+  // Invariant: every key whose top bits (under `bits`) exceed `prefix` is kept,
+  // and krem more are to come from the group of grp real keys whose top bits
+  // equal it.  The search stops as soon as that group holds no more keys than
+  // are still needed (then all of it is kept); only a group of equal full
+  // keys is split, by kb order.
   uint32_t prefix = 0, bits = 0;
-  int krem = kkeep;
-  for (int bit = 31; bit >= 0; --bit) {
+  int krem = kkeep, grp = nb;
+  for (int bit = 31; bit >= 0 && grp > krem; --bit) {
     const uint32_t bmask = bits | (1u << bit), cand = prefix | (1u << bit);
     int cnt = 0;
 #pragma unroll
     for (int m = 0; m < MAXK; ++m)
       if (m < kpl) cnt += __popcll(__ballot((key[m] & bmask) == cand));
-    if (cnt >= krem) prefix = cand;
-    else krem -= cnt;
+    if (cnt >= krem) {
+      prefix = cand;
+      grp = cnt;
+    } else {
+      krem -= cnt;
+      grp -= cnt;
+    }
     bits = bmask;
   }
   const int64_t base = row_ptr[(int64_t)bh * nb + r];
@@ -605,9 +617,10 @@ k_topk_select(Geom g, HeadTable ht, const float* __restrict__ scores, int bh0,
   for (int m = 0; m < MAXK; ++m) {
     if (m < kpl) {
       const int kb = m * 64 + lane;
-      const bool eq = key[m] == prefix;
+      const uint32_t top = key[m] & bits;
+      const bool eq = top == prefix && kb < nb;
       const uint64_t me = __ballot(eq);
-      const bool keep = key[m] > prefix || (eq && eq_seen + __popcll(me & lt) < krem);
+      const bool keep = top > prefix || (eq && eq_seen + __popcll(me & lt) < krem);
       eq_seen += __popcll(me);
       const uint64_t mk = __ballot(keep);
       if (keep) {
