@@ -46,10 +46,10 @@ ATTN_KERNEL = "k_attn_bf16 (block-sparse flash attention + linear epilogue)"
 # taken on (sha256 prefix); scaled by a plain 512 MiB copy, which reads
 # FETCH_SIZE = 262157.9 KiB and WRITE_SIZE = 524288 KiB.
 ATTN_COUNTERS = {
-    "source_sha256": "5d5ed860335f9a3f",
+    "source_sha256": "a60b71697c2430d2",
     "fetch_scale": 524288.0 / 262157.9,
     "write_scale": 1.0,
-    "c3": {"fetch_kib": 203247.8, "write_kib": 98304.0},
+    "c3": {"fetch_kib": 202408.0, "write_kib": 98304.0},
 }
 
 

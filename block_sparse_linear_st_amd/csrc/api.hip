@@ -217,8 +217,7 @@ Workspace plan_workspace(const Geom& g, const Cuboid& cu, int dtype) {
   L.off_zpart = off;  off = align_up(off + (size_t)splits * BH * D * 4);
   L.off_z = off;      off = align_up(off + BH * D * 4);
   const size_t esz = dtype == SALAD_BF16 ? 2 : 4;
-  L.off_sft_hi = off; off = align_up(off + BH * D * D * esz);
-  L.off_sft_lo = off; off = align_up(off + (dtype == SALAD_BF16 ? BH * D * D * 2 : 0));
+  L.off_sft = off;    off = align_up(off + BH * D * D * esz);
   L.off_split = off;  off = align_up(off + (9 + kPairModeSlots) * 4);
   L.lin_end = off;
   L.bytes = std::max(L.mask_end, L.lin_end);
@@ -431,7 +430,7 @@ int fwd_run(const salad_shape* shape, const Geom& g, const Workspace& L, const v
   AttnArgs a{};
   a.q = q; a.k = k; a.v = v; a.out = out;
   a.row_ptr = row_ptr; a.col_idx = col_idx;
-  a.sft_hi = w + L.off_sft_hi; a.sft_lo = w + L.off_sft_lo;
+  a.sft = w + L.off_sft;
   a.split = reinterpret_cast<int32_t*>(w + L.off_split);
   a.z = reinterpret_cast<const float*>(w + L.off_z);
   a.gate = gate; a.drop_tau = drop_tau; a.eps = eps;
@@ -479,7 +478,7 @@ int salad_attn_apply(const salad_shape* shape, const void* q, const void* k, con
   AttnArgs a{};
   a.q = q; a.k = k; a.v = v; a.out = out;
   a.row_ptr = row_ptr; a.col_idx = col_idx;
-  a.sft_hi = w + L.off_sft_hi; a.sft_lo = w + L.off_sft_lo;
+  a.sft = w + L.off_sft;
   a.split = reinterpret_cast<int32_t*>(w + L.off_split);
   a.z = reinterpret_cast<const float*>(w + L.off_z);
   a.gate = gate; a.drop_tau = drop_tau; a.eps = eps;
@@ -541,7 +540,7 @@ int salad_attn_fwd_branches(const salad_shape* shape, const void* q, const void*
   AttnArgs a{};
   a.q = q; a.k = k; a.v = v;
   a.row_ptr = row_ptr; a.col_idx = col_idx;
-  a.sft_hi = w + L.off_sft_hi; a.sft_lo = w + L.off_sft_lo;
+  a.sft = w + L.off_sft;
   a.split = reinterpret_cast<int32_t*>(w + L.off_split);
   a.z = reinterpret_cast<const float*>(w + L.off_z);
   a.gate = nullptr; a.drop_tau = 0.0f; a.eps = eps;

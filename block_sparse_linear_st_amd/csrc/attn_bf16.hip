@@ -32,9 +32,9 @@
 // Epilogue: o_s = O / l (and, when asked, each row's log2-sum-exp m + log2 l
 // for the backward pass); the linear branch ("SALAD" explainer, section 2.1)
 // and its gated projection (section 2.2) arrive pre-folded as S''^T =
-// (g S W_lin)^T in hi + lo bf16, so g*(o_l W_lin) = (S''^T ReLU(Q)^T) /
-// (ReLU(Q) z + eps) is 2*(D/32)*(D/16) more MFMAs on the Q fragments already
-// in registers.  Heads whose gate is below drop_tau skip it (section 2.3).  The
+// (g S W_lin)^T in bf16 (rounded once, as P is before the PV product), so
+// g*(o_l W_lin) = (S''^T ReLU(Q)^T) / (ReLU(Q) z + eps) is (D/32)*(D/16) more
+// MFMAs on the Q fragments already in registers.  Heads whose gate is below drop_tau skip it (section 2.3).  The
 // 128 x D bf16 result is staged through LDS for 16-byte coalesced stores.
 //
 // The per-lane LDS read offsets inside a tile are computed once; the tile loop
@@ -312,9 +312,7 @@ k_attn_bf16(Geom g, AttnArgs a, int n_items, float c_log2) {
   constexpr int NT = D / 32;
   constexpr int TPB = BLK / KT;   // tiles per key block
   constexpr int SMEM_B = ROWS * LY::OST * 2 > 2 * LY::BUF_B ? ROWS * LY::OST * 2 : 2 * LY::BUF_B;
-  // the folded linear state (hi, lo) goes through LDS in one pass when both fit, else one part at a time
-  constexpr int LIN_PASSES = 2 * D * D * 2 <= SMEM_B ? 1 : 2;
-  static_assert(D * D * 2 <= SMEM_B, "one part of the folded linear state must fit");
+  static_assert(D * D * 2 <= SMEM_B, "the folded linear state must fit in the tile buffers");
   constexpr int THREADS = NW * 64;
   __shared__ __align__(1024) unsigned char smem[SMEM_B];
 
@@ -551,111 +549,64 @@ k_attn_bf16(Geom g, AttnArgs a, int n_items, float c_log2) {
   bool lin = a.has_lin != 0;
   if (lin && a.gate != nullptr && a.gate[bh] < a.drop_tau) lin = false;  // uniform
   if (lin) {
-    if constexpr (LIN_PASSES == 1) {
-      // S''^T (hi, lo) of this head into LDS, rows swizzled like K tiles: every
-      // wave reads all of it, so one copy per workgroup instead of one per wave
-      const __bf16* hi = static_cast<const __bf16*>(a.sft_hi) + (int64_t)bh * D * D;
-      const __bf16* lo = static_cast<const __bf16*>(a.sft_lo) + (int64_t)bh * D * D;
-      const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
-      const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-      constexpr int PER = D * LY::CPR / THREADS;  // 1 KiB loads per wave per matrix
-      __syncthreads();  // the tile buffers are free
-  #pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        const int blk1k = wave_u * PER + i;
-        const int P = blk1k * 64 + lane;
-        const int r = P / LY::CPR, p = P % LY::CPR;
-        lds_dma16(hi + r * D + (p ^ LY::kswz(r)) * 8, lds0 + blk1k * 1024);
-        lds_dma16(lo + r * D + (p ^ LY::kswz(r)) * 8, lds0 + D * D * 2 + blk1k * 1024);
-      }
-      const float* z = a.z + (int64_t)bh * D;
-      bf16x8 rq[NC];
-      float den = 0.0f;
-  #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        rq[c] = relu8(qf[c]);
-  #pragma unroll
-        for (int j = 0; j < 8; ++j) den += (float)rq[c][j] * z[c * 16 + g32 * 8 + j];
-      }
-      den = pair_sum(den);
-      const float inv_den = 1.0f / (den + a.eps);
-      wait_vmem();
-      __syncthreads();
-      if (wave_rows) {
-  #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const int row = t * 32 + l32;
-          const unsigned char* rh = smem + row * LY::ROW_B;
-          const unsigned char* rl = rh + D * D * 2;
-          const int sw = LY::kswz(row);
+    // S''^T of this head into LDS, rows swizzled like K tiles: every wave reads
+    // all of it, so one copy per workgroup instead of one per wave
+    const __bf16* st = static_cast<const __bf16*>(a.sft) + (int64_t)bh * D * D;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    constexpr int PER = D * LY::CPR / THREADS;  // 1 KiB loads per wave
+    __syncthreads();  // the tile buffers are free
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int blk1k = wave_u * PER + i;
+      const int P = blk1k * 64 + lane;
+      const int r = P / LY::CPR, p = P % LY::CPR;
+      lds_dma16(st + r * D + (p ^ LY::kswz(r)) * 8, lds0 + blk1k * 1024);
+    }
+    const float* z = a.z + (int64_t)bh * D;
+    bf16x8 rq[NC];
+    float den = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      rq[c] = relu8(qf[c]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) den += (float)rq[c][j] * z[c * 16 + g32 * 8 + j];
+    }
+    den = pair_sum(den) + a.eps;
+    const float inv_den = 1.0f / den;
+    wait_vmem();
+    __syncthreads();
+    if (wave_rows) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int row = t * 32 + l32;
+        const unsigned char* rh = smem + row * LY::ROW_B;
+        const int sw = LY::kswz(row);
+        if constexpr (BLK == 64) {
           f32x16 la;
-  #pragma unroll
+#pragma unroll
           for (int i = 0; i < 16; ++i) la[i] = 0.0f;
-  #pragma unroll
-          for (int c = 0; c < NC; ++c) {
-            const int off = ((2 * c + g32) ^ sw) << 4;
+#pragma unroll
+          for (int c = 0; c < NC; ++c)
             la = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(rh + off)), rq[c], la, 0, 0, 0);
-            la = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(rl + off)), rq[c], la, 0, 0, 0);
-          }
-  #pragma unroll
+                __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(rh + (((2 * c + g32) ^ sw) << 4))),
+                rq[c], la, 0, 0, 0);
+#pragma unroll
           for (int i = 0; i < 16; ++i) o[t][i] += la[i] * inv_den;
+        } else {
+          // no spare registers for a separate sum at 168 per lane: the term goes
+          // straight into O, o = (o_s den + S''^T relu(q)) / den
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[t][i] *= den;
+#pragma unroll
+          for (int c = 0; c < NC; ++c)
+            o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(rh + (((2 * c + g32) ^ sw) << 4))),
+                rq[c], o[t], 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[t][i] *= inv_den;
         }
       }
-  
-    } else {
-      // S''^T hi, then lo, through LDS one part at a time; the linear term goes
-      // straight into O: o = (o_s den + S''^T relu(q)) / den
-      const __bf16* part[2] = {static_cast<const __bf16*>(a.sft_hi) + (int64_t)bh * D * D,
-                               static_cast<const __bf16*>(a.sft_lo) + (int64_t)bh * D * D};
-      const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
-      const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-      constexpr int PER = D * LY::CPR / THREADS;  // 1 KiB loads per wave per matrix
-      const float* z = a.z + (int64_t)bh * D;
-      bf16x8 rq[NC];
-      float den = 0.0f;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        rq[c] = relu8(qf[c]);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) den += (float)rq[c][j] * z[c * 16 + g32 * 8 + j];
-      }
-      den = pair_sum(den) + a.eps;
-      const float inv_den = 1.0f / den;
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[t][i] *= den;
-#pragma unroll
-      for (int pp = 0; pp < 2; ++pp) {
-        __syncthreads();  // the buffers are free
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-          const int blk1k = wave_u * PER + i;
-          const int P = blk1k * 64 + lane;
-          const int r = P / LY::CPR, p = P % LY::CPR;
-          lds_dma16(part[pp] + r * D + (p ^ LY::kswz(r)) * 8, lds0 + blk1k * 1024);
-        }
-        wait_vmem();
-        __syncthreads();
-        if (wave_rows) {
-#pragma unroll
-          for (int t = 0; t < NT; ++t) {
-            const unsigned char* rh = smem + (t * 32 + l32) * LY::ROW_B;
-            const int sw = LY::kswz(t * 32 + l32);
-#pragma unroll
-            for (int c = 0; c < NC; ++c)
-              o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                  __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(rh + (((2 * c + g32) ^ sw) << 4))),
-                  rq[c], o[t], 0, 0, 0);
-          }
-        }
-      }
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[t][i] *= inv_den;
     }
   }
 

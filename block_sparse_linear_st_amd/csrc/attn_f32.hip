@@ -84,7 +84,7 @@ k_attn_f32(Geom g, AttnArgs a, float scale) {
   bool lin = a.has_lin != 0;
   if (lin && a.gate != nullptr && a.gate[bh] < a.drop_tau) lin = false;
   float inv_den = 0.0f;
-  const float* sft = static_cast<const float*>(a.sft_hi) + (int64_t)bh * D * D;
+  const float* sft = static_cast<const float*>(a.sft) + (int64_t)bh * D * D;
   if (lin) {
     const float* z = a.z + (int64_t)bh * D;
     float den = 0.0f;

@@ -75,7 +75,7 @@ struct Workspace {
   int lin_splits, lin_chunk;
   size_t off_spart, off_zpart;     // float [splits][B*H][D*D], [splits][B*H][D]
   size_t off_z;                    // float [B*H][D]
-  size_t off_sft_hi, off_sft_lo;   // folded state, transposed: bf16 or f32 [B*H][D*D]
+  size_t off_sft;                  // folded state, transposed: bf16 or f32 [B*H][D*D]
   size_t off_split;                // int32 [9 + kPairModeSlots]: attention items per XCD, layout modes
   size_t mask_end, lin_end;
 };
@@ -230,8 +230,7 @@ struct AttnArgs {
   void* out;
   const int32_t* row_ptr;
   const int32_t* col_idx;
-  const void* sft_hi;   // folded linear state, transposed [BH][D][D] (bf16 hi or f32)
-  const void* sft_lo;   // bf16 lo part (bf16 path only)
+  const void* sft;      // folded linear state, transposed [BH][D][D] (bf16 or f32)
   const float* z;       // [BH][D]
   const float* gate;    // [BH] (branch dropping), may be null
   float* lse;           // [BH][n_pad] log2-sum-exp of the scaled scores (bf16 path), may be null

@@ -24,8 +24,8 @@
 //     epilogue computes g*(o_l W_lin) = ReLU(q)^T S'' / (ReLU(q)^T z + eps) with
 //     one product.  S'' is stored transposed ([dv][dk]) because that is the
 //     operand layout the attention epilogue reads; for the bf16 kernels it is
-//     split into hi + lo bf16 parts (hi = bf16(S''), lo = bf16(S'' - hi)), which
-//     keeps about 16 significant bits through the bf16 MFMA.
+//     rounded to bf16 once, the MFMA operand type, as the attention kernel
+//     rounds the probabilities P before the PV product.
 #include <algorithm>
 
 #include "internal.h"
@@ -352,7 +352,7 @@ __global__ void __launch_bounds__(256)
 k_lin_fold(Geom g, int splits, const float* __restrict__ spart, const float* __restrict__ zpart,
            const float* __restrict__ gate, const WT* __restrict__ w, int mode, float drop_tau,
            float* __restrict__ S_out, float* __restrict__ z_out, float* __restrict__ z_ws,
-           void* __restrict__ sft_hi, void* __restrict__ sft_lo) {
+           void* __restrict__ sft) {
   constexpr int FR = 2;  // rows of S per workgroup
   __shared__ float Srows[FR][128];
   __shared__ float4 parts[256];
@@ -446,14 +446,8 @@ k_lin_fold(Geom g, int splits, const float* __restrict__ spart, const float* __r
       v = gv * Srows[rr][j];
     }
     const int64_t o = (int64_t)bh * D * D + (int64_t)j * D + r0 + rr;
-    if (BF16OUT) {
-      const __bf16 hi = (__bf16)v;
-      const __bf16 lo = (__bf16)(v - (float)hi);
-      static_cast<__bf16*>(sft_hi)[o] = hi;
-      static_cast<__bf16*>(sft_lo)[o] = lo;
-    } else {
-      static_cast<float*>(sft_hi)[o] = v;
-    }
+    if (BF16OUT) static_cast<__bf16*>(sft)[o] = (__bf16)v;
+    else static_cast<float*>(sft)[o] = v;
   }
 }
 
@@ -503,21 +497,19 @@ hipError_t launch_linear_fold(const Geom& g, int dtype, const float* gate, const
   const float* spart = reinterpret_cast<const float*>(ws + L.off_spart);
   const float* zpart = reinterpret_cast<const float*>(ws + L.off_zpart);
   float* z_ws = reinterpret_cast<float*>(ws + L.off_z);
-  void* hi = ws + L.off_sft_hi;
-  void* lo = ws + L.off_sft_lo;
+  void* sft = ws + L.off_sft;
   dim3 grid(g.B * g.Hh, g.D / 2);
   if (dtype == SALAD_BF16)  // mode 0: the bf16 partials already carry W_lin
     hipLaunchKernelGGL((k_lin_fold<__bf16, true, false>), grid, dim3(256), 0, st, g, L.lin_splits, spart,
                        zpart, gate, static_cast<const __bf16*>(nullptr), mode == 0 ? 3 : mode, drop_tau, S_out,
-                       z_out, z_ws, hi, lo);
+                       z_out, z_ws, sft);
   else if (mode == 0)
     hipLaunchKernelGGL((k_lin_fold<float, false, true>), grid, dim3(256), 0, st, g, L.lin_splits, spart,
-                       zpart, gate, static_cast<const float*>(w_lin), mode, drop_tau, S_out, z_out, z_ws, hi,
-                       lo);
+                       zpart, gate, static_cast<const float*>(w_lin), mode, drop_tau, S_out, z_out, z_ws, sft);
   else
     hipLaunchKernelGGL((k_lin_fold<float, false, false>), grid, dim3(256), 0, st, g, L.lin_splits, spart,
                        zpart, gate, static_cast<const float*>(nullptr), mode, drop_tau, S_out, z_out, z_ws,
-                       hi, lo);
+                       sft);
   return hipGetLastError();
 }
 

@@ -327,7 +327,7 @@ def test_noalloc_forward_refuses_layers_beyond_its_scratch():
     """salad_attn_fwd_noalloc checks its arguments and the 32 MiB scratch limit before any HIP call."""
     L = _lib()
     fake = ctypes.c_void_p(0x100000)
-    big = S.make_shape(2, 128, 128, 21, 30, 52, 64, S.SALAD_BF16)  # 256 (b, h): linear state over 32 MiB
+    big = S.make_shape(4, 128, 128, 21, 30, 52, 64, S.SALAD_BF16)  # 512 (b, h): linear state over 32 MiB
     args = [fake] * 7 + [1e-6, 0.0, 0.0, fake, None, None]
     assert L.salad_attn_fwd_noalloc(ctypes.byref(big), *args) == S.SALAD_ENOSPACE
     sh = _shape("c3")
