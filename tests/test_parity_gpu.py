@@ -246,6 +246,44 @@ def test_linear_branch_shifted_v_c2():
     assert_close(to_numpy(out), ref, BF16_MAX_ABS, BF16_REL_L2, "c2 out, V+1")
 
 
+@pytest.mark.parametrize("head_dim", [64, 128])
+def test_fused_linear_term_with_shifted_v(head_dim):
+    """V + 1 (rounded to bf16 on the host) and unit gates make the linear term of order 1 (rms ~1), so the fused
+    forward's gated, projected linear term out - o_s is compared on its own: head_dim 64 (two waves of the linear-state kernel
+    hold the two V-channel halves of a row tile and add them through LDS) and 128, a ragged last token chunk,
+    several splits per head."""
+    from synth import bf16_bits_to_f32, bf16_round
+    print(f"fused linear term head_dim {head_dim}", flush=True)
+    cfg = LayerConfig(name=f"lin{head_dim}", seed=41, batch=1, heads=3, head_dim=head_dim, T=3, H=8, W=20, block=64,
+                      dtype="bf16", specs=(HeadSpec(0, 1, -1, 0.0),) * 3, gate_kind="uniform")
+    inp = make_inputs(cfg)
+    v1_bits = bf16_round(inp.v + np.float32(1.0))
+    v1 = bf16_bits_to_f32(v1_bits)
+    layer = make_layer(cfg)
+    q, k, _, w = device_tensors(inp)
+    v = torch.from_numpy(np.ascontiguousarray(v1_bits).view(np.int16)).view(torch.bfloat16).cuda()
+    layer.build_mask(q, k)
+    g1 = np.ones(cfg.batch * cfg.heads, dtype=np.float32)
+    gate = torch.from_numpy(g1).cuda()
+    out = torch.empty_like(q)
+    layer.forward(q, k, v, gate, w, out, eps=cfg.eps)
+    o_s = torch.empty_like(q)
+    layer.branches(q, k, v, o_s, None, eps=cfg.eps)
+    torch.cuda.synchronize()
+    keep = oracle.build_masks(cfg.T, cfg.H, cfg.W, cfg.block, cfg.specs, cfg.batch, inp.q, inp.k)
+    rp, ci = oracle.csr_from_keep(keep)
+    np.testing.assert_array_equal(layer.row_ptr.cpu().numpy(), rp)
+    ref, ref_s, _ = oracle.layer_forward(inp.q, inp.k, v1, rp, ci, g1, inp.w_lin, cfg.N, cfg.block, cfg.eps)
+    N = cfg.N
+    assert_close(to_numpy(out)[:, :, :N], ref[:, :, :N], BF16_MAX_ABS, BF16_REL_L2, f"d{head_dim} out, V+1")
+    term = (to_numpy(out) - to_numpy(o_s))[:, :, :N]
+    want = (ref - ref_s)[:, :, :N]
+    rel = float(np.linalg.norm(term - want) / np.linalg.norm(want))
+    print(f"d{head_dim} linear term: rel-L2 {rel:.3e}, rms {float(np.sqrt(np.mean(want ** 2))):.3e}", flush=True)
+    # out and o_s each rounded to bf16 (relative 2^-9 of values of order 1): 3e-3 from that alone
+    assert rel <= 2e-2
+
+
 def test_gate_zero_and_projection_zero_give_sparse_bitwise():
     cfg = CONFIGS["c2"]
     zero_g = torch.zeros(cfg.batch * cfg.heads, dtype=torch.float32, device="cuda")
