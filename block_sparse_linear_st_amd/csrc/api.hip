@@ -310,6 +310,16 @@ int salad_build_mask(const salad_shape* shape, const salad_mask_spec* specs, con
     ht.r_max[h] = specs[h].r_max;
     ht.count[h] = (int)count[h];  // <= nb * nb < 2^31, or -1
   }
+  // per[h] is exact for window and top-k heads (a bound for SICS heads)
+  bool any_sics = false;
+  for (int h = 0; h < g.Hh; ++h) any_sics |= specs[h].kind == SALAD_MASK_SICS;
+  ht.direct_rows = !any_sics && g.nb <= kDirectRowsMaxNb;
+  int64_t run = 0;
+  for (int h = 0; h < g.Hh; ++h) {
+    ht.base[h] = (int)run;  // need <= INT32_MAX, checked above
+    run += per[h];
+  }
+  ht.batch_nnz = (int)run;
   Cuboid cu;
   make_cuboid(shape, &cu);
   return hip_status(launch_build_mask(g, cu, shape->dtype, ht, q, k, row_ptr, col_idx, col_cap, w_g,

@@ -57,7 +57,16 @@ struct HeadTable {
   int count[SALAD_MAX_HEADS];      // window: K pairs (-1 = keep all); top-k: k per row
   int pool[SALAD_MAX_HEADS];       // pool Q (bit 0) / K (bit 1) for this head
   int group[SALAD_MAX_HEADS];      // window heads: index of their (t_window, r_max) group
+  // Direct row pointers (no SICS head, nb <= kDirectRowsMaxNb): every head's
+  // entry count per batch is known before the launch, so row (b, h, qb)
+  // starts at b * batch_nnz + base[h] + (the head's entries in rows < qb).
+  int direct_rows;
+  int batch_nnz;
+  int base[SALAD_MAX_HEADS];
 };
+// Largest block count for direct row pointers: each window row sums the
+// counts of the rows before it in its head (nb^2 / 2 reads per head).
+constexpr int kDirectRowsMaxNb = 4096;
 
 // Workspace layout for one shape, computed on the host.
 struct Workspace {

@@ -341,11 +341,14 @@ __device__ inline bool window_keep(const uint16_t* rt, const Geom& g, int qb, in
 
 // grid (nb, heads), one wave: kept blocks per row, replicated over the batch.
 // Window heads of group `grp` count from the r* table; top-k heads (when
-// `topk` is set) have k per row.
+// `topk` is set) have k per row.  With direct row pointers the top-k rows
+// (closed form) and the final entry go straight to row_ptr instead.
 __global__ void __launch_bounds__(64)
 k_row_counts(Geom g, HeadTable ht, int grp, int topk, const uint16_t* rt, const int64_t* thr,
-             int32_t* rowcnt) {
+             int32_t* rowcnt, int32_t* row_ptr) {
   const int qb = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+  if (ht.direct_rows && topk && qb == 0 && h == 0 && lane == 0)
+    row_ptr[(int64_t)g.B * g.Hh * g.nb] = g.B * ht.batch_nnz;
   int cnt;
   if (ht.kind[h] == SALAD_MASK_WINDOW) {
     if (ht.group[h] != grp) return;
@@ -357,6 +360,11 @@ k_row_counts(Geom g, HeadTable ht, int grp, int topk, const uint16_t* rt, const 
   } else if (ht.kind[h] == SALAD_MASK_TOPK) {
     if (!topk) return;
     cnt = ht.count[h];
+    if (ht.direct_rows) {
+      for (int b = lane; b < g.B; b += 64)
+        row_ptr[((int64_t)b * g.Hh + h) * g.nb + qb] = b * ht.batch_nnz + ht.base[h] + qb * cnt;
+      return;
+    }
   } else {
     return;  // SICS heads: k_sics_counts
   }
@@ -398,10 +406,21 @@ k_scan_rows(const int32_t* rowcnt, int64_t rows, int32_t* row_ptr) {
 // grid (nb, heads), one wave: kept key blocks of the window rows of group `grp`, ascending.
 __global__ void __launch_bounds__(64)
 k_window_emit(Geom g, HeadTable ht, int grp, const uint16_t* rt, const int64_t* thr,
-              const int32_t* row_ptr, int32_t* col_idx, int64_t col_cap) {
+              int32_t* row_ptr, const int32_t* rowcnt, int32_t* col_idx, int64_t col_cap) {
   const int qb = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
   if (ht.kind[h] != SALAD_MASK_WINDOW || ht.group[h] != grp) return;
   const int64_t th = thr[h];
+  int64_t first = 0;  // this row's first entry in batch 0 (direct row pointers)
+  if (ht.direct_rows) {
+    // the head's entries in rows 0 .. qb-1 (the counts are the same in every batch)
+    const int32_t* hc = rowcnt + (int64_t)h * g.nb;
+    int part = 0;
+    for (int r = lane; r < qb; r += 64) part += hc[r];
+    for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o);
+    first = (int64_t)ht.base[h] + part;
+    for (int b = lane; b < g.B; b += 64)
+      row_ptr[((int64_t)b * g.Hh + h) * g.nb + qb] = (int32_t)(first + (int64_t)b * ht.batch_nnz);
+  }
   int off = 0;
   for (int kb0 = 0; kb0 < g.nb; kb0 += 64) {
     const int kb = kb0 + lane;
@@ -410,7 +429,9 @@ k_window_emit(Geom g, HeadTable ht, int grp, const uint16_t* rt, const int64_t* 
     const int rank = __popcll(m & ((1ull << lane) - 1ull));
     if (keep) {
       for (int b = 0; b < g.B; ++b) {
-        const int64_t pos = (int64_t)row_ptr[((int64_t)b * g.Hh + h) * g.nb + qb] + off + rank;
+        const int64_t row0 = ht.direct_rows ? first + (int64_t)b * ht.batch_nnz
+                                            : (int64_t)row_ptr[((int64_t)b * g.Hh + h) * g.nb + qb];
+        const int64_t pos = row0 + off + rank;
         if (pos < col_cap) col_idx[pos] = kb;
       }
     }
@@ -957,11 +978,11 @@ hipError_t launch_build_mask(const Geom& g, const Cuboid& cu, int dtype, const H
     rstar(gi, h_ptr);
     hipLaunchKernelGGL(k_window_threshold, dim3(g.Hh), dim3(kScanThreads), 0, st, g, ht, gi, rt, hist,
                        (int64_t)L.hist_bins, thr);
-    hipLaunchKernelGGL(k_row_counts, dim3(g.nb, g.Hh), dim3(64), 0, st, g, ht, gi,
-                       (int)(any_topk && gi == 0), rt, thr, rowcnt);
+    hipLaunchKernelGGL(k_row_counts, dim3(g.nb, g.Hh), dim3(64), 0, st, g, ht, gi, (int)(gi == 0), rt, thr,
+                       rowcnt, row_ptr);
   }
   if (n_groups == 0)
-    hipLaunchKernelGGL(k_row_counts, dim3(g.nb, g.Hh), dim3(64), 0, st, g, ht, -1, 1, rt, thr, rowcnt);
+    hipLaunchKernelGGL(k_row_counts, dim3(g.nb, g.Hh), dim3(64), 0, st, g, ht, -1, 1, rt, thr, rowcnt, row_ptr);
   const int64_t rows = (int64_t)g.B * g.Hh * g.nb;
   float* sics = reinterpret_cast<float*>(ws + L.off_sics);
   int32_t* pack = reinterpret_cast<int32_t*>(ws + L.off_sics_pack);
@@ -977,14 +998,15 @@ hipError_t launch_build_mask(const Geom& g, const Cuboid& cu, int dtype, const H
     hipLaunchKernelGGL(k_sics_counts, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, g, ht, pack,
                        rowcnt);
   }
-  hipLaunchKernelGGL(k_scan_rows, dim3(1), dim3(kScanThreads), 0, st, rowcnt, rows, row_ptr);
+  if (!ht.direct_rows)
+    hipLaunchKernelGGL(k_scan_rows, dim3(1), dim3(kScanThreads), 0, st, rowcnt, rows, row_ptr);
   if (any_sics)
     hipLaunchKernelGGL(k_sics_emit, dim3(g.nb, g.B * g.Hh), dim3(64), 0, st, g, ht, pack, row_ptr, col_idx,
                        col_cap);
   // emit: the last group's table is still current; the others are rebuilt
   for (int gi = n_groups - 1; gi >= 0; --gi) {
     if (gi != n_groups - 1) rstar(gi, nullptr);
-    hipLaunchKernelGGL(k_window_emit, dim3(g.nb, g.Hh), dim3(64), 0, st, g, ht, gi, rt, thr, row_ptr,
+    hipLaunchKernelGGL(k_window_emit, dim3(g.nb, g.Hh), dim3(64), 0, st, g, ht, gi, rt, thr, row_ptr, rowcnt,
                        col_idx, col_cap);
   }
   if (any_topk) {
