@@ -515,20 +515,24 @@ __device__ inline uint32_t ordered_bits(float s) {
 }
 
 // Scores of the pooled top-k rule for a batch of heads (bh0 ..): grid
-// (ceil(nb / 64) key tiles, ceil(nb / 64) row chunks, heads in the batch),
+// (ceil(nb / 64) key tiles, ceil(nb / 32) row chunks, heads in the batch),
 // 256 threads.  Lane = key block: the tile's 64 key blocks' pooled means sit in
 // LDS rows of D + 1 floats (lane l reads row l, channel c: bank (l + c) % 32,
-// no conflicts); each wave copies its 16 query blocks' means into its own LDS
+// no conflicts); each wave copies its 8 query blocks' means into its own LDS
 // rows and reads them as broadcasts (every lane the same address), 4 rows at a
 // time.  Each score is the sequential float32 sum over channels 0..D-1 of
 // separately rounded products (this file is compiled without FMA
-// contraction), the order the ranking is defined in.
+// contraction), the order the ranking is defined in.  Eight query blocks per
+// wave keep the workgroup's LDS at 49 KiB and three workgroups (three waves per
+// SIMD, at most 168 registers) fit on a CU: against 16 per wave and two
+// workgroups, c4's mask build 2 us and c5's 8 us faster, output bitwise equal.
+constexpr int kScoreRowsPerWave = 8;
 template <int D>
-__global__ void __launch_bounds__(256, 2)
+__global__ void __launch_bounds__(256, 3)
 k_topk_scores(Geom g, HeadTable ht, const float* __restrict__ pmean_q, const float* __restrict__ pmean_k,
               float* __restrict__ scores, int bh0) {
   constexpr int KS = D + 1;  // key row stride in LDS (floats)
-  constexpr int QR = 16;     // query blocks per wave
+  constexpr int QR = kScoreRowsPerWave;  // query blocks per wave
   constexpr int RG = 4;      // rows in flight per lane
   __shared__ __align__(16) float keys[64 * KS];
   __shared__ __align__(16) float qrows[4][QR * D];
@@ -537,7 +541,7 @@ k_topk_scores(Geom g, HeadTable ht, const float* __restrict__ pmean_q, const flo
   const int nb = g.nb, t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int kb0 = blockIdx.x * 64, kb = kb0 + lane;
-  const int qb0 = blockIdx.y * 64 + wave * QR;
+  const int qb0 = blockIdx.y * 4 * QR + wave * QR;
   const int rows = min(QR, nb - qb0);  // may be <= 0 for the last chunk
 #pragma unroll
   for (int i = t; i < 64 * D / 4; i += 256) {  // 16-byte loads, issued together
@@ -883,7 +887,7 @@ hipError_t launch_topk(const Geom& g, const HeadTable& ht, const float* pq, cons
   const int per = topk_heads_per_batch(g);
   for (int bh0 = 0; bh0 < BH; bh0 += per) {
     const int nbh = std::min(per, BH - bh0);
-    dim3 grid((g.nb + 63) / 64, (g.nb + 63) / 64, nbh);
+    dim3 grid((g.nb + 63) / 64, (g.nb + 4 * kScoreRowsPerWave - 1) / (4 * kScoreRowsPerWave), nbh);
     hipLaunchKernelGGL(k_topk_scores<D>, grid, dim3(256), 0, st, g, ht, pq, pk, scores, bh0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
